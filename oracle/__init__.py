@@ -1,0 +1,137 @@
+"""CPU oracle for the complex SSD scan (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The product library never loads it, and the two share no
+code: the oracle is the plain sequential recurrence written in C
+(``ssd_oracle.c``), evaluated in double precision.
+
+Functions
+---------
+build(out_dir=None, extra_cflags=(), source=None) -> path of the shared object
+scan(x, A, B_t, C_t, dt, initial_state=None, threads=0, lib=None)
+    -> (y complex128 (B,T,H,D), final_state complex128 (B,H,N,D))
+discretise(dt, A, chunk=0, lib=None)
+    -> (A_bar complex128 (B,T,H), Lambda complex128 (B,H,nc,chunk) or None)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ssd_oracle.c")
+LIBPATH = os.path.join(_HERE, "liboracle.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(out_path: str | None = None, extra_cflags=(), source: str | None = None) -> str:
+    """Compile the oracle with gcc (plain -O2, IEEE semantics, OpenMP)."""
+    out_path = out_path or LIBPATH
+    source = source or SOURCE
+    tmp = out_path + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           *extra_cflags, source, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def _bind(lib):
+    i64 = ctypes.c_int64
+    p = ctypes.c_void_p
+    lib.oracle_scan.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, p, p, ctypes.c_int]
+    lib.oracle_scan.restype = ctypes.c_int
+    lib.oracle_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p]
+    lib.oracle_discretise.restype = ctypes.c_int
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle shared object."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBPATH) or os.path.getmtime(LIBPATH) < os.path.getmtime(SOURCE):
+                build()
+            _lib = _bind(ctypes.CDLL(LIBPATH))
+    return _lib
+
+
+def _as_f32(a, complex_=False) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu()
+            if complex_:
+                a = torch.view_as_real(a.to(torch.complex64).resolve_conj()).contiguous()
+            a = a.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(a)
+    if complex_ and np.iscomplexobj(a):
+        a = np.stack([a.real, a.imag], axis=-1)
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).oracle_max_threads()
+
+
+def scan(x, A, B_t, C_t, dt, initial_state=None, threads: int = 0, lib=None):
+    lib = lib or load()
+    xf = _as_f32(x, True)
+    Af = _as_f32(A, True)
+    Bf = _as_f32(B_t, True)
+    Cf = _as_f32(C_t, True)
+    dtf = _as_f32(dt)
+    Bsz, T, H, D = xf.shape[:4]
+    N = Bf.shape[3]
+    assert Af.shape == (H, 2) and Bf.shape == (Bsz, T, H, N, 2) and Cf.shape == Bf.shape
+    assert dtf.shape == (Bsz, T, H)
+    y = np.zeros((Bsz, T, H, D, 2), np.float64)
+    fs = np.zeros((Bsz, H, N, D, 2), np.float64)
+    init_p = None
+    if initial_state is not None:
+        init = np.asarray(initial_state)
+        if np.iscomplexobj(init):
+            init = np.stack([init.real, init.imag], -1)
+        init = np.ascontiguousarray(init, np.float64)
+        assert init.shape == (Bsz, H, N, D, 2)
+        init_p = init.ctypes.data
+    rc = lib.oracle_scan(xf.ctypes.data, Af.ctypes.data, Bf.ctypes.data, Cf.ctypes.data,
+                         dtf.ctypes.data, Bsz, T, H, N, D, init_p, y.ctypes.data, fs.ctypes.data,
+                         int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan failed with %d" % rc)
+    return y[..., 0] + 1j * y[..., 1], fs[..., 0] + 1j * fs[..., 1]
+
+
+def discretise(dt, A, chunk: int = 0, lib=None):
+    lib = lib or load()
+    dtf = _as_f32(dt)
+    Af = _as_f32(A, True)
+    Bsz, T, H = dtf.shape
+    abar = np.zeros((Bsz, T, H, 2), np.float64)
+    lam = None
+    lam_p = None
+    if chunk > 0:
+        nc = (T + chunk - 1) // chunk
+        lam = np.zeros((Bsz, H, nc, chunk, 2), np.float64)
+        lam_p = lam.ctypes.data
+    rc = lib.oracle_discretise(dtf.ctypes.data, Af.ctypes.data, Bsz, T, H, int(chunk),
+                               abar.ctypes.data, lam_p)
+    if rc != 0:
+        raise RuntimeError("oracle_discretise failed with %d" % rc)
+    abar_c = abar[..., 0] + 1j * abar[..., 1]
+    lam_c = None if lam is None else lam[..., 0] + 1j * lam[..., 1]
+    return abar_c, lam_c

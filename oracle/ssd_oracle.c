@@ -1,0 +1,163 @@
+/*
+ * ssd_oracle.c -- plain, slow, obviously correct CPU oracle for the complex
+ * SSD scan of the Mamba-3-Lite pages.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or
+ * calls this file. It exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can check and time the GPU path against the
+ * plain definition. It shares no code, header or table with the GPU path.
+ *
+ * What it computes (all arithmetic in double / double complex):
+ *
+ *   discretisation   -- "Extending" guide, Path A Step 1 (the _discretise
+ *                       call) and index.html lab 03 "NAIVE" line:
+ *                         Abar_t = exp(softplus(dt_t) * A_h)
+ *   recurrence       -- "Extending" guide, Path A Step 1 code block
+ *                       (ssd_naive_complex) and index.html lab 03:
+ *                         s_t = Abar_t * s_{t-1} + B_t (outer) x_t
+ *                         y_t = sum_n C_t[n] * s_t[n, :]
+ *                       state s is (N, D) per (batch, head), zero at start;
+ *                       no conjugation anywhere (plain products in the code).
+ *   per-chunk log-decay -- "Extending" guide, Path B Step 2 and index.html
+ *                       lab 03 "CHUNK" line: the inclusive running sum of
+ *                       softplus(dt)*A inside each chunk (A_cs).
+ *
+ * The y output is the full complex y_t; the chunkwise function of the pages
+ * returns its real part ("Extending", Path A Step 3), which callers take.
+ * final_state is s after the last token t = T-1 (zero-initialised unless an
+ * initial state is supplied).
+ *
+ * softplus is the mathematical log(1 + e^x), evaluated without overflow as
+ * max(x, 0) + log1p(exp(-|x|)).
+ *
+ * Layouts: dense row-major, complex values interleaved (re, im).
+ *   x  (B, T, H, D)    Bt, Ct (B, T, H, N)    dt (B, T, H)    A (H)
+ *   y  (B, T, H, D)    state  (B, H, N, D)
+ *
+ * Parallelism: the (batch, head) sequences are independent; an OpenMP loop
+ * runs them side by side. Within a sequence the loop is the plain recurrence.
+ */
+#include <complex.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef double complex cplx;
+
+static double softplus(double v)
+{
+    return fmax(v, 0.0) + log1p(exp(-fabs(v)));
+}
+
+static cplx load_c(const float *p, int64_t i)
+{
+    return (double)p[2 * i] + I * (double)p[2 * i + 1];
+}
+
+static void store_c(double *p, int64_t i, cplx v)
+{
+    p[2 * i] = creal(v);
+    p[2 * i + 1] = cimag(v);
+}
+
+int oracle_version(void) { return 1; }
+
+/* Abar (B,T,H) and, when chunk > 0, the per-chunk inclusive cumulative
+ * log-decay Lambda (B,H,nc,chunk). Positions of the last chunk that lie past
+ * T hold the running sum of the last real token (a padded token adds zero). */
+int oracle_discretise(const float *dt, const float *A, int64_t Bsz, int64_t T, int64_t H,
+                      int64_t chunk, double *A_bar, double *Lambda)
+{
+    if (!dt || !A || Bsz <= 0 || T <= 0 || H <= 0 || chunk < 0)
+        return -1;
+    int64_t nc = chunk > 0 ? (T + chunk - 1) / chunk : 0;
+    for (int64_t b = 0; b < Bsz; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            cplx Ah = load_c(A, h);
+            cplx run = 0.0;
+            for (int64_t t = 0; t < (chunk > 0 ? nc * chunk : T); ++t) {
+                cplx a = 0.0;
+                if (t < T)
+                    a = softplus((double)dt[(b * T + t) * H + h]) * Ah;
+                if (A_bar && t < T)
+                    store_c(A_bar, (b * T + t) * H + h, cexp(a));
+                if (chunk > 0) {
+                    if (t % chunk == 0)
+                        run = 0.0;
+                    run += a;
+                    if (Lambda)
+                        store_c(Lambda, ((b * H + h) * nc + t / chunk) * chunk + t % chunk, run);
+                }
+            }
+        }
+    return 0;
+}
+
+/* The naive O(T) recurrence. y is complex (B,T,H,D); final_state (B,H,N,D).
+ * init_state may be NULL (zero state). nthreads <= 0 uses the OpenMP default. */
+int oracle_scan(const float *x, const float *A, const float *Bt, const float *Ct, const float *dt,
+                int64_t Bsz, int64_t T, int64_t H, int64_t N, int64_t D,
+                const double *init_state, double *y, double *final_state, int nthreads)
+{
+    if (!x || !A || !Bt || !Ct || !dt || Bsz <= 0 || T < 0 || H <= 0 || N <= 0 || D <= 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t nseq = Bsz * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nseq; ++q) {
+        int64_t b = q / H, h = q % H;
+        cplx *s = malloc(sizeof(cplx) * (size_t)(N * D));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        for (int64_t i = 0; i < N * D; ++i) {
+            int64_t off = (b * H + h) * N * D + i;
+            s[i] = init_state ? init_state[2 * off] + I * init_state[2 * off + 1] : 0.0;
+        }
+        cplx Ah = load_c(A, h);
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * H + h;
+            cplx Abar = cexp(softplus((double)dt[row]) * Ah);
+            /* s = Abar * s + B_t (outer) x_t */
+            for (int64_t n = 0; n < N; ++n) {
+                cplx bn = load_c(Bt, row * N + n);
+                for (int64_t d = 0; d < D; ++d)
+                    s[n * D + d] = Abar * s[n * D + d] + bn * load_c(x, row * D + d);
+            }
+            /* y_t = sum_n C_t[n] * s[n, :] */
+            if (y)
+                for (int64_t d = 0; d < D; ++d) {
+                    cplx acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n)
+                        acc += load_c(Ct, row * N + n) * s[n * D + d];
+                    store_c(y, row * D + d, acc);
+                }
+        }
+        if (final_state)
+            for (int64_t i = 0; i < N * D; ++i)
+                store_c(final_state, (b * H + h) * N * D + i, s[i]);
+        free(s);
+    }
+    return failed ? -2 : 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

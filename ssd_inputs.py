@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for the complex chunkwise SSD scan.
+
+This module only draws random numbers. It holds none of the scan's
+arithmetic, so both the HIP path and the CPU oracle can be fed from it.
+
+Shapes and distributions follow the Mamba-3-Lite pages:
+  * "Skills Reference", Skill 2 (the tiny equivalence recipe): torch seed 0,
+    draw x, A (= randn - 1), B_t, C_t in that order, all complex64, dt zero.
+  * "index.html", lab 01 (eigen-spectrum explorer): decay range
+    alpha in [-3.0, -0.05], rotation |omega| in [0.35, 2.20].
+  * "index.html", stat card: one layer is ctx 2048, chunk 64, 16 heads x 64,
+    state N = 64 complex64; 28 layers.
+
+Conventions (readings where the pages are silent):
+  * "complex N(0, s^2)" means torch's complex randn (re and im each carry
+    half the variance) times s.
+  * Im A is a magnitude uniform in [0.35, 2.20] with an independent fair sign.
+  * Draw order for the layer recipe: A (re, |im|, sign), dt, x, B_t, C_t.
+
+Every tensor is produced by ``torch.randn``/``torch.rand`` with an explicit
+``torch.Generator`` on the requested device, so a given (seed, device) pair is
+reproducible. The CUDA generator's stream differs from the CPU one; parity
+tests that compare against the oracle copy the very same tensors to the host.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass
+class ScanInputs:
+    x: torch.Tensor     # (B, T, H, D) complex64
+    A: torch.Tensor     # (H,) complex64
+    B_t: torch.Tensor   # (B, T, H, N) complex64
+    C_t: torch.Tensor   # (B, T, H, N) complex64
+    dt: torch.Tensor    # (B, T, H) float32
+
+    @property
+    def shape(self):
+        b, t, h, d = self.x.shape
+        return b, t, h, self.B_t.shape[-1], d
+
+    def to(self, device) -> "ScanInputs":
+        return ScanInputs(*(v.to(device) for v in (self.x, self.A, self.B_t, self.C_t, self.dt)))
+
+    def select(self, b: int, h: int) -> "ScanInputs":
+        """One (batch row, head) sequence as a B=1, H=1 problem (views copied)."""
+        return ScanInputs(
+            self.x[b:b + 1, :, h:h + 1].contiguous(),
+            self.A[h:h + 1].contiguous(),
+            self.B_t[b:b + 1, :, h:h + 1].contiguous(),
+            self.C_t[b:b + 1, :, h:h + 1].contiguous(),
+            self.dt[b:b + 1, :, h:h + 1].contiguous(),
+        )
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def tiny_case(time_varying_dt: bool, device="cpu") -> ScanInputs:
+    """B=2, T=16, H=2, D=N=4 recipe of the Skills page (seed 0).
+
+    x, A, B_t, C_t are drawn exactly in the page's order. dt is zeros, or
+    (time_varying_dt) the next randn(B, T, H) draw of the same stream.
+    """
+    B, T, H, D, N = 2, 16, 2, 4, 4
+    g = _gen(0, "cpu")
+    x = torch.randn(B, T, H, D, dtype=torch.complex64, generator=g)
+    A = torch.randn(H, dtype=torch.complex64, generator=g) - 1.0
+    B_t = torch.randn(B, T, H, N, dtype=torch.complex64, generator=g)
+    C_t = torch.randn(B, T, H, N, dtype=torch.complex64, generator=g)
+    if time_varying_dt:
+        dt = torch.randn(B, T, H, generator=g)
+    else:
+        dt = torch.zeros(B, T, H)
+    return ScanInputs(x, A, B_t, C_t, dt).to(device)
+
+
+def layer_case(batch: int, T: int, H: int, N: int, D: int, seed: int,
+               dt_mean: float = 0.0, device="cpu") -> ScanInputs:
+    """One Mamba-3-Lite-shaped layer of scan inputs.
+
+    A: Re ~ U[-3.0, -0.05], Im = +-U[0.35, 2.20]; dt ~ N(dt_mean, 1);
+    x ~ complex N(0, 1); B_t, C_t ~ complex N(0, 1/N).
+    """
+    g = _gen(seed, device)
+    a_re = -3.0 + 2.95 * torch.rand(H, generator=g, device=device)
+    a_im = 0.35 + 1.85 * torch.rand(H, generator=g, device=device)
+    sign = torch.where(torch.rand(H, generator=g, device=device) < 0.5, -1.0, 1.0)
+    A = torch.complex(a_re, a_im * sign).to(torch.complex64)
+    dt = torch.randn(batch, T, H, generator=g, device=device) + dt_mean
+    x = torch.randn(batch, T, H, D, dtype=torch.complex64, generator=g, device=device)
+    s = 1.0 / math.sqrt(N)
+    B_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
+    C_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
+    return ScanInputs(x, A, B_t, C_t, dt)
+
+
+# Named workloads. Each entry: (batch, T, H, N, D, chunk sizes, seed, dt_mean).
+WORKLOADS = {
+    # single Mamba-3-Lite layer, one sequence per head
+    "layer_b1_t2048": dict(batch=1, T=2048, H=16, N=64, D=64, chunks=(64,), seed=1, dt_mean=0.0),
+    # training-batch slice
+    "layer_b8_t2048": dict(batch=8, T=2048, H=16, N=64, D=64, chunks=(64,), seed=1, dt_mean=0.0),
+    # long-context chunk-size sweep; one input set shared by all four chunk sizes
+    "sweep_b4_t8192": dict(batch=4, T=8192, H=16, N=64, D=64, chunks=(32, 64, 128, 256), seed=3,
+                           dt_mean=0.5),
+    # full 28-layer network scan load; layer l uses seed l
+    "network_28x_b32_t2048": dict(batch=32, T=2048, H=16, N=64, D=64, chunks=(64,), seed=None,
+                                  dt_mean=0.0, layers=28),
+}
+
+
+def random_case(batch, T, H, N, D, seed, device="cpu", dt_scale=1.0, dt_mean=0.0,
+                a_re_range=(-3.0, -0.05)) -> ScanInputs:
+    """Small irregular shapes for edge-case tests (same families as layer_case)."""
+    g = _gen(seed, device)
+    lo, hi = a_re_range
+    a_re = lo + (hi - lo) * torch.rand(H, generator=g, device=device)
+    a_im = 0.35 + 1.85 * torch.rand(H, generator=g, device=device)
+    sign = torch.where(torch.rand(H, generator=g, device=device) < 0.5, -1.0, 1.0)
+    A = torch.complex(a_re, a_im * sign).to(torch.complex64)
+    dt = torch.randn(batch, T, H, generator=g, device=device) * dt_scale + dt_mean
+    x = torch.randn(batch, T, H, D, dtype=torch.complex64, generator=g, device=device)
+    s = 1.0 / math.sqrt(max(N, 1))
+    B_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
+    C_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
+    return ScanInputs(x, A, B_t, C_t, dt)
