@@ -1,0 +1,224 @@
+"""Throughput of the complex chunkwise SSD scan on one MI355X.
+
+Default workload: the full-network scan load of a 28-layer Mamba-3-Lite
+(each layer B=32, T=2048, H=16, N=D=64, chunk 64; layer l drawn with seed l),
+all 28 layers resident in HBM and scanned back to back. One step is one pass
+over the 28 layers. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "complex_chunkwise_ssd_amd", "csrc", "ssd_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_kernel_network_b32_t2048.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_tokens_heads):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layer0, batch_rows=2):
+    """The oracle as it stands, on a bounded sample of layer 0: batch rows
+    0..batch_rows-1, all heads, full T (host cores, OpenMP over sequences)."""
+    import oracle
+    x, A, B_t, C_t, dt = (layer0.x[:batch_rows].cpu(), layer0.A.cpu(), layer0.B_t[:batch_rows].cpu(),
+                          layer0.C_t[:batch_rows].cpu(), layer0.dt[:batch_rows].cpu())
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    lib = oracle.load()
+    threads = min(cores, batch_rows * A.shape[0])
+    t = time.perf_counter()
+    oracle.scan(x, A, B_t, C_t, dt, threads=threads, lib=lib)
+    el = time.perf_counter() - t
+    T = x.shape[1]
+    return {"value": batch_rows * T / el, "unit": "tokens*layers/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "layer 0, batch rows 0-%d, all %d heads, T=%d (%d sequences, %.1f s wall)"
+                      % (batch_rows - 1, A.shape[0], T, batch_rows * A.shape[0], el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="network_28x_b32_t2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the single-layer side figures")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences are independent; see the sharding note in the design document)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import complex_chunkwise_ssd_amd as ssd
+    import ssd_inputs
+
+    dev = torch.device("cuda:0")
+    wl = dict(ssd_inputs.WORKLOADS[args.workload])
+    B, T, H, N, D = wl["batch"], wl["T"], wl["H"], wl["N"], wl["D"]
+    Q = wl["chunks"][0]
+    L = wl.get("layers", 1)
+    log("bench: workload %s (%d layer(s) of B=%d T=%d H=%d N=%d D=%d Q=%d)" % (args.workload, L, B, T,
+                                                                                 H, N, D, Q))
+    layers, ys, fss = [], [], []
+    for l in range(L):
+        seed = l if wl["seed"] is None else wl["seed"]
+        layers.append(ssd_inputs.layer_case(B, T, H, N, D, seed=seed, dt_mean=wl["dt_mean"],
+                                            device=dev))
+        ys.append(torch.empty((B, T, H, D), dtype=torch.float32, device=dev))
+        fss.append(torch.empty((B, H, N, D), dtype=torch.complex64, device=dev))
+    wsn = ssd.workspace_bytes(B, T, H, N, D, Q)
+    ws = torch.empty(max(wsn, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log("bench: inputs resident (%.1f GB)" % (torch.cuda.memory_allocated() / 1e9))
+
+    def step(ev=None):
+        for l, g in enumerate(layers):
+            if ev is not None:
+                ev[l][0].record()
+            ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=Q, y=ys[l], final_state=fss[l],
+                              workspace=ws)
+            if ev is not None:
+                ev[l][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    per_launch = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(L)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(per_launch[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    launch_ms = [a.elapsed_time(b) for row in per_launch for a, b in row]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    log("bench: %d steps in %.1f ms (wall %.2f s), %.3f ms per layer call" % (args.steps, total_ms,
+                                                                            wall, avg_launch_ms))
+
+    th_per_launch = B * T * H
+    flops_launch = th_per_launch * ssd.algorithmic_flops_per_token_head(N, D, Q)
+    bytes_launch = th_per_launch * ssd.algorithmic_bytes_per_token_head(N, D, T)
+    achieved = flops_launch / (avg_launch_ms * 1e-3) / 1e12
+    tokens_layers = B * T * L
+    value = tokens_layers / (ms_per_step * 1e-3)
+    traffic = measured_traffic(th_per_launch)
+    out = {
+        "metric": "complex-SSD scan tokens/s at T=2048,H=16,N=D=64,Q=64 + % of roofline",
+        "value": value,
+        "unit": "tokens*layers/s" if L > 1 else "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and value ranges of the Mamba-3-Lite pages)",
+        "config": {"workload": args.workload, "layers": L, "batch": B, "seq_len": T, "heads": H,
+                   "state_N": N, "head_dim_D": D, "chunk_size": Q},
+        "token_heads_per_s": value * H,
+        "tokens_per_s_network": B * T / (ms_per_step * 1e-3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+            "traffic": traffic,
+            "kernel": "scan_kernel<64,true> (one launch per layer)",
+            "avg_launch_ms": avg_launch_ms,
+            "algorithmic_flops_per_launch": flops_launch,
+            "algorithmic_bytes_per_launch": bytes_launch,
+            "achieved_hbm_GBs_algorithmic": bytes_launch / (avg_launch_ms * 1e-3) / 1e9,
+            "kernel_source_sha256_16": kernel_source_hash(),
+        },
+    }
+
+    if not args.no_extra:
+        extra = {}
+        for name in ("layer_b1_t2048", "layer_b8_t2048"):
+            w = ssd_inputs.WORKLOADS[name]
+            g = ssd_inputs.layer_case(w["batch"], w["T"], w["H"], w["N"], w["D"], seed=w["seed"],
+                                      device=dev)
+            q = w["chunks"][0]
+            y = torch.empty((w["batch"], w["T"], w["H"], w["D"]), device=dev)
+            f = torch.empty((w["batch"], w["H"], w["N"], w["D"]), dtype=torch.complex64, device=dev)
+            n = ssd.workspace_bytes(w["batch"], w["T"], w["H"], w["N"], w["D"], q)
+            wsp = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            call = lambda: ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=q, y=y,
+                                             final_state=f, workspace=wsp)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(50):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                times.append((a, b))
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+            th = w["batch"] * w["T"] * w["H"]
+            fl = th * ssd.algorithmic_flops_per_token_head(w["N"], w["D"], q)
+            extra[name] = {"median_ms": ms, "tokens_per_s": w["batch"] * w["T"] / (ms * 1e-3),
+                           "token_heads_per_s": th / (ms * 1e-3),
+                           "roofline_frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+            del g, y, f, wsp
+        out["single_layer"] = extra
+
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(layers[0])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

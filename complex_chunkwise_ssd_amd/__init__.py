@@ -1,0 +1,190 @@
+"""Python binding of the MI355X complex chunkwise SSD scan library.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libssd.so`` (C ABI in include/ssd.h). PyTorch supplies device memory and the
+current stream. Importing works without a GPU; calling needs the built library
+and a visible GPU, and fails loudly otherwise (there is no fallback path).
+
+    y, final_state = chunk_forward(x, A, B_t, C_t, dt, chunk_size=64)
+    A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_PKG, "libssd.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
+
+SSD_OK = 0
+SSD_ERR_NULL = -1
+SSD_ERR_SHAPE = -2
+SSD_ERR_ODD_N = -3
+SSD_ERR_BLOCK_DIMS = -4
+SSD_ERR_WORKSPACE = -5
+SSD_ERR_ALIGN = -6
+SSD_ERR_HIP = -7
+SSD_ERR_UNSUPPORTED = -8
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SSDError(ValueError):
+    """A call was rejected by the library (status < 0)."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def load_library(path: str | None = None):
+    """Load libssd.so (raises OSError if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIBPATH
+        if not os.path.exists(p):
+            raise OSError("libssd.so not found at %s; build it with "
+                          "`python -m complex_chunkwise_ssd_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.ssd_discretise.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+        lib.ssd_discretise.restype = ctypes.c_int
+        lib.ssd_chunk_forward_workspace_bytes.argtypes = [i64] * 6
+        lib.ssd_chunk_forward_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                          vp, vp, ctypes.c_size_t, vp]
+        lib.ssd_chunk_forward.restype = ctypes.c_int
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_version.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions declared in include/ssd.h."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(ssd_\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def workspace_bytes(batch, T, H, N, D, chunk_size) -> int:
+    return int(load_library().ssd_chunk_forward_workspace_bytes(batch, T, H, N, D, chunk_size))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous() or t.is_conj():
+        raise ValueError("%s must be contiguous and not a lazy conjugate view" % name)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_forward(x, A, B_t, C_t, dt, chunk_size: int = 64, initial_state=None,
+                  want_final_state: bool = True, y=None, final_state=None, workspace=None):
+    """Chunkwise complex SSD scan forward on the current stream.
+
+    x (B,T,H,D) complex64; A (H,) complex64; B_t, C_t (B,T,H,N) complex64;
+    dt (B,T,H) float32; optional initial_state (B,H,N,D) complex64.
+    Returns (y (B,T,H,D) float32 = real part, final_state (B,H,N,D) complex64 or None).
+    Outputs and the workspace may be passed in preallocated.
+    """
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a (B, T, H, D) tensor")
+    Bsz, T, H, D = x.shape
+    if not isinstance(B_t, torch.Tensor) or B_t.dim() != 4:
+        raise ValueError("B_t must be a (B, T, H, N) tensor")
+    N = B_t.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(x, "x", torch.complex64, (Bsz, T, H, D), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    _check(B_t, "B_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(C_t, "C_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(dt, "dt", torch.float32, (Bsz, T, H), dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    if y is None:
+        y = torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev)
+    _check(y, "y", torch.float32, (Bsz, T, H, D), dev)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((Bsz, H, N, D), dtype=torch.complex64, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", torch.complex64, (Bsz, H, N, D), dev)
+    ws_n = int(lib.ssd_chunk_forward_workspace_bytes(Bsz, T, H, N, D, chunk_size))
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_forward(_ptr(x), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(dt), Bsz, T, H, N, D,
+                               int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(final_state),
+                               _ptr(workspace), ws_size, _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_forward")
+    return y, final_state
+
+
+def discretise(dt, A, chunk_size: int = 0, want_abar: bool = True):
+    """A_bar = exp(softplus(dt) A) (B,T,H) and, if chunk_size > 0, the per-chunk
+    running sums of softplus(dt) A (B,H,nc,chunk_size), both complex64."""
+    lib = load_library()
+    if not isinstance(dt, torch.Tensor) or dt.dim() != 3:
+        raise ValueError("dt must be a (B, T, H) tensor")
+    Bsz, T, H = dt.shape
+    dev = dt.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(dt, "dt", torch.float32, (Bsz, T, H), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    abar = torch.empty((Bsz, T, H), dtype=torch.complex64, device=dev) if want_abar else None
+    lam = None
+    if chunk_size > 0:
+        nc = (T + chunk_size - 1) // chunk_size
+        lam = torch.empty((Bsz, H, nc, chunk_size), dtype=torch.complex64, device=dev)
+    st = lib.ssd_discretise(_ptr(dt), _ptr(A), Bsz, T, H, int(chunk_size), _ptr(abar), _ptr(lam),
+                            _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_discretise")
+    return abar, lam
+
+
+def algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
+    """Real flops the chunkwise method must do per (token, head): the causal
+    C B^T (8N per pair), Re((C B^T o L) X) (4D per pair), the chunk state
+    B^T X (8ND), the state-to-output term Re(C H) (4ND) and the state passing
+    (8ND/Q). Transcendentals are not counted."""
+    return 8 * N * (Q + 1) / 2 + 4 * D * (Q + 1) / 2 + 12 * N * D + 8 * N * D / Q
+
+
+def algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
+    """Bytes the scan must move per (token, head): x, B_t, C_t (complex64),
+    dt, y (float32) and the final state amortised over T."""
+    return 8 * D + 16 * N + 4 + 4 * D + 8 * N * D / T

@@ -1,0 +1,190 @@
+// ssd_api.hip -- C ABI of the complex chunkwise SSD scan (declared in
+// include/ssd.h): argument checks, work planning and kernel launches on the
+// caller's stream. The library allocates nothing.
+#include "ssd.h"
+
+#include <ssd_kernels.h>
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int launch_status()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+unsigned grid_1d(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk)
+{
+    if (batch < 0 || T < 0 || H < 0 || N < 1 || D < 1 || chunk < 1)
+        return SSD_ERR_SHAPE;
+    if (N % 2 != 0)
+        return SSD_ERR_ODD_N;
+    if (N > SSD_MAX_BLOCK || D > SSD_MAX_BLOCK || chunk > SSD_MAX_BLOCK)
+        return SSD_ERR_BLOCK_DIMS;
+    if (N > ssd::kNPad || chunk > 64)
+        return SSD_ERR_UNSUPPORTED;
+    // 32-bit token indices inside the kernels
+    if (T > (1LL << 30) || batch * H > (1LL << 30))
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+template <int R>
+int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs, hipStream_t stream)
+{
+    ssd::ScanParams prm = base;
+    if (plan.P > 1) {
+        prm.groups_per_seq = plan.P - 1;
+        const int64_t grid = seqs * (plan.P - 1) * plan.ndb;
+        hipLaunchKernelGGL((ssd::scan_kernel<R, false>), dim3((unsigned)grid), dim3(ssd::kThreads),
+                           0, stream, prm);
+        if (int st = launch_status())
+            return st;
+    }
+    prm.groups_per_seq = plan.P;
+    const int64_t grid = seqs * plan.P * plan.ndb;
+    hipLaunchKernelGGL((ssd::scan_kernel<R, true>), dim3((unsigned)grid), dim3(ssd::kThreads), 0,
+                       stream, prm);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_version(void) { return 100; }
+
+const char *ssd_status_string(int status)
+{
+    switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid size: negative, or N, D or chunk_size below 1";
+    case SSD_ERR_ODD_N: return "N must be even so the complex state packs into real pairs";
+    case SSD_ERR_BLOCK_DIMS: return "N, D and chunk_size must not exceed 256";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_ALIGN: return "pointer not aligned as required";
+    case SSD_ERR_HIP: return "HIP runtime error";
+    case SSD_ERR_UNSUPPORTED: return "size not covered by this build (N <= 64, chunk_size <= 64)";
+    default: return "unknown status";
+    }
+}
+
+int ssd_discretise(const float *dt, const ssd_c64 *A, int64_t batch, int64_t T, int64_t H,
+                   int64_t chunk_size, ssd_c64 *A_bar, ssd_c64 *log_decay_cumsum,
+                   ssd_stream_t stream)
+{
+    if (batch < 0 || T < 0 || H < 0 || chunk_size < 0)
+        return SSD_ERR_SHAPE;
+    if (chunk_size > SSD_MAX_BLOCK)
+        return SSD_ERR_BLOCK_DIMS;
+    if (log_decay_cumsum && chunk_size == 0)
+        return SSD_ERR_SHAPE;
+    if (batch == 0 || T == 0 || H == 0)
+        return SSD_OK;
+    if (!dt || !A)
+        return SSD_ERR_NULL;
+    if (!aligned(dt, 4) || !aligned(A, 8) || (A_bar && !aligned(A_bar, 8)) ||
+        (log_decay_cumsum && !aligned(log_decay_cumsum, 8)))
+        return SSD_ERR_ALIGN;
+    if (batch * T * H > (1LL << 40))
+        return SSD_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (A_bar) {
+        const int64_t n = batch * T * H;
+        hipLaunchKernelGGL(ssd::discretise_abar_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s, dt,
+                           (const float *)A, n, (int)H, (float *)A_bar);
+        if (int st = launch_status())
+            return st;
+    }
+    if (log_decay_cumsum) {
+        const int64_t nc = (T + chunk_size - 1) / chunk_size;
+        const int64_t n = batch * nc * H;
+        hipLaunchKernelGGL(ssd::discretise_cumsum_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                           dt, (const float *)A, (int)batch, (int)T, (int)H, (int)chunk_size,
+                           (int)nc, (float *)log_decay_cumsum);
+        if (int st = launch_status())
+            return st;
+    }
+    return SSD_OK;
+}
+
+size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,
+                                         int64_t D, int64_t chunk_size)
+{
+    if (check_sizes(batch, T, H, N, D, chunk_size) != SSD_OK || batch == 0 || H == 0 || T == 0)
+        return 0;
+    return ssd::make_plan(batch, T, H, N, D, chunk_size).workspace_bytes;
+}
+
+int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, const ssd_c64 *C_t,
+                      const float *dt, int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                      int64_t chunk_size, const ssd_c64 *initial_state, float *y,
+                      ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                      ssd_stream_t stream)
+{
+    if (int st = check_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    if (batch == 0 || H == 0)
+        return SSD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!final_state)
+            return SSD_OK;
+        if (!aligned(final_state, 8) || (initial_state && !aligned(initial_state, 8)))
+            return SSD_ERR_ALIGN;
+        const int64_t n = batch * H * N * D * 2;
+        hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                           (const float *)initial_state, (float *)final_state, n);
+        return launch_status();
+    }
+    if (!x || !A || !B_t || !C_t || !dt || !y)
+        return SSD_ERR_NULL;
+    if (!aligned(B_t, 16) || !aligned(C_t, 16) || !aligned(x, 8) || !aligned(A, 8) ||
+        !aligned(dt, 4) || !aligned(y, 4) || (initial_state && !aligned(initial_state, 8)) ||
+        (final_state && !aligned(final_state, 8)))
+        return SSD_ERR_ALIGN;
+
+    const ssd::Plan plan = ssd::make_plan(batch, T, H, N, D, chunk_size);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes)
+            return SSD_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return SSD_ERR_ALIGN;
+    }
+
+    ssd::ScanParams prm{};
+    prm.x = (const float *)x;
+    prm.A = (const float *)A;
+    prm.Bt = (const float *)B_t;
+    prm.Ct = (const float *)C_t;
+    prm.dt = dt;
+    prm.init_state = (const float *)initial_state;
+    prm.y = y;
+    prm.final_state = (float *)final_state;
+    prm.seg_state = plan.P > 1 ? (float *)workspace : nullptr;
+    prm.seg_logdecay = plan.P > 1 ? (float *)((char *)workspace + plan.seg_state_bytes) : nullptr;
+    prm.B = (int)batch;
+    prm.T = (int)T;
+    prm.H = (int)H;
+    prm.N = (int)N;
+    prm.D = (int)D;
+    prm.Q = (int)chunk_size;
+    prm.nc = plan.nc;
+    prm.P = plan.P;
+    prm.spc = plan.spc;
+    prm.ndb = plan.ndb;
+
+    const int64_t seqs = batch * H;
+    switch (plan.R) {
+    case 16: return launch_scan<16>(prm, plan, seqs, s);
+    case 32: return launch_scan<32>(prm, plan, seqs, s);
+    default: return launch_scan<64>(prm, plan, seqs, s);
+    }
+}
+
+}  // extern "C"

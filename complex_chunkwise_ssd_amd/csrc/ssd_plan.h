@@ -1,0 +1,84 @@
+// ssd_plan.h -- host-side work decomposition of the fused scan, shared by the
+// C ABI and its tests. Plain C++: no HIP calls.
+//
+// One workgroup walks the chunks of one (batch row, head, sequence segment,
+// 64-wide slice of D) in order, keeping the N x 64 state on chip. When there
+// are too few (batch, head) sequences to fill the GPU, each sequence is cut
+// into P segments: a first pass computes every segment's end state from a
+// zero start (and its total log-decay), and the full pass then starts segment
+// p from the composition of the earlier segments' results.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kThreads = 512;     // eight wave64s per workgroup
+constexpr int kNPad = 64;         // state rows handled per workgroup (N padded)
+constexpr int kDBlock = 64;       // state columns (D) per workgroup
+constexpr int kTargetGroups = 256;  // one workgroup per compute unit of an MI355X
+constexpr int kMaxBlock = 256;
+
+// Kernel arguments. Complex arrays are interleaved (re, im) float pairs.
+struct ScanParams {
+    const float *x;           // (B, T, H, D) complex
+    const float *A;           // (H) complex
+    const float *Bt;          // (B, T, H, N) complex
+    const float *Ct;          // (B, T, H, N) complex
+    const float *dt;          // (B, T, H)
+    const float *init_state;  // (B, H, N, D) complex or null
+    float *y;                 // (B, T, H, D)
+    float *final_state;       // (B, H, N, D) complex or null
+    float *seg_state;         // (B, H, P-1, N, D) complex, zero-start segment end states
+    float *seg_logdecay;      // (B, H, P-1) complex, sum of softplus(dt)*A over a segment
+    int B, T, H, N, D, Q;
+    int nc;    // chunks per sequence
+    int P;     // segments per sequence
+    int spc;   // chunks per segment
+    int ndb;   // 64-wide D slices
+    int groups_per_seq;  // P (full pass) or P - 1 (state pass)
+};
+
+struct Plan {
+    int R = 0;     // padded chunk rows held by the kernel (16, 32 or 64)
+    int nc = 0;
+    int P = 1;
+    int spc = 0;
+    int ndb = 0;
+    size_t seg_state_bytes = 0;
+    size_t seg_decay_bytes = 0;
+    size_t workspace_bytes = 0;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Sizes are assumed validated (positive, within the supported envelope).
+inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int64_t Q)
+{
+    Plan p;
+    p.R = Q <= 16 ? 16 : (Q <= 32 ? 32 : 64);
+    p.nc = (int)((T + Q - 1) / Q);
+    p.ndb = (int)((D + kDBlock - 1) / kDBlock);
+    if (p.nc <= 0) {
+        p.P = 1;
+        p.spc = 0;
+        return p;
+    }
+    int64_t seqs = B * H * p.ndb;
+    int64_t want = (kTargetGroups + seqs - 1) / seqs;
+    if (want < 1)
+        want = 1;
+    if (want > p.nc)
+        want = p.nc;
+    p.spc = (int)((p.nc + want - 1) / want);
+    p.P = (p.nc + p.spc - 1) / p.spc;
+    if (p.P > 1) {
+        p.seg_state_bytes = align_up((size_t)B * H * (p.P - 1) * N * D * 8, 256);
+        p.seg_decay_bytes = align_up((size_t)B * H * (p.P - 1) * 8, 256);
+    }
+    p.workspace_bytes = p.seg_state_bytes + p.seg_decay_bytes;
+    return p;
+}
+
+}  // namespace ssd

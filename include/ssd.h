@@ -1,0 +1,136 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) complex chunkwise SSD scan library.
+ *
+ * The operation is the complex-valued selective state-space scan of the
+ * Mamba-3-Lite pages. For every batch row b and head h, independently:
+ *
+ *   Abar_t = exp(softplus(dt_t) * A_h)                       (discretisation)
+ *   s_t    = Abar_t * s_{t-1} + B_t (outer) x_t              (state, N x D)
+ *   y_t    = Re( sum_n C_t[n] * s_t[n, :] )                   (output, D)
+ *
+ * with no conjugation anywhere, s_{-1} the initial state (zero by default)
+ * and final_state = s_{T-1}. Sources: "Extending -- SSM variants & Triton
+ * kernels" (Path A Step 1: the naive scan and the discretisation; Step 3: the
+ * chunkwise function returns the real part), "index.html" lab 03 (the
+ * chunkwise decomposition: per-chunk log-decay running sums, the masked
+ * decay matrix L, the intra-chunk term, per-chunk states and the passing of
+ * states between chunks), and "Skills Reference" Skill 3 (chunk_size 32..256,
+ * default 64).
+ *
+ * Conventions common to every call:
+ *   * All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates no memory and keeps no state between calls.
+ *   * Layouts are dense row-major. Complex numbers are interleaved (re, im)
+ *     pairs of float32, bit-identical to torch.complex64.
+ *   * Argument checks run before anything is launched; a failed check returns
+ *     a negative status and touches no memory. Work is launched on `stream`
+ *     and is asynchronous; a launch failure returns SSD_ERR_HIP.
+ *   * There is one code path: no fallback exists when a check fails.
+ *   * Calls on different streams with different workspaces are independent.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque stream handle; pass a hipStream_t (or NULL for the null stream). */
+typedef void *ssd_stream_t;
+
+/* One complex64 value, laid out as torch.complex64. */
+typedef struct {
+    float re, im;
+} ssd_c64;
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,       /* a size is negative, or N, D, chunk_size < 1 */
+    SSD_ERR_ODD_N = -3,       /* N is odd: the state must pack into real pairs */
+    SSD_ERR_BLOCK_DIMS = -4,  /* N, D or chunk_size above 256 */
+    SSD_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+    SSD_ERR_ALIGN = -6,       /* a pointer is not aligned as documented */
+    SSD_ERR_HIP = -7,         /* the HIP runtime reported an error */
+    SSD_ERR_UNSUPPORTED = -8  /* a valid size this build does not cover yet */
+};
+
+/* Largest N, D and chunk_size accepted (the pages cap kernel blocks at 256). */
+#define SSD_MAX_BLOCK 256
+
+/*
+ * ssd_discretise -- the discretisation step and the per-chunk cumulative
+ * log-decay ("Extending", Path A Step 1 and Path B Step 2; index.html lab 03).
+ *
+ *   dt        (batch, T, H) float32, step logits.
+ *   A         (H) complex64, one eigenvalue per head.
+ *   A_bar     out, nullable: (batch, T, H) complex64, exp(softplus(dt) * A).
+ *   log_decay_cumsum
+ *             out, nullable: (batch, H, nc, chunk_size) complex64 with
+ *             nc = ceil(T / chunk_size). Entry [b,h,c,l] is the sum of
+ *             softplus(dt_t) * A_h over t = c*chunk_size .. c*chunk_size + l.
+ *             Positions of a last partial chunk past T repeat the final sum.
+ *   chunk_size 0 when log_decay_cumsum is NULL, else 1..256.
+ * Alignment: 4 bytes for dt, 8 bytes for the complex arrays.
+ * batch, T or H equal to 0 is a no-op.
+ */
+int ssd_discretise(const float *dt, const ssd_c64 *A, int64_t batch, int64_t T, int64_t H,
+                   int64_t chunk_size, ssd_c64 *A_bar, ssd_c64 *log_decay_cumsum,
+                   ssd_stream_t stream);
+
+/*
+ * ssd_chunk_forward_workspace_bytes -- device workspace that ssd_chunk_forward
+ * needs for these sizes (0 when none is needed). The value depends only on
+ * the arguments. Negative or invalid sizes return 0.
+ */
+size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,
+                                         int64_t D, int64_t chunk_size);
+
+/*
+ * ssd_chunk_forward -- the chunkwise complex SSD scan forward
+ * ("Extending", Path A Step 3: the chunkwise function; index.html lab 03).
+ *
+ *   x            (batch, T, H, D) complex64, token content.
+ *   A            (H) complex64.
+ *   B_t, C_t     (batch, T, H, N) complex64, input and output maps.
+ *   dt           (batch, T, H) float32.
+ *   chunk_size   1..256; a last chunk shorter than chunk_size is allowed
+ *                (T need not be a multiple of it). It sets the span of the
+ *                intra-chunk quadratic term; the result does not depend on it
+ *                beyond rounding.
+ *   initial_state nullable: (batch, H, N, D) complex64 state s_{-1}; NULL
+ *                means zero.
+ *   y            out: (batch, T, H, D) float32, the real part of the output.
+ *   final_state  out, nullable: (batch, H, N, D) complex64, s_{T-1}.
+ *   workspace    device scratch of at least
+ *                ssd_chunk_forward_workspace_bytes(...) bytes, 256-byte
+ *                aligned; may be NULL when that size is 0. Its contents on
+ *                entry are ignored.
+ * Constraints: N even (SSD_ERR_ODD_N); N, D, chunk_size <= 256
+ * (SSD_ERR_BLOCK_DIMS); this build covers N <= 64 and chunk_size <= 64
+ * (SSD_ERR_UNSUPPORTED otherwise).
+ * Alignment: B_t and C_t 16 bytes; x, A, initial_state, final_state 8 bytes;
+ * dt and y 4 bytes.
+ * batch or H equal to 0 is a no-op; T equal to 0 copies initial_state (or
+ * zeros) into final_state.
+ */
+int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, const ssd_c64 *C_t,
+                      const float *dt, int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                      int64_t chunk_size, const ssd_c64 *initial_state, float *y,
+                      ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                      ssd_stream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *ssd_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

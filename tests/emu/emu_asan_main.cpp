@@ -1,0 +1,57 @@
+// Bounds check of the scan kernels under AddressSanitizer on the host
+// (TEST INFRASTRUCTURE). Every buffer is an exact-size heap allocation, so any
+// read or write past a tensor, or past a shared-memory array, aborts the run.
+#include "../../complex_chunkwise_ssd_amd/csrc/ssd_api.hip"
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <vector>
+
+static float *alloc_fill(size_t n, unsigned &seed)
+{
+    float *p = (float *)malloc(n * sizeof(float) + (n == 0));
+    for (size_t i = 0; i < n; ++i) {
+        seed = seed * 1664525u + 1013904223u;
+        p[i] = ((seed >> 8) * (1.0f / 16777216.0f) - 0.5f);
+    }
+    return p;
+}
+
+static int run(int B, int T, int H, int N, int D, int Q, bool init, bool fin)
+{
+    unsigned seed = 12345u + B * 7 + T * 13 + H * 17 + N * 19 + D * 23 + Q * 29;
+    float *x = alloc_fill((size_t)B * T * H * D * 2, seed);
+    float *A = alloc_fill((size_t)H * 2, seed);
+    for (int h = 0; h < H; ++h)
+        A[2 * h] = -0.05f - 2.9f * (A[2 * h] + 0.5f);
+    float *Bt = alloc_fill((size_t)B * T * H * N * 2, seed);
+    float *Ct = alloc_fill((size_t)B * T * H * N * 2, seed);
+    float *dt = alloc_fill((size_t)B * T * H, seed);
+    float *is = init ? alloc_fill((size_t)B * H * N * D * 2, seed) : nullptr;
+    float *y = (float *)malloc(((size_t)B * T * H * D + 1) * sizeof(float));
+    float *fs = fin ? (float *)malloc((size_t)B * H * N * D * 2 * sizeof(float)) : nullptr;
+    size_t ws = ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q);
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
+    int st = ssd_chunk_forward((ssd_c64 *)x, (ssd_c64 *)A, (ssd_c64 *)Bt, (ssd_c64 *)Ct, dt, B, T, H,
+                               N, D, Q, (ssd_c64 *)is, y, (ssd_c64 *)fs, w, ws, nullptr);
+    int bad = 0;
+    for (size_t i = 0; i < (size_t)B * T * H * D; ++i)
+        bad += !isfinite(y[i]);
+    printf("B=%d T=%d H=%d N=%d D=%d Q=%d ws=%zu status=%d nonfinite=%d\n", B, T, H, N, D, Q, ws,
+           st, bad);
+    free(x); free(A); free(Bt); free(Ct); free(dt); free(is); free(y); free(fs); free(w);
+    return st != 0 || bad != 0;
+}
+
+int main()
+{
+    int fails = 0;
+    fails += run(1, 40, 2, 4, 5, 16, true, true);    // padded N, D; partial chunk
+    fails += run(1, 70, 1, 64, 64, 64, false, true);  // full tiles, partial last chunk
+    fails += run(1, 45, 1, 6, 70, 32, true, true);    // two D slices
+    fails += run(2, 9, 1, 2, 3, 4, false, false);     // Q < 16, no final state
+    fails += run(1, 130, 1, 8, 8, 3, true, true);     // many segments
+    printf("%s\n", fails ? "FAIL" : "OK");
+    return fails;
+}

@@ -1,0 +1,6 @@
+// Host-emulated build of the scan library (TEST INFRASTRUCTURE): the C-ABI
+// source is compiled unchanged against the emulated device header that sits
+// next to this file.
+#include "../../complex_chunkwise_ssd_amd/csrc/ssd_api.hip"
+
+extern "C" long emu_mfma_count(void) { return emu::g_mfma_count; }

@@ -1,0 +1,289 @@
+// ssd_device.h (host emulation) -- TEST INFRASTRUCTURE.
+//
+// Provides the same primitives as the gfx950 header of the same name, but for
+// a plain x86-64 host build, so that the unchanged kernel and C-ABI sources can
+// run on the CPU. Each GPU thread is a fiber; a wave64's lanes meet at every
+// MFMA and shuffle, all threads of a workgroup meet at every barrier, and the
+// collective is evaluated once every participant has arrived. Workgroups run
+// one after another. A sync point that not every participant reaches (a
+// divergent MFMA, shuffle or barrier) is reported as a deadlock and aborts.
+//
+// MFMA 16x16x4 fp32 data layout emulated here (one wave64):
+//   lane L supplies A[L % 16][L / 16] and B[L / 16][L % 16];
+//   component r of lane L's accumulator is D[4 * (L / 16) + r][L % 16].
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <functional>
+
+#if defined(__has_feature)
+#if __has_feature(address_sanitizer)
+#define EMU_ASAN 1
+#endif
+#endif
+#ifdef EMU_ASAN
+#include <sanitizer/common_interface_defs.h>
+#endif
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+#define SSD_DEVICE static inline
+#define SSD_KERNEL(threads)
+#define SSD_LDS static __attribute__((aligned(16)))
+
+// ---------------------------------------------------------------- HIP host API
+typedef void *hipStream_t;
+typedef int hipError_t;
+#define hipSuccess 0
+struct dim3 {
+    unsigned x, y, z;
+    dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
+
+namespace emu {
+
+enum { RUN = 0, AT_MFMA, AT_BARRIER, AT_SHFL, DONE };
+enum { SH_UP16 = 0, SH_DOWN16, SH_IDX };
+
+struct Fiber {
+    void *sp;
+    char *stack;
+    int state;
+    // MFMA operands / result
+    float a, b;
+    v4f c, d;
+    // shuffle operands / result
+    int mode, arg;
+    float sv, sr;
+    long sync_count;  // number of collectives this thread has joined
+};
+
+static const size_t kStack = 256 * 1024;
+static Fiber *g_f = nullptr;
+static int g_cap = 0;
+static int g_n = 0;
+static int g_cur = -1;
+static int64_t g_block = 0;
+static void *g_sched_sp = nullptr;
+static std::function<void()> *g_fn = nullptr;
+static long g_mfma_count = 0;
+static int g_error = 0;
+#ifdef EMU_ASAN
+static void *g_fake_stack = nullptr;
+static const void *g_sched_bottom = nullptr;
+static size_t g_sched_size = 0;
+#endif
+
+extern "C" void emu_swap(void **save_sp, void *load_sp);
+__asm__(".text\n"
+        ".globl emu_swap\n"
+        ".type emu_swap,@function\n"
+        "emu_swap:\n"
+        "  pushq %rbp\n  pushq %rbx\n  pushq %r12\n  pushq %r13\n  pushq %r14\n  pushq %r15\n"
+        "  movq %rsp, (%rdi)\n"
+        "  movq %rsi, %rsp\n"
+        "  popq %r15\n  popq %r14\n  popq %r13\n  popq %r12\n  popq %rbx\n  popq %rbp\n"
+        "  ret\n");
+
+static void to_scheduler()
+{
+    Fiber &f = g_f[g_cur];
+#ifdef EMU_ASAN
+    void *fake = nullptr;
+    __sanitizer_start_switch_fiber(f.state == DONE ? nullptr : &fake, g_sched_bottom, g_sched_size);
+#endif
+    emu_swap(&f.sp, g_sched_sp);
+#ifdef EMU_ASAN
+    __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
+#endif
+}
+
+static void trampoline()
+{
+#ifdef EMU_ASAN
+    __sanitizer_finish_switch_fiber(nullptr, &g_sched_bottom, &g_sched_size);
+#endif
+    (*g_fn)();
+    g_f[g_cur].state = DONE;
+    to_scheduler();
+    abort();  // never resumed
+}
+
+static void run_fiber(int i)
+{
+    g_cur = i;
+#ifdef EMU_ASAN
+    __sanitizer_start_switch_fiber(&g_fake_stack, g_f[i].stack, kStack);
+#endif
+    emu_swap(&g_sched_sp, g_f[i].sp);
+#ifdef EMU_ASAN
+    __sanitizer_finish_switch_fiber(g_fake_stack, &g_sched_bottom, &g_sched_size);
+#endif
+}
+
+static void init_fiber(int i)
+{
+    Fiber &f = g_f[i];
+    uintptr_t top = ((uintptr_t)f.stack + kStack) & ~(uintptr_t)15;
+    uint64_t *sp = (uint64_t *)top;
+    *--sp = 0;                          // fake return address of the trampoline
+    *--sp = (uint64_t)(void *)&trampoline;
+    for (int k = 0; k < 6; ++k)
+        *--sp = 0;                      // rbp rbx r12 r13 r14 r15
+    f.sp = sp;
+    f.state = RUN;
+    f.sync_count = 0;
+}
+
+static void resolve_wave(int w, bool &progress)
+{
+    const int lo = 64 * w;
+    if (lo + 64 > g_n)
+        return;
+    const int st = g_f[lo].state;
+    if (st != AT_MFMA && st != AT_SHFL)
+        return;
+    for (int l = 0; l < 64; ++l)
+        if (g_f[lo + l].state != st)
+            return;
+    if (st == AT_MFMA) {
+        for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 16; ++j) {
+                Fiber &out = g_f[lo + j + 16 * (i / 4)];
+                float acc = out.c[i % 4];
+                for (int k = 0; k < 4; ++k)
+                    acc += g_f[lo + i + 16 * k].a * g_f[lo + j + 16 * k].b;
+                out.d[i % 4] = acc;
+            }
+        ++g_mfma_count;
+    } else {
+        const int mode = g_f[lo].mode;
+        for (int l = 0; l < 64; ++l)
+            if (g_f[lo + l].mode != mode) {
+                fprintf(stderr, "emu: mixed shuffle kinds in wave %d\n", w);
+                abort();
+            }
+        for (int l = 0; l < 64; ++l) {
+            Fiber &f = g_f[lo + l];
+            int src = l;
+            if (mode == SH_UP16)
+                src = (l & 15) >= f.arg ? l - f.arg : l;
+            else if (mode == SH_DOWN16)
+                src = (l & 15) + f.arg < 16 ? l + f.arg : l;
+            else
+                src = lo + (f.arg & 63) - lo;
+            f.sr = g_f[lo + src].sv;
+        }
+    }
+    for (int l = 0; l < 64; ++l)
+        g_f[lo + l].state = RUN;
+    progress = true;
+}
+
+static void launch(dim3 grid, dim3 block, std::function<void()> fn)
+{
+    const int n = (int)(block.x * block.y * block.z);
+    if (n > g_cap) {
+        for (int i = 0; i < g_cap; ++i)
+            free(g_f[i].stack);
+        free(g_f);
+        g_f = (Fiber *)calloc((size_t)n, sizeof(Fiber));
+        for (int i = 0; i < n; ++i)
+            g_f[i].stack = (char *)aligned_alloc(64, kStack);
+        g_cap = n;
+    }
+    g_n = n;
+    g_fn = &fn;
+    const int64_t blocks = (int64_t)grid.x * grid.y * grid.z;
+    for (int64_t blk = 0; blk < blocks; ++blk) {
+        g_block = blk;
+        for (int i = 0; i < n; ++i)
+            init_fiber(i);
+        for (;;) {
+            bool progress = false;
+            for (int i = 0; i < n; ++i)
+                if (g_f[i].state == RUN) {
+                    run_fiber(i);
+                    progress = true;
+                }
+            int done = 0, at_bar = 0;
+            for (int i = 0; i < n; ++i) {
+                done += g_f[i].state == DONE;
+                at_bar += g_f[i].state == AT_BARRIER;
+            }
+            if (done == n)
+                break;
+            for (int w = 0; w * 64 < n; ++w)
+                resolve_wave(w, progress);
+            if (at_bar == n) {
+                for (int i = 0; i < n; ++i)
+                    g_f[i].state = RUN;
+                progress = true;
+            } else if (at_bar > 0 && done > 0) {
+                fprintf(stderr, "emu: barrier reached while %d threads already exited (block %lld)\n",
+                        done, (long long)blk);
+                abort();
+            }
+            if (!progress) {
+                fprintf(stderr, "emu: deadlock in block %lld:", (long long)blk);
+                for (int i = 0; i < n; i += 64)
+                    fprintf(stderr, " w%d=%d", i / 64, g_f[i].state);
+                fprintf(stderr, "\n");
+                abort();
+            }
+        }
+    }
+    g_fn = nullptr;
+}
+
+}  // namespace emu
+
+#define hipLaunchKernelGGL(K, G, B, S, ST, ...) \
+    (::emu::launch(dim3(G), dim3(B), [&]() { K(__VA_ARGS__); }))
+
+static inline hipError_t hipGetLastError() { return emu::g_error; }
+
+// ------------------------------------------------------------ device primitives
+SSD_DEVICE int thread_id() { return emu::g_cur; }
+SSD_DEVICE int64_t block_id() { return emu::g_block; }
+SSD_DEVICE int wave_id() { return emu::g_cur >> 6; }
+
+SSD_DEVICE v4f mfma_16x16x4(float a, float b, v4f c)
+{
+    emu::Fiber &f = emu::g_f[emu::g_cur];
+    f.a = a;
+    f.b = b;
+    f.c = c;
+    f.state = emu::AT_MFMA;
+    ++f.sync_count;
+    emu::to_scheduler();
+    return emu::g_f[emu::g_cur].d;
+}
+
+SSD_DEVICE float emu_shfl(float v, int mode, int arg)
+{
+    emu::Fiber &f = emu::g_f[emu::g_cur];
+    f.sv = v;
+    f.mode = mode;
+    f.arg = arg;
+    f.state = emu::AT_SHFL;
+    ++f.sync_count;
+    emu::to_scheduler();
+    return emu::g_f[emu::g_cur].sr;
+}
+
+SSD_DEVICE float shfl_up16(float v, int d) { return emu_shfl(v, emu::SH_UP16, d); }
+SSD_DEVICE float shfl_down16(float v, int d) { return emu_shfl(v, emu::SH_DOWN16, d); }
+SSD_DEVICE float shfl_idx(float v, int src) { return emu_shfl(v, emu::SH_IDX, src); }
+
+SSD_DEVICE void block_sync()
+{
+    emu::g_f[emu::g_cur].state = emu::AT_BARRIER;
+    emu::to_scheduler();
+}

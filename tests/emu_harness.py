@@ -1,0 +1,95 @@
+"""Host emulation of the scan library (TEST INFRASTRUCTURE).
+
+Builds the unchanged C-ABI and kernel sources against tests/emu/ssd_device.h,
+which runs each GPU thread as a fiber and evaluates wave64 MFMA tiles,
+shuffles and workgroup barriers on the CPU. The resulting shared object
+exports the same ssd_* functions; pointers are host pointers.
+"""
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+EMU = os.path.join(HERE, "emu")
+CSRC = os.path.join(ROOT, "complex_chunkwise_ssd_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+CLANG = "/opt/rocm/llvm/bin/clang++"
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _sources():
+    srcs = [os.path.join(EMU, f) for f in os.listdir(EMU)]
+    srcs += [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
+    srcs += [os.path.join(INCLUDE, "ssd.h")]
+    return srcs
+
+
+def _flags():
+    return ["-x", "c++", "-std=c++17", "-I" + EMU, "-I" + CSRC, "-I" + INCLUDE]
+
+
+def build_lib(out_dir):
+    out = os.path.join(out_dir, "libssd_emu.so")
+    cmd = [CLANG, *_flags(), "-O1", "-g", "-fPIC", "-shared", os.path.join(EMU, "emu_lib.cpp"),
+           "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def build_asan_exe(out_dir):
+    out = os.path.join(out_dir, "ssd_emu_asan")
+    cmd = [CLANG, *_flags(), "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+           os.path.join(EMU, "emu_asan_main.cpp"), "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(out_dir):
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build_lib(out_dir))
+            p = ctypes.c_void_p
+            i64 = ctypes.c_int64
+            lib.ssd_chunk_forward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p, p,
+                                              p, ctypes.c_size_t, p]
+            lib.ssd_chunk_forward.restype = ctypes.c_int
+            lib.ssd_chunk_forward_workspace_bytes.argtypes = [i64] * 6
+            lib.ssd_chunk_forward_workspace_bytes.restype = ctypes.c_size_t
+            lib.ssd_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
+            lib.ssd_discretise.restype = ctypes.c_int
+            lib.emu_mfma_count.restype = ctypes.c_long
+            _lib = lib
+    return _lib
+
+
+def _c64(t):
+    a = np.asarray(t.detach().cpu().numpy() if hasattr(t, "detach") else t)
+    return np.ascontiguousarray(a.astype(np.complex64))
+
+
+def chunk_forward(lib, inp, chunk, initial_state=None, want_final=True):
+    x, A, Bm, Cm = (_c64(v) for v in (inp.x, inp.A, inp.B_t, inp.C_t))
+    dt = np.ascontiguousarray(inp.dt.numpy().astype(np.float32))
+    Bsz, T, H, D = x.shape
+    N = Bm.shape[-1]
+    y = np.full((Bsz, T, H, D), np.nan, np.float32)
+    fs = np.full((Bsz, H, N, D), np.nan + 0j, np.complex64) if want_final else None
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, np.complex64)
+    ws_n = lib.ssd_chunk_forward_workspace_bytes(Bsz, T, H, N, D, chunk)
+    ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
+    ws_p = ws.ctypes.data
+    ws_p = ws_p + (-ws_p) % 256
+    st = lib.ssd_chunk_forward(x.ctypes.data, A.ctypes.data, Bm.ctypes.data, Cm.ctypes.data,
+                               dt.ctypes.data, Bsz, T, H, N, D, chunk,
+                               None if init is None else init.ctypes.data, y.ctypes.data,
+                               None if fs is None else fs.ctypes.data,
+                               ws_p if ws_n else None, ws_n, None)
+    return st, y, fs

@@ -1,0 +1,139 @@
+"""The C ABI boundary on the CPU: the library loads, exports what include/ssd.h
+declares, and rejects invalid arguments before launching anything (these calls
+never reach the HIP runtime, so no GPU is needed)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import complex_chunkwise_ssd_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIBPATH):
+        from complex_chunkwise_ssd_amd import build
+        build.build()
+    return ssd.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = set(ssd.header_functions())
+    assert {"ssd_discretise", "ssd_chunk_forward", "ssd_chunk_forward_workspace_bytes",
+            "ssd_status_string", "ssd_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in ssd.header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIBPATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(ssd.header_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    # the fat binary of our own build names its offload target
+    data = open(ssd.LIBPATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_status_strings(lib):
+    for st in range(-8, 1):
+        s = ssd.status_string(st)
+        assert s and s != "unknown status"
+    assert ssd.status_string(-99) == "unknown status"
+    assert lib.ssd_version() >= 100
+
+
+def _fwd(lib, B=1, T=16, H=2, N=4, D=4, Q=4, ptrs=True, ws=None, ws_n=0, align=0):
+    p = ctypes.c_void_p(0x100000 + align) if ptrs else None
+    p16 = ctypes.c_void_p(0x100000 + (align if align % 16 else 0)) if ptrs else None
+    return lib.ssd_chunk_forward(p, p, p16, p16, p, B, T, H, N, D, Q, None, p, None, ws, ws_n, None)
+
+
+def test_shape_errors(lib):
+    assert _fwd(lib, B=-1) == ssd.SSD_ERR_SHAPE
+    assert _fwd(lib, T=-1) == ssd.SSD_ERR_SHAPE
+    assert _fwd(lib, H=-1) == ssd.SSD_ERR_SHAPE
+    assert _fwd(lib, N=0) == ssd.SSD_ERR_SHAPE
+    assert _fwd(lib, D=0) == ssd.SSD_ERR_SHAPE
+    assert _fwd(lib, Q=0) == ssd.SSD_ERR_SHAPE
+
+
+def test_odd_n_rejected(lib):
+    for n in (1, 3, 63):
+        assert _fwd(lib, N=n) == ssd.SSD_ERR_ODD_N
+
+
+def test_block_dims_cap(lib):
+    assert _fwd(lib, N=258) == ssd.SSD_ERR_BLOCK_DIMS
+    assert _fwd(lib, D=257) == ssd.SSD_ERR_BLOCK_DIMS
+    assert _fwd(lib, Q=257) == ssd.SSD_ERR_BLOCK_DIMS
+
+
+def test_null_and_alignment(lib):
+    assert _fwd(lib, ptrs=False) == ssd.SSD_ERR_NULL
+    assert _fwd(lib, align=4) == ssd.SSD_ERR_ALIGN      # complex arrays need 8 bytes
+    assert _fwd(lib, align=8) == ssd.SSD_ERR_ALIGN      # B_t / C_t need 16 bytes
+
+
+def test_workspace_checks(lib):
+    need = lib.ssd_chunk_forward_workspace_bytes(1, 2048, 16, 64, 64, 64)
+    assert need > 0
+    args = dict(B=1, T=2048, H=16, N=64, D=64, Q=64)
+    assert _fwd(lib, ws=None, ws_n=need, **args) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p(0x200000), ws_n=need - 1, **args) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p(0x200010), ws_n=need, **args) == ssd.SSD_ERR_ALIGN
+
+
+def test_workspace_sizes(lib):
+    f = lib.ssd_chunk_forward_workspace_bytes
+    # 512 sequences fill the GPU: no segments, no workspace
+    assert f(32, 2048, 16, 64, 64, 64) == 0
+    # fewer sequences: segments whose end states need N*D complex each
+    n = f(8, 2048, 16, 64, 64, 64)
+    assert n >= 8 * 16 * 64 * 64 * 8
+    assert f(-1, 16, 2, 4, 4, 4) == 0 and f(1, 16, 2, 3, 4, 4) == 0
+    assert f(0, 16, 2, 4, 4, 4) == 0 and f(1, 0, 2, 4, 4, 4) == 0
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert lib.ssd_chunk_forward(None, None, None, None, None, 0, 16, 2, 4, 4, 4, None, None, None,
+                                 None, 0, None) == ssd.SSD_OK
+    assert lib.ssd_chunk_forward(None, None, None, None, None, 2, 16, 0, 4, 4, 4, None, None, None,
+                                 None, 0, None) == ssd.SSD_OK
+    assert lib.ssd_chunk_forward(None, None, None, None, None, 2, 0, 2, 4, 4, 4, None, None, None,
+                                 None, 0, None) == ssd.SSD_OK
+
+
+def test_discretise_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    assert lib.ssd_discretise(p, p, -1, 4, 2, 0, p, None, None) == ssd.SSD_ERR_SHAPE
+    assert lib.ssd_discretise(p, p, 1, 4, 2, 0, p, p, None) == ssd.SSD_ERR_SHAPE
+    assert lib.ssd_discretise(p, p, 1, 4, 2, 300, None, p, None) == ssd.SSD_ERR_BLOCK_DIMS
+    assert lib.ssd_discretise(None, p, 1, 4, 2, 4, None, p, None) == ssd.SSD_ERR_NULL
+    assert lib.ssd_discretise(p, ctypes.c_void_p(0x100004), 1, 4, 2, 4, None, p, None) == \
+        ssd.SSD_ERR_ALIGN
+    assert lib.ssd_discretise(p, p, 0, 4, 2, 4, None, p, None) == ssd.SSD_OK
+
+
+def test_python_layer_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 4, dtype=torch.complex64)
+    A = torch.zeros(2, dtype=torch.complex64)
+    B = torch.zeros(1, 4, 2, 4, dtype=torch.complex64)
+    dt = torch.zeros(1, 4, 2)
+    with pytest.raises(ValueError):
+        ssd.chunk_forward(x, A, B, B, dt)                # CPU tensors
+    with pytest.raises(ValueError):
+        ssd.discretise(dt, A, 4)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(OSError):
+        ssd.load_library(str(tmp_path / "libssd.so"))

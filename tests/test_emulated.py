@@ -1,0 +1,97 @@
+"""The unchanged kernel and C-ABI sources, run on the CPU under the host wave
+emulator (tests/emu), against the oracle. This checks the kernels' lane
+layouts, tiling, padding and segment logic without a GPU; the same cases run
+on the GPU in test_gpu_parity.py. An AddressSanitizer build checks every
+global and shared-memory access for bounds."""
+
+import subprocess
+
+import numpy as np
+import pytest
+
+import emu_harness
+import oracle
+import ssd_inputs
+
+
+@pytest.fixture(scope="module")
+def emu(tmp_path_factory):
+    return emu_harness.load(str(tmp_path_factory.mktemp("emu")))
+
+
+def _check(y, fs, yo, fo):
+    yr = yo.real
+    err = np.abs(y - yr)
+    assert np.isfinite(y).all()
+    bad = err > 1e-4 + 1e-4 * np.abs(yr)
+    assert not bad.any(), "max err %.3e at %s" % (err.max(), np.argwhere(bad)[:3])
+    if fs is not None:
+        ferr = np.abs(fs - fo)
+        assert (ferr <= 1e-4 + 1e-4 * np.abs(fo)).all(), ferr.max()
+
+
+CASES = [
+    # B, T, H, N, D, Q
+    (2, 16, 2, 4, 4, 4),       # the pages' tiny shape
+    (1, 64, 1, 64, 64, 64),    # one full chunk
+    (1, 150, 2, 64, 64, 64),   # ragged last chunk, several segments
+    (1, 97, 1, 8, 8, 32),
+    (2, 50, 2, 6, 10, 16),
+    (1, 45, 1, 10, 70, 32),    # two D slices
+    (1, 33, 1, 2, 3, 33),      # Q not a tile multiple
+    (1, 23, 2, 4, 5, 1),       # Q = 1
+    (1, 12, 1, 4, 4, 12),      # T == Q
+    (3, 7, 1, 2, 2, 64),       # T < Q
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_emulated_matches_oracle(emu, case):
+    B, T, H, N, D, Q = case
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=sum(case), dt_scale=1.0, dt_mean=0.3)
+    st, y, fs = emu_harness.chunk_forward(emu, inp, Q)
+    assert st == 0
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y, fs, yo, fo)
+
+
+@pytest.mark.parametrize("tv", [False, True])
+def test_emulated_tiny_recipe(emu, tv):
+    inp = ssd_inputs.tiny_case(tv)
+    st, y, fs = emu_harness.chunk_forward(emu, inp, 4)
+    assert st == 0
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y, fs, yo, fo)
+
+
+def test_emulated_initial_state(emu):
+    inp = ssd_inputs.random_case(2, 70, 2, 8, 6, seed=5)
+    rng = np.random.default_rng(1)
+    init = (rng.standard_normal((2, 2, 8, 6)) + 1j * rng.standard_normal((2, 2, 8, 6))) * 0.5
+    st, y, fs = emu_harness.chunk_forward(emu, inp, 16, initial_state=init)
+    assert st == 0
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt,
+                         initial_state=init.astype(np.complex64))
+    _check(y, fs, yo, fo)
+
+
+def test_emulated_zero_length(emu):
+    inp = ssd_inputs.random_case(2, 0, 2, 4, 4, seed=6)
+    init = np.arange(2 * 2 * 4 * 4, dtype=np.float32).reshape(2, 2, 4, 4).astype(np.complex64)
+    st, y, fs = emu_harness.chunk_forward(emu, inp, 4, initial_state=init)
+    assert st == 0 and y.size == 0
+    assert np.array_equal(fs, init)
+
+
+def test_emulated_chunk_size_invariance(emu):
+    inp = ssd_inputs.random_case(1, 100, 1, 8, 8, seed=7, dt_mean=0.5)
+    outs = [emu_harness.chunk_forward(emu, inp, q)[1] for q in (5, 16, 40, 64)]
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-4 * (1 + np.abs(outs[0]).max())
+
+
+def test_asan_bounds(tmp_path):
+    exe = emu_harness.build_asan_exe(str(tmp_path))
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "OK" in res.stdout
