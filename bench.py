@@ -45,7 +45,7 @@ def measured_traffic(launch_tokens_heads):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layer0, batch_rows=2):
+def cpu_baseline(layer0, batch_rows=16):
     """The oracle as it stands, on a bounded sample of layer 0: batch rows
     0..batch_rows-1, all heads, full T (host cores, OpenMP over sequences)."""
     import oracle
@@ -75,6 +75,10 @@ def main():
     ap.add_argument("--workload", default="network_28x_b32_t2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the single-layer side figures")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="override the layer count (counter runs; the headline uses all layers)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -88,10 +92,20 @@ def main():
     import ssd_inputs
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 3}))
+        return 0
     wl = dict(ssd_inputs.WORKLOADS[args.workload])
     B, T, H, N, D = wl["batch"], wl["T"], wl["H"], wl["N"], wl["D"]
     Q = wl["chunks"][0]
-    L = wl.get("layers", 1)
+    L = wl.get("layers", 1) if args.layers is None else args.layers
     log("bench: workload %s (%d layer(s) of B=%d T=%d H=%d N=%d D=%d Q=%d)" % (args.workload, L, B, T,
                                                                                  H, N, D, Q))
     layers, ys, fss = [], [], []
