@@ -27,8 +27,10 @@ int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64
         return SSD_ERR_BLOCK_DIMS;
     if (N > ssd::kNPad || chunk > 64)
         return SSD_ERR_UNSUPPORTED;
-    // 32-bit token indices inside the kernels
+    // 32-bit token indices, and 32-bit byte offsets inside one chunk of one sequence
     if (T > (1LL << 30) || batch * H > (1LL << 30))
+        return SSD_ERR_UNSUPPORTED;
+    if (H * (N > D ? N : D) * 8 * 64 > (1LL << 30))
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }

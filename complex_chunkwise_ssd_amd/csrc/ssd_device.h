@@ -22,14 +22,61 @@ SSD_DEVICE v4f mfma_16x16x4(float a, float b, v4f c)
 }
 
 SSD_DEVICE void block_sync() { __syncthreads(); }
+
+// Buffer resources: 32-bit byte offsets from a wave-uniform base. An access
+// at or past `bytes` reads zero and a store there is dropped, which is how the
+// kernels mask padded rows and columns.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+SSD_DEVICE buf_t make_buf(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+SSD_DEVICE v4f buf_load4(buf_t r, uint32_t off)
+{
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+SSD_DEVICE v2f buf_load2(buf_t r, uint32_t off)
+{
+    return __builtin_bit_cast(v2f, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+SSD_DEVICE float buf_load1(buf_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
+}
+
+// Shared-memory float accumulate (ds_add_f32).
+SSD_DEVICE void lds_add(float *p, float v) { atomicAdd(p, v); }
 SSD_DEVICE int thread_id() { return (int)threadIdx.x; }
 SSD_DEVICE int64_t block_id() { return (int64_t)blockIdx.x; }
 // Wave index as a wave-uniform (scalar) value.
 SSD_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
-// Shuffles inside aligned groups of 16 lanes; a lane whose source falls
-// outside its group keeps its own value.
-SSD_DEVICE float shfl_up16(float v, int d) { return __shfl_up(v, (unsigned)d, 16); }
-SSD_DEVICE float shfl_down16(float v, int d) { return __shfl_down(v, (unsigned)d, 16); }
-// Value of lane `src` (0..63) of the wave.
-SSD_DEVICE float shfl_idx(float v, int src) { return __shfl(v, src, 64); }
+// Row shifts inside aligned groups of 16 lanes (DPP row_shr / row_shl): lane i
+// of a row receives lane i - n (shr) or i + n (shl) of the same row, or 0 when
+// that lane is outside the row.
+template <int n>
+SSD_DEVICE float row_shr(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x110 + n, 0xf, 0xf, true));
+}
+template <int n>
+SSD_DEVICE float row_shl(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x100 + n, 0xf, 0xf, true));
+}
+// Value of lane `src` (wave-uniform) for every lane.
+SSD_DEVICE float lane_read(float v, int src)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+// A wave-uniform value kept in scalar registers.
+SSD_DEVICE float uniform(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}

@@ -89,47 +89,80 @@ SSD_KERNEL(256) void copy_state_kernel(const float *src, float *dst, int64_t n)
 
 // ------------------------------------------------------------------ the scan
 
-// Chunk tile pair of causal tile k (0 <= k < NR(NR+1)/2): the NR diagonal tiles
-// first, then the strictly lower ones (st < lt) by increasing lt.
-SSD_DEVICE void tile_pair(int k, int nr, int &st, int &lt)
+// Causal 16x16 tile pair (st <= lt) of tile index k: the nr diagonal tiles
+// first, then the strictly lower ones by increasing lt.
+constexpr int tile_lt(int k, int nr)
 {
-    if (k < nr) {
-        st = lt = k;
-        return;
-    }
-    int idx = k - nr;
-    lt = 1;
+    if (k < nr)
+        return k;
+    int idx = k - nr, lt = 1;
     while (idx >= lt) {
         idx -= lt;
         ++lt;
     }
-    st = idx;
+    return lt;
+}
+constexpr int tile_st(int k, int nr)
+{
+    if (k < nr)
+        return k;
+    int idx = k - nr, lt = 1;
+    while (idx >= lt) {
+        idx -= lt;
+        ++lt;
+    }
+    return idx;
 }
 
 // R: chunk rows held on chip (chunk_size rounded up to 16, 32 or 64; extra
 // rows are identity padding). FULL: produce y and the final state; otherwise
 // only the zero-start end state and total log-decay of each segment.
+//
+// Per chunk c (three barriers):
+//   stage   B_t, C_t rows (loaded during chunk c-1) copied into LDS as
+//           interleaved complex, plus C' = exp(Lam) C stored as (re, -im); x
+//           stays in the registers it was loaded into.
+//   phase 1 (a) M = (B C^T)^T o L^T on the causal tiles (stored as (re, -im)),
+//           (b) Re(C' H), (c) H = exp(sum a) H + B^T (decay' o x); wave 0 then
+//           forms chunk c+1's per-tile running sums from its dt (already loaded).
+//   phase 2 Re(M X); all threads evaluate chunk c+1's decay factors, at most
+//           one complex exponential each.
+//   store   the two waves sharing a column tile combine their partial y.
+//
+// L on a diagonal 16x16 tile: each lane holds four consecutive s of one row l;
+// it takes exp(Lam[l] - Lam[s]) once at the largest causal s of its four and
+// walks down with L[l, s] = L[l, s+1] exp(a_{s+1}). Off the diagonal:
+// L[l, s] = W[l] K(st, lt) V[s] with W the decay from the start of l's tile,
+// V the decay from s to the end of its tile and K the whole tiles in between.
 template <int R, bool FULL>
 SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 {
     constexpr int NR = R / 16;               // 16-row tiles per chunk
     constexpr int NT = NR * (NR + 1) / 2;    // causal tile pairs
-    constexpr int LDB = kNPad + 4;           // [row][n] plane stride (floats)
-    constexpr int LDT = R + 4;               // [n][row] plane stride (floats)
+    constexpr int NWHOLE = NT < 8 ? NT : 8;  // tiles k < NWHOLE: produced whole by wave k
+    constexpr int NSPLIT = NT - NWHOLE;      // the rest: two K halves, waves 2i and 2i+1
+    static_assert(NSPLIT == 0 || NSPLIT == 2, "unsupported tile count");
+    constexpr int LDI = 2 * kNPad + 4;       // row stride (floats) of an interleaved plane
     constexpr int LOADS = R * (kNPad / 2) / kThreads;  // 16-byte loads per thread per B or C tile
     static_assert(LOADS >= 1, "tile too small for the thread count");
+    constexpr uint32_t kOut = 0x80000000u;   // a byte offset past every buffer
 
-    SSD_LDS float sBre[FULL ? R * LDB : 1], sBim[FULL ? R * LDB : 1];  // B[s][n]
-    SSD_LDS float sCre[FULL ? R * LDB : 1], sCim[FULL ? R * LDB : 1];  // C[l][n]
-    SSD_LDS float sTre[kNPad * LDT], sTim[kNPad * LDT];                // B[s][n] stored at [n][s]
-    SSD_LDS v4f sMre[FULL ? NT * 64 : 1], sMim[FULL ? NT * 64 : 1];    // M tiles, lane-major
+    SSD_LDS float sB[R * LDI];                // B[s][n] interleaved (re, im)
+    SSD_LDS float sC[FULL ? R * LDI : 1];     // C[l][n]
+    SSD_LDS float sP[FULL ? R * LDI : 1];     // exp(Lam[l]) C[l][n] as (re, -im)
+    SSD_LDS v4f sMre[FULL ? NT * 64 : 1], sMim[FULL ? NT * 64 : 1];    // M tiles (re, -im), lane-major
     SSD_LDS v4f sYx[FULL ? 4 * NR * 64 : 1];                           // partial-y exchange
-    SSD_LDS v2f sLam[R];       // running sum of a inside the 16-row tile (inclusive)
-    SSD_LDS v2f sEin[R];       // exp(Lam[l]) from the chunk start
-    SSD_LDS v2f sDout[R];      // exp(sum of a over rows s+1 .. end of chunk)
+    SSD_LDS v4f sLdre[FULL ? NR * 64 : 1], sLdim[FULL ? NR * 64 : 1];  // L on diagonal tiles, lane-major
+    SSD_LDS v2f sDout[R];      // exp(sum of a over rows s+1 .. chunk end)
+    SSD_LDS v2f sW[R];         // exp(sum of a over rows tile start .. l)
     SSD_LDS v2f sV[R];         // exp(sum of a over rows s+1 .. end of its tile)
-    SSD_LDS v2f sU[R * NR];    // exp(sum of a over rows after tile st .. l), st < tile(l)
-    SSD_LDS v2f sDecay[1];     // exp(sum of a over the chunk)
+    SSD_LDS v2f sK[NR * NR];   // [st * NR + lt]: exp(sum of a over the tiles strictly between);
+                               // [lt * NR + lt]: over the tiles before lt
+    SSD_LDS v2f sLam[R];       // running sum of a inside the 16-row tile (inclusive)
+    SSD_LDS v2f sSig[R];       // sum of a over rows s+1 .. end of the tile
+    SSD_LDS v2f sAbar[R];      // exp(a)
+    SSD_LDS v2f sTau[NR + 1];  // tile totals; [NR] = chunk total
+    SSD_LDS v2f sDecay[1];     // exp(chunk total)
 
     const int tid = thread_id();
     const int lane = tid & 63;
@@ -148,16 +181,22 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int b = (int)(blk / p.H);
 
     const int64_t row0 = (int64_t)b * p.T * p.H + h;  // flat (b, t=0, h) index
-    const int64_t sx = (int64_t)p.H * p.D;            // token stride of x and y
-    const int64_t sbc = (int64_t)p.H * p.N;           // token stride of B_t and C_t
-    const float *xb = p.x + (row0 * p.D + (int64_t)db * kDBlock) * 2;
-    const float *Bb = p.Bt + row0 * p.N * 2;
-    const float *Cb = p.Ct + row0 * p.N * 2;
-    const float *dtb = p.dt + row0;
-    const v2f Ah = v2f{p.A[2 * h], p.A[2 * h + 1]};
-    const int dcol = db * kDBlock + 16 * dtl + Lr;    // this lane's column of D
-    const bool dvalid = dcol < p.D;
     const int64_t bh = (int64_t)b * p.H + h;
+    const v2f Ah = v2f{uniform(p.A[2 * h]), uniform(p.A[2 * h + 1])};
+    const uint32_t xrow = (uint32_t)(p.H * p.D) * 8u;  // bytes between tokens: x
+    const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;  //                      y
+    const uint32_t brow = (uint32_t)(p.H * p.N) * 8u;  //                      B_t, C_t
+    const uint32_t drow = (uint32_t)p.H * 4u;          //                      dt
+    const int dsl = p.D - db * kDBlock;                // columns of D from this slice on
+    const int dl = 16 * dtl + Lr;                      // this lane's column in the slice
+    const bool dvalid = dl < dsl;
+    const int dcol = db * kDBlock + dl;
+
+    // Loop-invariant lane offsets; masked lanes point past the buffer.
+    const int ncol = (tid & 31) * 2;
+    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * 8u : kOut;
+    const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * 8u : kOut;
+    const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
 
     // State rows n = 16 * (2 * nh + i) + 4 * Lk + r, column dcol.
     v4f Hre[2], Him[2];
@@ -166,12 +205,12 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         Him[i] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     auto add_state = [&](const float *base, v2f scale) {
-        // H = scale * H + base[n, dcol] over this lane's elements (base may be null).
+        // H = scale * H + base[n, dcol] over this lane's elements.
         for (int i = 0; i < 2; ++i)
             for (int r = 0; r < 4; ++r) {
                 const int n = 16 * (2 * nh + i) + 4 * Lk + r;
                 v2f e = v2f{0.f, 0.f};
-                if (base && n < p.N && dvalid)
+                if (n < p.N && dvalid)
                     e = *(const v2f *)&base[((int64_t)n * p.D + dcol) * 2];
                 const v2f hv = cmul(scale, v2f{Hre[i][r], Him[i][r]});
                 Hre[i][r] = hv.x + e.x;
@@ -192,180 +231,253 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int c_end = c_begin + p.spc < p.nc ? c_begin + p.spc : p.nc;
     v2f seg_log = v2f{0.f, 0.f};
 
+    auto rows_of = [&](int c) { return p.Q < p.T - c * p.Q ? p.Q : p.T - c * p.Q; };
+    auto tok0 = [&](int c) { return row0 + (int64_t)c * p.Q * p.H; };  // flat (b, cQ, h)
+
     // Registers holding the next chunk's inputs while the current one runs.
     v4f pB[LOADS], pC[LOADS];
     float pdt = 0.f;
     v2f pX[NR][4];
     auto fetch = [&](int c) {
-        const int t0 = c * p.Q;
-        const int rows = p.Q < p.T - t0 ? p.Q : p.T - t0;
+        const uint32_t rows = (uint32_t)rows_of(c);
+        const int64_t r0 = tok0(c);
+        const buf_t bB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+        const buf_t bC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+        const buf_t bX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
+        const buf_t bT = make_buf(p.dt + r0, (rows - 1) * drow + 4u);
         for (int i = 0; i < LOADS; ++i) {
-            const int e = i * kThreads + tid;
-            const int row = e >> 5;
-            const int n = (e & 31) * 2;
-            const bool ok = row < rows && n < p.N;
-            const int64_t off = ((int64_t)(t0 + row) * sbc + n) * 2;
-            pB[i] = ok ? *(const v4f *)&Bb[off] : v4f{0.f, 0.f, 0.f, 0.f};
+            pB[i] = buf_load4(bB, offB + (uint32_t)(16 * i) * brow);
             if (FULL)
-                pC[i] = ok ? *(const v4f *)&Cb[off] : v4f{0.f, 0.f, 0.f, 0.f};
+                pC[i] = buf_load4(bC, offB + (uint32_t)(16 * i) * brow);
         }
-        if (w == 0)
-            pdt = lane < rows ? dtb[(int64_t)(t0 + lane) * p.H] : 0.f;
+        pdt = buf_load1(bT, w == 0 ? (uint32_t)lane * drow : kOut);
         for (int q = 0; q < NR; ++q)
-            for (int j = 0; j < 4; ++j) {
-                const int s = 16 * q + 4 * Lk + j;
-                const bool ok = s < rows && dvalid;
-                pX[q][j] = ok ? *(const v2f *)&xb[((int64_t)(t0 + s) * sx + 16 * dtl + Lr) * 2]
-                              : v2f{0.f, 0.f};
-            }
+            for (int j = 0; j < 4; ++j)
+                pX[q][j] = buf_load2(bX, offX + (uint32_t)(16 * q + j) * xrow);
     };
 
-    if (c_begin < c_end)
+    // Wave 0: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
+    auto scan = [&](int c) {
+        const int rows = rows_of(c);
+        const float sp = softplus_f(pdt);
+        const v2f a = lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
+        // inclusive running sums inside the tile, forwards (lam) and backwards (rs)
+        v2f lam = a, rs = a;
+        lam += v2f{row_shr<1>(lam.x), row_shr<1>(lam.y)};
+        rs += v2f{row_shl<1>(rs.x), row_shl<1>(rs.y)};
+        lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
+        rs += v2f{row_shl<2>(rs.x), row_shl<2>(rs.y)};
+        lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
+        rs += v2f{row_shl<4>(rs.x), row_shl<4>(rs.y)};
+        lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
+        rs += v2f{row_shl<8>(rs.x), row_shl<8>(rs.y)};
+        const v2f sig = v2f{row_shl<1>(rs.x), row_shl<1>(rs.y)};  // rows s+1 .. tile end
+        v2f tau[NR];
+        v2f tot = v2f{0.f, 0.f};
+        for (int t = 0; t < NR; ++t) {
+            tau[t] = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
+            tot += tau[t];
+        }
+        if (lane < R) {
+            sLam[lane] = lam;
+            sSig[lane] = sig;
+            if (FULL)
+                sAbar[lane] = cexp_f(a);
+        }
+        if (lane == 0) {
+            for (int t = 0; t < NR; ++t)
+                sTau[t] = tau[t];
+            sTau[NR] = tot;
+        }
+        seg_log += tot;
+    };
+
+    // All threads: chunk c's decay factors from sLam, sSig, sAbar, sTau, at most one
+    // complex exponential per thread. Waves 0-3: diagonal-tile L, one lane-quad each;
+    // wave 4: W; wave 5: the tile constants K and the chunk decay; wave 6: the decay
+    // to the chunk end; wave 7: V.
+    auto factors = [&]() {
+        if (tid < 256) {
+            if (FULL && tid < NR * 64) {
+                const int tile = tid >> 6, ln = tid & 63;
+                const int l = ln & 15, g = 4 * (ln >> 4);
+                const v2f *lam = sLam + 16 * tile;
+                v2f L = l >= g + 3 ? cexp_f(lam[l] - lam[g + 3]) : v2f{0.f, 0.f};
+                v4f lre, lim;
+                lre[3] = L.x;
+                lim[3] = L.y;
+                for (int r = 2; r >= 0; --r) {
+                    if (l > g + r)
+                        L = cmul(L, sAbar[16 * tile + g + r + 1]);
+                    else
+                        L = l == g + r ? v2f{1.f, 0.f} : v2f{0.f, 0.f};
+                    lre[r] = L.x;
+                    lim[r] = L.y;
+                }
+                sLdre[tid] = lre;
+                sLdim[tid] = lim;
+            }
+            return;
+        }
+        const int role = (tid >> 6) - 4, ri = tid & 63;
+        if (role == 0) {
+            if (FULL && ri < R)
+                sW[ri] = cexp_f(sLam[ri]);
+        } else if (role == 1) {
+            if (FULL && ri < NR * NR) {
+                // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before lt
+                const int st = ri / NR, lt = ri % NR;
+                if (st <= lt) {
+                    v2f z = v2f{0.f, 0.f};
+                    for (int t = 0; t < NR; ++t)
+                        if (st < lt ? (t > st && t < lt) : t < lt)
+                            z += sTau[t];
+                    sK[ri] = cexp_f(z);
+                }
+            } else if (ri == 63) {
+                sDecay[0] = cexp_f(sTau[NR]);
+            }
+        } else if (role == 2) {
+            if (ri < R) {
+                v2f z = sSig[ri];
+                for (int t = 0; t < NR; ++t)
+                    if (t > (ri >> 4))
+                        z += sTau[t];
+                sDout[ri] = cexp_f(z);
+            }
+        } else {
+            if (FULL && ri < R)
+                sV[ri] = cexp_f(sSig[ri]);
+        }
+    };
+    static_assert(R <= 64 && NR * NR < 63, "role layout assumes at most 64 rows");
+
+    if (c_begin < c_end) {
         fetch(c_begin);
+        if (w == 0)
+            scan(c_begin);
+        block_sync();
+        factors();
+        block_sync();
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
-        const int t0 = c * p.Q;
-        const int rows = p.Q < p.T - t0 ? p.Q : p.T - t0;
+        const int rows = rows_of(c);
+        const int64_t r0 = tok0(c);
 
-        // ---- stage 1 (wave 0): per-token log-decay and the decay factors.
-        if (w == 0) {
-            const float sp = softplus_f(pdt);
-            const v2f a = lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
-            v2f lam = a;  // inclusive running sum inside the 16-row tile
-            v2f rs = a;   // inclusive running sum towards the end of the tile
-            for (int off = 1; off < 16; off <<= 1) {
-                const float ux = shfl_up16(lam.x, off), uy = shfl_up16(lam.y, off);
-                const float dx = shfl_down16(rs.x, off), dy = shfl_down16(rs.y, off);
-                if (Lr >= off) {
-                    lam.x += ux;
-                    lam.y += uy;
-                }
-                if (Lr + off < 16) {
-                    rs.x += dx;
-                    rs.y += dy;
-                }
-            }
-            const float sgx = shfl_down16(rs.x, 1), sgy = shfl_down16(rs.y, 1);
-            const v2f sig = Lr < 15 ? v2f{sgx, sgy} : v2f{0.f, 0.f};  // rows s+1 .. tile end
-            v2f tau[NR];
-            for (int t = 0; t < NR; ++t)
-                tau[t] = v2f{shfl_idx(lam.x, 16 * t + 15), shfl_idx(lam.y, 16 * t + 15)};
-            v2f pre = v2f{0.f, 0.f}, post = v2f{0.f, 0.f}, tot = v2f{0.f, 0.f};
-            for (int t = 0; t < NR; ++t) {
-                tot += tau[t];
-                if (t < Lk)
-                    pre += tau[t];
-                if (t > Lk)
-                    post += tau[t];
-            }
-            if (lane < R) {
-                sLam[lane] = lam;
-                sEin[lane] = cexp_f(lam + pre);
-                sDout[lane] = cexp_f(sig + post);
-                sV[lane] = cexp_f(sig);
-                for (int st = 0; st < NR; ++st) {
-                    if (st < Lk) {
-                        v2f z = lam;
-                        for (int t = st + 1; t < Lk; ++t)
-                            z += tau[t];
-                        sU[lane * NR + st] = cexp_f(z);
-                    }
-                }
-            }
-            if (lane == 0)
-                sDecay[0] = cexp_f(tot);
-            seg_log += tot;
-        }
-
-        // ---- stage 2 (all): chunk inputs into LDS planes, x into registers.
+        // ---- stage: chunk inputs into LDS, x into registers.
         for (int i = 0; i < LOADS; ++i) {
-            const int e = i * kThreads + tid;
-            const int row = e >> 5;
-            const int n = (e & 31) * 2;
-            const v4f vb = pB[i];
+            const int row = 16 * i + (tid >> 5);
+            *(v4f *)&sB[row * LDI + 2 * ncol] = pB[i];
             if (FULL) {
                 const v4f vc = pC[i];
-                *(v2f *)&sBre[row * LDB + n] = v2f{vb.x, vb.z};
-                *(v2f *)&sBim[row * LDB + n] = v2f{vb.y, vb.w};
-                *(v2f *)&sCre[row * LDB + n] = v2f{vc.x, vc.z};
-                *(v2f *)&sCim[row * LDB + n] = v2f{vc.y, vc.w};
+                *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
+                const v2f e = cmul(sW[row], sK[(row >> 4) * (NR + 1)]);  // exp(Lam[row])
+                const v2f c0 = cmul(e, v2f{vc.x, vc.y}), c1 = cmul(e, v2f{vc.z, vc.w});
+                *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
             }
-            sTre[n * LDT + row] = vb.x;
-            sTim[n * LDT + row] = vb.y;
-            sTre[(n + 1) * LDT + row] = vb.z;
-            sTim[(n + 1) * LDT + row] = vb.w;
         }
-        v2f X[NR][4];
+        v2f X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
                 X[q][j] = pX[q][j];
+        if (FULL && NSPLIT > 0 && tid < NSPLIT * 64 * 2) {
+            const int slot = NWHOLE * 64 + (tid & (NSPLIT * 64 - 1));
+            if (tid < NSPLIT * 64)
+                sMre[slot] = v4f{0.f, 0.f, 0.f, 0.f};
+            else
+                sMim[slot] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
         block_sync();
-        if (c + 1 < c_end)
+        const bool more = c + 1 < c_end;
+        if (more)
             fetch(c + 1);
 
         v4f Y[NR];
+        for (int lt = 0; lt < NR; ++lt)
+            Y[lt] = v4f{0.f, 0.f, 0.f, 0.f};
         if (FULL) {
-            // ---- phase 1a: M tiles = (B C^T)^T o L^T, produced round-robin by the waves.
-            for (int k = w; k < NT; k += 8) {
-                int st, lt;
-                tile_pair(k, NR, st, lt);
+            // ---- phase 1a: M tiles. Whole tiles k < NWHOLE by wave k; the others as
+            // two K halves accumulated into LDS (two adds onto zero: order-free).
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                const int st = tile_st(k, NR), lt = tile_lt(k, NR);
+                int q0 = 0, q1 = kNPad / 16;
+                if (k < NWHOLE) {
+                    if (w != k)
+                        continue;
+                } else {
+                    const int half = w - 2 * (k - NWHOLE);
+                    if (half != 0 && half != 1)
+                        continue;
+                    q0 = 2 * half;
+                    q1 = q0 + 2;
+                }
+                // G^T[s][l] = sum_n B[s][n] C[l][n]: re = Bre Cre - Bim Cim,
+                // im = Bre Cim + Bim Cre (the second sum kept apart to avoid negations).
                 v4f gre = v4f{0.f, 0.f, 0.f, 0.f}, gim = v4f{0.f, 0.f, 0.f, 0.f};
-                for (int q = 0; q < kNPad / 16; ++q) {
-                    const int col = 16 * q + 4 * Lk;
-                    const v4f bre = *(const v4f *)&sBre[(16 * st + Lr) * LDB + col];
-                    const v4f bim = *(const v4f *)&sBim[(16 * st + Lr) * LDB + col];
-                    const v4f cre = *(const v4f *)&sCre[(16 * lt + Lr) * LDB + col];
-                    const v4f cim = *(const v4f *)&sCim[(16 * lt + Lr) * LDB + col];
+                v4f gsub = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int q = q0; q < q1; ++q) {
+                    const int col = 2 * (16 * q + 4 * Lk);
+                    const float *bp = &sB[(16 * st + Lr) * LDI + col];
+                    const float *cp = &sC[(16 * lt + Lr) * LDI + col];
+                    const v4f b01 = *(const v4f *)bp, b23 = *(const v4f *)(bp + 4);
+                    const v4f c01 = *(const v4f *)cp, c23 = *(const v4f *)(cp + 4);
+                    const float bre[4] = {b01.x, b01.z, b23.x, b23.z};
+                    const float bim[4] = {b01.y, b01.w, b23.y, b23.w};
+                    const float cre[4] = {c01.x, c01.z, c23.x, c23.z};
+                    const float cim[4] = {c01.y, c01.w, c23.y, c23.w};
                     for (int j = 0; j < 4; ++j) {
                         gre = mfma_16x16x4(bre[j], cre[j], gre);
-                        gre = mfma_16x16x4(bim[j], -cim[j], gre);
+                        gsub = mfma_16x16x4(bim[j], cim[j], gsub);
                         gim = mfma_16x16x4(bre[j], cim[j], gim);
                         gim = mfma_16x16x4(bim[j], cre[j], gim);
                     }
                 }
+                gre -= gsub;
                 // Accumulator element r of this lane: s = 16 st + 4 Lk + r, l = 16 lt + Lr.
-                const int l = 16 * lt + Lr;
                 v4f mre, mim;
-                for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * st + 4 * Lk + r;
-                    v2f L;
-                    if (st == lt) {
-                        const bool causal = Lr >= 4 * Lk + r;
-                        const v2f dl = causal ? sLam[l] - sLam[s] : v2f{0.f, 0.f};
-                        L = cexp_f(dl);
-                        if (!causal)
-                            L = v2f{0.f, 0.f};
-                    } else {
-                        L = cmul(sU[l * NR + st], sV[s]);
+                if (st == lt) {
+                    const v4f lre = sLdre[st * 64 + lane], lim = sLdim[st * 64 + lane];
+                    for (int r = 0; r < 4; ++r) {
+                        mre[r] = gre[r] * lre[r] - gim[r] * lim[r];
+                        mim[r] = -(gre[r] * lim[r] + gim[r] * lre[r]);
                     }
-                    const v2f m = cmul(v2f{gre[r], gim[r]}, L);
-                    mre[r] = m.x;
-                    mim[r] = m.y;
+                } else {
+                    const v2f wk = cmul(sW[16 * lt + Lr], sK[st * NR + lt]);
+                    for (int r = 0; r < 4; ++r) {
+                        const v2f L = cmul(wk, sV[16 * st + 4 * Lk + r]);
+                        mre[r] = gre[r] * L.x - gim[r] * L.y;
+                        mim[r] = -(gre[r] * L.y + gim[r] * L.x);
+                    }
                 }
-                sMre[k * 64 + lane] = mre;
-                sMim[k * 64 + lane] = mim;
+                if (k < NWHOLE) {
+                    sMre[k * 64 + lane] = mre;
+                    sMim[k * 64 + lane] = mim;
+                } else {
+                    for (int r = 0; r < 4; ++r) {
+                        lds_add(&((float *)sMre)[(k * 64 + lane) * 4 + r], mre[r]);
+                        lds_add(&((float *)sMim)[(k * 64 + lane) * 4 + r], mim[r]);
+                    }
+                }
             }
 
-            // ---- phase 1b: state-to-output term Re(C' H) with C' = exp(Lam) C, this
-            // wave's half of the state rows.
-            for (int lt = 0; lt < NR; ++lt) {
-                Y[lt] = v4f{0.f, 0.f, 0.f, 0.f};
-                const v2f e = sEin[16 * lt + Lr];
+            // ---- phase 1b: Re(C' H) over this wave's half of the state rows; H is the
+            // B operand straight from its accumulator layout.
+            for (int lt = 0; lt < NR; ++lt)
                 for (int i = 0; i < 2; ++i) {
-                    const int col = 16 * (2 * nh + i) + 4 * Lk;
-                    const v4f cre = *(const v4f *)&sCre[(16 * lt + Lr) * LDB + col];
-                    const v4f cim = *(const v4f *)&sCim[(16 * lt + Lr) * LDB + col];
+                    const float *pp = &sP[(16 * lt + Lr) * LDI + 2 * (16 * (2 * nh + i) + 4 * Lk)];
+                    const v4f a01 = *(const v4f *)pp, a23 = *(const v4f *)(pp + 4);
+                    const float are[4] = {a01.x, a01.z, a23.x, a23.z};
+                    const float aim[4] = {a01.y, a01.w, a23.y, a23.w};
                     for (int r = 0; r < 4; ++r) {
-                        const float ar = cre[r] * e.x - cim[r] * e.y;
-                        const float ain = -(cre[r] * e.y + cim[r] * e.x);
-                        Y[lt] = mfma_16x16x4(ar, Hre[i][r], Y[lt]);
-                        Y[lt] = mfma_16x16x4(ain, Him[i][r], Y[lt]);
+                        Y[lt] = mfma_16x16x4(are[r], Hre[i][r], Y[lt]);
+                        Y[lt] = mfma_16x16x4(aim[r], Him[i][r], Y[lt]);
                     }
                 }
-            }
         }
 
-        // ---- phase 1c: H = exp(sum a) H + B^T (decay' o X).
+        // ---- phase 1c: H = exp(sum a) H + B^T (decay' o x).
         {
             const v2f g = sDecay[0];
             for (int i = 0; i < 2; ++i)
@@ -380,46 +492,61 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     xs[j] = cmul(sDout[16 * q + 4 * Lk + j], X[q][j]);
                 for (int i = 0; i < 2; ++i) {
                     const int n = 16 * (2 * nh + i) + Lr;
-                    const v4f tre = *(const v4f *)&sTre[n * LDT + 16 * q + 4 * Lk];
-                    const v4f tim = *(const v4f *)&sTim[n * LDT + 16 * q + 4 * Lk];
                     for (int j = 0; j < 4; ++j) {
-                        Hre[i] = mfma_16x16x4(tre[j], xs[j].x, Hre[i]);
-                        Hre[i] = mfma_16x16x4(tim[j], -xs[j].y, Hre[i]);
-                        Him[i] = mfma_16x16x4(tre[j], xs[j].y, Him[i]);
-                        Him[i] = mfma_16x16x4(tim[j], xs[j].x, Him[i]);
+                        const v2f bv = *(const v2f *)&sB[(16 * q + 4 * Lk + j) * LDI + 2 * n];
+                        Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
+                        Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
+                        Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
+                        Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
                     }
                 }
             }
         }
+        if (more && w == 0)
+            scan(c + 1);
         block_sync();
 
+        // ---- phase 2: intra-chunk term Re(M X) = Mre Xre + (-Mim) Xim; the tiles of a
+        // column tile are split between its two waves by parity. Then the next
+        // chunk's decay factors.
         if (FULL) {
-            // ---- phase 2: intra-chunk term Re(M X); tiles split between the two
-            // waves that share this column tile.
-            for (int k = nh; k < NT; k += 2) {
-                int st, lt;
-                tile_pair(k, NR, st, lt);
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                if ((k & 1) != nh)
+                    continue;
+                const int st = tile_st(k, NR), lt = tile_lt(k, NR);
                 const v4f mre = sMre[k * 64 + lane];
                 const v4f mim = sMim[k * 64 + lane];
                 for (int r = 0; r < 4; ++r) {
                     Y[lt] = mfma_16x16x4(mre[r], X[st][r].x, Y[lt]);
-                    Y[lt] = mfma_16x16x4(mim[r], -X[st][r].y, Y[lt]);
+                    Y[lt] = mfma_16x16x4(mim[r], X[st][r].y, Y[lt]);
                 }
             }
-            // Row tile lt is finished and stored by the wave with nh == lt % 2.
-            for (int lt = 0; lt < NR; ++lt)
-                if ((lt & 1) != nh)
-                    sYx[(dtl * NR + lt) * 64 + lane] = Y[lt];
-            block_sync();
-            for (int lt = 0; lt < NR; ++lt) {
-                if ((lt & 1) != nh)
-                    continue;
-                const v4f o = sYx[(dtl * NR + lt) * 64 + lane];
-                for (int r = 0; r < 4; ++r) {
-                    const int l = 16 * lt + 4 * Lk + r;
-                    if (l < rows && dvalid)
-                        p.y[(row0 + (int64_t)(t0 + l) * p.H) * p.D + dcol] = Y[lt][r] + o[r];
-                }
+            // Row tile lt is finished and stored by the wave with nh == lt % 2; each wave
+            // hands its partial sums of the other tiles over through LDS.
+            for (int j = 0; j < (NR + 1) / 2; ++j) {
+                const int lt = 2 * j + 1 - nh;  // a tile this wave does not own
+                if (lt < NR)
+                    sYx[(dtl * NR + lt) * 64 + lane] = nh ? Y[2 * j] : Y[2 * j + 1 < NR ? 2 * j + 1 : 0];
+            }
+        }
+        if (more)
+            factors();
+        block_sync();
+
+        if (FULL) {
+            // Straight-line stores (a tile this wave does not own is aimed past the
+            // buffer), so the wait counters stay exact across the loop.
+            const buf_t bY = make_buf(p.y + r0 * p.D + db * kDBlock,
+                                      (uint32_t)(rows - 1) * yrow + dsl * 4u);
+            for (int j = 0; j < (NR + 1) / 2; ++j) {
+                const int lt = 2 * j + nh;
+                const bool own = lt < NR;
+                const v4f mine = nh && 2 * j + 1 < NR ? Y[2 * j + 1] : Y[2 * j];
+                const v4f o = sYx[(dtl * NR + (own ? lt : 0)) * 64 + lane];
+                const uint32_t off = own ? offY + (uint32_t)(16 * lt) * yrow : kOut;
+                for (int r = 0; r < 4; ++r)
+                    buf_store1(bY, off + (uint32_t)r * yrow, mine[r] + o[r]);
             }
         }
     }

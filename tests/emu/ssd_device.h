@@ -49,7 +49,7 @@ struct dim3 {
 namespace emu {
 
 enum { RUN = 0, AT_MFMA, AT_BARRIER, AT_SHFL, DONE };
-enum { SH_UP16 = 0, SH_DOWN16, SH_IDX };
+enum { SH_SHR = 0, SH_SHL, SH_READ };
 
 struct Fiber {
     void *sp;
@@ -172,13 +172,21 @@ static void resolve_wave(int w, bool &progress)
         for (int l = 0; l < 64; ++l) {
             Fiber &f = g_f[lo + l];
             int src = l;
-            if (mode == SH_UP16)
-                src = (l & 15) >= f.arg ? l - f.arg : l;
-            else if (mode == SH_DOWN16)
-                src = (l & 15) + f.arg < 16 ? l + f.arg : l;
-            else
-                src = lo + (f.arg & 63) - lo;
-            f.sr = g_f[lo + src].sv;
+            bool zero = false;
+            if (mode == SH_SHR) {
+                zero = (l & 15) < f.arg;
+                src = l - f.arg;
+            } else if (mode == SH_SHL) {
+                zero = (l & 15) + f.arg >= 16;
+                src = l + f.arg;
+            } else {
+                if (f.arg != g_f[lo].arg) {
+                    fprintf(stderr, "emu: lane_read with a non-uniform source lane\n");
+                    abort();
+                }
+                src = f.arg & 63;
+            }
+            f.sr = zero ? 0.f : g_f[lo + src].sv;
         }
     }
     for (int l = 0; l < 64; ++l)
@@ -278,9 +286,58 @@ SSD_DEVICE float emu_shfl(float v, int mode, int arg)
     return emu::g_f[emu::g_cur].sr;
 }
 
-SSD_DEVICE float shfl_up16(float v, int d) { return emu_shfl(v, emu::SH_UP16, d); }
-SSD_DEVICE float shfl_down16(float v, int d) { return emu_shfl(v, emu::SH_DOWN16, d); }
-SSD_DEVICE float shfl_idx(float v, int src) { return emu_shfl(v, emu::SH_IDX, src); }
+template <int n>
+SSD_DEVICE float row_shr(float v) { return emu_shfl(v, emu::SH_SHR, n); }
+template <int n>
+SSD_DEVICE float row_shl(float v) { return emu_shfl(v, emu::SH_SHL, n); }
+SSD_DEVICE float lane_read(float v, int src) { return emu_shfl(v, emu::SH_READ, src); }
+SSD_DEVICE float uniform(float v) { return v; }
+
+// Buffer resources: an access must lie wholly inside [0, bytes) or wholly
+// outside it (outside reads zero, outside stores are dropped); a straddling
+// access is a layout error and aborts.
+struct buf_t {
+    const char *base;
+    uint32_t n;
+};
+SSD_DEVICE buf_t make_buf(const void *base, uint32_t bytes) { return buf_t{(const char *)base, bytes}; }
+SSD_DEVICE bool emu_buf_in(buf_t r, uint32_t off, uint32_t sz)
+{
+    if ((uint64_t)off + sz <= r.n)
+        return true;
+    if (off < r.n) {
+        fprintf(stderr, "emu: buffer access straddles the end (off %u size %u bytes %u)\n", off, sz, r.n);
+        abort();
+    }
+    return false;
+}
+SSD_DEVICE v4f buf_load4(buf_t r, uint32_t off)
+{
+    v4f v = {0.f, 0.f, 0.f, 0.f};
+    if (emu_buf_in(r, off, 16))
+        memcpy(&v, r.base + off, 16);
+    return v;
+}
+SSD_DEVICE v2f buf_load2(buf_t r, uint32_t off)
+{
+    v2f v = {0.f, 0.f};
+    if (emu_buf_in(r, off, 8))
+        memcpy(&v, r.base + off, 8);
+    return v;
+}
+SSD_DEVICE float buf_load1(buf_t r, uint32_t off)
+{
+    float v = 0.f;
+    if (emu_buf_in(r, off, 4))
+        memcpy(&v, r.base + off, 4);
+    return v;
+}
+SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
+{
+    if (emu_buf_in(r, off, 4))
+        memcpy((char *)r.base + off, &v, 4);
+}
+SSD_DEVICE void lds_add(float *p, float v) { *p += v; }
 
 SSD_DEVICE void block_sync()
 {
