@@ -48,6 +48,10 @@ SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
 }
 
+// Keeps the instruction scheduler from moving anything across this point (used to
+// hold a software pipeline's loads ahead of the MFMAs that consume older ones).
+SSD_DEVICE void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Shared-memory float accumulate (ds_add_f32).
 SSD_DEVICE void lds_add(float *p, float v) { atomicAdd(p, v); }
 SSD_DEVICE int thread_id() { return (int)threadIdx.x; }

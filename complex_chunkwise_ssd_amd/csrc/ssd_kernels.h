@@ -25,16 +25,45 @@
 #include <ssd_device.h>
 #include <ssd_plan.h>
 
+#include <type_traits>
+
 namespace ssd {
 
 SSD_DEVICE float softplus_f(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
 
 SSD_DEVICE v2f cmul(v2f a, v2f b) { return v2f{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
 
+// sin and cos by Cody and Waite's additive range reduction (x - k pi/2 with pi/2
+// split into three float parts, each step one fused multiply-add) followed by
+// the Taylor series of sin and cos on |r| <= pi/4, truncated after r^9 and r^10
+// (truncation error below 2e-9). Absolute error about 7e-8 for |x| up to 1e5,
+// far beyond the phases the scan produces.
+SSD_DEVICE void sincos_cw(float x, float *sp, float *cp)
+{
+    const float k = rintf(x * 0x1.45f306p-1f);  // nearest multiple of pi/2
+    float r = fmaf(-k, 0x1.921fb6p+0f, x);
+    r = fmaf(-k, -0x1.777a5cp-25f, r);
+    r = fmaf(-k, -0x1.ee59dap-50f, r);
+    const float r2 = r * r;
+    float ps = fmaf(r2, 0x1.71de3ap-19f, -0x1.a01a02p-13f);  // 1/9!, -1/7!
+    ps = fmaf(r2, ps, 0x1.111112p-7f);                       // 1/5!
+    ps = fmaf(r2, ps, -0x1.555556p-3f);                      // -1/3!
+    const float s = fmaf(r * r2, ps, r);
+    float pc = fmaf(r2, -0x1.27e4fcp-22f, 0x1.a01a02p-16f);  // -1/10!, 1/8!
+    pc = fmaf(r2, pc, -0x1.6c16c2p-10f);                     // -1/6!
+    pc = fmaf(r2, pc, 0x1.555556p-5f);                       // 1/4!
+    pc = fmaf(r2, pc, -0.5f);                                // -1/2!
+    const float c = fmaf(r2, pc, 1.0f);
+    const int q = (int)k;
+    const float sv = (q & 1) ? c : s, cv = (q & 1) ? s : c;
+    *sp = (q & 2) ? -sv : sv;
+    *cp = ((q + 1) & 2) ? -cv : cv;
+}
+
 SSD_DEVICE v2f cexp_f(v2f z)
 {
     float s, c;
-    sincosf(z.y, &s, &c);
+    sincos_cw(z.y, &s, &c);
     const float m = expf(z.x);
     return v2f{m * c, m * s};
 }
@@ -88,6 +117,16 @@ SSD_KERNEL(256) void copy_state_kernel(const float *src, float *dst, int64_t n)
 }
 
 // ------------------------------------------------------------------ the scan
+
+// Calls f(std::integral_constant<int, i>) for i = B .. E-1 (compile-time loop).
+template <int B, int E, class F>
+SSD_DEVICE void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // Causal 16x16 tile pair (st <= lt) of tile index k: the nr diagonal tiles
 // first, then the strictly lower ones by increasing lt.
@@ -238,22 +277,52 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     v4f pB[LOADS], pC[LOADS];
     float pdt = 0.f;
     v2f pX[NR][4];
-    auto fetch = [&](int c) {
-        const uint32_t rows = (uint32_t)rows_of(c);
-        const int64_t r0 = tok0(c);
-        const buf_t bB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
-        const buf_t bC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
-        const buf_t bX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
-        const buf_t bT = make_buf(p.dt + r0, (rows - 1) * drow + 4u);
-        for (int i = 0; i < LOADS; ++i) {
-            pB[i] = buf_load4(bB, offB + (uint32_t)(16 * i) * brow);
-            if (FULL)
-                pC[i] = buf_load4(bC, offB + (uint32_t)(16 * i) * brow);
+    // The next chunk's loads are spread over the MFMA steps of phase 1 (a burst of
+    // them would hold each wave's in-order issue). Item i < LOADS: a B_t block;
+    // then (FULL) the C_t blocks; then x at (q, j).
+    constexpr int NLOAD = (FULL ? 2 : 1) * LOADS + 4 * NR;
+    buf_t nbB, nbC, nbX;
+    // Chunk c's buffers; past the segment's last chunk they are empty, so the loads
+    // still issue (keeping the wait counters exact) but read zero.
+    auto fetch_begin = [&](int c) {
+        if (c < c_end) {
+            const uint32_t rows = (uint32_t)rows_of(c);
+            const int64_t r0 = tok0(c);
+            nbB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+            nbC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+            nbX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
+        } else {
+            nbB = make_buf(p.Bt, 0u);
+            nbC = make_buf(p.Ct, 0u);
+            nbX = make_buf(p.x, 0u);
         }
+    };
+    auto fetch_item = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < LOADS) {
+            pB[i] = buf_load4(nbB, offB + (uint32_t)(16 * i) * brow);
+        } else if constexpr (FULL && i < 2 * LOADS) {
+            pC[i - LOADS] = buf_load4(nbC, offB + (uint32_t)(16 * (i - LOADS)) * brow);
+        } else if constexpr (i < NLOAD) {
+            constexpr int x = i - (FULL ? 2 : 1) * LOADS, q = x >> 2, j = x & 3;
+            pX[q][j] = buf_load2(nbX, offX + (uint32_t)(16 * q + j) * xrow);
+        }
+    };
+    auto fetch = [&](int c) {
+        fetch_begin(c);
+        static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
+    };
+    // FULL: the B_t and C_t items go out with the Re(C' H) steps of phase 1 and the x
+    // items with the Re(M X) steps of phase 2 (x of the next chunk then shares no
+    // registers' lifetime with phase 1). State-only: everything with the state steps.
+    constexpr int NBC = (FULL ? 2 : 1) * LOADS;
+    constexpr int PER_Y = FULL ? (NBC + 2 * NR - 1) / (2 * NR) : 0;
+    constexpr int PER_S = FULL ? 0 : (NLOAD + 2 * NR - 1) / (2 * NR);
+    // The step logits of chunk c (wave 0 scans them), loaded a phase ahead of the rest.
+    auto fetch_dt = [&](int c) {
+        const buf_t bT = c < c_end ? make_buf(p.dt + tok0(c), (uint32_t)(rows_of(c) - 1) * drow + 4u)
+                                   : make_buf(p.dt, 0u);
         pdt = buf_load1(bT, w == 0 ? (uint32_t)lane * drow : kOut);
-        for (int q = 0; q < NR; ++q)
-            for (int j = 0; j < 4; ++j)
-                pX[q][j] = buf_load2(bX, offX + (uint32_t)(16 * q + j) * xrow);
     };
 
     // Wave 0: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
@@ -324,18 +393,19 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             if (FULL && ri < R)
                 sW[ri] = cexp_f(sLam[ri]);
         } else if (role == 1) {
-            if (FULL && ri < NR * NR) {
-                // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before lt
-                const int st = ri / NR, lt = ri % NR;
-                if (st <= lt) {
-                    v2f z = v2f{0.f, 0.f};
-                    for (int t = 0; t < NR; ++t)
-                        if (st < lt ? (t > st && t < lt) : t < lt)
-                            z += sTau[t];
-                    sK[ri] = cexp_f(z);
-                }
-            } else if (ri == 63) {
-                sDecay[0] = cexp_f(sTau[NR]);
+            // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before
+            // lt; slot NR * NR: the whole chunk (the decay of the state).
+            const int st = ri / NR, lt = ri % NR;
+            if (ri <= NR * NR && (ri == NR * NR || (FULL && st <= lt))) {
+                v2f z = v2f{0.f, 0.f};
+                for (int t = 0; t < NR; ++t)
+                    if (ri == NR * NR || (st < lt ? (t > st && t < lt) : t < lt))
+                        z += sTau[t];
+                const v2f e = cexp_f(z);
+                if (ri == NR * NR)
+                    sDecay[0] = e;
+                else
+                    sK[ri] = e;
             }
         } else if (role == 2) {
             if (ri < R) {
@@ -354,6 +424,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
     if (c_begin < c_end) {
         fetch(c_begin);
+        fetch_dt(c_begin);
         if (w == 0)
             scan(c_begin);
         block_sync();
@@ -390,8 +461,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         }
         block_sync();
         const bool more = c + 1 < c_end;
-        if (more)
-            fetch(c + 1);
+        fetch_dt(c + 1);
+        fetch_begin(c + 1);
 
         v4f Y[NR];
         for (int lt = 0; lt < NR; ++lt)
@@ -399,45 +470,43 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         if (FULL) {
             // ---- phase 1a: M tiles. Whole tiles k < NWHOLE by wave k; the others as
             // two K halves accumulated into LDS (two adds onto zero: order-free).
-#pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                const int st = tile_st(k, NR), lt = tile_lt(k, NR);
-                int q0 = 0, q1 = kNPad / 16;
-                if (k < NWHOLE) {
-                    if (w != k)
-                        continue;
-                } else {
-                    const int half = w - 2 * (k - NWHOLE);
-                    if (half != 0 && half != 1)
-                        continue;
-                    q0 = 2 * half;
-                    q1 = q0 + 2;
-                }
+            auto produce = [&](auto kc, auto q0c, auto q1c) {
+                constexpr int k = decltype(kc)::value;
+                constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
                 // G^T[s][l] = sum_n B[s][n] C[l][n]: re = Bre Cre - Bim Cim,
                 // im = Bre Cim + Bim Cre (the second sum kept apart to avoid negations).
                 v4f gre = v4f{0.f, 0.f, 0.f, 0.f}, gim = v4f{0.f, 0.f, 0.f, 0.f};
                 v4f gsub = v4f{0.f, 0.f, 0.f, 0.f};
-                for (int q = q0; q < q1; ++q) {
-                    const int col = 2 * (16 * q + 4 * Lk);
-                    const float *bp = &sB[(16 * st + Lr) * LDI + col];
-                    const float *cp = &sC[(16 * lt + Lr) * LDI + col];
-                    const v4f b01 = *(const v4f *)bp, b23 = *(const v4f *)(bp + 4);
-                    const v4f c01 = *(const v4f *)cp, c23 = *(const v4f *)(cp + 4);
-                    const float bre[4] = {b01.x, b01.z, b23.x, b23.z};
-                    const float bim[4] = {b01.y, b01.w, b23.y, b23.w};
-                    const float cre[4] = {c01.x, c01.z, c23.x, c23.z};
-                    const float cim[4] = {c01.y, c01.w, c23.y, c23.w};
-                    for (int j = 0; j < 4; ++j) {
+                constexpr int Q0 = decltype(q0c)::value, Q1 = decltype(q1c)::value;
+                // operand blocks of half-step h (B and C rows, two n each), in flight one
+                // half-step ahead
+                v4f ob[2][2];
+                auto load = [&](int hs, v4f *o) {
+                    const int col = 2 * (16 * (hs >> 1) + 4 * Lk + 2 * (hs & 1));
+                    o[0] = *(const v4f *)&sB[(16 * st + Lr) * LDI + col];
+                    o[1] = *(const v4f *)&sC[(16 * lt + Lr) * LDI + col];
+                };
+                load(2 * Q0, ob[0]);
+                static_for<2 * Q0, 2 * Q1>([&](auto hc) {
+                    constexpr int hs = decltype(hc)::value, cur = hs & 1;
+                    if constexpr (hs + 1 < 2 * Q1)
+                        load(hs + 1, ob[cur ^ 1]);
+                    sched_fence();
+                    const v4f bb = ob[cur][0], cc = ob[cur][1];
+                    const float bre[2] = {bb.x, bb.z}, bim[2] = {bb.y, bb.w};
+                    const float cre[2] = {cc.x, cc.z}, cim[2] = {cc.y, cc.w};
+                    for (int j = 0; j < 2; ++j) {
                         gre = mfma_16x16x4(bre[j], cre[j], gre);
                         gsub = mfma_16x16x4(bim[j], cim[j], gsub);
                         gim = mfma_16x16x4(bre[j], cim[j], gim);
                         gim = mfma_16x16x4(bim[j], cre[j], gim);
                     }
-                }
+                    sched_fence();
+                });
                 gre -= gsub;
                 // Accumulator element r of this lane: s = 16 st + 4 Lk + r, l = 16 lt + Lr.
                 v4f mre, mim;
-                if (st == lt) {
+                if constexpr (st == lt) {
                     const v4f lre = sLdre[st * 64 + lane], lim = sLdim[st * 64 + lane];
                     for (int r = 0; r < 4; ++r) {
                         mre[r] = gre[r] * lre[r] - gim[r] * lim[r];
@@ -451,7 +520,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                         mim[r] = -(gre[r] * L.y + gim[r] * L.x);
                     }
                 }
-                if (k < NWHOLE) {
+                if constexpr (k < NWHOLE) {
                     sMre[k * 64 + lane] = mre;
                     sMim[k * 64 + lane] = mim;
                 } else {
@@ -460,21 +529,51 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                         lds_add(&((float *)sMim)[(k * 64 + lane) * 4 + r], mim[r]);
                     }
                 }
-            }
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I2 = std::integral_constant<int, 2>;
+            using I4 = std::integral_constant<int, kNPad / 16>;
+            static_for<0, NT>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NWHOLE) {
+                    if (w == k)
+                        produce(kc, I0{}, I4{});
+                } else {
+                    if (w == 2 * (k - NWHOLE))
+                        produce(kc, I0{}, I2{});
+                    else if (w == 2 * (k - NWHOLE) + 1)
+                        produce(kc, I2{}, I4{});
+                }
+            });
 
             // ---- phase 1b: Re(C' H) over this wave's half of the state rows; H is the
             // B operand straight from its accumulator layout.
-            for (int lt = 0; lt < NR; ++lt)
-                for (int i = 0; i < 2; ++i) {
+            {
+                v4f oa[2][2];
+                auto load = [&](int g, v4f *o) {  // step g = (lt, i)
+                    const int lt = g >> 1, i = g & 1;
                     const float *pp = &sP[(16 * lt + Lr) * LDI + 2 * (16 * (2 * nh + i) + 4 * Lk)];
-                    const v4f a01 = *(const v4f *)pp, a23 = *(const v4f *)(pp + 4);
+                    o[0] = *(const v4f *)pp;
+                    o[1] = *(const v4f *)(pp + 4);
+                };
+                load(0, oa[0]);
+                static_for<0, 2 * NR>([&](auto gc) {
+                    constexpr int g = decltype(gc)::value, lt = g >> 1, i = g & 1, cur = g & 1;
+                    if constexpr (g + 1 < 2 * NR)
+                        load(g + 1, oa[cur ^ 1]);
+                    static_for<g * PER_Y, ((g + 1) * PER_Y < NBC ? (g + 1) * PER_Y : NBC)>(
+                        [&](auto ic) { fetch_item(ic); });
+                    sched_fence();
+                    const v4f a01 = oa[cur][0], a23 = oa[cur][1];
                     const float are[4] = {a01.x, a01.z, a23.x, a23.z};
                     const float aim[4] = {a01.y, a01.w, a23.y, a23.w};
                     for (int r = 0; r < 4; ++r) {
                         Y[lt] = mfma_16x16x4(are[r], Hre[i][r], Y[lt]);
                         Y[lt] = mfma_16x16x4(aim[r], Him[i][r], Y[lt]);
                     }
-                }
+                    sched_fence();
+                });
+            }
         }
 
         // ---- phase 1c: H = exp(sum a) H + B^T (decay' o x).
@@ -486,21 +585,39 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     Hre[i][r] = hv.x;
                     Him[i][r] = hv.y;
                 }
-            for (int q = 0; q < NR; ++q) {
-                v2f xs[4];
-                for (int j = 0; j < 4; ++j)
-                    xs[j] = cmul(sDout[16 * q + 4 * Lk + j], X[q][j]);
-                for (int i = 0; i < 2; ++i) {
-                    const int n = 16 * (2 * nh + i) + Lr;
-                    for (int j = 0; j < 4; ++j) {
-                        const v2f bv = *(const v2f *)&sB[(16 * q + 4 * Lk + j) * LDI + 2 * n];
-                        Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
-                        Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
-                        Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
-                        Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
-                    }
+            // operands of group g = (q, i): B at four rows of step q for this wave's state-row
+            // tile i, and (with i = 0) the decay of those rows to the chunk end; in flight
+            // one group ahead
+            v2f ob[2][4], od[2][4];
+            auto load = [&](int g, v2f *bb, v2f *d) {
+                const int q = g >> 1, i = g & 1;
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * q + 4 * Lk + j;
+                    bb[j] = *(const v2f *)&sB[s * LDI + 2 * (16 * (2 * nh + i) + Lr)];
+                    if (i == 0)
+                        d[j] = sDout[s];
                 }
-            }
+            };
+            load(0, ob[0], od[0]);
+            v2f xs[4];
+            static_for<0, 2 * NR>([&](auto gc) {
+                constexpr int g = decltype(gc)::value, q = g >> 1, i = g & 1, cur = g & 1;
+                if constexpr (g + 1 < 2 * NR)
+                    load(g + 1, ob[cur ^ 1], od[q & 1 ^ (i == 1 ? 1 : 0)]);
+                static_for<g * PER_S, (g + 1) * PER_S>([&](auto ic) { fetch_item(ic); });
+                sched_fence();
+                if constexpr (i == 0)
+                    for (int j = 0; j < 4; ++j)
+                        xs[j] = cmul(od[q & 1][j], X[q][j]);
+                for (int j = 0; j < 4; ++j) {
+                    const v2f bv = ob[cur][j];
+                    Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
+                    Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
+                    Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
+                    Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
+                }
+                sched_fence();
+            });
         }
         if (more && w == 0)
             scan(c + 1);
@@ -510,18 +627,40 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         // column tile are split between its two waves by parity. Then the next
         // chunk's decay factors.
         if (FULL) {
-#pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                if ((k & 1) != nh)
-                    continue;
-                const int st = tile_st(k, NR), lt = tile_lt(k, NR);
-                const v4f mre = sMre[k * 64 + lane];
-                const v4f mim = sMim[k * 64 + lane];
-                for (int r = 0; r < 4; ++r) {
-                    Y[lt] = mfma_16x16x4(mre[r], X[st][r].x, Y[lt]);
-                    Y[lt] = mfma_16x16x4(mim[r], X[st][r].y, Y[lt]);
+            auto ydiag = [&](auto nhc) {
+                constexpr int NH = decltype(nhc)::value;
+                constexpr int NK = (NT + 1 - NH) / 2;  // tiles k = NH, NH + 2, ...
+                constexpr int NX = NLOAD - NBC;         // x items of the next chunk
+                constexpr int PER_K = NK > 0 ? (NX + NK - 1) / NK : 0;
+                // M tiles in flight one tile ahead
+                v4f mre[2], mim[2];
+                if constexpr (NK > 0) {
+                    mre[0] = sMre[NH * 64 + lane];
+                    mim[0] = sMim[NH * 64 + lane];
                 }
-            }
+                static_for<0, NK>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value, k = 2 * i + NH, cur = i & 1;
+                    constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
+                    if constexpr (i + 1 < NK) {
+                        mre[cur ^ 1] = sMre[(k + 2) * 64 + lane];
+                        mim[cur ^ 1] = sMim[(k + 2) * 64 + lane];
+                    }
+                    constexpr int a = NBC + i * PER_K, e = NBC + (i + 1) * PER_K;
+                    static_for<a, (e < NLOAD ? e : NLOAD)>([&](auto xc) { fetch_item(xc); });
+                    sched_fence();
+                    for (int r = 0; r < 4; ++r) {
+                        Y[lt] = mfma_16x16x4(mre[cur][r], X[st][r].x, Y[lt]);
+                        Y[lt] = mfma_16x16x4(mim[cur][r], X[st][r].y, Y[lt]);
+                    }
+                    sched_fence();
+                });
+                if constexpr (NK == 0)
+                    static_for<NBC, NLOAD>([&](auto xc) { fetch_item(xc); });
+            };
+            if (nh == 0)
+                ydiag(std::integral_constant<int, 0>{});
+            else
+                ydiag(std::integral_constant<int, 1>{});
             // Row tile lt is finished and stored by the wave with nh == lt % 2; each wave
             // hands its partial sums of the other tiles over through LDS.
             for (int j = 0; j < (NR + 1) / 2; ++j) {

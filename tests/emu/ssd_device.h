@@ -338,6 +338,7 @@ SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
         memcpy((char *)r.base + off, &v, 4);
 }
 SSD_DEVICE void lds_add(float *p, float v) { *p += v; }
+SSD_DEVICE void sched_fence() {}
 
 SSD_DEVICE void block_sync()
 {
