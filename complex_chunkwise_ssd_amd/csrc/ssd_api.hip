@@ -25,7 +25,7 @@ int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64
         return SSD_ERR_ODD_N;
     if (N > SSD_MAX_BLOCK || D > SSD_MAX_BLOCK || chunk > SSD_MAX_BLOCK)
         return SSD_ERR_BLOCK_DIMS;
-    if (N > ssd::kNPad || chunk > 64)
+    if (N > ssd::kNPad)
         return SSD_ERR_UNSUPPORTED;
     // 32-bit token indices, and 32-bit byte offsets inside one chunk of one sequence
     if (T > (1LL << 30) || batch * H > (1LL << 30))
@@ -71,7 +71,7 @@ const char *ssd_status_string(int status)
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
-    case SSD_ERR_UNSUPPORTED: return "size not covered by this build (N <= 64, chunk_size <= 64)";
+    case SSD_ERR_UNSUPPORTED: return "size not covered by this build (N <= 64)";
     default: return "unknown status";
     }
 }
@@ -175,7 +175,7 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     prm.H = (int)H;
     prm.N = (int)N;
     prm.D = (int)D;
-    prm.Q = (int)chunk_size;
+    prm.Q = (int)ssd::block_rows(chunk_size);
     prm.nc = plan.nc;
     prm.P = plan.P;
     prm.spc = plan.spc;

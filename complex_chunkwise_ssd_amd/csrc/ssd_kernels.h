@@ -185,6 +185,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     constexpr int LOADS = R * (kNPad / 2) / kThreads;  // 16-byte loads per thread per B or C tile
     static_assert(LOADS >= 1, "tile too small for the thread count");
     constexpr uint32_t kOut = 0x80000000u;   // a byte offset past every buffer
+    constexpr int kScanWave = 0;             // the wave that scans each chunk's log-decay
 
     SSD_LDS float sB[R * LDI];                // B[s][n] interleaved (re, im)
     SSD_LDS float sC[FULL ? R * LDI : 1];     // C[l][n]
@@ -312,20 +313,19 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         fetch_begin(c);
         static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
     };
-    // FULL: the B_t and C_t items go out with the Re(C' H) steps of phase 1 and the x
+    // FULL: the B_t and C_t items go out with the state steps of phase 1 and the x
     // items with the Re(M X) steps of phase 2 (x of the next chunk then shares no
     // registers' lifetime with phase 1). State-only: everything with the state steps.
     constexpr int NBC = (FULL ? 2 : 1) * LOADS;
-    constexpr int PER_Y = FULL ? (NBC + 2 * NR - 1) / (2 * NR) : 0;
-    constexpr int PER_S = FULL ? 0 : (NLOAD + 2 * NR - 1) / (2 * NR);
-    // The step logits of chunk c (wave 0 scans them), loaded a phase ahead of the rest.
+    constexpr int PER_S = (FULL ? NBC + 2 * NR - 1 : NLOAD + 2 * NR - 1) / (2 * NR);
+    // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
         const buf_t bT = c < c_end ? make_buf(p.dt + tok0(c), (uint32_t)(rows_of(c) - 1) * drow + 4u)
                                    : make_buf(p.dt, 0u);
-        pdt = buf_load1(bT, w == 0 ? (uint32_t)lane * drow : kOut);
+        pdt = buf_load1(bT, w == kScanWave ? (uint32_t)lane * drow : kOut);
     };
 
-    // Wave 0: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
+    // One wave: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
     auto scan = [&](int c) {
         const int rows = rows_of(c);
         const float sp = softplus_f(pdt);
@@ -425,7 +425,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     if (c_begin < c_end) {
         fetch(c_begin);
         fetch_dt(c_begin);
-        if (w == 0)
+        if (w == kScanWave)
             scan(c_begin);
         block_sync();
         factors();
@@ -561,8 +561,6 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     constexpr int g = decltype(gc)::value, lt = g >> 1, i = g & 1, cur = g & 1;
                     if constexpr (g + 1 < 2 * NR)
                         load(g + 1, oa[cur ^ 1]);
-                    static_for<g * PER_Y, ((g + 1) * PER_Y < NBC ? (g + 1) * PER_Y : NBC)>(
-                        [&](auto ic) { fetch_item(ic); });
                     sched_fence();
                     const v4f a01 = oa[cur][0], a23 = oa[cur][1];
                     const float are[4] = {a01.x, a01.z, a23.x, a23.z};
@@ -604,7 +602,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 constexpr int g = decltype(gc)::value, q = g >> 1, i = g & 1, cur = g & 1;
                 if constexpr (g + 1 < 2 * NR)
                     load(g + 1, ob[cur ^ 1], od[q & 1 ^ (i == 1 ? 1 : 0)]);
-                static_for<g * PER_S, (g + 1) * PER_S>([&](auto ic) { fetch_item(ic); });
+                constexpr int SL = FULL ? NBC : NLOAD;  // items the state steps issue
+                static_for<g * PER_S, ((g + 1) * PER_S < SL ? (g + 1) * PER_S : SL)>(
+                    [&](auto ic) { fetch_item(ic); });
                 sched_fence();
                 if constexpr (i == 0)
                     for (int j = 0; j < 4; ++j)
@@ -619,7 +619,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 sched_fence();
             });
         }
-        if (more && w == 0)
+        if (more && w == kScanWave)
             scan(c + 1);
         block_sync();
 
@@ -698,7 +698,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     } else {
         const int64_t sidx = bh * (p.P - 1) + seg;
         out = p.seg_state + sidx * p.N * p.D * 2;
-        if (db == 0 && tid == 0)
+        if (db == 0 && tid == kScanWave * 64)  // the scan wave holds the segment total
             *(v2f *)&p.seg_logdecay[sidx * 2] = seg_log;
     }
     if (out) {

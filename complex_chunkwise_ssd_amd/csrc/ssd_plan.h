@@ -53,10 +53,18 @@ struct Plan {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Tokens the kernel treats as one chunk: chunk_size itself up to 64; a longer
+// chunk is evaluated as consecutive 64-token sub-chunks with the state passed
+// between them, which is the same sum re-associated (the result does not depend
+// on the chunk size beyond rounding) and keeps every block on chip.
+constexpr int kMaxRows = 64;
+inline int64_t block_rows(int64_t chunk_size) { return chunk_size < kMaxRows ? chunk_size : kMaxRows; }
+
 // Sizes are assumed validated (positive, within the supported envelope).
-inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int64_t Q)
+inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk_size)
 {
     Plan p;
+    const int64_t Q = block_rows(chunk_size);
     p.R = Q <= 16 ? 16 : (Q <= 32 ? 32 : 64);
     p.nc = (int)((T + Q - 1) / Q);
     p.ndb = (int)((D + kDBlock - 1) / kDBlock);

@@ -99,8 +99,9 @@ size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, in
  *   dt           (batch, T, H) float32.
  *   chunk_size   1..256; a last chunk shorter than chunk_size is allowed
  *                (T need not be a multiple of it). It sets the span of the
- *                intra-chunk quadratic term; the result does not depend on it
- *                beyond rounding.
+ *                intra-chunk quadratic term, up to 64 tokens: a longer chunk is
+ *                evaluated as 64-token sub-chunks with the state passed between
+ *                them. The result does not depend on chunk_size beyond rounding.
  *   initial_state nullable: (batch, H, N, D) complex64 state s_{-1}; NULL
  *                means zero.
  *   y            out: (batch, T, H, D) float32, the real part of the output.
@@ -110,8 +111,8 @@ size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, in
  *                aligned; may be NULL when that size is 0. Its contents on
  *                entry are ignored.
  * Constraints: N even (SSD_ERR_ODD_N); N, D, chunk_size <= 256
- * (SSD_ERR_BLOCK_DIMS); this build covers N <= 64 and chunk_size <= 64
- * (SSD_ERR_UNSUPPORTED otherwise).
+ * (SSD_ERR_BLOCK_DIMS); this build covers N <= 64 (SSD_ERR_UNSUPPORTED
+ * otherwise).
  * Alignment: B_t and C_t 16 bytes; x, A, initial_state, final_state 8 bytes;
  * dt and y 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 copies initial_state (or

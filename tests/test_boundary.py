@@ -91,6 +91,11 @@ def test_workspace_checks(lib):
     assert _fwd(lib, ws=ctypes.c_void_p(0x200010), ws_n=need, **args) == ssd.SSD_ERR_ALIGN
 
 
+def test_unsupported_state_size(lib):
+    assert _fwd(lib, N=66, D=4) == ssd.SSD_ERR_UNSUPPORTED
+    assert _fwd(lib, N=64, Q=256) != ssd.SSD_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes(lib):
     f = lib.ssd_chunk_forward_workspace_bytes
     # 512 sequences fill the GPU: no segments, no workspace

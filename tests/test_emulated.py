@@ -42,6 +42,8 @@ CASES = [
     (1, 23, 2, 4, 5, 1),       # Q = 1
     (1, 12, 1, 4, 4, 12),      # T == Q
     (3, 7, 1, 2, 2, 64),       # T < Q
+    (1, 300, 1, 8, 8, 128),    # chunk longer than the 64-row block
+    (1, 200, 1, 4, 4, 256),
 ]
 
 

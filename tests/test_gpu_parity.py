@@ -125,8 +125,6 @@ def test_layer_b8_sampled():
 def test_sweep_b4_t8192(Q):
     """Long-context sweep B=4, T=8192, dt ~ N(0.5, 1): sampled sequences against the
     oracle, and every output against the chunk-64 run (one input set for all Q)."""
-    if Q > 64:
-        pytest.skip("chunk_size > 64 is not built yet (SSD_ERR_UNSUPPORTED)")
     w = ssd_inputs.WORKLOADS["sweep_b4_t8192"]
     g = ssd_inputs.layer_case(w["batch"], w["T"], 16, 64, 64, seed=w["seed"], dt_mean=w["dt_mean"],
                               device=DEV)
