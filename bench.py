@@ -45,7 +45,7 @@ def measured_traffic(launch_tokens_heads):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layer0, batch_rows=16):
+def cpu_baseline(layer0, batch_rows=32):
     """The oracle as it stands, on a bounded sample of layer 0: batch rows
     0..batch_rows-1, all heads, full T (host cores, OpenMP over sequences)."""
     import oracle
