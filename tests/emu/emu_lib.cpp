@@ -4,3 +4,10 @@
 #include "../../complex_chunkwise_ssd_amd/csrc/ssd_api.hip"
 
 extern "C" long emu_mfma_count(void) { return emu::g_mfma_count; }
+
+// The kernels' own sin/cos, for an accuracy test against double precision.
+extern "C" void emu_sincos(const float *x, float *s, float *c, long n)
+{
+    for (long i = 0; i < n; ++i)
+        ssd::sincos_cw(x[i], &s[i], &c[i]);
+}

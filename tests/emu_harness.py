@@ -66,6 +66,8 @@ def load(out_dir):
             lib.ssd_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
             lib.ssd_discretise.restype = ctypes.c_int
             lib.emu_mfma_count.restype = ctypes.c_long
+            lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
+            lib.emu_sincos.restype = None
             _lib = lib
     return _lib
 
