@@ -12,10 +12,16 @@ scan(x, A, B_t, C_t, dt, initial_state=None, threads=0, lib=None)
     -> (y complex128 (B,T,H,D), final_state complex128 (B,H,N,D))
 discretise(dt, A, chunk=0, lib=None)
     -> (A_bar complex128 (B,T,H), Lambda complex128 (B,H,nc,chunk) or None)
+scan_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None,
+              initial_state=None, threads=0, lib=None)
+    -> Grads(x, A, B_t, C_t, dt, initial_state): the gradients of
+       sum(grad_y * y.real) + sum(Re(conj(grad_final_state) * final_state)),
+       complex ones as dl/dRe + i dl/dIm (torch's convention), in float64
 """
 
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import subprocess
@@ -51,6 +57,9 @@ def _bind(lib):
     lib.oracle_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p]
     lib.oracle_discretise.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_scan_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, p, p,
+                                         p, p, p, p, p, p, ctypes.c_int]
+    lib.oracle_scan_backward.restype = ctypes.c_int
     return lib
 
 
@@ -135,3 +144,51 @@ def discretise(dt, A, chunk: int = 0, lib=None):
     abar_c = abar[..., 0] + 1j * abar[..., 1]
     lam_c = None if lam is None else lam[..., 0] + 1j * lam[..., 1]
     return abar_c, lam_c
+
+
+Grads = collections.namedtuple("Grads", "x A B_t C_t dt initial_state")
+
+
+def _as_f64_complex(a, shape):
+    a = np.asarray(a.detach().cpu().numpy() if hasattr(a, "detach") else a)
+    if np.iscomplexobj(a):
+        a = np.stack([a.real, a.imag], -1)
+    a = np.ascontiguousarray(a, np.float64)
+    assert a.shape == shape + (2,), (a.shape, shape)
+    return a
+
+
+def scan_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None, initial_state=None,
+                  threads: int = 0, lib=None):
+    lib = lib or load()
+    xf = _as_f32(x, True)
+    Af = _as_f32(A, True)
+    Bf = _as_f32(B_t, True)
+    Cf = _as_f32(C_t, True)
+    dtf = _as_f32(dt)
+    gyf = _as_f32(grad_y)
+    Bsz, T, H, D = xf.shape[:4]
+    N = Bf.shape[3]
+    assert gyf.shape == (Bsz, T, H, D)
+    gff = None
+    if grad_final_state is not None:
+        gff = _as_f32(grad_final_state, True)
+        assert gff.shape == (Bsz, H, N, D, 2)
+    init = None
+    if initial_state is not None:
+        init = _as_f64_complex(initial_state, (Bsz, H, N, D))
+    gx = np.zeros((Bsz, T, H, D, 2))
+    gA = np.zeros((H, 2))
+    gB = np.zeros((Bsz, T, H, N, 2))
+    gC = np.zeros((Bsz, T, H, N, 2))
+    gdt = np.zeros((Bsz, T, H))
+    gi = np.zeros((Bsz, H, N, D, 2))
+    rc = lib.oracle_scan_backward(
+        xf.ctypes.data, Af.ctypes.data, Bf.ctypes.data, Cf.ctypes.data, dtf.ctypes.data,
+        Bsz, T, H, N, D, None if init is None else init.ctypes.data, gyf.ctypes.data,
+        None if gff is None else gff.ctypes.data, gx.ctypes.data, gA.ctypes.data,
+        gB.ctypes.data, gC.ctypes.data, gdt.ctypes.data, gi.ctypes.data, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_backward failed with %d" % rc)
+    c = lambda v: v[..., 0] + 1j * v[..., 1]
+    return Grads(c(gx), c(gA), c(gB), c(gC), gdt, c(gi))

@@ -34,6 +34,20 @@
  *   x  (B, T, H, D)    Bt, Ct (B, T, H, N)    dt (B, T, H)    A (H)
  *   y  (B, T, H, D)    state  (B, H, N, D)
  *
+ * Gradients (oracle_scan_backward) -- reverse-mode differentiation of the same
+ * recurrence, for the backward that the "Extending" guide (Path B Step 3, the
+ * autograd Function) asks of every scan: true upstream gradients for y and
+ * final_state, a gradient for every differentiated input. For a real loss l
+ * and a complex input z the gradient is dl/dRe(z) + i dl/dIm(z) (the value
+ * torch's autograd stores for complex tensors). The forward states are kept
+ * for every step and the adjoint state is walked back from the last token:
+ *   lam  <- lam + conj(C_t) (outer) gy_t          (adjoint of s_t)
+ *   gC_t = sum_d conj(s_t) gy_t,  gB_t = lam conj(x_t),  gx_t = conj(B_t)^T lam
+ *   ga_t = conj(Abar_t) * sum conj(s_{t-1}) lam    (a_t = softplus(dt_t) A)
+ *   gdt_t = Re(conj(A) ga_t) * sigmoid(dt_t),  gA += softplus(dt_t) ga_t
+ *   lam  <- conj(Abar_t) lam
+ * and the gradient of the initial state is the final lam.
+ *
  * Parallelism: the (batch, head) sequences are independent; an OpenMP loop
  * runs them side by side. Within a sequence the loop is the plain recurrence.
  */
@@ -64,7 +78,9 @@ static void store_c(double *p, int64_t i, cplx v)
     p[2 * i + 1] = cimag(v);
 }
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 /* Abar (B,T,H) and, when chunk > 0, the per-chunk inclusive cumulative
  * log-decay Lambda (B,H,nc,chunk). Positions of the last chunk that lie past
@@ -150,6 +166,122 @@ int oracle_scan(const float *x, const float *A, const float *Bt, const float *Ct
                 store_c(final_state, (b * H + h) * N * D + i, s[i]);
         free(s);
     }
+    return failed ? -2 : 0;
+}
+
+/* Gradients of l = sum_t gy_t . Re(y_t) + sum Re(conj(g_final) * final_state)
+ * with respect to x, A, Bt, Ct, dt and the initial state.
+ *   grad_y (B,T,H,D) real; grad_final (B,H,N,D) complex or NULL (zero).
+ *   gx (B,T,H,D), gB and gC (B,T,H,N), g_init (B,H,N,D) complex; gdt (B,T,H);
+ *   gA (H) complex, summed over batch rows in a fixed order.
+ * init_state may be NULL (zero); g_init may be NULL. Returns 0, -1 on bad
+ * arguments, -2 when memory runs out. */
+int oracle_scan_backward(const float *x, const float *A, const float *Bt, const float *Ct,
+                         const float *dt, int64_t Bsz, int64_t T, int64_t H, int64_t N, int64_t D,
+                         const double *init_state, const float *grad_y, const float *grad_final,
+                         double *gx, double *gA, double *gB, double *gC, double *gdt,
+                         double *g_init, int nthreads)
+{
+    if (!x || !A || !Bt || !Ct || !dt || !grad_y || !gx || !gA || !gB || !gC || !gdt ||
+        Bsz <= 0 || T < 0 || H <= 0 || N <= 0 || D <= 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t nseq = Bsz * H;
+    int64_t ND = N * D;
+    cplx *gA_seq = malloc(sizeof(cplx) * (size_t)nseq);
+    if (!gA_seq)
+        return -2;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nseq; ++q) {
+        int64_t b = q / H, h = q % H;
+        /* states[t + 1] = s_t, states[0] = the initial state */
+        cplx *states = malloc(sizeof(cplx) * (size_t)((T + 1) * ND));
+        cplx *lam = malloc(sizeof(cplx) * (size_t)ND);
+        if (!states || !lam) {
+            free(states);
+            free(lam);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        for (int64_t i = 0; i < ND; ++i) {
+            int64_t off = (b * H + h) * ND + i;
+            states[i] = init_state ? init_state[2 * off] + I * init_state[2 * off + 1] : 0.0;
+        }
+        cplx Ah = load_c(A, h);
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * H + h;
+            cplx Abar = cexp(softplus((double)dt[row]) * Ah);
+            const cplx *prev = states + t * ND;
+            cplx *cur = states + (t + 1) * ND;
+            for (int64_t n = 0; n < N; ++n) {
+                cplx bn = load_c(Bt, row * N + n);
+                for (int64_t d = 0; d < D; ++d)
+                    cur[n * D + d] = Abar * prev[n * D + d] + bn * load_c(x, row * D + d);
+            }
+        }
+        for (int64_t i = 0; i < ND; ++i) {
+            int64_t off = (b * H + h) * ND + i;
+            lam[i] = grad_final ? (double)grad_final[2 * off] + I * (double)grad_final[2 * off + 1]
+                                : 0.0;
+        }
+        cplx gA_acc = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            int64_t row = (b * T + t) * H + h;
+            double sp = softplus((double)dt[row]);
+            cplx Abar = cexp(sp * Ah);
+            const cplx *s_t = states + (t + 1) * ND;
+            const cplx *s_prev = states + t * ND;
+            /* y_t = Re(sum_n C_t[n] s_t[n, :]) feeds lam with conj(C_t) gy_t */
+            for (int64_t n = 0; n < N; ++n) {
+                cplx cn = conj(load_c(Ct, row * N + n));
+                for (int64_t d = 0; d < D; ++d)
+                    lam[n * D + d] += cn * (double)grad_y[row * D + d];
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                cplx acc_c = 0.0, acc_b = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    acc_c += conj(s_t[n * D + d]) * (double)grad_y[row * D + d];
+                    acc_b += lam[n * D + d] * conj(load_c(x, row * D + d));
+                }
+                store_c(gC, row * N + n, acc_c);
+                store_c(gB, row * N + n, acc_b);
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                cplx acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += conj(load_c(Bt, row * N + n)) * lam[n * D + d];
+                store_c(gx, row * D + d, acc);
+            }
+            cplx g_abar = 0.0;
+            for (int64_t i = 0; i < ND; ++i)
+                g_abar += conj(s_prev[i]) * lam[i];
+            cplx ga = conj(Abar) * g_abar;
+            gdt[row] = creal(conj(Ah) * ga) * sigmoid((double)dt[row]);
+            gA_acc += sp * ga;
+            for (int64_t i = 0; i < ND; ++i)
+                lam[i] = conj(Abar) * lam[i];
+        }
+        gA_seq[q] = gA_acc;
+        if (g_init)
+            for (int64_t i = 0; i < ND; ++i)
+                store_c(g_init, (b * H + h) * ND + i, lam[i]);
+        free(states);
+        free(lam);
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        cplx acc = 0.0;
+        for (int64_t b = 0; b < Bsz; ++b)
+            acc += gA_seq[b * H + h];
+        store_c(gA, h, acc);
+    }
+    free(gA_seq);
     return failed ? -2 : 0;
 }
 
