@@ -6,11 +6,13 @@ current stream. Importing works without a GPU; calling needs the built library
 and a visible GPU, and fails loudly otherwise (there is no fallback path).
 
     y, final_state = chunk_forward(x, A, B_t, C_t, dt, chunk_size=64)
+    grads = chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None)
     A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
 """
 
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import re
@@ -63,6 +65,11 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                           vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_forward.restype = ctypes.c_int
+        lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
+        lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ssd_chunk_backward.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.restype = ctypes.c_int
@@ -152,6 +159,71 @@ def chunk_forward(x, A, B_t, C_t, dt, chunk_size: int = 64, initial_state=None,
     return y, final_state
 
 
+Grads = collections.namedtuple("Grads", "x A B_t C_t dt initial_state")
+
+
+def backward_workspace_bytes(batch, T, H, N, D, chunk_size) -> int:
+    return int(load_library().ssd_chunk_backward_workspace_bytes(batch, T, H, N, D, chunk_size))
+
+
+def chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None, chunk_size: int = 64,
+                   initial_state=None, want_initial_state_grad: bool = True, out=None,
+                   workspace=None):
+    """Gradients of sum(grad_y * y) + sum(Re(conj(grad_final_state) * final_state))
+    for the forward call with the same inputs, on the current stream.
+
+    grad_y (B,T,H,D) float32; grad_final_state (B,H,N,D) complex64 or None.
+    Returns Grads(x, A, B_t, C_t, dt, initial_state): complex64 gradients as
+    dl/dRe + i dl/dIm (torch's convention), dt's float32; initial_state's is
+    None unless requested. `out` may supply preallocated Grads.
+    """
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a (B, T, H, D) tensor")
+    Bsz, T, H, D = x.shape
+    if not isinstance(B_t, torch.Tensor) or B_t.dim() != 4:
+        raise ValueError("B_t must be a (B, T, H, N) tensor")
+    N = B_t.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(x, "x", torch.complex64, (Bsz, T, H, D), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    _check(B_t, "B_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(C_t, "C_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(dt, "dt", torch.float32, (Bsz, T, H), dev)
+    _check(grad_y, "grad_y", torch.float32, (Bsz, T, H, D), dev)
+    if grad_final_state is not None:
+        _check(grad_final_state, "grad_final_state", torch.complex64, (Bsz, H, N, D), dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    if out is None:
+        c64 = dict(dtype=torch.complex64, device=dev)
+        out = Grads(torch.empty((Bsz, T, H, D), **c64), torch.empty((H,), **c64),
+                    torch.empty((Bsz, T, H, N), **c64), torch.empty((Bsz, T, H, N), **c64),
+                    torch.empty((Bsz, T, H), dtype=torch.float32, device=dev),
+                    torch.empty((Bsz, H, N, D), **c64) if want_initial_state_grad else None)
+    _check(out.x, "grad x", torch.complex64, (Bsz, T, H, D), dev)
+    _check(out.A, "grad A", torch.complex64, (H,), dev)
+    _check(out.B_t, "grad B_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(out.C_t, "grad C_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(out.dt, "grad dt", torch.float32, (Bsz, T, H), dev)
+    if out.initial_state is not None:
+        _check(out.initial_state, "grad initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    ws_n = int(lib.ssd_chunk_backward_workspace_bytes(Bsz, T, H, N, D, chunk_size))
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_backward(_ptr(x), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(dt), Bsz, T, H, N, D,
+                                int(chunk_size), _ptr(initial_state), _ptr(grad_y),
+                                _ptr(grad_final_state), _ptr(out.x), _ptr(out.A), _ptr(out.B_t),
+                                _ptr(out.C_t), _ptr(out.dt), _ptr(out.initial_state),
+                                _ptr(workspace), ws_size, _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_backward")
+    return out
+
+
 def discretise(dt, A, chunk_size: int = 0, want_abar: bool = True):
     """A_bar = exp(softplus(dt) A) (B,T,H) and, if chunk_size > 0, the per-chunk
     running sums of softplus(dt) A (B,H,nc,chunk_size), both complex64."""
@@ -188,3 +260,24 @@ def algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
     """Bytes the scan must move per (token, head): x, B_t, C_t (complex64),
     dt, y (float32) and the final state amortised over T."""
     return 8 * D + 16 * N + 4 + 4 * D + 8 * N * D / T
+
+
+def backward_block_rows(chunk_size: int) -> int:
+    """Tokens the backward evaluates per chunk (the state spacing it stores)."""
+    return min(int(chunk_size), 32)
+
+
+def backward_algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
+    """Real flops the chunkwise gradients need per (token, head) at chunk Q:
+    the forward chunk states B^T X (8ND) and the adjoint's C'^T gy (4ND), each
+    passed between chunks (8ND/Q each); the causal Gram C B^T and its two uses
+    V^T C and V B (8N per pair each); gy x^T and M^T gy (4D per pair each);
+    and the edge terms B G (8ND), x G^T (8ND) and gy H^T (4ND)."""
+    pairs = (Q + 1) / 2
+    return 32 * N * D + 16 * N * D / Q + 24 * N * pairs + 8 * D * pairs
+
+
+def backward_algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
+    """Bytes the gradients must move per (token, head): x, B_t, C_t, dt, grad_y
+    in; grad_x, grad_B_t, grad_C_t, grad_dt out; the state gradients amortised."""
+    return (8 * D + 16 * N + 4 + 4 * D) + (8 * D + 16 * N + 4) + 16 * N * D / T

@@ -3,7 +3,7 @@
 // caller's stream. The library allocates nothing.
 #include "ssd.h"
 
-#include <ssd_kernels.h>
+#include <ssd_bwd_kernels.h>
 
 namespace {
 
@@ -54,6 +54,35 @@ int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs
     return launch_status();
 }
 
+template <int R>
+int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
+{
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false>), dim3((unsigned)seqs), dim3(512), 0,
+                       stream, prm);
+    if (int st = launch_status())
+        return st;
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true>), dim3((unsigned)seqs), dim3(512), 0,
+                       stream, prm);
+    if (int st = launch_status())
+        return st;
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R>), dim3((unsigned)(seqs * prm.nc)), dim3(512), 0,
+                       stream, prm);
+    if (int st = launch_status())
+        return st;
+    hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3(grid_1d(prm.H, 64)), dim3(64), 0, stream,
+                       prm.gA_part, prm.B, prm.H, prm.nc, prm.gA);
+    return launch_status();
+}
+
+int check_backward_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk)
+{
+    if (int st = check_sizes(batch, T, H, N, D, chunk))
+        return st;
+    if (D > 64)
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,7 +100,8 @@ const char *ssd_status_string(int status)
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
-    case SSD_ERR_UNSUPPORTED: return "size not covered by this build (N <= 64)";
+    case SSD_ERR_UNSUPPORTED:
+        return "size not covered by this build (N <= 64; for gradients also D <= 64)";
     default: return "unknown status";
     }
 }
@@ -187,6 +217,88 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     case 32: return launch_scan<32>(prm, plan, seqs, s);
     default: return launch_scan<64>(prm, plan, seqs, s);
     }
+}
+
+size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,
+                                          int64_t D, int64_t chunk_size)
+{
+    if (check_backward_sizes(batch, T, H, N, D, chunk_size) != SSD_OK || batch == 0 || H == 0 ||
+        T == 0)
+        return 0;
+    return ssd::make_bwd_plan(batch, T, H, chunk_size).workspace_bytes;
+}
+
+int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, const ssd_c64 *C_t,
+                       const float *dt, int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                       int64_t chunk_size, const ssd_c64 *initial_state, const float *grad_y,
+                       const ssd_c64 *grad_final_state, ssd_c64 *grad_x, ssd_c64 *grad_A,
+                       ssd_c64 *grad_B_t, ssd_c64 *grad_C_t, float *grad_dt,
+                       ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
+                       ssd_stream_t stream)
+{
+    if (int st = check_backward_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    if (batch == 0 || H == 0)
+        return SSD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (!grad_A)
+        return SSD_ERR_NULL;
+    if (!aligned(grad_A, 8) || (grad_final_state && !aligned(grad_final_state, 8)) ||
+        (grad_initial_state && !aligned(grad_initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    if (T == 0) {
+        if (grad_initial_state) {
+            const int64_t n = batch * H * N * D * 2;
+            hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                               (const float *)grad_final_state, (float *)grad_initial_state, n);
+            if (int st = launch_status())
+                return st;
+        }
+        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3(grid_1d(H, 64)), dim3(64), 0, s,
+                           (const float *)nullptr, (int)batch, (int)H, 0, (float *)grad_A);
+        return launch_status();
+    }
+    if (!x || !A || !B_t || !C_t || !dt || !grad_y || !grad_x || !grad_B_t || !grad_C_t ||
+        !grad_dt)
+        return SSD_ERR_NULL;
+    if (!aligned(x, 8) || !aligned(A, 8) || !aligned(B_t, 8) || !aligned(C_t, 8) ||
+        !aligned(dt, 4) || !aligned(grad_y, 4) || !aligned(grad_x, 8) || !aligned(grad_B_t, 8) ||
+        !aligned(grad_C_t, 8) || !aligned(grad_dt, 4) ||
+        (initial_state && !aligned(initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+        return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return SSD_ERR_ALIGN;
+
+    ssd::BwdParams prm{};
+    prm.x = (const float *)x;
+    prm.A = (const float *)A;
+    prm.Bt = (const float *)B_t;
+    prm.Ct = (const float *)C_t;
+    prm.dt = dt;
+    prm.init = (const float *)initial_state;
+    prm.gy = grad_y;
+    prm.gfinal = (const float *)grad_final_state;
+    prm.gx = (float *)grad_x;
+    prm.gA = (float *)grad_A;
+    prm.gB = (float *)grad_B_t;
+    prm.gC = (float *)grad_C_t;
+    prm.gdt = grad_dt;
+    prm.ginit = (float *)grad_initial_state;
+    prm.fwd_states = (float *)workspace;
+    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
+    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
+    prm.B = (int)batch;
+    prm.T = (int)T;
+    prm.H = (int)H;
+    prm.N = (int)N;
+    prm.D = (int)D;
+    prm.Q = plan.Q;
+    prm.nc = plan.nc;
+    const int64_t seqs = batch * H;
+    return plan.R == 16 ? launch_backward<16>(prm, seqs, s) : launch_backward<32>(prm, seqs, s);
 }
 
 }  // extern "C"

@@ -1,0 +1,611 @@
+// ssd_bwd_kernels.h -- gfx950 kernels of the backward of the complex chunkwise
+// SSD scan: the gradients that the "Extending" guide (Path B Step 3, the
+// autograd Function of a scan kernel) asks for -- true upstream gradients for
+// y and final_state, a gradient for every input (x, A, B_t, C_t, dt and the
+// initial state). A complex input z receives dl/dRe(z) + i dl/dIm(z).
+//
+// Per (b, h) and chunk c of Q tokens (running sums Lam inside the chunk,
+// L[l,s] = exp(Lam[l] - Lam[s]) on l >= s, e_in = exp(Lam),
+// e_end = exp(Lam[Q-1] - Lam)), with H the state entering the chunk and G the
+// adjoint of the state leaving it, written without conjugation:
+//   M = (C B^T) o L,   V = (gy x^T) o L
+//   conj(gx) = M^T gy + diag(e_end) B G
+//   conj(gB) = V^T C  + diag(e_end) x G^T
+//   conj(gC) = V B    + diag(e_in) gy H^T
+// and the gradient of a_t = softplus(dt_t) A collects, for every pair of
+// tokens l >= s whose decay exp(Lam_l - Lam_s) spans t, that pair's share of
+// the loss: with O/I the output/input-side row sums of the pairs inside the
+// chunk and Off/In those of the pairs that cross its edges,
+//   dF/da_t = sum_{j>=t} (O_j - I_j + Off_j) + sum_{s<t} In_s + exp(Lam[Q-1]) <H, G>
+//   O_l = C_l . (V B)_l,  I_s = B_s . (V^T C)_s,
+//   Off_l = C_l . (e_in gy H^T)_l,  In_s = B_s . (e_end x G^T)_s
+//   ga = conj(dF/da),  gdt = Re(conj(A) ga) sigmoid(dt),  gA = sum softplus(dt) ga.
+// G moves left by G <- exp(Lam[Q-1]) G + (diag(e_in) C)^T gy, H right by the
+// forward's H <- exp(Lam[Q-1]) H + (diag(e_end) B)^T x.
+//
+// Three launches: bwd_state_kernel<R, false> writes every chunk's entering
+// state H, bwd_state_kernel<R, true> every chunk's leaving adjoint G (and the
+// initial-state gradient), then bwd_chunk_kernel<R> evaluates all chunks in
+// parallel from those; bwd_reduce_gA_kernel sums the per-chunk shares of gA
+// in a fixed order. Every contraction is a real-split fp32 MFMA 16x16x4 with
+// operands from LDS planes; running sums of a are taken in double.
+#pragma once
+
+#include <ssd_kernels.h>
+
+namespace ssd {
+
+constexpr int kBwdMaxRows = 32;  // tokens the backward evaluates per chunk, at most
+constexpr int kBwdLd = 81;       // row stride (floats) of the [row][64] LDS planes
+constexpr int kStLd = 65;        // row stride (floats) of the 64 x 64 state planes
+constexpr int kStateFloats = 64 * 64 * 2;  // one padded complex 64 x 64 state
+
+struct BwdParams {
+    const float *x;         // (B, T, H, D) complex
+    const float *A;         // (H) complex
+    const float *Bt;        // (B, T, H, N) complex
+    const float *Ct;        // (B, T, H, N) complex
+    const float *dt;        // (B, T, H)
+    const float *init;      // (B, H, N, D) complex or null
+    const float *gy;        // (B, T, H, D)
+    const float *gfinal;    // (B, H, N, D) complex or null
+    float *gx;              // (B, T, H, D) complex
+    float *gA;              // (H) complex
+    float *gB;              // (B, T, H, N) complex
+    float *gC;              // (B, T, H, N) complex
+    float *gdt;             // (B, T, H)
+    float *ginit;           // (B, H, N, D) complex or null
+    float *fwd_states;      // (B, H, nc, 64, 64) complex: state entering each chunk
+    float *adj_states;      // (B, H, nc, 64, 64) complex: adjoint leaving each chunk, conjugated
+    float *gA_part;         // (B, H, nc) complex: each chunk's share of gA
+    int B, T, H, N, D, Q, nc;
+};
+
+inline int64_t bwd_block_rows(int64_t chunk) { return chunk < kBwdMaxRows ? chunk : kBwdMaxRows; }
+
+struct BwdPlan {
+    int R = 0, Q = 0, nc = 0;
+    size_t states_bytes = 0, part_bytes = 0, workspace_bytes = 0;
+};
+
+inline BwdPlan make_bwd_plan(int64_t B, int64_t T, int64_t H, int64_t chunk)
+{
+    BwdPlan p;
+    p.Q = (int)bwd_block_rows(chunk);
+    p.R = p.Q <= 16 ? 16 : 32;
+    p.nc = (int)((T + p.Q - 1) / p.Q);
+    p.states_bytes = align_up((size_t)B * H * p.nc * kStateFloats * 4, 256);
+    p.part_bytes = align_up((size_t)B * H * p.nc * 8, 256);
+    p.workspace_bytes = 2 * p.states_bytes + p.part_bytes;
+    return p;
+}
+
+SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i]; }
+SSD_DEVICE v2f cmul_d(v2f a, v2f b) { return cmul(a, b); }
+
+// Running sums of a over one chunk, in double, and the per-row factors.
+// Called by every thread; tid < R rows hold a and the factors afterwards.
+template <int R>
+SSD_DEVICE void bwd_decays(const BwdParams &p, int b, int h, int c, float Ar, float Ai,
+                           float *sAl, double *sLam, float *sDt)
+{
+    const int tid = thread_id();
+    if (tid < R) {
+        const int t = c * p.Q + tid;
+        const bool valid = tid < p.Q && t < p.T;
+        const float dtv = valid ? p.dt[((int64_t)b * p.T + t) * p.H + h] : 0.f;
+        const float sp = valid ? softplus_f(dtv) : 0.f;
+        sAl[2 * tid] = sp * Ar;
+        sAl[2 * tid + 1] = sp * Ai;
+        if (sDt)
+            sDt[tid] = dtv;
+    }
+    block_sync();
+    if (tid == 0) {
+        double lr = 0.0, li = 0.0;
+        for (int l = 0; l < R; ++l) {
+            lr += (double)sAl[2 * l];
+            li += (double)sAl[2 * l + 1];
+            sLam[2 * l] = lr;
+            sLam[2 * l + 1] = li;
+        }
+    }
+    block_sync();
+}
+
+// exp of the difference of two running sums (taken in double, then rounded).
+SSD_DEVICE v2f cexp_diff(const double *sLam, int l, int s)
+{
+    const double dr = (l >= 0 ? sLam[2 * l] : 0.0) - (s >= 0 ? sLam[2 * s] : 0.0);
+    const double di = (l >= 0 ? sLam[2 * l + 1] : 0.0) - (s >= 0 ? sLam[2 * s + 1] : 0.0);
+    return cexp_f(v2f{(float)dr, (float)di});
+}
+
+// ------------------------------------------------------- state and adjoint passes
+
+// One workgroup per (b, h) walks the chunks (left to right for the state,
+// right to left for the adjoint) and writes the value that enters (state) or
+// leaves (adjoint) each chunk before folding the chunk in. The 64 x 64 value
+// lives in MFMA accumulators: wave w holds tiles w and w + 8 of the 4 x 4 grid
+// (rows n, columns d).
+template <int R, bool REV>
+SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
+{
+    constexpr int LD = kBwdLd;
+    SSD_LDS float sAre[R * LD];
+    SSD_LDS float sAim[R * LD];
+    SSD_LDS float sAimN[R * LD];
+    SSD_LDS float sXre[R * LD];
+    SSD_LDS float sXim[R * LD];
+    SSD_LDS float sAl[2 * R];
+    SSD_LDS double sLam[2 * R];
+    SSD_LDS float sF[2 * R];
+    SSD_LDS float sDec[2];
+
+    const int tid = thread_id();
+    const int lane = tid & 63;
+    const int w = wave_id();
+    const int64_t seq = block_id();
+    const int b = (int)(seq / p.H), h = (int)(seq % p.H);
+    const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
+    const int N = p.N, D = p.D;
+
+    v4f sre[2], sim[2];
+    for (int k = 0; k < 2; ++k) {
+        const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
+        const int d = dtl * 16 + (lane & 15);
+        for (int r = 0; r < 4; ++r) {
+            const int n = nt * 16 + 4 * (lane >> 4) + r;
+            v2f v = v2f{0.f, 0.f};
+            const float *src = REV ? p.gfinal : p.init;
+            if (src && n < N && d < D)
+                v = ld_c(src, (seq * N + n) * D + d);
+            sre[k][r] = v.x;
+            sim[k][r] = REV ? -v.y : v.y;
+        }
+    }
+
+    for (int ci = 0; ci < p.nc; ++ci) {
+        const int c = REV ? p.nc - 1 - ci : ci;
+        float *slot = (REV ? p.adj_states : p.fwd_states) + (seq * p.nc + c) * (int64_t)kStateFloats;
+        for (int k = 0; k < 2; ++k) {
+            const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
+            const int d = dtl * 16 + (lane & 15);
+            for (int r = 0; r < 4; ++r) {
+                const int n = nt * 16 + 4 * (lane >> 4) + r;
+                *(v2f *)&slot[2 * (n * 64 + d)] = v2f{sre[k][r], sim[k][r]};
+            }
+        }
+        bwd_decays<R>(p, b, h, c, Ar, Ai, sAl, sLam, nullptr);
+        if (tid < R)  // REV: e_in = exp(Lam[l]); forward: e_end = exp(Lam[R-1] - Lam[l])
+            *(v2f *)&sF[2 * tid] = REV ? cexp_diff(sLam, tid, -1) : cexp_diff(sLam, R - 1, tid);
+        if (tid == R)
+            *(v2f *)&sDec[0] = cexp_diff(sLam, R - 1, -1);
+        block_sync();
+        for (int i = tid; i < R * 64; i += 512) {
+            const int l = i >> 6, col = i & 63;
+            const int t = c * p.Q + l;
+            const bool valid = l < p.Q && t < p.T;
+            const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
+            v2f a = v2f{0.f, 0.f};
+            if (valid && col < N)
+                a = ld_c(REV ? p.Ct : p.Bt, row * N + col);
+            a = cmul(a, *(const v2f *)&sF[2 * l]);
+            sAre[l * LD + col] = a.x;
+            sAim[l * LD + col] = a.y;
+            sAimN[l * LD + col] = -a.y;
+            if (REV) {
+                sXre[l * LD + col] = (valid && col < D) ? p.gy[row * D + col] : 0.f;
+            } else {
+                v2f xv = v2f{0.f, 0.f};
+                if (valid && col < D)
+                    xv = ld_c(p.x, row * D + col);
+                sXre[l * LD + col] = xv.x;
+                sXim[l * LD + col] = xv.y;
+            }
+        }
+        block_sync();
+        const float dr = sDec[0], di = sDec[1];
+        for (int k = 0; k < 2; ++k) {
+            const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
+            v4f re = dr * sre[k] - di * sim[k];
+            v4f im = dr * sim[k] + di * sre[k];
+            const int n = nt * 16 + (lane & 15);
+            const int d = dtl * 16 + (lane & 15);
+            for (int l0 = 0; l0 < R; l0 += 4) {
+                const int l = l0 + (lane >> 4);
+                const float a_re = sAre[l * LD + n], a_im = sAim[l * LD + n];
+                if (REV) {
+                    const float g = sXre[l * LD + d];
+                    re = mfma_16x16x4(a_re, g, re);
+                    im = mfma_16x16x4(a_im, g, im);
+                } else {
+                    const float a_imn = sAimN[l * LD + n];
+                    const float x_re = sXre[l * LD + d], x_im = sXim[l * LD + d];
+                    re = mfma_16x16x4(a_re, x_re, re);
+                    re = mfma_16x16x4(a_imn, x_im, re);
+                    im = mfma_16x16x4(a_re, x_im, im);
+                    im = mfma_16x16x4(a_im, x_re, im);
+                }
+            }
+            sre[k] = re;
+            sim[k] = im;
+        }
+        block_sync();
+    }
+
+    if (REV && p.ginit) {
+        for (int k = 0; k < 2; ++k) {
+            const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
+            const int d = dtl * 16 + (lane & 15);
+            for (int r = 0; r < 4; ++r) {
+                const int n = nt * 16 + 4 * (lane >> 4) + r;
+                if (n < N && d < D)
+                    *(v2f *)&p.ginit[2 * ((seq * N + n) * D + d)] = v2f{sre[k][r], -sim[k][r]};
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ the chunk pass
+
+// Sum over the 16 lanes of each row of a 16 x 16 accumulator tile: lane 15 of
+// each group of 16 ends with the total of its 4 rows (inclusive prefix sums).
+SSD_DEVICE v4f row_total(v4f v)
+{
+    for (int r = 0; r < 4; ++r) {
+        float s = v[r];
+        s += row_shr<1>(s);
+        s += row_shr<2>(s);
+        s += row_shr<4>(s);
+        s += row_shr<8>(s);
+        v[r] = s;
+    }
+    return v;
+}
+
+// One workgroup per (b, h, chunk); all chunks run in parallel from the stored
+// entering states and leaving adjoints.
+template <int R>
+SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
+{
+    constexpr int LD = kBwdLd;
+    constexpr int SL = kStLd;
+    constexpr int RL = R + 1;
+    constexpr int NT = R / 16;                   // row tiles of the chunk
+    constexpr int NPAIR = NT * (NT + 1) / 2;     // causal tile pairs
+    SSD_LDS float sBre[R * LD];
+    SSD_LDS float sBim[R * LD];
+    SSD_LDS float sCre[R * LD];
+    SSD_LDS float sCim[R * LD];
+    SSD_LDS float sXre[R * LD];
+    SSD_LDS float sXim[R * LD];
+    SSD_LDS float sGy[R * LD];
+    SSD_LDS float sHre[64 * SL];
+    SSD_LDS float sHim[64 * SL];
+    SSD_LDS float sGre[64 * SL];
+    SSD_LDS float sGim[64 * SL];
+    SSD_LDS float sMre[R * RL];
+    SSD_LDS float sMim[R * RL];
+    SSD_LDS float sVre[R * RL];
+    SSD_LDS float sVim[R * RL];
+    SSD_LDS float sAl[2 * R];
+    SSD_LDS double sLam[2 * R];
+    SSD_LDS float sDt[R];
+    SSD_LDS float sEin[2 * R];
+    SSD_LDS float sEend[2 * R];
+    SSD_LDS float sRow[4 * 4 * 2 * R];  // [O, I, Off, In][column tile][row] complex
+    SSD_LDS float sTc[16];
+
+    const int tid = thread_id();
+    const int lane = tid & 63;
+    const int w = wave_id();
+    const int64_t blk = block_id();
+    const int64_t seq = blk / p.nc;
+    const int c = (int)(blk % p.nc);
+    const int b = (int)(seq / p.H), h = (int)(seq % p.H);
+    const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
+    const int N = p.N, D = p.D;
+
+    bwd_decays<R>(p, b, h, c, Ar, Ai, sAl, sLam, sDt);
+    if (tid < R) {
+        *(v2f *)&sEin[2 * tid] = cexp_diff(sLam, tid, -1);
+        *(v2f *)&sEend[2 * tid] = cexp_diff(sLam, R - 1, tid);
+    }
+    for (int i = tid; i < R * 64; i += 512) {
+        const int l = i >> 6, col = i & 63;
+        const int t = c * p.Q + l;
+        const bool valid = l < p.Q && t < p.T;
+        const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
+        v2f bv = v2f{0.f, 0.f}, cv = v2f{0.f, 0.f}, xv = v2f{0.f, 0.f};
+        float g = 0.f;
+        if (valid && col < N) {
+            bv = ld_c(p.Bt, row * N + col);
+            cv = ld_c(p.Ct, row * N + col);
+        }
+        if (valid && col < D) {
+            xv = ld_c(p.x, row * D + col);
+            g = p.gy[row * D + col];
+        }
+        sBre[l * LD + col] = bv.x;
+        sBim[l * LD + col] = bv.y;
+        sCre[l * LD + col] = cv.x;
+        sCim[l * LD + col] = cv.y;
+        sXre[l * LD + col] = xv.x;
+        sXim[l * LD + col] = xv.y;
+        sGy[l * LD + col] = g;
+    }
+    {
+        const float *hs = p.fwd_states + (seq * p.nc + c) * (int64_t)kStateFloats;
+        const float *gs = p.adj_states + (seq * p.nc + c) * (int64_t)kStateFloats;
+        for (int i = tid; i < 64 * 64; i += 512) {
+            const int n = i >> 6, d = i & 63;
+            const v2f hv = ld_c(hs, i), gv = ld_c(gs, i);
+            sHre[n * SL + d] = hv.x;
+            sHim[n * SL + d] = hv.y;
+            sGre[n * SL + d] = gv.x;
+            sGim[n * SL + d] = gv.y;
+        }
+    }
+    block_sync();
+
+    // Raw Gram (C B^T) tiles on waves 0.., raw gy x^T tiles on waves 4..
+    if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
+        const bool gram = w < 4;
+        const int k = gram ? w : w - 4;
+        const int lt = k < NT ? k : NT - 1, st = k < NT ? k : 0;  // (0,0), (1,1), (1,0)
+        const int lrow = lt * 16 + (lane & 15), scol = st * 16 + (lane & 15);
+        v4f rp = {0.f, 0.f, 0.f, 0.f}, rn = rp, im = rp;
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int kk = k0 + (lane >> 4);
+            if (gram) {
+                const float cr = sCre[lrow * LD + kk], cim = sCim[lrow * LD + kk];
+                const float br = sBre[scol * LD + kk], bim = sBim[scol * LD + kk];
+                rp = mfma_16x16x4(cr, br, rp);
+                rn = mfma_16x16x4(cim, bim, rn);
+                im = mfma_16x16x4(cr, bim, im);
+                im = mfma_16x16x4(cim, br, im);
+            } else {
+                const float g = sGy[lrow * LD + kk];
+                rp = mfma_16x16x4(g, sXre[scol * LD + kk], rp);
+                im = mfma_16x16x4(g, sXim[scol * LD + kk], im);
+            }
+        }
+        float *dre = gram ? sMre : sVre;
+        float *dim = gram ? sMim : sVim;
+        for (int r = 0; r < 4; ++r) {
+            const int l = lt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
+            dre[l * RL + s] = rp[r] - rn[r];
+            dim[l * RL + s] = im[r];
+        }
+    }
+    // <H, G> partial sums
+    {
+        float tr = 0.f, ti = 0.f;
+        for (int i = tid; i < 64 * 64; i += 512) {
+            const int n = i >> 6, d = i & 63;
+            const float hr = sHre[n * SL + d], hi = sHim[n * SL + d];
+            const float gr = sGre[n * SL + d], gi = sGim[n * SL + d];
+            tr += hr * gr - hi * gi;
+            ti += hr * gi + hi * gr;
+        }
+        tr += row_shr<1>(tr);
+        tr += row_shr<2>(tr);
+        tr += row_shr<4>(tr);
+        tr += row_shr<8>(tr);
+        ti += row_shr<1>(ti);
+        ti += row_shr<2>(ti);
+        ti += row_shr<4>(ti);
+        ti += row_shr<8>(ti);
+        const float t0r = lane_read(tr, 15), t1r = lane_read(tr, 31);
+        const float t2r = lane_read(tr, 47), t3r = lane_read(tr, 63);
+        const float t0i = lane_read(ti, 15), t1i = lane_read(ti, 31);
+        const float t2i = lane_read(ti, 47), t3i = lane_read(ti, 63);
+        if (lane == 0) {
+            sTc[2 * w] = (t0r + t1r) + (t2r + t3r);
+            sTc[2 * w + 1] = (t0i + t1i) + (t2i + t3i);
+        }
+    }
+    block_sync();
+
+    // M = Gram o L and V = (gy x^T) o L, zero above the diagonal.
+    for (int i = tid; i < R * R; i += 512) {
+        const int l = i / R, s = i % R;
+        float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
+        if (l >= s) {
+            const v2f L = cexp_diff(sLam, l, s);
+            const v2f m = cmul(v2f{sMre[l * RL + s], sMim[l * RL + s]}, L);
+            const v2f v = cmul(v2f{sVre[l * RL + s], sVim[l * RL + s]}, L);
+            mr = m.x;
+            mi = m.y;
+            vr = v.x;
+            vi = v.y;
+        }
+        sMre[l * RL + s] = mr;
+        sMim[l * RL + s] = mi;
+        sVre[l * RL + s] = vr;
+        sVim[l * RL + s] = vi;
+    }
+    block_sync();
+
+    // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
+    // columns n); NT x 4 tiles of each, dealt round-robin over the eight waves.
+    for (int tile = w; tile < 3 * NT * 4; tile += 8) {
+        const int kind = tile / (NT * 4);
+        const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
+        const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
+        const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
+        v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
+        v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
+        if (kind == 0) {
+            // conj(gx) = M^T gy + e_end (B G)
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+                const int n = k0 + (lane >> 4);
+                const float br = sBre[arow * LD + n], bi = sBim[arow * LD + n];
+                const float gr = sGre[n * SL + bcol], gi = sGim[n * SL + bcol];
+                p2r = mfma_16x16x4(br, gr, p2r);
+                p2n = mfma_16x16x4(bi, gi, p2n);
+                p2i = mfma_16x16x4(br, gi, p2i);
+                p2i = mfma_16x16x4(bi, gr, p2i);
+            }
+            for (int k0 = rt * 16; k0 < R; k0 += 4) {
+                const int l = k0 + (lane >> 4);
+                const float g = sGy[l * LD + bcol];
+                p1r = mfma_16x16x4(sMre[l * RL + arow], g, p1r);
+                p1i = mfma_16x16x4(sMim[l * RL + arow], g, p1i);
+            }
+        } else if (kind == 1) {
+            // conj(gB) = V^T C + e_end (x G^T)
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+                const int d = k0 + (lane >> 4);
+                const float xr = sXre[arow * LD + d], xi = sXim[arow * LD + d];
+                const float gr = sGre[bcol * SL + d], gi = sGim[bcol * SL + d];
+                p2r = mfma_16x16x4(xr, gr, p2r);
+                p2n = mfma_16x16x4(xi, gi, p2n);
+                p2i = mfma_16x16x4(xr, gi, p2i);
+                p2i = mfma_16x16x4(xi, gr, p2i);
+            }
+            for (int k0 = rt * 16; k0 < R; k0 += 4) {
+                const int l = k0 + (lane >> 4);
+                const float vr = sVre[l * RL + arow], vi = sVim[l * RL + arow];
+                const float cr = sCre[l * LD + bcol], cim = sCim[l * LD + bcol];
+                p1r = mfma_16x16x4(vr, cr, p1r);
+                p1n = mfma_16x16x4(vi, cim, p1n);
+                p1i = mfma_16x16x4(vr, cim, p1i);
+                p1i = mfma_16x16x4(vi, cr, p1i);
+            }
+        } else {
+            // conj(gC) = V B + e_in (gy H^T)
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+                const int d = k0 + (lane >> 4);
+                const float g = sGy[arow * LD + d];
+                p2r = mfma_16x16x4(g, sHre[bcol * SL + d], p2r);
+                p2i = mfma_16x16x4(g, sHim[bcol * SL + d], p2i);
+            }
+            for (int k0 = 0; k0 < rt * 16 + 16; k0 += 4) {
+                const int s = k0 + (lane >> 4);
+                const float vr = sVre[arow * RL + s], vi = sVim[arow * RL + s];
+                const float br = sBre[s * LD + bcol], bi = sBim[s * LD + bcol];
+                p1r = mfma_16x16x4(vr, br, p1r);
+                p1n = mfma_16x16x4(vi, bi, p1n);
+                p1i = mfma_16x16x4(vr, bi, p1i);
+                p1i = mfma_16x16x4(vi, br, p1i);
+            }
+        }
+        // Rows of this lane's accumulator entries and the row factor of the edge term.
+        const int col = ct * 16 + (lane & 15);
+        const float *fac = kind == 2 ? sEin : sEend;
+        const float *dre = kind == 2 ? sCre : sBre;   // the row dot products' other factor
+        const float *dim = kind == 2 ? sCim : sBim;
+        v4f outr, outi, d1r, d1i, d2r, d2i;
+        for (int r = 0; r < 4; ++r) {
+            const int row = rt * 16 + 4 * (lane >> 4) + r;
+            const v2f f = *(const v2f *)&fac[2 * row];
+            const v2f e2 = cmul(f, v2f{p2r[r] - p2n[r], p2i[r]});
+            const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
+            outr[r] = e1.x + e2.x;
+            outi[r] = e1.y + e2.y;
+            const v2f q = v2f{dre[row * LD + col], dim[row * LD + col]};
+            const v2f q1 = cmul(q, e1), q2 = cmul(q, e2);
+            d1r[r] = q1.x;
+            d1i[r] = q1.y;
+            d2r[r] = q2.x;
+            d2i[r] = q2.y;
+        }
+        if (kind != 0) {
+            d1r = row_total(d1r);
+            d1i = row_total(d1i);
+            d2r = row_total(d2r);
+            d2i = row_total(d2i);
+            if ((lane & 15) == 15) {
+                // kind 1 (gB): I and In; kind 2 (gC): O and Off
+                const int q1 = kind == 2 ? 0 : 1, q2 = kind == 2 ? 2 : 3;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rt * 16 + 4 * (lane >> 4) + r;
+                    sRow[((q1 * 4 + ct) * R + row) * 2] = d1r[r];
+                    sRow[((q1 * 4 + ct) * R + row) * 2 + 1] = d1i[r];
+                    sRow[((q2 * 4 + ct) * R + row) * 2] = d2r[r];
+                    sRow[((q2 * 4 + ct) * R + row) * 2 + 1] = d2i[r];
+                }
+            }
+        }
+        float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
+        const int width = kind == 0 ? D : N;
+        for (int r = 0; r < 4; ++r) {
+            const int row = rt * 16 + 4 * (lane >> 4) + r;
+            const int t = c * p.Q + row;
+            if (row < p.Q && t < p.T && col < width) {
+                const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
+                *(v2f *)&dst[2 * (g * width + col)] = v2f{outr[r], -outi[r]};
+            }
+        }
+    }
+    block_sync();
+
+    if (tid == 0) {
+        float tr = 0.f, ti = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            tr += sTc[2 * i];
+            ti += sTc[2 * i + 1];
+        }
+        const v2f dec = cexp_diff(sLam, R - 1, -1);
+        const v2f Tc = cmul(dec, v2f{tr, ti});
+        auto part = [&](int q, int row) {
+            v2f s = v2f{0.f, 0.f};
+            for (int ct = 0; ct < 4; ++ct) {
+                s.x += sRow[((q * 4 + ct) * R + row) * 2];
+                s.y += sRow[((q * 4 + ct) * R + row) * 2 + 1];
+            }
+            return s;
+        };
+        // tail[t] = sum_{j >= t} (O - I + Off)_j, kept in sAl (a is no longer needed)
+        v2f tail = v2f{0.f, 0.f};
+        for (int j = R - 1; j >= 0; --j) {
+            const v2f o = part(0, j), in = part(1, j), off = part(2, j);
+            tail.x += o.x - in.x + off.x;
+            tail.y += o.y - in.y + off.y;
+            sAl[2 * j] = tail.x;
+            sAl[2 * j + 1] = tail.y;
+        }
+        v2f head = v2f{0.f, 0.f}, gA = v2f{0.f, 0.f};
+        for (int t0 = 0; t0 < R; ++t0) {
+            const float fr = sAl[2 * t0] + head.x + Tc.x;
+            const float fi = sAl[2 * t0 + 1] + head.y + Tc.y;
+            const v2f edge = part(3, t0);
+            head.x += edge.x;
+            head.y += edge.y;
+            const int t = c * p.Q + t0;
+            if (t0 < p.Q && t < p.T) {
+                // ga = conj(dF/da)
+                const float gar = fr, gai = -fi;
+                const float dtv = sDt[t0];
+                const float sig = 1.f / (1.f + expf(-dtv));
+                p.gdt[((int64_t)b * p.T + t) * p.H + h] = (Ar * gar + Ai * gai) * sig;
+                const float sp = softplus_f(dtv);
+                gA.x += sp * gar;
+                gA.y += sp * gai;
+            }
+        }
+        *(v2f *)&p.gA_part[2 * blk] = gA;
+    }
+}
+
+// gA[h] = sum over batch rows and chunks of the per-chunk shares, in order.
+SSD_KERNEL(64) void bwd_reduce_gA_kernel(const float *part, int B, int H, int nc, float *gA)
+{
+    const int h = (int)(block_id() * 64 + thread_id());
+    if (h >= H)
+        return;
+    float sr = 0.f, si = 0.f;
+    for (int b = 0; b < B; ++b) {
+        const float *q = part + ((int64_t)b * H + h) * nc * 2;
+        for (int c = 0; c < nc; ++c) {
+            sr += q[2 * c];
+            si += q[2 * c + 1];
+        }
+    }
+    gA[2 * h] = sr;
+    gA[2 * h + 1] = si;
+}
+
+}  // namespace ssd

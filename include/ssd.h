@@ -17,6 +17,9 @@
  * states between chunks), and "Skills Reference" Skill 3 (chunk_size 32..256,
  * default 64).
  *
+ * Gradients (ssd_chunk_backward) follow from the same recurrence by reverse-mode
+ * differentiation.
+ *
  * Conventions common to every call:
  *   * All tensor pointers are DEVICE pointers owned by the caller. The library
  *     allocates no memory and keeps no state between calls.
@@ -123,6 +126,52 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
                       int64_t chunk_size, const ssd_c64 *initial_state, float *y,
                       ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
                       ssd_stream_t stream);
+
+/*
+ * ssd_chunk_backward_workspace_bytes -- device workspace that
+ * ssd_chunk_backward needs for these sizes (0 when T, batch or H is 0, or the
+ * sizes are invalid). It holds the state entering and the adjoint leaving
+ * every chunk: about 2 * batch * H * ceil(T / min(chunk_size, 32)) * 32 KiB.
+ */
+size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,
+                                          int64_t D, int64_t chunk_size);
+
+/*
+ * ssd_chunk_backward -- gradients of the chunkwise scan ("Extending", Path B
+ * Step 3: the backward of a scan's autograd Function is seeded with the true
+ * upstream gradients of y and final_state and returns a gradient for every
+ * differentiated input).
+ *
+ * For the loss l = sum(grad_y * y) + sum(Re(conj(grad_final_state) * final_state))
+ * of the forward call with the same inputs, each output receives dl/dRe(z) +
+ * i dl/dIm(z) for a complex input z (the convention of torch's autograd for
+ * complex tensors) and dl/dz for a real one:
+ *   x, A, B_t, C_t, dt, initial_state, chunk_size
+ *                  as for ssd_chunk_forward (initial_state nullable = zero).
+ *   grad_y         (batch, T, H, D) float32, upstream gradient of y.
+ *   grad_final_state nullable: (batch, H, N, D) complex64; NULL means zero.
+ *   grad_x         out: (batch, T, H, D) complex64.
+ *   grad_A         out: (H) complex64, summed over batch rows and time.
+ *   grad_B_t, grad_C_t out: (batch, T, H, N) complex64.
+ *   grad_dt        out: (batch, T, H) float32.
+ *   grad_initial_state out, nullable: (batch, H, N, D) complex64.
+ *   workspace      device scratch of at least
+ *                  ssd_chunk_backward_workspace_bytes(...) bytes, 256-byte
+ *                  aligned (required whenever T > 0). Contents on entry ignored.
+ * The chunk evaluated at once is min(chunk_size, 32) tokens; the result does
+ * not depend on chunk_size beyond rounding.
+ * Constraints: as ssd_chunk_forward, and D <= 64 (SSD_ERR_UNSUPPORTED).
+ * Alignment: complex arrays 8 bytes; dt, grad_y, grad_dt 4 bytes.
+ * batch or H equal to 0 is a no-op; T equal to 0 writes grad_final_state (or
+ * zeros) to grad_initial_state and zeros to grad_A.
+ */
+int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, const ssd_c64 *C_t,
+                       const float *dt, int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                       int64_t chunk_size, const ssd_c64 *initial_state, const float *grad_y,
+                       const ssd_c64 *grad_final_state, ssd_c64 *grad_x, ssd_c64 *grad_A,
+                       ssd_c64 *grad_B_t, ssd_c64 *grad_C_t, float *grad_dt,
+                       ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
+                       ssd_stream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int status);

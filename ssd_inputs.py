@@ -133,3 +133,14 @@ def random_case(batch, T, H, N, D, seed, device="cpu", dt_scale=1.0, dt_mean=0.0
     B_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
     C_t = torch.randn(batch, T, H, N, dtype=torch.complex64, generator=g, device=device) * s
     return ScanInputs(x, A, B_t, C_t, dt)
+
+
+def upstream_grads(batch, T, H, N, D, seed, device="cpu", with_final=True):
+    """Seeded upstream gradients for the backward: grad_y ~ N(0, 1) (B,T,H,D)
+    float32 and grad_final_state ~ complex N(0, 1) (B,H,N,D) complex64 (or None)."""
+    g = _gen(seed + 7919, device)
+    gy = torch.randn((batch, T, H, D), generator=g, device=device, dtype=torch.float32)
+    gf = None
+    if with_final:
+        gf = torch.randn((batch, H, N, D), generator=g, device=device, dtype=torch.complex64)
+    return gy, gf

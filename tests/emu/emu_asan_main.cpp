@@ -44,6 +44,45 @@ static int run(int B, int T, int H, int N, int D, int Q, bool init, bool fin)
     return st != 0 || bad != 0;
 }
 
+static int run_bwd(int B, int T, int H, int N, int D, int Q, bool init, bool fin, bool ginit)
+{
+    unsigned seed = 777u + B * 7 + T * 13 + H * 17 + N * 19 + D * 23 + Q * 29;
+    float *x = alloc_fill((size_t)B * T * H * D * 2, seed);
+    float *A = alloc_fill((size_t)H * 2, seed);
+    for (int h = 0; h < H; ++h)
+        A[2 * h] = -0.05f - 2.9f * (A[2 * h] + 0.5f);
+    float *Bt = alloc_fill((size_t)B * T * H * N * 2, seed);
+    float *Ct = alloc_fill((size_t)B * T * H * N * 2, seed);
+    float *dt = alloc_fill((size_t)B * T * H, seed);
+    float *gy = alloc_fill((size_t)B * T * H * D, seed);
+    float *is = init ? alloc_fill((size_t)B * H * N * D * 2, seed) : nullptr;
+    float *gf = fin ? alloc_fill((size_t)B * H * N * D * 2, seed) : nullptr;
+    float *gx = (float *)malloc((size_t)B * T * H * D * 2 * sizeof(float) + 1);
+    float *gA = (float *)malloc((size_t)H * 2 * sizeof(float));
+    float *gB = (float *)malloc((size_t)B * T * H * N * 2 * sizeof(float) + 1);
+    float *gC = (float *)malloc((size_t)B * T * H * N * 2 * sizeof(float) + 1);
+    float *gdt = (float *)malloc((size_t)B * T * H * sizeof(float) + 1);
+    float *gi = ginit ? (float *)malloc((size_t)B * H * N * D * 2 * sizeof(float)) : nullptr;
+    size_t ws = ssd_chunk_backward_workspace_bytes(B, T, H, N, D, Q);
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
+    int st = ssd_chunk_backward((ssd_c64 *)x, (ssd_c64 *)A, (ssd_c64 *)Bt, (ssd_c64 *)Ct, dt, B, T,
+                                H, N, D, Q, (ssd_c64 *)is, gy, (ssd_c64 *)gf, (ssd_c64 *)gx,
+                                (ssd_c64 *)gA, (ssd_c64 *)gB, (ssd_c64 *)gC, gdt, (ssd_c64 *)gi, w,
+                                ws, nullptr);
+    int bad = 0;
+    for (size_t i = 0; i < (size_t)B * T * H * D * 2; ++i)
+        bad += !isfinite(gx[i]);
+    for (size_t i = 0; i < (size_t)B * T * H * N * 2; ++i)
+        bad += !isfinite(gB[i]) + !isfinite(gC[i]);
+    for (size_t i = 0; i < (size_t)B * T * H; ++i)
+        bad += !isfinite(gdt[i]);
+    printf("backward B=%d T=%d H=%d N=%d D=%d Q=%d ws=%zu status=%d nonfinite=%d\n", B, T, H, N, D,
+           Q, ws, st, bad);
+    free(x); free(A); free(Bt); free(Ct); free(dt); free(gy); free(is); free(gf);
+    free(gx); free(gA); free(gB); free(gC); free(gdt); free(gi); free(w);
+    return st != 0 || bad != 0;
+}
+
 int main()
 {
     int fails = 0;
@@ -52,6 +91,10 @@ int main()
     fails += run(1, 45, 1, 6, 70, 32, true, true);    // two D slices
     fails += run(2, 9, 1, 2, 3, 4, false, false);     // Q < 16, no final state
     fails += run(1, 130, 1, 8, 8, 3, true, true);     // many segments
+    fails += run_bwd(1, 40, 2, 4, 5, 16, true, true, true);     // padded N, D; partial chunk
+    fails += run_bwd(1, 70, 1, 64, 64, 64, false, true, true);  // full tiles, R = 32
+    fails += run_bwd(2, 9, 1, 2, 3, 4, false, false, false);    // R = 16, no optional arrays
+    fails += run_bwd(1, 33, 3, 8, 64, 256, true, false, true);  // long chunk as 32-token chunks
     printf("%s\n", fails ? "FAIL" : "OK");
     return fails;
 }

@@ -65,6 +65,11 @@ def load(out_dir):
             lib.ssd_chunk_forward_workspace_bytes.restype = ctypes.c_size_t
             lib.ssd_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
             lib.ssd_discretise.restype = ctypes.c_int
+            lib.ssd_chunk_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p,
+                                               p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
+            lib.ssd_chunk_backward.restype = ctypes.c_int
+            lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
+            lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
             lib.emu_mfma_count.restype = ctypes.c_long
             lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
             lib.emu_sincos.restype = None
@@ -95,3 +100,30 @@ def chunk_forward(lib, inp, chunk, initial_state=None, want_final=True):
                                None if fs is None else fs.ctypes.data,
                                ws_p if ws_n else None, ws_n, None)
     return st, y, fs
+
+
+def chunk_backward(lib, inp, chunk, grad_y, grad_final=None, initial_state=None, want_init=True):
+    """Returns (status, gx, gA, gB, gC, gdt, ginit) from the emulated library."""
+    x, A, Bm, Cm = (_c64(v) for v in (inp.x, inp.A, inp.B_t, inp.C_t))
+    dt = np.ascontiguousarray(inp.dt.numpy().astype(np.float32))
+    Bsz, T, H, D = x.shape
+    N = Bm.shape[-1]
+    gy = np.ascontiguousarray(grad_y, np.float32)
+    gf = None if grad_final is None else np.ascontiguousarray(grad_final, np.complex64)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, np.complex64)
+    nan = np.nan + 1j * np.nan
+    gx = np.full(x.shape, nan, np.complex64)
+    gA = np.full((H,), nan, np.complex64)
+    gB = np.full(Bm.shape, nan, np.complex64)
+    gC = np.full(Bm.shape, nan, np.complex64)
+    gdt = np.full(dt.shape, np.nan, np.float32)
+    gi = np.full((Bsz, H, N, D), nan, np.complex64) if want_init else None
+    ws_n = lib.ssd_chunk_backward_workspace_bytes(Bsz, T, H, N, D, chunk)
+    ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
+    ws_p = ws.ctypes.data
+    ws_p = ws_p + (-ws_p) % 256
+    ptr = lambda a: None if a is None else a.ctypes.data
+    st = lib.ssd_chunk_backward(ptr(x), ptr(A), ptr(Bm), ptr(Cm), ptr(dt), Bsz, T, H, N, D, chunk,
+                                ptr(init), ptr(gy), ptr(gf), ptr(gx), ptr(gA), ptr(gB), ptr(gC),
+                                ptr(gdt), ptr(gi), ws_p if ws_n else None, ws_n, None)
+    return st, gx, gA, gB, gC, gdt, gi

@@ -24,6 +24,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = set(ssd.header_functions())
     assert {"ssd_discretise", "ssd_chunk_forward", "ssd_chunk_forward_workspace_bytes",
+            "ssd_chunk_backward", "ssd_chunk_backward_workspace_bytes",
             "ssd_status_string", "ssd_version"} <= names
 
 
@@ -142,3 +143,48 @@ def test_python_layer_rejects_bad_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(OSError):
         ssd.load_library(str(tmp_path / "libssd.so"))
+
+
+def _bwd(lib, B=1, T=16, H=2, N=4, D=4, Q=4, ptrs=True, ws=None, ws_n=0, align=0, gA=True):
+    p = ctypes.c_void_p(0x100000 + align) if ptrs else None
+    a = ctypes.c_void_p(0x100000) if gA else None
+    return lib.ssd_chunk_backward(p, p, p, p, p, B, T, H, N, D, Q, None, p, None, p, a, p, p, p,
+                                  None, ws, ws_n, None)
+
+
+def test_backward_argument_checks(lib):
+    need = lib.ssd_chunk_backward_workspace_bytes(1, 16, 2, 4, 4, 4)
+    ws = ctypes.c_void_p(0x200000)
+    assert _bwd(lib, B=-1) == ssd.SSD_ERR_SHAPE
+    assert _bwd(lib, Q=0) == ssd.SSD_ERR_SHAPE
+    assert _bwd(lib, N=3) == ssd.SSD_ERR_ODD_N
+    assert _bwd(lib, D=257) == ssd.SSD_ERR_BLOCK_DIMS
+    assert _bwd(lib, N=66) == ssd.SSD_ERR_UNSUPPORTED
+    assert _bwd(lib, D=65) == ssd.SSD_ERR_UNSUPPORTED     # gradients: D <= 64
+    assert _bwd(lib, gA=False) == ssd.SSD_ERR_NULL
+    assert _bwd(lib, ptrs=False) == ssd.SSD_ERR_NULL
+    assert _bwd(lib, align=4, ws=ws, ws_n=need) == ssd.SSD_ERR_ALIGN
+    assert _bwd(lib, ws=None, ws_n=need) == ssd.SSD_ERR_WORKSPACE
+    assert _bwd(lib, ws=ws, ws_n=need - 1) == ssd.SSD_ERR_WORKSPACE
+    assert _bwd(lib, ws=ctypes.c_void_p(0x200010), ws_n=need) == ssd.SSD_ERR_ALIGN
+    assert lib.ssd_chunk_backward(None, None, None, None, None, 0, 16, 2, 4, 4, 4, None, None, None,
+                                  None, None, None, None, None, None, None, 0, None) == ssd.SSD_OK
+
+
+def test_backward_workspace_sizes(lib):
+    f = lib.ssd_chunk_backward_workspace_bytes
+    # two (B, H, chunks, 64, 64) complex state arrays + per-chunk gA shares
+    assert f(32, 2048, 16, 64, 64, 64) >= 2 * 32 * 16 * 64 * 64 * 64 * 8
+    assert f(1, 100, 2, 4, 4, 8) >= 2 * 2 * 13 * 64 * 64 * 8
+    assert f(1, 16, 2, 4, 65, 4) == 0 and f(0, 16, 2, 4, 4, 4) == 0 and f(1, 0, 2, 4, 4, 4) == 0
+    assert ssd.backward_workspace_bytes(1, 100, 2, 4, 4, 8) == f(1, 100, 2, 4, 4, 8)
+
+
+def test_python_backward_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 4, dtype=torch.complex64)
+    A = torch.zeros(2, dtype=torch.complex64)
+    B = torch.zeros(1, 4, 2, 4, dtype=torch.complex64)
+    dt = torch.zeros(1, 4, 2)
+    with pytest.raises(ValueError):
+        ssd.chunk_backward(x, A, B, B, dt, torch.zeros(1, 4, 2, 4))  # CPU tensors

@@ -118,3 +118,52 @@ def test_kernel_sincos_accuracy(emu):
     assert np.abs(c - np.cos(xd)).max() < 1.5e-7
     small = np.abs(xd) < 1e-3  # sin keeps its relative accuracy near zero
     assert (np.abs(s[small] - xd[small]) <= 1e-7 * np.abs(xd[small])).all()
+
+
+BWD_CASES = [
+    # B, T, H, N, D, Q
+    (2, 16, 2, 4, 4, 4),       # the pages' tiny shape
+    (1, 32, 1, 64, 64, 32),    # one full 32-row chunk
+    (1, 97, 1, 64, 64, 64),    # chunks of 32 with a ragged last one
+    (2, 50, 2, 6, 10, 16),
+    (1, 45, 2, 10, 40, 8),
+    (1, 23, 2, 4, 5, 1),       # Q = 1
+    (3, 7, 1, 2, 2, 64),       # T < Q
+    (1, 130, 1, 8, 8, 256),
+]
+
+
+def _check_grads(got, ref):
+    for name, a, r in zip(ref._fields, got, ref):
+        a = np.asarray(a)
+        assert np.isfinite(a).all(), name
+        err = np.abs(a - r)
+        bad = err > 1e-4 + 1e-4 * np.abs(r)
+        assert not bad.any(), "%s: max err %.3e at %s" % (name, err.max(), np.argwhere(bad)[:3])
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+@pytest.mark.parametrize("edges", ["none", "both"])
+def test_emulated_backward_matches_oracle(emu, case, edges):
+    B, T, H, N, D, Q = case
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=sum(case) + 1, dt_scale=1.0, dt_mean=0.3)
+    rng = np.random.default_rng(sum(case))
+    gy = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    gf = init = None
+    if edges == "both":
+        gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+        init = ((rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))) * 0.5).astype(np.complex64)
+    st, *got = emu_harness.chunk_backward(emu, inp, Q, gy, gf, init)
+    assert st == 0
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf, init)
+    _check_grads(got, ref)
+
+
+def test_emulated_backward_zero_length(emu):
+    inp = ssd_inputs.random_case(2, 0, 2, 4, 4, seed=6)
+    rng = np.random.default_rng(2)
+    gf = (rng.standard_normal((2, 2, 4, 4)) + 1j * rng.standard_normal((2, 2, 4, 4))).astype(np.complex64)
+    st, gx, gA, gB, gC, gdt, gi = emu_harness.chunk_backward(
+        emu, inp, 4, np.zeros((2, 0, 2, 4), np.float32), gf)
+    assert st == 0 and gx.size == 0
+    assert np.array_equal(gi, gf) and np.all(gA == 0)

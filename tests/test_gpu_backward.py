@@ -1,0 +1,218 @@
+"""GPU parity of the gradients: ssd_chunk_backward, called through the C ABI,
+against the oracle's reverse-mode gradients (oracle_scan_backward).
+
+Bar (written here, applied elementwise to every gradient, per complex
+component): |g_gpu - g_oracle| <= 1e-4 + 1e-4 |g_oracle| -- the forward's bar,
+since each gradient is, like y, a sum of decayed products of the inputs. The
+gradient of A is a sum over every token of the batch; its bar scales with the
+number of tokens summed: |dgA| <= 1e-4 (1 + |gA|) + 1e-6 * B*T.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import complex_chunkwise_ssd_amd as ssd
+import oracle
+import ssd_inputs
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-4
+RTOL = 1e-4
+DEV = torch.device("cuda:0")
+
+
+def _close(name, got, ref, atol=ATOL):
+    got = np.asarray(got)
+    assert np.isfinite(got).all(), name
+    comps = (np.real, np.imag) if np.iscomplexobj(ref) else (lambda v: v,)
+    for comp in comps:
+        e = np.abs(comp(got) - comp(ref))
+        bad = e > atol + RTOL * np.abs(comp(ref))
+        assert not bad.any(), "%s: %d violations, max err %.3e (max |ref| %.3e) at %s" % (
+            name, int(bad.sum()), e.max(), np.abs(ref).max(), np.argwhere(bad)[:3].tolist())
+
+
+def _gpu_grads(inp, Q, gy, gf=None, init=None):
+    g = inp.to(DEV)
+    t = lambda a, dt: None if a is None else torch.as_tensor(a, dtype=dt).to(DEV)
+    out = ssd.chunk_backward(g.x, g.A, g.B_t, g.C_t, g.dt, t(gy, torch.float32),
+                             t(gf, torch.complex64), chunk_size=Q,
+                             initial_state=t(init, torch.complex64))
+    torch.cuda.synchronize()
+    return [None if v is None else v.cpu().numpy() for v in out]
+
+
+def _oracle_grads(inp, gy, gf=None, init=None):
+    return oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf, init)
+
+
+def _check_all(got, ref, what, tokens):
+    for name, a, r in zip(ref._fields, got, ref):
+        if name == "A":
+            _close("%s grad A" % what, a, r, atol=ATOL + 1e-6 * tokens)
+        elif a is not None:
+            _close("%s grad %s" % (what, name), a, r)
+
+
+def _edges(B, H, N, D, seed):
+    rng = np.random.default_rng(seed)
+    gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+    init = ((rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))) * 0.5).astype(np.complex64)
+    return gf, init
+
+
+@pytest.mark.parametrize("tv", [False, True])
+def test_tiny_recipe_gradients(tv):
+    inp = ssd_inputs.tiny_case(tv)
+    gy, _ = ssd_inputs.upstream_grads(2, 16, 2, 4, 4, seed=0, with_final=False)
+    gf, init = _edges(2, 2, 4, 4, 1)
+    got = _gpu_grads(inp, 4, gy, gf, init)
+    _check_all(got, _oracle_grads(inp, gy, gf, init), "tiny", 32)
+
+
+SMALL = [
+    # B, T, H, N, D, Q
+    (2, 16, 2, 4, 4, 4),
+    (1, 64, 1, 64, 64, 64),
+    (2, 150, 3, 64, 64, 64),
+    (1, 97, 2, 8, 8, 32),
+    (2, 50, 2, 6, 10, 16),
+    (1, 45, 1, 10, 40, 32),
+    (1, 33, 1, 2, 3, 33),
+    (1, 23, 2, 4, 5, 1),
+    (1, 12, 1, 4, 4, 12),
+    (3, 7, 1, 2, 2, 64),
+    (2, 300, 4, 32, 64, 48),
+    (1, 260, 2, 64, 64, 256),
+]
+
+
+@pytest.mark.parametrize("edges", [False, True])
+@pytest.mark.parametrize("case", SMALL)
+def test_small_shapes_gradients(case, edges):
+    B, T, H, N, D, Q = case
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=sum(case) + 5, dt_mean=0.3)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=sum(case), with_final=False)
+    gf, init = _edges(B, H, N, D, sum(case)) if edges else (None, None)
+    got = _gpu_grads(inp, Q, gy, gf, init)
+    _check_all(got, _oracle_grads(inp, gy, gf, init), str(case), B * T)
+
+
+def test_layer_b1_gradients_full():
+    """Single layer B=1, T=2048, H=16, N=D=64: every gradient compared."""
+    w = ssd_inputs.WORKLOADS["layer_b1_t2048"]
+    inp = ssd_inputs.layer_case(w["batch"], w["T"], 16, 64, 64, seed=w["seed"])
+    gy, gf = ssd_inputs.upstream_grads(1, 2048, 16, 64, 64, seed=w["seed"])
+    got = _gpu_grads(inp, 64, gy, gf)
+    _check_all(got, _oracle_grads(inp, gy, gf), "layer_b1", 2048)
+
+
+def _select(inp, gy, gf, pairs):
+    parts = [inp.select(b, h) for b, h in pairs]
+    cat = lambda k, dim: torch.cat([getattr(p, k) for p in parts], dim=dim).contiguous()
+    host = ssd_inputs.ScanInputs(cat("x", 2), cat("A", 0), cat("B_t", 2), cat("C_t", 2), cat("dt", 2))
+    gys = torch.stack([gy[b, :, h] for b, h in pairs], dim=1)[None].contiguous()
+    gfs = None if gf is None else torch.stack([gf[b, h] for b, h in pairs], dim=0)[None].contiguous()
+    return host, gys, gfs
+
+
+def _check_sampled_and_head(inp_dev, gy_dev, gf_dev, Q, pairs, head, what):
+    """Per-token gradients on sampled (b, h) sequences; grad A of one head over
+    every batch row."""
+    out = ssd.chunk_backward(inp_dev.x, inp_dev.A, inp_dev.B_t, inp_dev.C_t, inp_dev.dt, gy_dev,
+                             gf_dev, chunk_size=Q)
+    torch.cuda.synchronize()
+    got = [v.cpu().numpy() for v in out]
+    inp, gy = inp_dev.to("cpu"), gy_dev.cpu()
+    gf = None if gf_dev is None else gf_dev.cpu()
+    host, gys, gfs = _select(inp, gy, gf, pairs)
+    ref = _oracle_grads(host, gys.numpy(), None if gfs is None else gfs.numpy())
+    for k, (b, h) in enumerate(pairs):
+        _close("%s gx %s" % (what, (b, h)), got[0][b, :, h], ref.x[0, :, k])
+        _close("%s gB %s" % (what, (b, h)), got[2][b, :, h], ref.B_t[0, :, k])
+        _close("%s gC %s" % (what, (b, h)), got[3][b, :, h], ref.C_t[0, :, k])
+        _close("%s gdt %s" % (what, (b, h)), got[4][b, :, h], ref.dt[0, :, k])
+        _close("%s ginit %s" % (what, (b, h)), got[5][b, h], ref.initial_state[0, k])
+    Bsz, T = inp.x.shape[:2]
+    hp = [(b, head) for b in range(Bsz)]
+    host, gys, gfs = _select(inp, gy, gf, hp)
+    ref = _oracle_grads(host, gys.numpy(), None if gfs is None else gfs.numpy())
+    _close("%s gA head %d" % (what, head), got[1][head], ref.A.sum(), atol=ATOL + 1e-6 * Bsz * T)
+
+
+def test_layer_b8_gradients_sampled():
+    w = ssd_inputs.WORKLOADS["layer_b8_t2048"]
+    g = ssd_inputs.layer_case(w["batch"], w["T"], 16, 64, 64, seed=w["seed"], device=DEV)
+    gy, gf = ssd_inputs.upstream_grads(8, 2048, 16, 64, 64, seed=w["seed"], device=DEV)
+    pairs = [(0, 0), (3, 9), (7, 15), (5, 4)]
+    _check_sampled_and_head(g, gy, gf, 64, pairs, 6, "layer_b8")
+
+
+def test_network_layer_gradients_sampled():
+    """One layer of the full-network load (B=32, T=2048, seed 0) at full size."""
+    g = ssd_inputs.layer_case(32, 2048, 16, 64, 64, seed=0, device=DEV)
+    gy, gf = ssd_inputs.upstream_grads(32, 2048, 16, 64, 64, seed=0, device=DEV)
+    pairs = [(0, 0), (31, 15), (17, 8)]
+    _check_sampled_and_head(g, gy, gf, 64, pairs, 11, "network layer 0")
+
+
+@pytest.mark.parametrize("Q", [16, 64])
+def test_sweep_b4_t8192_gradients(Q):
+    """Long context, dt ~ N(0.5, 1): sampled sequences; the chunk-16 and chunk-64
+    runs (16- and 32-token chunks inside) agree on every gradient."""
+    w = ssd_inputs.WORKLOADS["sweep_b4_t8192"]
+    g = ssd_inputs.layer_case(w["batch"], w["T"], 16, 64, 64, seed=w["seed"], dt_mean=w["dt_mean"],
+                              device=DEV)
+    gy, gf = ssd_inputs.upstream_grads(4, 8192, 16, 64, 64, seed=w["seed"], device=DEV)
+    _check_sampled_and_head(g, gy, gf, Q, [(0, 0), (3, 11)], 2, "sweep Q=%d" % Q)
+
+
+def test_backward_determinism_bitwise():
+    inp = ssd_inputs.random_case(2, 300, 4, 64, 64, seed=77)
+    gy, gf = ssd_inputs.upstream_grads(2, 300, 4, 64, 64, seed=77)
+    a = _gpu_grads(inp, 64, gy.numpy(), gf.numpy())
+    b = _gpu_grads(inp, 64, gy.numpy(), gf.numpy())
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_backward_chunk_size_invariance():
+    inp = ssd_inputs.random_case(2, 333, 2, 64, 64, seed=81, dt_mean=0.5)
+    gy, gf = ssd_inputs.upstream_grads(2, 333, 2, 64, 64, seed=81)
+    ref = _gpu_grads(inp, 64, gy.numpy(), gf.numpy())
+    for Q in (7, 16, 20):
+        got = _gpu_grads(inp, Q, gy.numpy(), gf.numpy())
+        for name, a, r in zip(ssd.Grads._fields, got, ref):
+            tol = 2 * (ATOL + RTOL * np.abs(r)) + (1e-6 * 666 if name == "A" else 0)
+            assert (np.abs(a - r) <= tol).all(), (Q, name)
+
+
+def test_backward_zero_length():
+    inp = ssd_inputs.random_case(2, 0, 3, 4, 4, seed=80)
+    gf = (np.arange(2 * 3 * 4 * 4, dtype=np.float32).reshape(2, 3, 4, 4) * (1 - 0.5j)).astype(np.complex64)
+    got = _gpu_grads(inp, 4, np.zeros((2, 0, 3, 4), np.float32), gf)
+    assert got[0].size == 0 and np.array_equal(got[5], gf) and np.all(got[1] == 0)
+
+
+def test_backward_through_initial_state_composes():
+    """Gradients of run(T1) -> run(T2 | final state) chained by hand equal the
+    gradients of run(T1 + T2): the second run's initial-state gradient is the
+    first run's final-state gradient."""
+    inp = ssd_inputs.random_case(2, 190, 2, 64, 32, seed=79)
+    gy, gf = ssd_inputs.upstream_grads(2, 190, 2, 64, 32, seed=79)
+    gy, gf = gy.numpy(), gf.numpy()
+    whole = _gpu_grads(inp, 64, gy, gf)
+    cut = 77
+    a = ssd_inputs.ScanInputs(inp.x[:, :cut].contiguous(), inp.A, inp.B_t[:, :cut].contiguous(),
+                              inp.C_t[:, :cut].contiguous(), inp.dt[:, :cut].contiguous())
+    b = ssd_inputs.ScanInputs(inp.x[:, cut:].contiguous(), inp.A, inp.B_t[:, cut:].contiguous(),
+                              inp.C_t[:, cut:].contiguous(), inp.dt[:, cut:].contiguous())
+    ga_dev = a.to(DEV)
+    _, fa = ssd.chunk_forward(ga_dev.x, ga_dev.A, ga_dev.B_t, ga_dev.C_t, ga_dev.dt, chunk_size=64)
+    gb = _gpu_grads(b, 64, gy[:, cut:], gf, init=fa.cpu().numpy())
+    ga = _gpu_grads(a, 64, gy[:, :cut], gb[5])
+    _close("composed gx", np.concatenate([ga[0], gb[0]], axis=1), whole[0])
+    _close("composed gdt", np.concatenate([ga[4], gb[4]], axis=1), whole[4])
+    _close("composed gA", ga[1] + gb[1], whole[1], atol=ATOL + 1e-6 * 380)
