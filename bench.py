@@ -6,6 +6,10 @@ all 28 layers resident in HBM and scanned back to back. One step is one pass
 over the 28 layers. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The line also carries side figures: the single-layer workloads (B=1, B=8) and
+the backward (ssd_chunk_backward, all its passes) on layer 0 of the network
+load. `--backward-only` times just that backward leg (for profiling runs).
 """
 
 import argparse
@@ -67,6 +71,49 @@ def cpu_baseline(layer0, batch_rows=32):
                       % (batch_rows - 1, A.shape[0], T, batch_rows * A.shape[0], el)}
 
 
+def backward_leg(ssd, torch, g, reps=10, warmup=3):
+    """ssd_chunk_backward on one network layer (B=32, T=2048, H=16, N=D=64,
+    chunk 64) with seeded upstream gradients; median of `reps` calls, each
+    bracketed by HIP events on the stream the library launches on."""
+    import ssd_inputs
+    B, T, H, D = g.x.shape
+    N = g.B_t.shape[-1]
+    Q = 64
+    gy, gf = ssd_inputs.upstream_grads(B, T, H, N, D, seed=0, device=g.x.device)
+    ws = torch.empty(max(ssd.backward_workspace_bytes(B, T, H, N, D, Q), 1), dtype=torch.uint8,
+                     device=g.x.device)
+    out = ssd.chunk_backward(g.x, g.A, g.B_t, g.C_t, g.dt, gy, gf, chunk_size=Q, workspace=ws)
+    call = lambda: ssd.chunk_backward(g.x, g.A, g.B_t, g.C_t, g.dt, gy, gf, chunk_size=Q, out=out,
+                                      workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    th = B * T * H
+    qb = ssd.backward_block_rows(Q)
+    fl = th * ssd.backward_algorithmic_flops_per_token_head(N, D, qb)
+    by = th * ssd.backward_algorithmic_bytes_per_token_head(N, D, T)
+    tf = fl / (ms * 1e-3) / 1e12
+    del ws, out, gy, gf
+    return {"workload": "network layer 0 backward (B=%d, T=%d, H=%d, N=D=%d, chunk %d)"
+                        % (B, T, H, N, Q),
+            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "token_heads_per_s": th / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS,
+                         "scope": "whole call: state pass, adjoint pass, chunk pass, gA sum",
+                         "algorithmic_flops": fl, "algorithmic_bytes": by,
+                         "evaluated_chunk": qb}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +124,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the single-layer side figures")
     ap.add_argument("--layers", type=int, default=None,
                     help="override the layer count (counter runs; the headline uses all layers)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward side figure")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward on layer 0 of the workload and print it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -104,6 +154,12 @@ def main():
         return 0
     wl = dict(ssd_inputs.WORKLOADS[args.workload])
     B, T, H, N, D = wl["batch"], wl["T"], wl["H"], wl["N"], wl["D"]
+    if args.backward_only:
+        g = ssd_inputs.layer_case(B, T, H, N, D, seed=0 if wl["seed"] is None else wl["seed"],
+                                  dt_mean=wl["dt_mean"], device=dev)
+        print(json.dumps({"backward": backward_leg(ssd, torch, g, reps=max(args.steps, 1),
+                                                   warmup=args.warmup)}), flush=True)
+        return 0
     Q = wl["chunks"][0]
     L = wl.get("layers", 1) if args.layers is None else args.layers
     log("bench: workload %s (%d layer(s) of B=%d T=%d H=%d N=%d D=%d Q=%d)" % (args.workload, L, B, T,
@@ -224,6 +280,9 @@ def main():
                            "roofline_frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
             del g, y, f, wsp
         out["single_layer"] = extra
+    if not args.no_backward:
+        log("bench: timing the backward on layer 0")
+        out["backward"] = backward_leg(ssd, torch, layers[0])
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

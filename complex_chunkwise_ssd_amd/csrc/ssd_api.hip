@@ -65,11 +65,13 @@ int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
                        stream, prm);
     if (int st = launch_status())
         return st;
-    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R>), dim3((unsigned)(seqs * prm.nc)), dim3(512), 0,
-                       stream, prm);
+    const int64_t chunks = seqs * prm.nc;
+    const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R>), dim3((unsigned)groups), dim3(512), 0, stream,
+                       prm);
     if (int st = launch_status())
         return st;
-    hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3(grid_1d(prm.H, 64)), dim3(64), 0, stream,
+    hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)prm.H), dim3(256), 0, stream,
                        prm.gA_part, prm.B, prm.H, prm.nc, prm.gA);
     return launch_status();
 }
@@ -254,7 +256,7 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
             if (int st = launch_status())
                 return st;
         }
-        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3(grid_1d(H, 64)), dim3(64), 0, s,
+        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)H), dim3(256), 0, s,
                            (const float *)nullptr, (int)batch, (int)H, 0, (float *)grad_A);
         return launch_status();
     }

@@ -39,6 +39,7 @@ constexpr int kBwdMaxRows = 32;  // tokens the backward evaluates per chunk, at 
 constexpr int kBwdLd = 81;       // row stride (floats) of the [row][64] LDS planes
 constexpr int kStLd = 65;        // row stride (floats) of the 64 x 64 state planes
 constexpr int kStateFloats = 64 * 64 * 2;  // one padded complex 64 x 64 state
+constexpr int kBwdGroups = 256;  // workgroups of the chunk pass: one per compute unit
 
 struct BwdParams {
     const float *x;         // (B, T, H, D) complex
@@ -83,34 +84,43 @@ inline BwdPlan make_bwd_plan(int64_t B, int64_t T, int64_t H, int64_t chunk)
 SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i]; }
 SSD_DEVICE v2f cmul_d(v2f a, v2f b) { return cmul(a, b); }
 
-// Running sums of a over one chunk, in double, and the per-row factors.
-// Called by every thread; tid < R rows hold a and the factors afterwards.
+// Running sums of a over one chunk, in double. Thread tid < R passes the dt of
+// chunk row tid (ignored past the chunk or past T, where a = 0); afterwards
+// sAl holds a and sLam the running sums, for every thread.
 template <int R>
-SSD_DEVICE void bwd_decays(const BwdParams &p, int b, int h, int c, float Ar, float Ai,
-                           float *sAl, double *sLam, float *sDt)
+SSD_DEVICE void bwd_decays(const BwdParams &p, int c, float dtv, float Ar, float Ai, float *sAl,
+                           double *sLam, float *sDt)
 {
     const int tid = thread_id();
     if (tid < R) {
         const int t = c * p.Q + tid;
         const bool valid = tid < p.Q && t < p.T;
-        const float dtv = valid ? p.dt[((int64_t)b * p.T + t) * p.H + h] : 0.f;
         const float sp = valid ? softplus_f(dtv) : 0.f;
         sAl[2 * tid] = sp * Ar;
         sAl[2 * tid + 1] = sp * Ai;
         if (sDt)
-            sDt[tid] = dtv;
+            sDt[tid] = valid ? dtv : 0.f;
     }
     block_sync();
-    if (tid == 0) {
+    if (tid < R) {  // each row sums its own prefix, in order
         double lr = 0.0, li = 0.0;
-        for (int l = 0; l < R; ++l) {
+        for (int l = 0; l <= tid; ++l) {
             lr += (double)sAl[2 * l];
             li += (double)sAl[2 * l + 1];
-            sLam[2 * l] = lr;
-            sLam[2 * l + 1] = li;
         }
+        sLam[2 * tid] = lr;
+        sLam[2 * tid + 1] = li;
     }
     block_sync();
+}
+
+// dt of chunk row tid (tid < R), or 0 past the chunk or past T.
+template <int R>
+SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
+{
+    const int tid = thread_id();
+    const int t = c * p.Q + tid;
+    return (tid < R && tid < p.Q && t < p.T) ? p.dt[((int64_t)b * p.T + t) * p.H + h] : 0.f;
 }
 
 // exp of the difference of two running sums (taken in double, then rounded).
@@ -165,6 +175,27 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
         }
     }
 
+    // The rows of the next chunk are loaded into registers while the current
+    // chunk's MFMA update runs: PER elements of each operand per thread.
+    constexpr int PER = R * 64 / 512;
+    v2f pa[PER], px[PER];
+    float pdt = 0.f;
+    auto fetch = [&](int c) {
+        pdt = bwd_load_dt<R>(p, b, h, c);
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+            const int t = c * p.Q + l;
+            const bool valid = l < p.Q && t < p.T;
+            const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
+            pa[j] = (valid && col < N) ? ld_c(REV ? p.Ct : p.Bt, row * N + col) : v2f{0.f, 0.f};
+            if (REV)
+                px[j] = v2f{(valid && col < D) ? p.gy[row * D + col] : 0.f, 0.f};
+            else
+                px[j] = (valid && col < D) ? ld_c(p.x, row * D + col) : v2f{0.f, 0.f};
+        }
+    };
+    fetch(REV ? p.nc - 1 : 0);
+
     for (int ci = 0; ci < p.nc; ++ci) {
         const int c = REV ? p.nc - 1 - ci : ci;
         float *slot = (REV ? p.adj_states : p.fwd_states) + (seq * p.nc + c) * (int64_t)kStateFloats;
@@ -176,35 +207,25 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
                 *(v2f *)&slot[2 * (n * 64 + d)] = v2f{sre[k][r], sim[k][r]};
             }
         }
-        bwd_decays<R>(p, b, h, c, Ar, Ai, sAl, sLam, nullptr);
+        bwd_decays<R>(p, c, pdt, Ar, Ai, sAl, sLam, nullptr);
         if (tid < R)  // REV: e_in = exp(Lam[l]); forward: e_end = exp(Lam[R-1] - Lam[l])
             *(v2f *)&sF[2 * tid] = REV ? cexp_diff(sLam, tid, -1) : cexp_diff(sLam, R - 1, tid);
         if (tid == R)
             *(v2f *)&sDec[0] = cexp_diff(sLam, R - 1, -1);
         block_sync();
-        for (int i = tid; i < R * 64; i += 512) {
-            const int l = i >> 6, col = i & 63;
-            const int t = c * p.Q + l;
-            const bool valid = l < p.Q && t < p.T;
-            const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
-            v2f a = v2f{0.f, 0.f};
-            if (valid && col < N)
-                a = ld_c(REV ? p.Ct : p.Bt, row * N + col);
-            a = cmul(a, *(const v2f *)&sF[2 * l]);
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+            const v2f a = cmul(pa[j], *(const v2f *)&sF[2 * l]);
             sAre[l * LD + col] = a.x;
             sAim[l * LD + col] = a.y;
             sAimN[l * LD + col] = -a.y;
-            if (REV) {
-                sXre[l * LD + col] = (valid && col < D) ? p.gy[row * D + col] : 0.f;
-            } else {
-                v2f xv = v2f{0.f, 0.f};
-                if (valid && col < D)
-                    xv = ld_c(p.x, row * D + col);
-                sXre[l * LD + col] = xv.x;
-                sXim[l * LD + col] = xv.y;
-            }
+            sXre[l * LD + col] = px[j].x;
+            if (!REV)
+                sXim[l * LD + col] = px[j].y;
         }
         block_sync();
+        if (ci + 1 < p.nc)
+            fetch(REV ? c - 1 : c + 1);
         const float dr = sDec[0], di = sDec[1];
         for (int k = 0; k < 2; ++k) {
             const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
@@ -264,8 +285,10 @@ SSD_DEVICE v4f row_total(v4f v)
     return v;
 }
 
-// One workgroup per (b, h, chunk); all chunks run in parallel from the stored
-// entering states and leaving adjoints.
+// Every chunk is independent given the stored entering states and leaving
+// adjoints. A fixed number of workgroups (about one per compute unit) take the
+// chunks in a strided loop, loading the next chunk's inputs into registers
+// while the current one is evaluated.
 template <int R>
 SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
 {
@@ -296,316 +319,382 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sEend[2 * R];
     SSD_LDS float sRow[4 * 4 * 2 * R];  // [O, I, Off, In][column tile][row] complex
     SSD_LDS float sTc[16];
+    SSD_LDS float sEv[2 * R];  // per row: (O - I + Off) and In, all column tiles
+    SSD_LDS float sEe[2 * R];
 
     const int tid = thread_id();
     const int lane = tid & 63;
     const int w = wave_id();
-    const int64_t blk = block_id();
-    const int64_t seq = blk / p.nc;
-    const int c = (int)(blk % p.nc);
-    const int b = (int)(seq / p.H), h = (int)(seq % p.H);
-    const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
     const int N = p.N, D = p.D;
+    const int64_t total = (int64_t)p.B * p.H * p.nc;
 
-    bwd_decays<R>(p, b, h, c, Ar, Ai, sAl, sLam, sDt);
-    if (tid < R) {
-        *(v2f *)&sEin[2 * tid] = cexp_diff(sLam, tid, -1);
-        *(v2f *)&sEend[2 * tid] = cexp_diff(sLam, R - 1, tid);
-    }
-    for (int i = tid; i < R * 64; i += 512) {
-        const int l = i >> 6, col = i & 63;
-        const int t = c * p.Q + l;
-        const bool valid = l < p.Q && t < p.T;
-        const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
-        v2f bv = v2f{0.f, 0.f}, cv = v2f{0.f, 0.f}, xv = v2f{0.f, 0.f};
-        float g = 0.f;
-        if (valid && col < N) {
-            bv = ld_c(p.Bt, row * N + col);
-            cv = ld_c(p.Ct, row * N + col);
+    // The next chunk's inputs are loaded into registers while the current one
+    // is evaluated (PER row elements and PS state elements per thread).
+    constexpr int PER = R * 64 / 512;
+    constexpr int PS = 64 * 64 / 512;
+    v2f pb[PER], pc[PER], px[PER], ph[PS], pg[PS];
+    float pgy[PER];
+    float pdt = 0.f;
+    auto fetch = [&](int64_t k) {
+        const int64_t sq = k / p.nc;
+        const int cc = (int)(k % p.nc);
+        const int bb = (int)(sq / p.H), hh = (int)(sq % p.H);
+        pdt = bwd_load_dt<R>(p, bb, hh, cc);
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+            const int t = cc * p.Q + l;
+            const bool valid = l < p.Q && t < p.T;
+            const int64_t row = ((int64_t)bb * p.T + t) * p.H + hh;
+            const bool vn = valid && col < N, vd = valid && col < D;
+            pb[j] = vn ? ld_c(p.Bt, row * N + col) : v2f{0.f, 0.f};
+            pc[j] = vn ? ld_c(p.Ct, row * N + col) : v2f{0.f, 0.f};
+            px[j] = vd ? ld_c(p.x, row * D + col) : v2f{0.f, 0.f};
+            pgy[j] = vd ? p.gy[row * D + col] : 0.f;
         }
-        if (valid && col < D) {
-            xv = ld_c(p.x, row * D + col);
-            g = p.gy[row * D + col];
+        const float *hs = p.fwd_states + k * (int64_t)kStateFloats;
+        const float *gs = p.adj_states + k * (int64_t)kStateFloats;
+        for (int j = 0; j < PS; ++j) {
+            ph[j] = ld_c(hs, tid + 512 * j);
+            pg[j] = ld_c(gs, tid + 512 * j);
         }
-        sBre[l * LD + col] = bv.x;
-        sBim[l * LD + col] = bv.y;
-        sCre[l * LD + col] = cv.x;
-        sCim[l * LD + col] = cv.y;
-        sXre[l * LD + col] = xv.x;
-        sXim[l * LD + col] = xv.y;
-        sGy[l * LD + col] = g;
-    }
-    {
-        const float *hs = p.fwd_states + (seq * p.nc + c) * (int64_t)kStateFloats;
-        const float *gs = p.adj_states + (seq * p.nc + c) * (int64_t)kStateFloats;
-        for (int i = tid; i < 64 * 64; i += 512) {
-            const int n = i >> 6, d = i & 63;
-            const v2f hv = ld_c(hs, i), gv = ld_c(gs, i);
-            sHre[n * SL + d] = hv.x;
-            sHim[n * SL + d] = hv.y;
-            sGre[n * SL + d] = gv.x;
-            sGim[n * SL + d] = gv.y;
+    };
+    auto stage = [&]() {
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+            sBre[l * LD + col] = pb[j].x;
+            sBim[l * LD + col] = pb[j].y;
+            sCre[l * LD + col] = pc[j].x;
+            sCim[l * LD + col] = pc[j].y;
+            sXre[l * LD + col] = px[j].x;
+            sXim[l * LD + col] = px[j].y;
+            sGy[l * LD + col] = pgy[j];
         }
-    }
-    block_sync();
+        for (int j = 0; j < PS; ++j) {
+            const int i = tid + 512 * j, n = i >> 6, d = i & 63;
+            sHre[n * SL + d] = ph[j].x;
+            sHim[n * SL + d] = ph[j].y;
+            sGre[n * SL + d] = pg[j].x;
+            sGim[n * SL + d] = pg[j].y;
+        }
+    };
 
-    // Raw Gram (C B^T) tiles on waves 0.., raw gy x^T tiles on waves 4..
-    if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
-        const bool gram = w < 4;
-        const int k = gram ? w : w - 4;
-        const int lt = k < NT ? k : NT - 1, st = k < NT ? k : 0;  // (0,0), (1,1), (1,0)
-        const int lrow = lt * 16 + (lane & 15), scol = st * 16 + (lane & 15);
-        v4f rp = {0.f, 0.f, 0.f, 0.f}, rn = rp, im = rp;
-        for (int k0 = 0; k0 < 64; k0 += 4) {
-            const int kk = k0 + (lane >> 4);
-            if (gram) {
-                const float cr = sCre[lrow * LD + kk], cim = sCim[lrow * LD + kk];
-                const float br = sBre[scol * LD + kk], bim = sBim[scol * LD + kk];
-                rp = mfma_16x16x4(cr, br, rp);
-                rn = mfma_16x16x4(cim, bim, rn);
-                im = mfma_16x16x4(cr, bim, im);
-                im = mfma_16x16x4(cim, br, im);
+    int64_t blk = block_id();
+    if (blk >= total)
+        return;
+    fetch(blk);
+    stage();
+    for (;;) {
+        const int64_t seq = blk / p.nc;
+        const int c = (int)(blk % p.nc);
+        const int b = (int)(seq / p.H), h = (int)(seq % p.H);
+        const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
+        bwd_decays<R>(p, c, pdt, Ar, Ai, sAl, sLam, sDt);
+        if (tid < R) {
+            *(v2f *)&sEin[2 * tid] = cexp_diff(sLam, tid, -1);
+            *(v2f *)&sEend[2 * tid] = cexp_diff(sLam, R - 1, tid);
+        }
+        const int64_t next = blk + grid_blocks();
+        const bool has_next = next < total;
+        if (has_next)
+            fetch(next);
+
+        // Raw Gram (C B^T) tiles on waves 0.., raw gy x^T tiles on waves 4..
+        if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
+            const bool gram = w < 4;
+            const int k = gram ? w : w - 4;
+            const int lt = k < NT ? k : NT - 1, st = k < NT ? k : 0;  // (0,0), (1,1), (1,0)
+            const int lrow = lt * 16 + (lane & 15), scol = st * 16 + (lane & 15);
+            v4f rp = {0.f, 0.f, 0.f, 0.f}, rn = rp, im = rp;
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+                const int kk = k0 + (lane >> 4);
+                if (gram) {
+                    const float cr = sCre[lrow * LD + kk], cim = sCim[lrow * LD + kk];
+                    const float br = sBre[scol * LD + kk], bim = sBim[scol * LD + kk];
+                    rp = mfma_16x16x4(cr, br, rp);
+                    rn = mfma_16x16x4(cim, bim, rn);
+                    im = mfma_16x16x4(cr, bim, im);
+                    im = mfma_16x16x4(cim, br, im);
+                } else {
+                    const float g = sGy[lrow * LD + kk];
+                    rp = mfma_16x16x4(g, sXre[scol * LD + kk], rp);
+                    im = mfma_16x16x4(g, sXim[scol * LD + kk], im);
+                }
+            }
+            float *dre = gram ? sMre : sVre;
+            float *dim = gram ? sMim : sVim;
+            for (int r = 0; r < 4; ++r) {
+                const int l = lt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
+                dre[l * RL + s] = rp[r] - rn[r];
+                dim[l * RL + s] = im[r];
+            }
+        }
+        // <H, G> partial sums
+        {
+            float tr = 0.f, ti = 0.f;
+            for (int i = tid; i < 64 * 64; i += 512) {
+                const int n = i >> 6, d = i & 63;
+                const float hr = sHre[n * SL + d], hi = sHim[n * SL + d];
+                const float gr = sGre[n * SL + d], gi = sGim[n * SL + d];
+                tr += hr * gr - hi * gi;
+                ti += hr * gi + hi * gr;
+            }
+            tr += row_shr<1>(tr);
+            tr += row_shr<2>(tr);
+            tr += row_shr<4>(tr);
+            tr += row_shr<8>(tr);
+            ti += row_shr<1>(ti);
+            ti += row_shr<2>(ti);
+            ti += row_shr<4>(ti);
+            ti += row_shr<8>(ti);
+            const float t0r = lane_read(tr, 15), t1r = lane_read(tr, 31);
+            const float t2r = lane_read(tr, 47), t3r = lane_read(tr, 63);
+            const float t0i = lane_read(ti, 15), t1i = lane_read(ti, 31);
+            const float t2i = lane_read(ti, 47), t3i = lane_read(ti, 63);
+            if (lane == 0) {
+                sTc[2 * w] = (t0r + t1r) + (t2r + t3r);
+                sTc[2 * w + 1] = (t0i + t1i) + (t2i + t3i);
+            }
+        }
+        block_sync();
+
+        // M = Gram o L and V = (gy x^T) o L, zero above the diagonal.
+        for (int i = tid; i < R * R; i += 512) {
+            const int l = i / R, s = i % R;
+            float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
+            if (l >= s) {
+                const v2f L = cexp_diff(sLam, l, s);
+                const v2f m = cmul(v2f{sMre[l * RL + s], sMim[l * RL + s]}, L);
+                const v2f v = cmul(v2f{sVre[l * RL + s], sVim[l * RL + s]}, L);
+                mr = m.x;
+                mi = m.y;
+                vr = v.x;
+                vi = v.y;
+            }
+            sMre[l * RL + s] = mr;
+            sMim[l * RL + s] = mi;
+            sVre[l * RL + s] = vr;
+            sVim[l * RL + s] = vi;
+        }
+        block_sync();
+
+        // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
+        // columns n); NT x 4 tiles of each, dealt round-robin over the eight waves.
+        for (int tile = w; tile < 3 * NT * 4; tile += 8) {
+            const int kind = tile / (NT * 4);
+            const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
+            const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
+            const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
+            v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
+            v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
+            if (kind == 0) {
+                // conj(gx) = M^T gy + e_end (B G)
+                for (int k0 = 0; k0 < 64; k0 += 4) {
+                    const int n = k0 + (lane >> 4);
+                    const float br = sBre[arow * LD + n], bi = sBim[arow * LD + n];
+                    const float gr = sGre[n * SL + bcol], gi = sGim[n * SL + bcol];
+                    p2r = mfma_16x16x4(br, gr, p2r);
+                    p2n = mfma_16x16x4(bi, gi, p2n);
+                    p2i = mfma_16x16x4(br, gi, p2i);
+                    p2i = mfma_16x16x4(bi, gr, p2i);
+                }
+                for (int k0 = rt * 16; k0 < R; k0 += 4) {
+                    const int l = k0 + (lane >> 4);
+                    const float g = sGy[l * LD + bcol];
+                    p1r = mfma_16x16x4(sMre[l * RL + arow], g, p1r);
+                    p1i = mfma_16x16x4(sMim[l * RL + arow], g, p1i);
+                }
+            } else if (kind == 1) {
+                // conj(gB) = V^T C + e_end (x G^T)
+                for (int k0 = 0; k0 < 64; k0 += 4) {
+                    const int d = k0 + (lane >> 4);
+                    const float xr = sXre[arow * LD + d], xi = sXim[arow * LD + d];
+                    const float gr = sGre[bcol * SL + d], gi = sGim[bcol * SL + d];
+                    p2r = mfma_16x16x4(xr, gr, p2r);
+                    p2n = mfma_16x16x4(xi, gi, p2n);
+                    p2i = mfma_16x16x4(xr, gi, p2i);
+                    p2i = mfma_16x16x4(xi, gr, p2i);
+                }
+                for (int k0 = rt * 16; k0 < R; k0 += 4) {
+                    const int l = k0 + (lane >> 4);
+                    const float vr = sVre[l * RL + arow], vi = sVim[l * RL + arow];
+                    const float cr = sCre[l * LD + bcol], cim = sCim[l * LD + bcol];
+                    p1r = mfma_16x16x4(vr, cr, p1r);
+                    p1n = mfma_16x16x4(vi, cim, p1n);
+                    p1i = mfma_16x16x4(vr, cim, p1i);
+                    p1i = mfma_16x16x4(vi, cr, p1i);
+                }
             } else {
-                const float g = sGy[lrow * LD + kk];
-                rp = mfma_16x16x4(g, sXre[scol * LD + kk], rp);
-                im = mfma_16x16x4(g, sXim[scol * LD + kk], im);
+                // conj(gC) = V B + e_in (gy H^T)
+                for (int k0 = 0; k0 < 64; k0 += 4) {
+                    const int d = k0 + (lane >> 4);
+                    const float g = sGy[arow * LD + d];
+                    p2r = mfma_16x16x4(g, sHre[bcol * SL + d], p2r);
+                    p2i = mfma_16x16x4(g, sHim[bcol * SL + d], p2i);
+                }
+                for (int k0 = 0; k0 < rt * 16 + 16; k0 += 4) {
+                    const int s = k0 + (lane >> 4);
+                    const float vr = sVre[arow * RL + s], vi = sVim[arow * RL + s];
+                    const float br = sBre[s * LD + bcol], bi = sBim[s * LD + bcol];
+                    p1r = mfma_16x16x4(vr, br, p1r);
+                    p1n = mfma_16x16x4(vi, bi, p1n);
+                    p1i = mfma_16x16x4(vr, bi, p1i);
+                    p1i = mfma_16x16x4(vi, br, p1i);
+                }
             }
-        }
-        float *dre = gram ? sMre : sVre;
-        float *dim = gram ? sMim : sVim;
-        for (int r = 0; r < 4; ++r) {
-            const int l = lt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
-            dre[l * RL + s] = rp[r] - rn[r];
-            dim[l * RL + s] = im[r];
-        }
-    }
-    // <H, G> partial sums
-    {
-        float tr = 0.f, ti = 0.f;
-        for (int i = tid; i < 64 * 64; i += 512) {
-            const int n = i >> 6, d = i & 63;
-            const float hr = sHre[n * SL + d], hi = sHim[n * SL + d];
-            const float gr = sGre[n * SL + d], gi = sGim[n * SL + d];
-            tr += hr * gr - hi * gi;
-            ti += hr * gi + hi * gr;
-        }
-        tr += row_shr<1>(tr);
-        tr += row_shr<2>(tr);
-        tr += row_shr<4>(tr);
-        tr += row_shr<8>(tr);
-        ti += row_shr<1>(ti);
-        ti += row_shr<2>(ti);
-        ti += row_shr<4>(ti);
-        ti += row_shr<8>(ti);
-        const float t0r = lane_read(tr, 15), t1r = lane_read(tr, 31);
-        const float t2r = lane_read(tr, 47), t3r = lane_read(tr, 63);
-        const float t0i = lane_read(ti, 15), t1i = lane_read(ti, 31);
-        const float t2i = lane_read(ti, 47), t3i = lane_read(ti, 63);
-        if (lane == 0) {
-            sTc[2 * w] = (t0r + t1r) + (t2r + t3r);
-            sTc[2 * w + 1] = (t0i + t1i) + (t2i + t3i);
-        }
-    }
-    block_sync();
-
-    // M = Gram o L and V = (gy x^T) o L, zero above the diagonal.
-    for (int i = tid; i < R * R; i += 512) {
-        const int l = i / R, s = i % R;
-        float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
-        if (l >= s) {
-            const v2f L = cexp_diff(sLam, l, s);
-            const v2f m = cmul(v2f{sMre[l * RL + s], sMim[l * RL + s]}, L);
-            const v2f v = cmul(v2f{sVre[l * RL + s], sVim[l * RL + s]}, L);
-            mr = m.x;
-            mi = m.y;
-            vr = v.x;
-            vi = v.y;
-        }
-        sMre[l * RL + s] = mr;
-        sMim[l * RL + s] = mi;
-        sVre[l * RL + s] = vr;
-        sVim[l * RL + s] = vi;
-    }
-    block_sync();
-
-    // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
-    // columns n); NT x 4 tiles of each, dealt round-robin over the eight waves.
-    for (int tile = w; tile < 3 * NT * 4; tile += 8) {
-        const int kind = tile / (NT * 4);
-        const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
-        const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
-        const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
-        v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
-        v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
-        if (kind == 0) {
-            // conj(gx) = M^T gy + e_end (B G)
-            for (int k0 = 0; k0 < 64; k0 += 4) {
-                const int n = k0 + (lane >> 4);
-                const float br = sBre[arow * LD + n], bi = sBim[arow * LD + n];
-                const float gr = sGre[n * SL + bcol], gi = sGim[n * SL + bcol];
-                p2r = mfma_16x16x4(br, gr, p2r);
-                p2n = mfma_16x16x4(bi, gi, p2n);
-                p2i = mfma_16x16x4(br, gi, p2i);
-                p2i = mfma_16x16x4(bi, gr, p2i);
+            // Rows of this lane's accumulator entries and the row factor of the edge term.
+            const int col = ct * 16 + (lane & 15);
+            const float *fac = kind == 2 ? sEin : sEend;
+            const float *dre = kind == 2 ? sCre : sBre;   // the row dot products' other factor
+            const float *dim = kind == 2 ? sCim : sBim;
+            v4f outr, outi, d1r, d1i, d2r, d2i;
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * (lane >> 4) + r;
+                const v2f f = *(const v2f *)&fac[2 * row];
+                const v2f e2 = cmul(f, v2f{p2r[r] - p2n[r], p2i[r]});
+                const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
+                outr[r] = e1.x + e2.x;
+                outi[r] = e1.y + e2.y;
+                const v2f q = v2f{dre[row * LD + col], dim[row * LD + col]};
+                const v2f q1 = cmul(q, e1), q2 = cmul(q, e2);
+                d1r[r] = q1.x;
+                d1i[r] = q1.y;
+                d2r[r] = q2.x;
+                d2i[r] = q2.y;
             }
-            for (int k0 = rt * 16; k0 < R; k0 += 4) {
-                const int l = k0 + (lane >> 4);
-                const float g = sGy[l * LD + bcol];
-                p1r = mfma_16x16x4(sMre[l * RL + arow], g, p1r);
-                p1i = mfma_16x16x4(sMim[l * RL + arow], g, p1i);
+            if (kind != 0) {
+                d1r = row_total(d1r);
+                d1i = row_total(d1i);
+                d2r = row_total(d2r);
+                d2i = row_total(d2i);
+                if ((lane & 15) == 15) {
+                    // kind 1 (gB): I and In; kind 2 (gC): O and Off
+                    const int q1 = kind == 2 ? 0 : 1, q2 = kind == 2 ? 2 : 3;
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = rt * 16 + 4 * (lane >> 4) + r;
+                        sRow[((q1 * 4 + ct) * R + row) * 2] = d1r[r];
+                        sRow[((q1 * 4 + ct) * R + row) * 2 + 1] = d1i[r];
+                        sRow[((q2 * 4 + ct) * R + row) * 2] = d2r[r];
+                        sRow[((q2 * 4 + ct) * R + row) * 2 + 1] = d2i[r];
+                    }
+                }
             }
-        } else if (kind == 1) {
-            // conj(gB) = V^T C + e_end (x G^T)
-            for (int k0 = 0; k0 < 64; k0 += 4) {
-                const int d = k0 + (lane >> 4);
-                const float xr = sXre[arow * LD + d], xi = sXim[arow * LD + d];
-                const float gr = sGre[bcol * SL + d], gi = sGim[bcol * SL + d];
-                p2r = mfma_16x16x4(xr, gr, p2r);
-                p2n = mfma_16x16x4(xi, gi, p2n);
-                p2i = mfma_16x16x4(xr, gi, p2i);
-                p2i = mfma_16x16x4(xi, gr, p2i);
-            }
-            for (int k0 = rt * 16; k0 < R; k0 += 4) {
-                const int l = k0 + (lane >> 4);
-                const float vr = sVre[l * RL + arow], vi = sVim[l * RL + arow];
-                const float cr = sCre[l * LD + bcol], cim = sCim[l * LD + bcol];
-                p1r = mfma_16x16x4(vr, cr, p1r);
-                p1n = mfma_16x16x4(vi, cim, p1n);
-                p1i = mfma_16x16x4(vr, cim, p1i);
-                p1i = mfma_16x16x4(vi, cr, p1i);
-            }
-        } else {
-            // conj(gC) = V B + e_in (gy H^T)
-            for (int k0 = 0; k0 < 64; k0 += 4) {
-                const int d = k0 + (lane >> 4);
-                const float g = sGy[arow * LD + d];
-                p2r = mfma_16x16x4(g, sHre[bcol * SL + d], p2r);
-                p2i = mfma_16x16x4(g, sHim[bcol * SL + d], p2i);
-            }
-            for (int k0 = 0; k0 < rt * 16 + 16; k0 += 4) {
-                const int s = k0 + (lane >> 4);
-                const float vr = sVre[arow * RL + s], vi = sVim[arow * RL + s];
-                const float br = sBre[s * LD + bcol], bi = sBim[s * LD + bcol];
-                p1r = mfma_16x16x4(vr, br, p1r);
-                p1n = mfma_16x16x4(vi, bi, p1n);
-                p1i = mfma_16x16x4(vr, bi, p1i);
-                p1i = mfma_16x16x4(vi, br, p1i);
-            }
-        }
-        // Rows of this lane's accumulator entries and the row factor of the edge term.
-        const int col = ct * 16 + (lane & 15);
-        const float *fac = kind == 2 ? sEin : sEend;
-        const float *dre = kind == 2 ? sCre : sBre;   // the row dot products' other factor
-        const float *dim = kind == 2 ? sCim : sBim;
-        v4f outr, outi, d1r, d1i, d2r, d2i;
-        for (int r = 0; r < 4; ++r) {
-            const int row = rt * 16 + 4 * (lane >> 4) + r;
-            const v2f f = *(const v2f *)&fac[2 * row];
-            const v2f e2 = cmul(f, v2f{p2r[r] - p2n[r], p2i[r]});
-            const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
-            outr[r] = e1.x + e2.x;
-            outi[r] = e1.y + e2.y;
-            const v2f q = v2f{dre[row * LD + col], dim[row * LD + col]};
-            const v2f q1 = cmul(q, e1), q2 = cmul(q, e2);
-            d1r[r] = q1.x;
-            d1i[r] = q1.y;
-            d2r[r] = q2.x;
-            d2i[r] = q2.y;
-        }
-        if (kind != 0) {
-            d1r = row_total(d1r);
-            d1i = row_total(d1i);
-            d2r = row_total(d2r);
-            d2i = row_total(d2i);
-            if ((lane & 15) == 15) {
-                // kind 1 (gB): I and In; kind 2 (gC): O and Off
-                const int q1 = kind == 2 ? 0 : 1, q2 = kind == 2 ? 2 : 3;
-                for (int r = 0; r < 4; ++r) {
-                    const int row = rt * 16 + 4 * (lane >> 4) + r;
-                    sRow[((q1 * 4 + ct) * R + row) * 2] = d1r[r];
-                    sRow[((q1 * 4 + ct) * R + row) * 2 + 1] = d1i[r];
-                    sRow[((q2 * 4 + ct) * R + row) * 2] = d2r[r];
-                    sRow[((q2 * 4 + ct) * R + row) * 2 + 1] = d2i[r];
+            float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
+            const int width = kind == 0 ? D : N;
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * (lane >> 4) + r;
+                const int t = c * p.Q + row;
+                if (row < p.Q && t < p.T && col < width) {
+                    const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
+                    *(v2f *)&dst[2 * (g * width + col)] = v2f{outr[r], -outi[r]};
                 }
             }
         }
-        float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
-        const int width = kind == 0 ? D : N;
-        for (int r = 0; r < 4; ++r) {
-            const int row = rt * 16 + 4 * (lane >> 4) + r;
-            const int t = c * p.Q + row;
-            if (row < p.Q && t < p.T && col < width) {
-                const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
-                *(v2f *)&dst[2 * (g * width + col)] = v2f{outr[r], -outi[r]};
-            }
-        }
-    }
-    block_sync();
+        block_sync();
 
-    if (tid == 0) {
-        float tr = 0.f, ti = 0.f;
-        for (int i = 0; i < 8; ++i) {
-            tr += sTc[2 * i];
-            ti += sTc[2 * i + 1];
-        }
-        const v2f dec = cexp_diff(sLam, R - 1, -1);
-        const v2f Tc = cmul(dec, v2f{tr, ti});
-        auto part = [&](int q, int row) {
-            v2f s = v2f{0.f, 0.f};
+        // Decay gradients. Rows j < R (wave 0): v_j = (O - I + Off)_j and the
+        // edge share In_j, summed over the four column tiles in order.
+        if (tid < R) {
+            v2f v = v2f{0.f, 0.f}, e = v2f{0.f, 0.f};
             for (int ct = 0; ct < 4; ++ct) {
-                s.x += sRow[((q * 4 + ct) * R + row) * 2];
-                s.y += sRow[((q * 4 + ct) * R + row) * 2 + 1];
+                const float *o = &sRow[((0 * 4 + ct) * R + tid) * 2];
+                const float *in = &sRow[((1 * 4 + ct) * R + tid) * 2];
+                const float *off = &sRow[((2 * 4 + ct) * R + tid) * 2];
+                const float *ed = &sRow[((3 * 4 + ct) * R + tid) * 2];
+                v.x += o[0] - in[0] + off[0];
+                v.y += o[1] - in[1] + off[1];
+                e.x += ed[0];
+                e.y += ed[1];
             }
-            return s;
-        };
-        // tail[t] = sum_{j >= t} (O - I + Off)_j, kept in sAl (a is no longer needed)
-        v2f tail = v2f{0.f, 0.f};
-        for (int j = R - 1; j >= 0; --j) {
-            const v2f o = part(0, j), in = part(1, j), off = part(2, j);
-            tail.x += o.x - in.x + off.x;
-            tail.y += o.y - in.y + off.y;
-            sAl[2 * j] = tail.x;
-            sAl[2 * j + 1] = tail.y;
+            *(v2f *)&sEv[2 * tid] = v;
+            *(v2f *)&sEe[2 * tid] = e;
         }
-        v2f head = v2f{0.f, 0.f}, gA = v2f{0.f, 0.f};
-        for (int t0 = 0; t0 < R; ++t0) {
-            const float fr = sAl[2 * t0] + head.x + Tc.x;
-            const float fi = sAl[2 * t0 + 1] + head.y + Tc.y;
-            const v2f edge = part(3, t0);
-            head.x += edge.x;
-            head.y += edge.y;
-            const int t = c * p.Q + t0;
-            if (t0 < p.Q && t < p.T) {
-                // ga = conj(dF/da)
-                const float gar = fr, gai = -fi;
-                const float dtv = sDt[t0];
-                const float sig = 1.f / (1.f + expf(-dtv));
-                p.gdt[((int64_t)b * p.T + t) * p.H + h] = (Ar * gar + Ai * gai) * sig;
-                const float sp = softplus_f(dtv);
-                gA.x += sp * gar;
-                gA.y += sp * gai;
+        block_sync();
+        if (w == 0) {
+            // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>
+            const int t0 = lane;
+            float gAr = 0.f, gAi = 0.f;
+            if (t0 < R) {
+                float tr = 0.f, ti = 0.f;
+                for (int i = 0; i < 8; ++i) {
+                    tr += sTc[2 * i];
+                    ti += sTc[2 * i + 1];
+                }
+                const v2f Tc = cmul(cexp_diff(sLam, R - 1, -1), v2f{tr, ti});
+                float fr = Tc.x, fi = Tc.y;
+                for (int j = R - 1; j >= t0; --j) {
+                    fr += sEv[2 * j];
+                    fi += sEv[2 * j + 1];
+                }
+                for (int j = 0; j < t0; ++j) {
+                    fr += sEe[2 * j];
+                    fi += sEe[2 * j + 1];
+                }
+                const int t = c * p.Q + t0;
+                if (t0 < p.Q && t < p.T) {
+                    // ga = conj(dF/da)
+                    const float gar = fr, gai = -fi;
+                    const float dtv = sDt[t0];
+                    const float sig = 1.f / (1.f + expf(-dtv));
+                    p.gdt[((int64_t)b * p.T + t) * p.H + h] = (Ar * gar + Ai * gai) * sig;
+                    const float sp = softplus_f(dtv);
+                    gAr = sp * gar;
+                    gAi = sp * gai;
+                }
             }
+            // this chunk's share of gA: a fixed-order sum over the wave
+            gAr += row_shr<1>(gAr);
+            gAr += row_shr<2>(gAr);
+            gAr += row_shr<4>(gAr);
+            gAr += row_shr<8>(gAr);
+            gAi += row_shr<1>(gAi);
+            gAi += row_shr<2>(gAi);
+            gAi += row_shr<4>(gAi);
+            gAi += row_shr<8>(gAi);
+            const float r0 = lane_read(gAr, 15), r1 = lane_read(gAr, 31);
+            const float i0 = lane_read(gAi, 15), i1 = lane_read(gAi, 31);
+            if (lane == 0)
+                *(v2f *)&p.gA_part[2 * blk] = v2f{r0 + r1, i0 + i1};
         }
-        *(v2f *)&p.gA_part[2 * blk] = gA;
+        // the planes are free once the output tiles are done: stage the next
+        // chunk while wave 0 finishes this one's decay gradients
+        if (has_next)
+            stage();
+        block_sync();
+        if (!has_next)
+            break;
+        blk = next;
     }
 }
 
-// gA[h] = sum over batch rows and chunks of the per-chunk shares, in order.
-SSD_KERNEL(64) void bwd_reduce_gA_kernel(const float *part, int B, int H, int nc, float *gA)
+// gA[h] = sum over batch rows and chunks of the per-chunk shares: one
+// workgroup per head; thread j adds shares j, j + 256, ... in order, then a
+// fixed tree over the threads (the result does not depend on timing).
+SSD_KERNEL(256) void bwd_reduce_gA_kernel(const float *part, int B, int H, int nc, float *gA)
 {
-    const int h = (int)(block_id() * 64 + thread_id());
-    if (h >= H)
-        return;
+    SSD_LDS float sre[256];
+    SSD_LDS float sim[256];
+    const int h = (int)block_id();
+    const int tid = thread_id();
+    const int64_t n = (int64_t)B * nc;
     float sr = 0.f, si = 0.f;
-    for (int b = 0; b < B; ++b) {
-        const float *q = part + ((int64_t)b * H + h) * nc * 2;
-        for (int c = 0; c < nc; ++c) {
-            sr += q[2 * c];
-            si += q[2 * c + 1];
-        }
+    for (int64_t k = tid; k < n; k += 256) {
+        const int64_t b = k / nc, c = k % nc;
+        const v2f v = ld_c(part, (b * H + h) * nc + c);
+        sr += v.x;
+        si += v.y;
     }
-    gA[2 * h] = sr;
-    gA[2 * h + 1] = si;
+    sre[tid] = sr;
+    sim[tid] = si;
+    block_sync();
+    for (int half = 128; half > 0; half >>= 1) {
+        if (tid < half) {
+            sre[tid] += sre[tid + half];
+            sim[tid] += sim[tid + half];
+        }
+        block_sync();
+    }
+    if (tid == 0)
+        *(v2f *)&gA[2 * h] = v2f{sre[0], sim[0]};
 }
 
 }  // namespace ssd

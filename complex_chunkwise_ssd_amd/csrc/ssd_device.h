@@ -56,6 +56,7 @@ SSD_DEVICE void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 SSD_DEVICE void lds_add(float *p, float v) { atomicAdd(p, v); }
 SSD_DEVICE int thread_id() { return (int)threadIdx.x; }
 SSD_DEVICE int64_t block_id() { return (int64_t)blockIdx.x; }
+SSD_DEVICE int64_t grid_blocks() { return (int64_t)gridDim.x; }
 // Wave index as a wave-uniform (scalar) value.
 SSD_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 

@@ -70,6 +70,7 @@ static int g_cap = 0;
 static int g_n = 0;
 static int g_cur = -1;
 static int64_t g_block = 0;
+static int64_t g_grid = 0;
 static void *g_sched_sp = nullptr;
 static std::function<void()> *g_fn = nullptr;
 static long g_mfma_count = 0;
@@ -209,6 +210,7 @@ static void launch(dim3 grid, dim3 block, std::function<void()> fn)
     g_n = n;
     g_fn = &fn;
     const int64_t blocks = (int64_t)grid.x * grid.y * grid.z;
+    g_grid = blocks;
     for (int64_t blk = 0; blk < blocks; ++blk) {
         g_block = blk;
         for (int i = 0; i < n; ++i)
@@ -260,6 +262,7 @@ static inline hipError_t hipGetLastError() { return emu::g_error; }
 // ------------------------------------------------------------ device primitives
 SSD_DEVICE int thread_id() { return emu::g_cur; }
 SSD_DEVICE int64_t block_id() { return emu::g_block; }
+SSD_DEVICE int64_t grid_blocks() { return emu::g_grid; }
 SSD_DEVICE int wave_id() { return emu::g_cur >> 6; }
 
 SSD_DEVICE v4f mfma_16x16x4(float a, float b, v4f c)

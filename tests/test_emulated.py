@@ -130,6 +130,7 @@ BWD_CASES = [
     (1, 23, 2, 4, 5, 1),       # Q = 1
     (3, 7, 1, 2, 2, 64),       # T < Q
     (1, 130, 1, 8, 8, 256),
+    (2, 600, 2, 4, 4, 4),      # 600 chunks: each workgroup of the chunk pass takes several
 ]
 
 
