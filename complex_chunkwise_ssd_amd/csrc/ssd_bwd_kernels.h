@@ -84,36 +84,6 @@ inline BwdPlan make_bwd_plan(int64_t B, int64_t T, int64_t H, int64_t chunk)
 SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i]; }
 SSD_DEVICE v2f cmul_d(v2f a, v2f b) { return cmul(a, b); }
 
-// Running sums of a over one chunk, in double. Thread tid < R passes the dt of
-// chunk row tid (ignored past the chunk or past T, where a = 0); afterwards
-// sAl holds a and sLam the running sums, for every thread.
-template <int R>
-SSD_DEVICE void bwd_decays(const BwdParams &p, int c, float dtv, float Ar, float Ai, float *sAl,
-                           double *sLam, float *sDt)
-{
-    const int tid = thread_id();
-    if (tid < R) {
-        const int t = c * p.Q + tid;
-        const bool valid = tid < p.Q && t < p.T;
-        const float sp = valid ? softplus_f(dtv) : 0.f;
-        sAl[2 * tid] = sp * Ar;
-        sAl[2 * tid + 1] = sp * Ai;
-        if (sDt)
-            sDt[tid] = valid ? dtv : 0.f;
-    }
-    block_sync();
-    if (tid < R) {  // each row sums its own prefix, in order
-        double lr = 0.0, li = 0.0;
-        for (int l = 0; l <= tid; ++l) {
-            lr += (double)sAl[2 * l];
-            li += (double)sAl[2 * l + 1];
-        }
-        sLam[2 * tid] = lr;
-        sLam[2 * tid + 1] = li;
-    }
-    block_sync();
-}
-
 // dt of chunk row tid (tid < R), or 0 past the chunk or past T.
 template <int R>
 SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
@@ -121,6 +91,52 @@ SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
     const int tid = thread_id();
     const int t = c * p.Q + tid;
     return (tid < R && tid < p.Q && t < p.T) ? p.dt[((int64_t)b * p.T + t) * p.H + h] : 0.f;
+}
+
+// Double-precision lane moves (two 32-bit DPP / readlane moves).
+template <int n>
+SSD_DEVICE double row_shr_d(double v)
+{
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = (unsigned)row_shr_i<n>((int)(unsigned)u);
+    const unsigned hi = (unsigned)row_shr_i<n>((int)(unsigned)(u >> 32));
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+SSD_DEVICE double lane_read_d(double v, int src)
+{
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = (unsigned)lane_read_i((int)(unsigned)u, src);
+    const unsigned hi = (unsigned)lane_read_i((int)(unsigned)(u >> 32), src);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Inclusive prefix sum over lanes 0..31 (a fixed tree: doubling inside each
+// row of 16 lanes, then the first row's total added to the second row).
+SSD_DEVICE double prefix32_d(double v)
+{
+    v += row_shr_d<1>(v);
+    v += row_shr_d<2>(v);
+    v += row_shr_d<4>(v);
+    v += row_shr_d<8>(v);
+    const double first = lane_read_d(v, 15);
+    return (thread_id() & 63) >= 16 ? v + first : v;
+}
+
+// Called by all 64 lanes of one wave: lane l < R gets a_l = softplus(dt_l) A
+// of chunk c (0 past the chunk or past T; dtv is lane l's dt) and its running
+// sum lam (double); lam_end is the running sum at row R - 1, in every lane.
+template <int R>
+SSD_DEVICE void wave_decays(const BwdParams &p, int c, float dtv, float Ar, float Ai, double &lr,
+                            double &li, double &er, double &ei)
+{
+    const int l = thread_id() & 63;
+    const int t = c * p.Q + l;
+    const bool valid = l < R && l < p.Q && t < p.T;
+    const float sp = valid ? softplus_f(dtv) : 0.f;
+    lr = prefix32_d((double)(sp * Ar));
+    li = prefix32_d((double)(sp * Ai));
+    er = lane_read_d(lr, R - 1);
+    ei = lane_read_d(li, R - 1);
 }
 
 // exp of the difference of two running sums (taken in double, then rounded).
@@ -147,8 +163,6 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
     SSD_LDS float sAimN[R * LD];
     SSD_LDS float sXre[R * LD];
     SSD_LDS float sXim[R * LD];
-    SSD_LDS float sAl[2 * R];
-    SSD_LDS double sLam[2 * R];
     SSD_LDS float sF[2 * R];
     SSD_LDS float sDec[2];
 
@@ -207,11 +221,16 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
                 *(v2f *)&slot[2 * (n * 64 + d)] = v2f{sre[k][r], sim[k][r]};
             }
         }
-        bwd_decays<R>(p, c, pdt, Ar, Ai, sAl, sLam, nullptr);
-        if (tid < R)  // REV: e_in = exp(Lam[l]); forward: e_end = exp(Lam[R-1] - Lam[l])
-            *(v2f *)&sF[2 * tid] = REV ? cexp_diff(sLam, tid, -1) : cexp_diff(sLam, R - 1, tid);
-        if (tid == R)
-            *(v2f *)&sDec[0] = cexp_diff(sLam, R - 1, -1);
+        if (w == 0) {
+            // REV: e_in = exp(Lam[l]); forward: e_end = exp(Lam[R-1] - Lam[l])
+            double lr, li, er, ei;
+            wave_decays<R>(p, c, pdt, Ar, Ai, lr, li, er, ei);
+            if (lane < R)
+                *(v2f *)&sF[2 * lane] = REV ? cexp_f(v2f{(float)lr, (float)li})
+                                            : cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
+            if (lane == 0)
+                *(v2f *)&sDec[0] = cexp_f(v2f{(float)er, (float)ei});
+        }
         block_sync();
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
@@ -270,6 +289,42 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
 
 // ------------------------------------------------------------ the chunk pass
 
+// Kinds of one MFMA step over a 4-wide K block: complex x complex (four MFMAs:
+// rp += ar br, rn += ai bi, im += ar bi + ai br), real x complex (rp += a br,
+// im += a bi) and complex x real (rp += ar b, im += ai b).
+enum { kCC = 0, kRC = 1, kCR = 2 };
+
+// Steps k0 .. k1-1 of a tile product. ld(k) returns this lane's operands of
+// step k as {ar, ai, br, bi}; the next step's operands are read from LDS before
+// this step's MFMAs issue, so their latency hides behind the MFMAs.
+template <int KIND, class Ld>
+SSD_DEVICE void mma_steps(int k0, int k1, Ld ld, v4f &rp, v4f &rn, v4f &im)
+{
+    if (k0 >= k1)
+        return;
+    v4f cur = ld(k0);
+    for (int k = k0; k < k1; ++k) {
+        v4f nxt = cur;
+        if (k + 1 < k1)
+            nxt = ld(k + 1);
+        sched_fence();
+        if (KIND == kCC) {
+            rp = mfma_16x16x4(cur.x, cur.z, rp);
+            rn = mfma_16x16x4(cur.y, cur.w, rn);
+            im = mfma_16x16x4(cur.x, cur.w, im);
+            im = mfma_16x16x4(cur.y, cur.z, im);
+        } else if (KIND == kRC) {
+            rp = mfma_16x16x4(cur.x, cur.z, rp);
+            im = mfma_16x16x4(cur.x, cur.w, im);
+        } else {
+            rp = mfma_16x16x4(cur.x, cur.z, rp);
+            im = mfma_16x16x4(cur.y, cur.z, im);
+        }
+        sched_fence();
+        cur = nxt;
+    }
+}
+
 // Sum over the 16 lanes of each row of a 16 x 16 accumulator tile: lane 15 of
 // each group of 16 ends with the total of its 4 rows (inclusive prefix sums).
 SSD_DEVICE v4f row_total(v4f v)
@@ -312,7 +367,6 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sMim[R * RL];
     SSD_LDS float sVre[R * RL];
     SSD_LDS float sVim[R * RL];
-    SSD_LDS float sAl[2 * R];
     SSD_LDS double sLam[2 * R];
     SSD_LDS float sDt[R];
     SSD_LDS float sEin[2 * R];
@@ -335,29 +389,50 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     v2f pb[PER], pc[PER], px[PER], ph[PS], pg[PS];
     float pgy[PER];
     float pdt = 0.f;
-    auto fetch = [&](int64_t k) {
+    // fetch(part, k): part 0 = dt, B_t and C_t rows; 1 = x and grad_y rows;
+    // 2 = the entering state; 3 = the leaving adjoint. The parts of the next
+    // chunk are issued at different points of the current one, so that no
+    // wave stalls behind a long burst of loads.
+    // fetch<part>(k): part 0 = dt, B_t and C_t rows; 1 = x and grad_y rows;
+    // 2 = the entering state; 3 = the leaving adjoint. The parts of the next
+    // chunk are issued at different points of the current one, so that no
+    // wave stalls behind a long burst of loads.
+    auto fetch = [&](auto part_c, int64_t k) {
+        constexpr int part = decltype(part_c)::value;
         const int64_t sq = k / p.nc;
         const int cc = (int)(k % p.nc);
         const int bb = (int)(sq / p.H), hh = (int)(sq % p.H);
-        pdt = bwd_load_dt<R>(p, bb, hh, cc);
-        for (int j = 0; j < PER; ++j) {
-            const int i = tid + 512 * j, l = i >> 6, col = i & 63;
-            const int t = cc * p.Q + l;
-            const bool valid = l < p.Q && t < p.T;
-            const int64_t row = ((int64_t)bb * p.T + t) * p.H + hh;
-            const bool vn = valid && col < N, vd = valid && col < D;
-            pb[j] = vn ? ld_c(p.Bt, row * N + col) : v2f{0.f, 0.f};
-            pc[j] = vn ? ld_c(p.Ct, row * N + col) : v2f{0.f, 0.f};
-            px[j] = vd ? ld_c(p.x, row * D + col) : v2f{0.f, 0.f};
-            pgy[j] = vd ? p.gy[row * D + col] : 0.f;
-        }
-        const float *hs = p.fwd_states + k * (int64_t)kStateFloats;
-        const float *gs = p.adj_states + k * (int64_t)kStateFloats;
-        for (int j = 0; j < PS; ++j) {
-            ph[j] = ld_c(hs, tid + 512 * j);
-            pg[j] = ld_c(gs, tid + 512 * j);
+        if constexpr (part == 0)
+            pdt = bwd_load_dt<R>(p, bb, hh, cc);
+        if constexpr (part <= 1) {
+            for (int j = 0; j < PER; ++j) {
+                const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                const int t = cc * p.Q + l;
+                const bool valid = l < p.Q && t < p.T;
+                const int64_t row = ((int64_t)bb * p.T + t) * p.H + hh;
+                const bool vn = valid && col < N, vd = valid && col < D;
+                if constexpr (part == 0) {
+                    pb[j] = vn ? ld_c(p.Bt, row * N + col) : v2f{0.f, 0.f};
+                    pc[j] = vn ? ld_c(p.Ct, row * N + col) : v2f{0.f, 0.f};
+                } else {
+                    px[j] = vd ? ld_c(p.x, row * D + col) : v2f{0.f, 0.f};
+                    pgy[j] = vd ? p.gy[row * D + col] : 0.f;
+                }
+            }
+        } else {
+            const float *src = (part == 2 ? p.fwd_states : p.adj_states) + k * (int64_t)kStateFloats;
+            for (int j = 0; j < PS; ++j) {
+                if constexpr (part == 2)
+                    ph[j] = ld_c(src, tid + 512 * j);
+                else
+                    pg[j] = ld_c(src, tid + 512 * j);
+            }
         }
     };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
     auto stage = [&]() {
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
@@ -381,22 +456,34 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     int64_t blk = block_id();
     if (blk >= total)
         return;
-    fetch(blk);
+    fetch(P0{}, blk);
+    fetch(P1{}, blk);
+    fetch(P2{}, blk);
+    fetch(P3{}, blk);
     stage();
+    block_sync();
     for (;;) {
         const int64_t seq = blk / p.nc;
         const int c = (int)(blk % p.nc);
         const int b = (int)(seq / p.H), h = (int)(seq % p.H);
         const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
-        bwd_decays<R>(p, c, pdt, Ar, Ai, sAl, sLam, sDt);
-        if (tid < R) {
-            *(v2f *)&sEin[2 * tid] = cexp_diff(sLam, tid, -1);
-            *(v2f *)&sEend[2 * tid] = cexp_diff(sLam, R - 1, tid);
+        if (w == 0) {
+            // running sums and row factors of this chunk; read after the next barrier
+            double lr, li, er, ei;
+            wave_decays<R>(p, c, pdt, Ar, Ai, lr, li, er, ei);
+            if (lane < R) {
+                const int t = c * p.Q + lane;
+                sLam[2 * lane] = lr;
+                sLam[2 * lane + 1] = li;
+                sDt[lane] = (lane < p.Q && t < p.T) ? pdt : 0.f;
+                *(v2f *)&sEin[2 * lane] = cexp_f(v2f{(float)lr, (float)li});
+                *(v2f *)&sEend[2 * lane] = cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
+            }
         }
         const int64_t next = blk + grid_blocks();
         const bool has_next = next < total;
         if (has_next)
-            fetch(next);
+            fetch(P0{}, next);
 
         // Raw Gram (C B^T) tiles on waves 0.., raw gy x^T tiles on waves 4..
         if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
@@ -405,20 +492,18 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int lt = k < NT ? k : NT - 1, st = k < NT ? k : 0;  // (0,0), (1,1), (1,0)
             const int lrow = lt * 16 + (lane & 15), scol = st * 16 + (lane & 15);
             v4f rp = {0.f, 0.f, 0.f, 0.f}, rn = rp, im = rp;
-            for (int k0 = 0; k0 < 64; k0 += 4) {
-                const int kk = k0 + (lane >> 4);
-                if (gram) {
-                    const float cr = sCre[lrow * LD + kk], cim = sCim[lrow * LD + kk];
-                    const float br = sBre[scol * LD + kk], bim = sBim[scol * LD + kk];
-                    rp = mfma_16x16x4(cr, br, rp);
-                    rn = mfma_16x16x4(cim, bim, rn);
-                    im = mfma_16x16x4(cr, bim, im);
-                    im = mfma_16x16x4(cim, br, im);
-                } else {
-                    const float g = sGy[lrow * LD + kk];
-                    rp = mfma_16x16x4(g, sXre[scol * LD + kk], rp);
-                    im = mfma_16x16x4(g, sXim[scol * LD + kk], im);
-                }
+            const int g4 = lane >> 4;
+            if (gram) {
+                mma_steps<kCC>(0, 16, [&](int k) {
+                    const int kk = 4 * k + g4;
+                    return v4f{sCre[lrow * LD + kk], sCim[lrow * LD + kk], sBre[scol * LD + kk],
+                               sBim[scol * LD + kk]};
+                }, rp, rn, im);
+            } else {
+                mma_steps<kRC>(0, 16, [&](int k) {
+                    const int kk = 4 * k + g4;
+                    return v4f{sGy[lrow * LD + kk], 0.f, sXre[scol * LD + kk], sXim[scol * LD + kk]};
+                }, rp, rn, im);
             }
             float *dre = gram ? sMre : sVre;
             float *dim = gram ? sMim : sVim;
@@ -457,6 +542,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         }
         block_sync();
 
+        if (has_next) {
+            fetch(P1{}, next);
+            fetch(P2{}, next);
+        }
         // M = Gram o L and V = (gy x^T) o L, zero above the diagonal.
         for (int i = tid; i < R * R; i += 512) {
             const int l = i / R, s = i % R;
@@ -479,6 +568,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
 
         // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
         // columns n); NT x 4 tiles of each, dealt round-robin over the eight waves.
+        if (has_next)
+            fetch(P3{}, next);
         for (int tile = w; tile < 3 * NT * 4; tile += 8) {
             const int kind = tile / (NT * 4);
             const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
@@ -486,60 +577,41 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
             v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
             v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
+            const int g4 = lane >> 4;
             if (kind == 0) {
                 // conj(gx) = M^T gy + e_end (B G)
-                for (int k0 = 0; k0 < 64; k0 += 4) {
-                    const int n = k0 + (lane >> 4);
-                    const float br = sBre[arow * LD + n], bi = sBim[arow * LD + n];
-                    const float gr = sGre[n * SL + bcol], gi = sGim[n * SL + bcol];
-                    p2r = mfma_16x16x4(br, gr, p2r);
-                    p2n = mfma_16x16x4(bi, gi, p2n);
-                    p2i = mfma_16x16x4(br, gi, p2i);
-                    p2i = mfma_16x16x4(bi, gr, p2i);
-                }
-                for (int k0 = rt * 16; k0 < R; k0 += 4) {
-                    const int l = k0 + (lane >> 4);
-                    const float g = sGy[l * LD + bcol];
-                    p1r = mfma_16x16x4(sMre[l * RL + arow], g, p1r);
-                    p1i = mfma_16x16x4(sMim[l * RL + arow], g, p1i);
-                }
+                mma_steps<kCC>(0, 16, [&](int k) {
+                    const int n = 4 * k + g4;
+                    return v4f{sBre[arow * LD + n], sBim[arow * LD + n], sGre[n * SL + bcol],
+                               sGim[n * SL + bcol]};
+                }, p2r, p2n, p2i);
+                mma_steps<kCR>(rt * 4, R / 4, [&](int k) {
+                    const int l = 4 * k + g4;
+                    return v4f{sMre[l * RL + arow], sMim[l * RL + arow], sGy[l * LD + bcol], 0.f};
+                }, p1r, p1n, p1i);
             } else if (kind == 1) {
                 // conj(gB) = V^T C + e_end (x G^T)
-                for (int k0 = 0; k0 < 64; k0 += 4) {
-                    const int d = k0 + (lane >> 4);
-                    const float xr = sXre[arow * LD + d], xi = sXim[arow * LD + d];
-                    const float gr = sGre[bcol * SL + d], gi = sGim[bcol * SL + d];
-                    p2r = mfma_16x16x4(xr, gr, p2r);
-                    p2n = mfma_16x16x4(xi, gi, p2n);
-                    p2i = mfma_16x16x4(xr, gi, p2i);
-                    p2i = mfma_16x16x4(xi, gr, p2i);
-                }
-                for (int k0 = rt * 16; k0 < R; k0 += 4) {
-                    const int l = k0 + (lane >> 4);
-                    const float vr = sVre[l * RL + arow], vi = sVim[l * RL + arow];
-                    const float cr = sCre[l * LD + bcol], cim = sCim[l * LD + bcol];
-                    p1r = mfma_16x16x4(vr, cr, p1r);
-                    p1n = mfma_16x16x4(vi, cim, p1n);
-                    p1i = mfma_16x16x4(vr, cim, p1i);
-                    p1i = mfma_16x16x4(vi, cr, p1i);
-                }
+                mma_steps<kCC>(0, 16, [&](int k) {
+                    const int d = 4 * k + g4;
+                    return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
+                               sGim[bcol * SL + d]};
+                }, p2r, p2n, p2i);
+                mma_steps<kCC>(rt * 4, R / 4, [&](int k) {
+                    const int l = 4 * k + g4;
+                    return v4f{sVre[l * RL + arow], sVim[l * RL + arow], sCre[l * LD + bcol],
+                               sCim[l * LD + bcol]};
+                }, p1r, p1n, p1i);
             } else {
                 // conj(gC) = V B + e_in (gy H^T)
-                for (int k0 = 0; k0 < 64; k0 += 4) {
-                    const int d = k0 + (lane >> 4);
-                    const float g = sGy[arow * LD + d];
-                    p2r = mfma_16x16x4(g, sHre[bcol * SL + d], p2r);
-                    p2i = mfma_16x16x4(g, sHim[bcol * SL + d], p2i);
-                }
-                for (int k0 = 0; k0 < rt * 16 + 16; k0 += 4) {
-                    const int s = k0 + (lane >> 4);
-                    const float vr = sVre[arow * RL + s], vi = sVim[arow * RL + s];
-                    const float br = sBre[s * LD + bcol], bi = sBim[s * LD + bcol];
-                    p1r = mfma_16x16x4(vr, br, p1r);
-                    p1n = mfma_16x16x4(vi, bi, p1n);
-                    p1i = mfma_16x16x4(vr, bi, p1i);
-                    p1i = mfma_16x16x4(vi, br, p1i);
-                }
+                mma_steps<kRC>(0, 16, [&](int k) {
+                    const int d = 4 * k + g4;
+                    return v4f{sGy[arow * LD + d], 0.f, sHre[bcol * SL + d], sHim[bcol * SL + d]};
+                }, p2r, p2n, p2i);
+                mma_steps<kCC>(0, rt * 4 + 4, [&](int k) {
+                    const int sx = 4 * k + g4;
+                    return v4f{sVre[arow * RL + sx], sVim[arow * RL + sx], sBre[sx * LD + bcol],
+                               sBim[sx * LD + bcol]};
+                }, p1r, p1n, p1i);
             }
             // Rows of this lane's accumulator entries and the row factor of the edge term.
             const int col = ct * 16 + (lane & 15);
@@ -610,36 +682,57 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         }
         block_sync();
         if (w == 0) {
-            // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>
+            // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>: the
+            // suffix and prefix sums over the chunk rows as lane scans (fixed trees)
             const int t0 = lane;
+            const bool row = t0 < R;
+            float vr = row ? sEv[2 * t0] : 0.f, vi = row ? sEv[2 * t0 + 1] : 0.f;
+            float er = row ? sEe[2 * t0] : 0.f, ei = row ? sEe[2 * t0 + 1] : 0.f;
+            vr += row_shl<1>(vr);
+            vi += row_shl<1>(vi);
+            vr += row_shl<2>(vr);
+            vi += row_shl<2>(vi);
+            vr += row_shl<4>(vr);
+            vi += row_shl<4>(vi);
+            vr += row_shl<8>(vr);
+            vi += row_shl<8>(vi);
+            const float nr = lane_read(vr, 16), ni = lane_read(vi, 16);
+            if (t0 < 16) {
+                vr += nr;
+                vi += ni;
+            }
+            er += row_shr<1>(er);
+            ei += row_shr<1>(ei);
+            er += row_shr<2>(er);
+            ei += row_shr<2>(ei);
+            er += row_shr<4>(er);
+            ei += row_shr<4>(ei);
+            er += row_shr<8>(er);
+            ei += row_shr<8>(ei);
+            float xr = row_shr<1>(er), xi = row_shr<1>(ei);  // exclusive
+            const float pr = lane_read(er, 15), pi = lane_read(ei, 15);
+            if (t0 >= 16) {
+                xr += pr;
+                xi += pi;
+            }
+            float tr = 0.f, ti = 0.f;
+            for (int i = 0; i < 8; ++i) {
+                tr += sTc[2 * i];
+                ti += sTc[2 * i + 1];
+            }
+            const v2f Tc = cmul(cexp_diff(sLam, R - 1, -1), v2f{tr, ti});
+            const float fr = (vr + xr) + Tc.x, fi = (vi + xi) + Tc.y;
             float gAr = 0.f, gAi = 0.f;
-            if (t0 < R) {
-                float tr = 0.f, ti = 0.f;
-                for (int i = 0; i < 8; ++i) {
-                    tr += sTc[2 * i];
-                    ti += sTc[2 * i + 1];
-                }
-                const v2f Tc = cmul(cexp_diff(sLam, R - 1, -1), v2f{tr, ti});
-                float fr = Tc.x, fi = Tc.y;
-                for (int j = R - 1; j >= t0; --j) {
-                    fr += sEv[2 * j];
-                    fi += sEv[2 * j + 1];
-                }
-                for (int j = 0; j < t0; ++j) {
-                    fr += sEe[2 * j];
-                    fi += sEe[2 * j + 1];
-                }
-                const int t = c * p.Q + t0;
-                if (t0 < p.Q && t < p.T) {
-                    // ga = conj(dF/da)
-                    const float gar = fr, gai = -fi;
-                    const float dtv = sDt[t0];
-                    const float sig = 1.f / (1.f + expf(-dtv));
-                    p.gdt[((int64_t)b * p.T + t) * p.H + h] = (Ar * gar + Ai * gai) * sig;
-                    const float sp = softplus_f(dtv);
-                    gAr = sp * gar;
-                    gAi = sp * gai;
-                }
+            const int t = c * p.Q + t0;
+            if (row && t0 < p.Q && t < p.T) {
+                // ga = conj(dF/da)
+                const float gar = fr, gai = -fi;
+                const float dtv = sDt[t0];
+                const float sig = 1.f / (1.f + expf(-dtv));
+                p.gdt[((int64_t)b * p.T + t) * p.H + h] = (Ar * gar + Ai * gai) * sig;
+                const float sp = softplus_f(dtv);
+                gAr = sp * gar;
+                gAi = sp * gai;
             }
             // this chunk's share of gA: a fixed-order sum over the wave
             gAr += row_shr<1>(gAr);

@@ -75,6 +75,17 @@ SSD_DEVICE float row_shl(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                  0x100 + n, 0xf, 0xf, true));
 }
+template <int n>
+SSD_DEVICE int row_shr_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x110 + n, 0xf, 0xf, true);
+}
+template <int n>
+SSD_DEVICE int row_shl_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x100 + n, 0xf, 0xf, true);
+}
+SSD_DEVICE int lane_read_i(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 // Value of lane `src` (wave-uniform) for every lane.
 SSD_DEVICE float lane_read(float v, int src)
 {

@@ -294,6 +294,20 @@ SSD_DEVICE float row_shr(float v) { return emu_shfl(v, emu::SH_SHR, n); }
 template <int n>
 SSD_DEVICE float row_shl(float v) { return emu_shfl(v, emu::SH_SHL, n); }
 SSD_DEVICE float lane_read(float v, int src) { return emu_shfl(v, emu::SH_READ, src); }
+template <int n>
+SSD_DEVICE int row_shr_i(int v)
+{
+    return __builtin_bit_cast(int, emu_shfl(__builtin_bit_cast(float, v), emu::SH_SHR, n));
+}
+template <int n>
+SSD_DEVICE int row_shl_i(int v)
+{
+    return __builtin_bit_cast(int, emu_shfl(__builtin_bit_cast(float, v), emu::SH_SHL, n));
+}
+SSD_DEVICE int lane_read_i(int v, int src)
+{
+    return __builtin_bit_cast(int, emu_shfl(__builtin_bit_cast(float, v), emu::SH_READ, src));
+}
 SSD_DEVICE float uniform(float v) { return v; }
 
 // Buffer resources: an access must lie wholly inside [0, bytes) or wholly
