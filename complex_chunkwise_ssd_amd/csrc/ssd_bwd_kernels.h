@@ -371,7 +371,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sDt[R];
     SSD_LDS float sEin[2 * R];
     SSD_LDS float sEend[2 * R];
-    SSD_LDS float sRow[4 * 4 * 2 * R];  // [O, I, Off, In][column tile][row] complex
+    SSD_LDS float sRow[3 * 4 * 2 * R];  // [O + Off, I, In][column tile][row] complex
     SSD_LDS float sTc[16];
     SSD_LDS float sEv[2 * R];  // per row: (O - I + Off) and In, all column tiles
     SSD_LDS float sEe[2 * R];
@@ -567,7 +567,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         block_sync();
 
         // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
-        // columns n); NT x 4 tiles of each, dealt round-robin over the eight waves.
+        // columns n); NT x 4 tiles of each, dealt round-robin over the eight
+        // waves. Each tile also leaves one row dot product for the decay
+        // gradients (sRow slot q, column tile ct):
+        //   gx: In_s = x_s . (e_end B G)_s            (q = 2)
+        //   gB: I_s  = B_s . (V^T C)_s                 (q = 1)
+        //   gC: (O + Off)_l = C_l . conj(gC)_l         (q = 0)
         if (has_next)
             fetch(P3{}, next);
         for (int tile = w; tile < 3 * NT * 4; tile += 8) {
@@ -575,9 +580,9 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
             const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
             const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
+            const int g4 = lane >> 4;
             v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
             v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
-            const int g4 = lane >> 4;
             if (kind == 0) {
                 // conj(gx) = M^T gy + e_end (B G)
                 mma_steps<kCC>(0, 16, [&](int k) {
@@ -613,12 +618,11 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                                sBim[sx * LD + bcol]};
                 }, p1r, p1n, p1i);
             }
-            // Rows of this lane's accumulator entries and the row factor of the edge term.
             const int col = ct * 16 + (lane & 15);
             const float *fac = kind == 2 ? sEin : sEend;
-            const float *dre = kind == 2 ? sCre : sBre;   // the row dot products' other factor
-            const float *dim = kind == 2 ? sCim : sBim;
-            v4f outr, outi, d1r, d1i, d2r, d2i;
+            const float *qre = kind == 0 ? sXre : (kind == 1 ? sBre : sCre);
+            const float *qim = kind == 0 ? sXim : (kind == 1 ? sBim : sCim);
+            v4f outr, outi, dr, di;
             for (int r = 0; r < 4; ++r) {
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
                 const v2f f = *(const v2f *)&fac[2 * row];
@@ -626,28 +630,20 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
                 outr[r] = e1.x + e2.x;
                 outi[r] = e1.y + e2.y;
-                const v2f q = v2f{dre[row * LD + col], dim[row * LD + col]};
-                const v2f q1 = cmul(q, e1), q2 = cmul(q, e2);
-                d1r[r] = q1.x;
-                d1i[r] = q1.y;
-                d2r[r] = q2.x;
-                d2i[r] = q2.y;
+                const v2f q = v2f{qre[row * LD + col], qim[row * LD + col]};
+                const v2f m = kind == 0 ? e2 : (kind == 1 ? e1 : v2f{outr[r], outi[r]});
+                const v2f d = cmul(q, m);
+                dr[r] = d.x;
+                di[r] = d.y;
             }
-            if (kind != 0) {
-                d1r = row_total(d1r);
-                d1i = row_total(d1i);
-                d2r = row_total(d2r);
-                d2i = row_total(d2i);
-                if ((lane & 15) == 15) {
-                    // kind 1 (gB): I and In; kind 2 (gC): O and Off
-                    const int q1 = kind == 2 ? 0 : 1, q2 = kind == 2 ? 2 : 3;
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = rt * 16 + 4 * (lane >> 4) + r;
-                        sRow[((q1 * 4 + ct) * R + row) * 2] = d1r[r];
-                        sRow[((q1 * 4 + ct) * R + row) * 2 + 1] = d1i[r];
-                        sRow[((q2 * 4 + ct) * R + row) * 2] = d2r[r];
-                        sRow[((q2 * 4 + ct) * R + row) * 2 + 1] = d2i[r];
-                    }
+            dr = row_total(dr);
+            di = row_total(di);
+            if ((lane & 15) == 15) {
+                const int q = 2 - kind;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rt * 16 + 4 * (lane >> 4) + r;
+                    sRow[((q * 4 + ct) * R + row) * 2] = dr[r];
+                    sRow[((q * 4 + ct) * R + row) * 2 + 1] = di[r];
                 }
             }
             float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
@@ -663,17 +659,16 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         }
         block_sync();
 
-        // Decay gradients. Rows j < R (wave 0): v_j = (O - I + Off)_j and the
+        // Decay gradients. Rows j < R (wave 0): v_j = (O + Off - I)_j and the
         // edge share In_j, summed over the four column tiles in order.
         if (tid < R) {
             v2f v = v2f{0.f, 0.f}, e = v2f{0.f, 0.f};
             for (int ct = 0; ct < 4; ++ct) {
-                const float *o = &sRow[((0 * 4 + ct) * R + tid) * 2];
+                const float *ooff = &sRow[((0 * 4 + ct) * R + tid) * 2];
                 const float *in = &sRow[((1 * 4 + ct) * R + tid) * 2];
-                const float *off = &sRow[((2 * 4 + ct) * R + tid) * 2];
-                const float *ed = &sRow[((3 * 4 + ct) * R + tid) * 2];
-                v.x += o[0] - in[0] + off[0];
-                v.y += o[1] - in[1] + off[1];
+                const float *ed = &sRow[((2 * 4 + ct) * R + tid) * 2];
+                v.x += ooff[0] - in[0];
+                v.y += ooff[1] - in[1];
                 e.x += ed[0];
                 e.y += ed[1];
             }
