@@ -95,6 +95,7 @@ int main()
     fails += run_bwd(1, 70, 1, 64, 64, 64, false, true, true);  // full tiles, R = 32
     fails += run_bwd(2, 9, 1, 2, 3, 4, false, false, false);    // R = 16, no optional arrays
     fails += run_bwd(1, 33, 3, 8, 64, 256, true, false, true);  // long chunk as 32-token chunks
+    fails += run_bwd(16, 37, 16, 4, 6, 32, true, true, true);   // 256 sequences
     printf("%s\n", fails ? "FAIL" : "OK");
     return fails;
 }

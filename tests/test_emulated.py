@@ -131,6 +131,8 @@ BWD_CASES = [
     (3, 7, 1, 2, 2, 64),       # T < Q
     (1, 130, 1, 8, 8, 256),
     (2, 600, 2, 4, 4, 4),      # 600 chunks: each workgroup of the chunk pass takes several
+    (16, 40, 16, 4, 6, 8),     # 256 sequences, 1280 chunks over 256 workgroups
+    (32, 70, 8, 8, 4, 32),     # the same with 32-row chunks and a ragged last one
 ]
 
 

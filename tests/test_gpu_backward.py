@@ -216,3 +216,15 @@ def test_backward_through_initial_state_composes():
     _close("composed gx", np.concatenate([ga[0], gb[0]], axis=1), whole[0])
     _close("composed gdt", np.concatenate([ga[4], gb[4]], axis=1), whole[4])
     _close("composed gA", ga[1] + gb[1], whole[1], atol=ATOL + 1e-6 * 380)
+
+
+@pytest.mark.parametrize("Q", [64, 10])
+def test_many_sequences_full(Q):
+    """256 sequences of T=300 (chunks of 32 and 10 tokens): every gradient
+    compared, with a final-state gradient and an initial state."""
+    B, T, H, N, D = 16, 300, 16, 64, 64
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=90 + Q, dt_mean=0.3)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=90, with_final=False)
+    gf, init = _edges(B, H, N, D, 91)
+    got = _gpu_grads(inp, Q, gy.numpy(), gf, init)
+    _check_all(got, _oracle_grads(inp, gy.numpy(), gf, init), "256 sequences Q=%d" % Q, B * T)
