@@ -49,6 +49,63 @@ def measured_traffic(launch_tokens_heads):
     return rec.get("hbm_bytes_per_launch")
 
 
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
+]
+
+
+def write_traffic_profile(root):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the scan kernel, each scaled by the
+    same counter on a plain 1 GiB device copy, written next to the kernel trace
+    summary (the source hash ties the figures to the kernel they were taken on)."""
+    import csv
+    import glob
+
+    def counter(sub, name, kernel_part):
+        vals = []
+        for f in glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True):
+            per = {}
+            for r in csv.DictReader(open(f)):
+                if kernel_part in r["Kernel_Name"] and r["Counter_Name"] == name:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            vals += list(per.values())
+        if not vals:
+            raise SystemExit("no %s records for %s under %s" % (name, kernel_part, sub))
+        return vals
+
+    fetch = counter("pmc_fetch", "FETCH_SIZE", "scan_kernel<64, true, false>")
+    write = counter("pmc_write", "WRITE_SIZE", "scan_kernel<64, true, false>")
+    cf = max(counter("pmc_fetch_copy", "FETCH_SIZE", "copyBuffer"))
+    cw = max(counter("pmc_write_copy", "WRITE_SIZE", "copyBuffer"))
+    copied = 1 << 30
+    fs, ws = copied / (cf * 1024), copied / (cw * 1024)
+    f_kib, w_kib = sum(fetch) / len(fetch), sum(write) / len(write)
+    rd, wr = f_kib * 1024 * fs, w_kib * 1024 * ws
+    import complex_chunkwise_ssd_amd as ssd
+    th = 32 * 2048 * 16
+    rec = {
+        "kernel": "ssd::scan_kernel<64, true, false>",
+        "workload": "one layer of the 28-layer network load: B=32, T=2048, H=16, N=D=64, chunk 64",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": f_kib,
+        "write_size_kib_per_dispatch": w_kib,
+        "copy_calibration": {"bytes_copied": copied, "fetch_size_kib": cf, "write_size_kib": cw,
+                             "fetch_scale": fs, "write_scale": ws},
+        "hbm_read_bytes_per_launch": rd,
+        "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr,
+        "algorithmic_bytes_per_launch": th * ssd.algorithmic_bytes_per_token_head(64, 64, 2048),
+        "commands": TRAFFIC_COMMANDS,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(layer0, batch_rows=32):
     """The oracle as it stands, on a bounded sample of layer 0: batch rows
     0..batch_rows-1, all heads, full T (host cores, OpenMP over sequences)."""
@@ -69,6 +126,42 @@ def cpu_baseline(layer0, batch_rows=32):
             "kind": "oracle",
             "sample": "layer 0, batch rows 0-%d, all %d heads, T=%d (%d sequences, %.1f s wall)"
                       % (batch_rows - 1, A.shape[0], T, batch_rows * A.shape[0], el)}
+
+
+def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20):
+    """The scan read straight from in_proj output rows (real x, B and C as
+    real/imaginary blocks; ssd_chunk_forward_proj) at the network layer shape,
+    layer 0's seed; median of `reps` event-timed calls."""
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev)
+    y = torch.empty((B, T, H, D), device=dev)
+    f = torch.empty((B, H, N, D), dtype=torch.complex64, device=dev)
+    n = ssd.workspace_bytes(B, T, H, N, D, Q)
+    wsp = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    call = lambda: ssd.chunk_forward_proj(proj, A, H, N, D, chunk_size=Q, y=y, final_state=f,
+                                          workspace=wsp)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    th = B * T * H
+    fl = th * ssd.proj_algorithmic_flops_per_token_head(N, D, Q)
+    tf = fl / (ms * 1e-3) / 1e12
+    del proj, y, f, wsp
+    return {"workload": "network layer in the in_proj layout (B=%d, T=%d, H=%d, N=D=%d, chunk %d)"
+                        % (B, T, H, N, Q),
+            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS,
+                         "algorithmic_flops": fl,
+                         "algorithmic_bytes": th * ssd.proj_algorithmic_bytes_per_token_head(N, D, T)}}
 
 
 def backward_leg(ssd, torch, g, reps=10, warmup=3):
@@ -127,9 +220,14 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward side figure")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward on layer 0 of the workload and print it")
+    ap.add_argument("--write-traffic-profile", metavar="DIR", default=None,
+                    help="read the four rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scan and a "
+                         "1 GiB copy) under DIR and write the committed traffic summary")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
+    if args.write_traffic_profile:
+        return write_traffic_profile(args.write_traffic_profile)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sequences are independent; see the sharding note in the design document)",
@@ -280,6 +378,7 @@ def main():
                            "roofline_frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
             del g, y, f, wsp
         out["single_layer"] = extra
+        out["proj_layer"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev)
     if not args.no_backward:
         log("bench: timing the backward on layer 0")
         out["backward"] = backward_leg(ssd, torch, layers[0])

@@ -6,6 +6,7 @@ current stream. Importing works without a GPU; calling needs the built library
 and a visible GPU, and fails loudly otherwise (there is no fallback path).
 
     y, final_state = chunk_forward(x, A, B_t, C_t, dt, chunk_size=64)
+    y, final_state = chunk_forward_proj(proj, A, H, N, D, chunk_size=64)
     grads = chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None)
     A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
 """
@@ -65,6 +66,9 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                           vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_forward.restype = ctypes.c_int
+        lib.ssd_chunk_forward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                               vp, vp, ctypes.c_size_t, vp]
+        lib.ssd_chunk_forward_proj.restype = ctypes.c_int
         lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
         lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_chunk_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
@@ -156,6 +160,47 @@ def chunk_forward(x, A, B_t, C_t, dt, chunk_size: int = 64, initial_state=None,
                                _ptr(workspace), ws_size, _stream(dev))
     if st != SSD_OK:
         raise SSDError(st, "ssd_chunk_forward")
+    return y, final_state
+
+
+def proj_width(H: int, N: int, D: int) -> int:
+    """Floats of one token's in_proj row that the scan reads: x, the four N-blocks, dt."""
+    return H * (D + 4 * N + 1)
+
+
+def chunk_forward_proj(proj, A, H: int, N: int, D: int, chunk_size: int = 64,
+                       initial_state=None, want_final_state: bool = True, y=None,
+                       final_state=None, workspace=None):
+    """The scan read from in_proj output rows: proj (B, T, S) float32, contiguous,
+    each token row [x (H*D) | Re B | Im B | Re C | Im C (H*N each) | dt (H) | ...]
+    with S >= H*(D + 4N + 1). Returns (y (B,T,H,D) float32, final_state or None)."""
+    lib = load_library()
+    if not isinstance(proj, torch.Tensor) or proj.dim() != 3:
+        raise ValueError("proj must be a (B, T, S) tensor")
+    Bsz, T, S = proj.shape
+    dev = proj.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(proj, "proj", torch.float32, (Bsz, T, S), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    if y is None:
+        y = torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev)
+    _check(y, "y", torch.float32, (Bsz, T, H, D), dev)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((Bsz, H, N, D), dtype=torch.complex64, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", torch.complex64, (Bsz, H, N, D), dev)
+    ws_n = int(lib.ssd_chunk_forward_workspace_bytes(Bsz, T, H, N, D, chunk_size))
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_forward_proj(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size),
+                                    _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                    _ptr(workspace), ws_size, _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_forward_proj")
     return y, final_state
 
 
@@ -254,6 +299,17 @@ def algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
     B^T X (8ND), the state-to-output term Re(C H) (4ND) and the state passing
     (8ND/Q). Transcendentals are not counted."""
     return 8 * N * (Q + 1) / 2 + 4 * D * (Q + 1) / 2 + 12 * N * D + 8 * N * D / Q
+
+
+def proj_algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
+    """As algorithmic_flops_per_token_head with real x: Re((C B^T o L) X) costs
+    2D per pair and the chunk state B^T X 4ND."""
+    return 8 * N * (Q + 1) / 2 + 2 * D * (Q + 1) / 2 + 8 * N * D + 8 * N * D / Q
+
+
+def proj_algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
+    """x (real), the four N-blocks and dt read, y written, final state amortised."""
+    return 4 * D + 16 * N + 4 + 4 * D + 8 * N * D / T
 
 
 def algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:

@@ -156,6 +156,10 @@ constexpr int tile_st(int k, int nr)
 // R: chunk rows held on chip (chunk_size rounded up to 16, 32 or 64; extra
 // rows are identity padding). FULL: produce y and the final state; otherwise
 // only the zero-start end state and total log-decay of each segment.
+// PROJ: the inputs are read from an in_proj output row per token, [x (H*D,
+// real) | Re B | Im B | Re C | Im C (H*N each) | dt (H)], p.tok_stride floats
+// apart: x is real, so Re(M X) needs only Re M and the state update only
+// (decay o B)^T x (half the MFMAs of the complex-x steps).
 //
 // Per chunk c (three barriers):
 //   stage   B_t, C_t rows (loaded during chunk c-1) copied into LDS as
@@ -173,7 +177,7 @@ constexpr int tile_st(int k, int nr)
 // walks down with L[l, s] = L[l, s+1] exp(a_{s+1}). Off the diagonal:
 // L[l, s] = W[l] K(st, lt) V[s] with W the decay from the start of l's tile,
 // V the decay from s to the end of its tile and K the whole tiles in between.
-template <int R, bool FULL>
+template <int R, bool FULL, bool PROJ>
 SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 {
     constexpr int NR = R / 16;               // 16-row tiles per chunk
@@ -223,10 +227,12 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int64_t row0 = (int64_t)b * p.T * p.H + h;  // flat (b, t=0, h) index
     const int64_t bh = (int64_t)b * p.H + h;
     const v2f Ah = v2f{uniform(p.A[2 * h]), uniform(p.A[2 * h + 1])};
-    const uint32_t xrow = (uint32_t)(p.H * p.D) * 8u;  // bytes between tokens: x
-    const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;  //                      y
-    const uint32_t brow = (uint32_t)(p.H * p.N) * 8u;  //                      B_t, C_t
-    const uint32_t drow = (uint32_t)p.H * 4u;          //                      dt
+    const uint32_t prow = (uint32_t)p.tok_stride * 4u;  // bytes between tokens: in_proj row
+    const uint32_t xrow = PROJ ? prow : (uint32_t)(p.H * p.D) * 8u;  //          x
+    const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;                //          y
+    const uint32_t brow = PROJ ? prow : (uint32_t)(p.H * p.N) * 8u;  //          B_t, C_t
+    const uint32_t drow = PROJ ? prow : (uint32_t)p.H * 4u;          //          dt
+    const int64_t bt0 = (int64_t)b * p.T;              // flat (b, t=0) token index
     const int dsl = p.D - db * kDBlock;                // columns of D from this slice on
     const int dl = 16 * dtl + Lr;                      // this lane's column in the slice
     const bool dvalid = dl < dsl;
@@ -234,8 +240,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
     // Loop-invariant lane offsets; masked lanes point past the buffer.
     const int ncol = (tid & 31) * 2;
-    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * 8u : kOut;
-    const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * 8u : kOut;
+    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? 4u : 8u) : kOut;
+    const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * (PROJ ? 4u : 8u) : kOut;
     const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
 
     // State rows n = 16 * (2 * nh + i) + 4 * Lk + r, column dcol.
@@ -273,25 +279,43 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
     auto rows_of = [&](int c) { return p.Q < p.T - c * p.Q ? p.Q : p.T - c * p.Q; };
     auto tok0 = [&](int c) { return row0 + (int64_t)c * p.Q * p.H; };  // flat (b, cQ, h)
+    // PROJ: the first float of chunk c's token row
+    auto prow0 = [&](int c) { return (bt0 + (int64_t)c * p.Q) * p.tok_stride; };
+    using XT = std::conditional_t<PROJ, float, v2f>;  // x is real in the in_proj layout
 
     // Registers holding the next chunk's inputs while the current one runs.
     v4f pB[LOADS], pC[LOADS];
     float pdt = 0.f;
-    v2f pX[NR][4];
+    XT pX[NR][4];
     // The next chunk's loads are spread over the MFMA steps of phase 1 (a burst of
     // them would hold each wave's in-order issue). Item i < LOADS: a B_t block;
     // then (FULL) the C_t blocks; then x at (q, j).
     constexpr int NLOAD = (FULL ? 2 : 1) * LOADS + 4 * NR;
     buf_t nbB, nbC, nbX;
+    // PROJ: one buffer covers both planes of B (and of C); the imaginary plane of a
+    // row starts H*N floats after its real plane
+    const uint32_t imoff = (uint32_t)(p.H * p.N) * 4u;
     // Chunk c's buffers; past the segment's last chunk they are empty, so the loads
     // still issue (keeping the wait counters exact) but read zero.
     auto fetch_begin = [&](int c) {
         if (c < c_end) {
             const uint32_t rows = (uint32_t)rows_of(c);
-            const int64_t r0 = tok0(c);
-            nbB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
-            nbC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
-            nbX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
+            if constexpr (PROJ) {
+                const int64_t t0 = prow0(c);
+                const int64_t hn = (int64_t)h * p.N;
+                // rows past the chunk lie past this size (a token row is longer than
+                // both planes), so they still read zero
+                const uint32_t nb = (rows - 1) * brow + imoff + p.N * 4u;
+                nbB = make_buf(p.Bt + t0 + hn, nb);
+                nbC = make_buf(p.Ct + t0 + hn, nb);
+                nbX = make_buf(p.x + t0 + (int64_t)h * p.D + db * kDBlock,
+                               (rows - 1) * xrow + dsl * 4u);
+            } else {
+                const int64_t r0 = tok0(c);
+                nbB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+                nbC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+                nbX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
+            }
         } else {
             nbB = make_buf(p.Bt, 0u);
             nbC = make_buf(p.Ct, 0u);
@@ -301,12 +325,27 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     auto fetch_item = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i < LOADS) {
-            pB[i] = buf_load4(nbB, offB + (uint32_t)(16 * i) * brow);
+            const uint32_t o = offB + (uint32_t)(16 * i) * brow;
+            if constexpr (PROJ) {  // two n of the real and of the imaginary plane
+                const v2f re = buf_load2(nbB, o), im = buf_load2(nbB, o + imoff);
+                pB[i] = v4f{re.x, im.x, re.y, im.y};
+            } else {
+                pB[i] = buf_load4(nbB, o);
+            }
         } else if constexpr (FULL && i < 2 * LOADS) {
-            pC[i - LOADS] = buf_load4(nbC, offB + (uint32_t)(16 * (i - LOADS)) * brow);
+            const uint32_t o = offB + (uint32_t)(16 * (i - LOADS)) * brow;
+            if constexpr (PROJ) {
+                const v2f re = buf_load2(nbC, o), im = buf_load2(nbC, o + imoff);
+                pC[i - LOADS] = v4f{re.x, im.x, re.y, im.y};
+            } else {
+                pC[i - LOADS] = buf_load4(nbC, o);
+            }
         } else if constexpr (i < NLOAD) {
             constexpr int x = i - (FULL ? 2 : 1) * LOADS, q = x >> 2, j = x & 3;
-            pX[q][j] = buf_load2(nbX, offX + (uint32_t)(16 * q + j) * xrow);
+            if constexpr (PROJ)
+                pX[q][j] = buf_load1(nbX, offX + (uint32_t)(16 * q + j) * xrow);
+            else
+                pX[q][j] = buf_load2(nbX, offX + (uint32_t)(16 * q + j) * xrow);
         }
     };
     auto fetch = [&](int c) {
@@ -320,7 +359,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     constexpr int PER_S = (FULL ? NBC + 2 * NR - 1 : NLOAD + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
-        const buf_t bT = c < c_end ? make_buf(p.dt + tok0(c), (uint32_t)(rows_of(c) - 1) * drow + 4u)
+        const float *dt0 = PROJ ? p.dt + prow0(c) + h : p.dt + tok0(c);
+        const buf_t bT = c < c_end ? make_buf(dt0, (uint32_t)(rows_of(c) - 1) * drow + 4u)
                                    : make_buf(p.dt, 0u);
         pdt = buf_load1(bT, w == kScanWave ? (uint32_t)lane * drow : kOut);
     };
@@ -448,7 +488,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
             }
         }
-        v2f X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
+        XT X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
                 X[q][j] = pX[q][j];
@@ -522,11 +562,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 }
                 if constexpr (k < NWHOLE) {
                     sMre[k * 64 + lane] = mre;
-                    sMim[k * 64 + lane] = mim;
+                    if constexpr (!PROJ)
+                        sMim[k * 64 + lane] = mim;
                 } else {
                     for (int r = 0; r < 4; ++r) {
                         lds_add(&((float *)sMre)[(k * 64 + lane) * 4 + r], mre[r]);
-                        lds_add(&((float *)sMim)[(k * 64 + lane) * 4 + r], mim[r]);
+                        if constexpr (!PROJ)
+                            lds_add(&((float *)sMim)[(k * 64 + lane) * 4 + r], mim[r]);
                     }
                 }
             };
@@ -606,15 +648,24 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 static_for<g * PER_S, ((g + 1) * PER_S < SL ? (g + 1) * PER_S : SL)>(
                     [&](auto ic) { fetch_item(ic); });
                 sched_fence();
-                if constexpr (i == 0)
-                    for (int j = 0; j < 4; ++j)
-                        xs[j] = cmul(od[q & 1][j], X[q][j]);
-                for (int j = 0; j < 4; ++j) {
-                    const v2f bv = ob[cur][j];
-                    Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
-                    Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
-                    Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
-                    Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
+                if constexpr (PROJ) {
+                    // real x: (decay o B) against x, two MFMAs per step
+                    for (int j = 0; j < 4; ++j) {
+                        const v2f bv = cmul(od[q & 1][j], ob[cur][j]);
+                        Hre[i] = mfma_16x16x4(bv.x, X[q][j], Hre[i]);
+                        Him[i] = mfma_16x16x4(bv.y, X[q][j], Him[i]);
+                    }
+                } else {
+                    if constexpr (i == 0)
+                        for (int j = 0; j < 4; ++j)
+                            xs[j] = cmul(od[q & 1][j], X[q][j]);
+                    for (int j = 0; j < 4; ++j) {
+                        const v2f bv = ob[cur][j];
+                        Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
+                        Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
+                        Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
+                        Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
+                    }
                 }
                 sched_fence();
             });
@@ -636,21 +687,27 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 v4f mre[2], mim[2];
                 if constexpr (NK > 0) {
                     mre[0] = sMre[NH * 64 + lane];
-                    mim[0] = sMim[NH * 64 + lane];
+                    if constexpr (!PROJ)
+                        mim[0] = sMim[NH * 64 + lane];
                 }
                 static_for<0, NK>([&](auto ic) {
                     constexpr int i = decltype(ic)::value, k = 2 * i + NH, cur = i & 1;
                     constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
                     if constexpr (i + 1 < NK) {
                         mre[cur ^ 1] = sMre[(k + 2) * 64 + lane];
-                        mim[cur ^ 1] = sMim[(k + 2) * 64 + lane];
+                        if constexpr (!PROJ)
+                            mim[cur ^ 1] = sMim[(k + 2) * 64 + lane];
                     }
                     constexpr int a = NBC + i * PER_K, e = NBC + (i + 1) * PER_K;
                     static_for<a, (e < NLOAD ? e : NLOAD)>([&](auto xc) { fetch_item(xc); });
                     sched_fence();
                     for (int r = 0; r < 4; ++r) {
-                        Y[lt] = mfma_16x16x4(mre[cur][r], X[st][r].x, Y[lt]);
-                        Y[lt] = mfma_16x16x4(mim[cur][r], X[st][r].y, Y[lt]);
+                        if constexpr (PROJ) {
+                            Y[lt] = mfma_16x16x4(mre[cur][r], X[st][r], Y[lt]);
+                        } else {
+                            Y[lt] = mfma_16x16x4(mre[cur][r], X[st][r].x, Y[lt]);
+                            Y[lt] = mfma_16x16x4(mim[cur][r], X[st][r].y, Y[lt]);
+                        }
                     }
                     sched_fence();
                 });

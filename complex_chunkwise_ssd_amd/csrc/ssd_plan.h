@@ -38,6 +38,7 @@ struct ScanParams {
     int spc;   // chunks per segment
     int ndb;   // 64-wide D slices
     int groups_per_seq;  // P (full pass) or P - 1 (state pass)
+    int64_t tok_stride;  // in_proj layout: floats between consecutive tokens' rows
 };
 
 struct Plan {

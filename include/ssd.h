@@ -128,6 +128,34 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
                       ssd_stream_t stream);
 
 /*
+ * ssd_chunk_forward_proj -- the same scan read straight from the in_proj output
+ * ("Extending", Path A Step 2: Mamba3Block._forward_impl slices the projection
+ * of each token into x (H*D), four H*N blocks and a trailing dt (H); the
+ * in_proj width is H*(D + 4N + 1)). x is real here, and B_t, C_t are given by
+ * their real and imaginary blocks.
+ *
+ *   proj         (batch, T, token_stride) float32; the row of token (b, t) is
+ *                  [ x (H, D) | Re B_t (H, N) | Im B_t (H, N) |
+ *                    Re C_t (H, N) | Im C_t (H, N) | dt (H) | unused ]
+ *                (the order of the four N-blocks is this library's reading).
+ *   token_stride floats between consecutive token rows, >= H*(D + 4N + 1),
+ *                even. Floats past the last block are never read.
+ *   A, chunk_size, initial_state, y, final_state, workspace: as for
+ *                ssd_chunk_forward; the workspace size is
+ *                ssd_chunk_forward_workspace_bytes(batch, T, H, N, D, chunk_size).
+ * Result: identical in exact arithmetic to ssd_chunk_forward with
+ * x = x_real + 0i, B_t = Re B + i Im B, C_t = Re C + i Im C.
+ * Constraints: as ssd_chunk_forward; token_stride <= 2^22 (SSD_ERR_UNSUPPORTED).
+ * Alignment: proj 8 bytes and H*D even (the N-blocks are read as float pairs),
+ * else SSD_ERR_ALIGN.
+ */
+int ssd_chunk_forward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,
+                           int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                           int64_t chunk_size, const ssd_c64 *initial_state, float *y,
+                           ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                           ssd_stream_t stream);
+
+/*
  * ssd_chunk_backward_workspace_bytes -- device workspace that
  * ssd_chunk_backward needs for these sizes (0 when T, batch or H is 0, or the
  * sizes are invalid). It holds the state entering and the adjoint leaving

@@ -144,3 +144,38 @@ def upstream_grads(batch, T, H, N, D, seed, device="cpu", with_final=True):
     if with_final:
         gf = torch.randn((batch, H, N, D), generator=g, device=device, dtype=torch.complex64)
     return gy, gf
+
+
+def proj_case(batch, T, H, N, D, seed, device="cpu", dt_mean=0.0, extra=0):
+    """One layer's scan inputs in the in_proj layout: (proj, A) with proj of shape
+    (batch, T, H*(D + 4N + 1) + extra) float32, each token row
+    [x | Re B | Im B | Re C | Im C | dt | extra], x ~ N(0, 1) real, every B and C
+    part ~ N(0, 1/(2N)) (complex variance 1/N as in layer_case), dt ~ N(dt_mean, 1),
+    A as in layer_case; the `extra` floats per row are NaN (they must never be read)."""
+    g = _gen(seed, device)
+    a_re = -3.0 + 2.95 * torch.rand(H, generator=g, device=device)
+    a_mag = 0.35 + 1.85 * torch.rand(H, generator=g, device=device)
+    a_sgn = torch.where(torch.rand(H, generator=g, device=device) < 0.5, -1.0, 1.0)
+    A = torch.complex(a_re, a_mag * a_sgn).to(torch.complex64)
+    W = H * (D + 4 * N + 1)
+    proj = torch.empty((batch, T, W + extra), dtype=torch.float32, device=device)
+    proj[..., :H * D] = torch.randn((batch, T, H * D), generator=g, device=device)
+    proj[..., H * D:H * (D + 4 * N)] = torch.randn((batch, T, 4 * H * N), generator=g,
+                                                   device=device) * (0.5 / N) ** 0.5
+    proj[..., H * (D + 4 * N):W] = dt_mean + torch.randn((batch, T, H), generator=g, device=device)
+    if extra:
+        proj[..., W:] = float("nan")
+    return proj, A
+
+
+def unpack_proj(proj, A, H, N, D):
+    """The complex-layout ScanInputs that the in_proj rows stand for (layout
+    marshalling only: x = x_real + 0i, B_t = Re B + i Im B, C_t likewise)."""
+    Bsz, T = proj.shape[:2]
+    HD, HN = H * D, H * N
+    x = torch.complex(proj[..., :HD], torch.zeros_like(proj[..., :HD])).reshape(Bsz, T, H, D)
+    blk = lambda k: proj[..., HD + k * HN:HD + (k + 1) * HN].reshape(Bsz, T, H, N)
+    B_t = torch.complex(blk(0), blk(1))
+    C_t = torch.complex(blk(2), blk(3))
+    dt = proj[..., HD + 4 * HN:HD + 4 * HN + H]
+    return ScanInputs(x.contiguous(), A, B_t.contiguous(), C_t.contiguous(), dt.contiguous())

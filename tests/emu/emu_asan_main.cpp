@@ -83,6 +83,29 @@ static int run_bwd(int B, int T, int H, int N, int D, int Q, bool init, bool fin
     return st != 0 || bad != 0;
 }
 
+static int run_proj(int B, int T, int H, int N, int D, int Q, int extra)
+{
+    unsigned seed = 999u + B * 7 + T * 13 + H * 17 + N * 19 + D * 23 + Q * 29;
+    const int64_t S = (int64_t)H * (D + 4 * N + 1) + extra;
+    float *proj = alloc_fill((size_t)B * T * S, seed);
+    float *A = alloc_fill((size_t)H * 2, seed);
+    for (int h = 0; h < H; ++h)
+        A[2 * h] = -0.05f - 2.9f * (A[2 * h] + 0.5f);
+    float *y = (float *)malloc(((size_t)B * T * H * D + 1) * sizeof(float));
+    float *fs = (float *)malloc((size_t)B * H * N * D * 2 * sizeof(float));
+    size_t ws = ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q);
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
+    int st = ssd_chunk_forward_proj(proj, S, (ssd_c64 *)A, B, T, H, N, D, Q, nullptr, y,
+                                    (ssd_c64 *)fs, w, ws, nullptr);
+    int bad = 0;
+    for (size_t i = 0; i < (size_t)B * T * H * D; ++i)
+        bad += !isfinite(y[i]);
+    printf("proj B=%d T=%d H=%d N=%d D=%d Q=%d ws=%zu status=%d nonfinite=%d\n", B, T, H, N, D, Q,
+           ws, st, bad);
+    free(proj); free(A); free(y); free(fs); free(w);
+    return st != 0 || bad != 0;
+}
+
 int main()
 {
     int fails = 0;
@@ -96,6 +119,9 @@ int main()
     fails += run_bwd(2, 9, 1, 2, 3, 4, false, false, false);    // R = 16, no optional arrays
     fails += run_bwd(1, 33, 3, 8, 64, 256, true, false, true);  // long chunk as 32-token chunks
     fails += run_bwd(16, 37, 16, 4, 6, 32, true, true, true);   // 256 sequences
+    fails += run_proj(1, 40, 2, 4, 6, 16, 0);    // the last row's dt is the last float read
+    fails += run_proj(1, 150, 1, 64, 64, 64, 1); // full tiles, segments (stride made even)
+    fails += run_proj(2, 9, 1, 2, 4, 4, 1);      // Q < 16
     printf("%s\n", fails ? "FAIL" : "OK");
     return fails;
 }

@@ -70,6 +70,9 @@ def load(out_dir):
             lib.ssd_chunk_backward.restype = ctypes.c_int
             lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
             lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
+            lib.ssd_chunk_forward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p, p,
+                                                   p, ctypes.c_size_t, p]
+            lib.ssd_chunk_forward_proj.restype = ctypes.c_int
             lib.emu_mfma_count.restype = ctypes.c_long
             lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
             lib.emu_sincos.restype = None
@@ -127,3 +130,21 @@ def chunk_backward(lib, inp, chunk, grad_y, grad_final=None, initial_state=None,
                                 ptr(init), ptr(gy), ptr(gf), ptr(gx), ptr(gA), ptr(gB), ptr(gC),
                                 ptr(gdt), ptr(gi), ws_p if ws_n else None, ws_n, None)
     return st, gx, gA, gB, gC, gdt, gi
+
+
+def chunk_forward_proj(lib, proj, A, H, N, D, chunk, initial_state=None):
+    """proj (B, T, S) float32 in the in_proj layout; returns (status, y, final_state)."""
+    pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
+    Av = _c64(A)
+    Bsz, T, S = pr.shape
+    y = np.full((Bsz, T, H, D), np.nan, np.float32)
+    fs = np.full((Bsz, H, N, D), np.nan + 0j, np.complex64)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, np.complex64)
+    ws_n = lib.ssd_chunk_forward_workspace_bytes(Bsz, T, H, N, D, chunk)
+    ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
+    ws_p = ws.ctypes.data
+    ws_p = ws_p + (-ws_p) % 256
+    st = lib.ssd_chunk_forward_proj(pr.ctypes.data, S, Av.ctypes.data, Bsz, T, H, N, D, chunk,
+                                    None if init is None else init.ctypes.data, y.ctypes.data,
+                                    fs.ctypes.data, ws_p if ws_n else None, ws_n, None)
+    return st, y, fs

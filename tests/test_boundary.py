@@ -188,3 +188,26 @@ def test_python_backward_rejects_bad_tensors():
     dt = torch.zeros(1, 4, 2)
     with pytest.raises(ValueError):
         ssd.chunk_backward(x, A, B, B, dt, torch.zeros(1, 4, 2, 4))  # CPU tensors
+
+
+def _proj(lib, B=1, T=16, H=2, N=4, D=4, Q=4, S=None, ptrs=True, align=0, ws=None, ws_n=0):
+    S = H * (D + 4 * N + 1) if S is None else S
+    p = ctypes.c_void_p(0x100000 + align) if ptrs else None
+    a = ctypes.c_void_p(0x100000) if ptrs else None
+    return lib.ssd_chunk_forward_proj(p, S, a, B, T, H, N, D, Q, None, a, None, ws, ws_n, None)
+
+
+def test_proj_argument_checks(lib):
+    assert _proj(lib, S=2 * (4 + 16 + 1) - 2) == ssd.SSD_ERR_SHAPE   # row shorter than its blocks
+    assert _proj(lib, N=3) == ssd.SSD_ERR_ODD_N
+    assert _proj(lib, N=66, D=4) == ssd.SSD_ERR_UNSUPPORTED
+    assert _proj(lib, S=1 << 23) == ssd.SSD_ERR_UNSUPPORTED
+    assert _proj(lib, ptrs=False) == ssd.SSD_ERR_NULL
+    assert _proj(lib, align=4) == ssd.SSD_ERR_ALIGN                  # proj needs 8 bytes
+    assert _proj(lib, S=2 * (4 + 16 + 1) + 1) == ssd.SSD_ERR_ALIGN    # odd row length
+    assert _proj(lib, H=1, D=3, S=(3 + 16 + 1) + 1) == ssd.SSD_ERR_ALIGN  # H*D odd
+    need = lib.ssd_chunk_forward_workspace_bytes(1, 2048, 16, 64, 64, 64)
+    assert _proj(lib, B=1, T=2048, H=16, N=64, D=64, Q=64, ws=None, ws_n=need) == \
+        ssd.SSD_ERR_WORKSPACE
+    assert lib.ssd_chunk_forward_proj(None, 42, None, 0, 16, 2, 4, 4, 4, None, None, None, None,
+                                      0, None) == ssd.SSD_OK

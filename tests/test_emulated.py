@@ -170,3 +170,25 @@ def test_emulated_backward_zero_length(emu):
         emu, inp, 4, np.zeros((2, 0, 2, 4), np.float32), gf)
     assert st == 0 and gx.size == 0
     assert np.array_equal(gi, gf) and np.all(gA == 0)
+
+
+PROJ_CASES = [
+    # B, T, H, N, D, Q, extra floats per row (NaN: must never be read; the row
+    # length must be even)
+    (2, 16, 2, 4, 4, 4, 0),
+    (1, 97, 2, 8, 6, 32, 6),
+    (1, 150, 1, 64, 64, 64, 1),    # several segments
+    (2, 45, 2, 10, 70, 16, 4),     # two D slices
+    (1, 300, 1, 8, 8, 128, 1),
+]
+
+
+@pytest.mark.parametrize("case", PROJ_CASES)
+def test_emulated_proj_layout_matches_oracle(emu, case):
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case), dt_mean=0.3, extra=extra)
+    st, y, fs = emu_harness.chunk_forward_proj(emu, proj, A, H, N, D, Q)
+    assert st == 0
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y, fs, yo, fo)

@@ -1,0 +1,105 @@
+"""GPU parity of the scan read straight from in_proj output rows
+(ssd_chunk_forward_proj) against the oracle on the complex inputs the rows
+stand for (x = x_real + 0i, B_t = Re B + i Im B, C_t likewise).
+
+Bar (elementwise, as for ssd_chunk_forward): |dy| <= 1e-4 + 1e-4 |y|, and the
+same per complex component of final_state. Unused floats at the end of each
+row are NaN, so any read outside the row's blocks would show in the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import complex_chunkwise_ssd_amd as ssd
+import oracle
+import ssd_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _check(y, fs, yo, fo, what):
+    assert np.isfinite(y).all(), what
+    e = np.abs(y - yo.real)
+    bad = e > 1e-4 + 1e-4 * np.abs(yo.real)
+    assert not bad.any(), "%s: %d violations, max |dy| %.3e" % (what, int(bad.sum()), e.max())
+    if fs is not None:
+        for comp in (np.real, np.imag):
+            d = np.abs(comp(fs) - comp(fo))
+            assert (d <= 1e-4 + 1e-4 * np.abs(comp(fo))).all(), "%s state %.3e" % (what, d.max())
+
+
+CASES = [
+    # B, T, H, N, D, Q, extra floats per row (row length even)
+    (2, 16, 2, 4, 4, 4, 0),
+    (1, 64, 1, 64, 64, 64, 1),
+    (2, 150, 3, 64, 64, 64, 5),
+    (1, 97, 2, 8, 8, 32, 2),
+    (2, 50, 2, 6, 10, 16, 4),
+    (1, 45, 1, 10, 70, 32, 1),
+    (1, 23, 2, 4, 6, 1, 0),
+    (3, 7, 1, 2, 2, 64, 1),
+    (2, 300, 4, 32, 64, 48, 0),
+    (1, 260, 2, 64, 64, 256, 6),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_proj_small_shapes(case):
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case), dt_mean=0.3, extra=extra)
+    y, fs = ssd.chunk_forward_proj(proj.to(DEV), A.to(DEV), H, N, D, chunk_size=Q)
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y.cpu().numpy(), fs.cpu().numpy(), yo, fo, str(case))
+
+
+def test_proj_layer_b1_full():
+    """One Mamba-3-Lite layer (B=1, T=2048, H=16, N=D=64, chunk 64) in the in_proj layout."""
+    proj, A = ssd_inputs.proj_case(1, 2048, 16, 64, 64, seed=1, extra=2)
+    y, fs = ssd.chunk_forward_proj(proj.to(DEV), A.to(DEV), 16, 64, 64, chunk_size=64)
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, 16, 64, 64)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y.cpu().numpy(), fs.cpu().numpy(), yo, fo, "proj layer_b1")
+
+
+def test_proj_network_layer_sampled_and_complex_path():
+    """The network layer shape (B=32): sampled sequences against the oracle, and
+    every output against the complex-layout entry point on the unpacked inputs."""
+    proj, A = ssd_inputs.proj_case(32, 2048, 16, 64, 64, seed=0, device=DEV)
+    y, fs = ssd.chunk_forward_proj(proj, A, 16, 64, 64, chunk_size=64)
+    inp = ssd_inputs.unpack_proj(proj, A, 16, 64, 64)
+    y2, fs2 = ssd.chunk_forward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, chunk_size=64)
+    torch.cuda.synchronize()
+    a, r = y.cpu().numpy(), y2.cpu().numpy()
+    assert (np.abs(a - r) <= 2e-4 + 2e-4 * np.abs(r)).all()
+    pairs = [(0, 0), (31, 15), (17, 6)]
+    host = inp.to("cpu")
+    for b, h in pairs:
+        one = host.select(b, h)
+        yo, fo = oracle.scan(one.x, one.A, one.B_t, one.C_t, one.dt)
+        _check(a[b:b + 1, :, h:h + 1], fs.cpu().numpy()[b:b + 1, h:h + 1], yo, fo,
+               "proj network (%d, %d)" % (b, h))
+
+
+def test_proj_initial_state_and_zero_length():
+    B, T, H, N, D = 2, 130, 2, 16, 16
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=5, extra=0)
+    rng = np.random.default_rng(4)
+    init = ((rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))) * 0.5
+            ).astype(np.complex64)
+    y, fs = ssd.chunk_forward_proj(proj.to(DEV), A.to(DEV), H, N, D, chunk_size=32,
+                                   initial_state=torch.as_tensor(init).to(DEV))
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, initial_state=init)
+    _check(y.cpu().numpy(), fs.cpu().numpy(), yo, fo, "proj initial state")
+    empty = torch.zeros((B, 0, H * (D + 4 * N + 1)), device=DEV)
+    y0, f0 = ssd.chunk_forward_proj(empty, A.to(DEV), H, N, D, chunk_size=32,
+                                    initial_state=torch.as_tensor(init).to(DEV))
+    torch.cuda.synchronize()
+    assert y0.numel() == 0 and np.array_equal(f0.cpu().numpy(), init)
