@@ -76,8 +76,8 @@ def write_traffic_profile(root):
             raise SystemExit("no %s records for %s under %s" % (name, kernel_part, sub))
         return vals
 
-    fetch = counter("pmc_fetch", "FETCH_SIZE", "scan_kernel<64, true, false>")
-    write = counter("pmc_write", "WRITE_SIZE", "scan_kernel<64, true, false>")
+    fetch = counter("pmc_fetch", "FETCH_SIZE", "scan_kernel<64, true, 0>")
+    write = counter("pmc_write", "WRITE_SIZE", "scan_kernel<64, true, 0>")
     cf = max(counter("pmc_fetch_copy", "FETCH_SIZE", "copyBuffer"))
     cw = max(counter("pmc_write_copy", "WRITE_SIZE", "copyBuffer"))
     copied = 1 << 30
@@ -87,7 +87,7 @@ def write_traffic_profile(root):
     import complex_chunkwise_ssd_amd as ssd
     th = 32 * 2048 * 16
     rec = {
-        "kernel": "ssd::scan_kernel<64, true, false>",
+        "kernel": "ssd::scan_kernel<64, true, 0>",
         "workload": "one layer of the 28-layer network load: B=32, T=2048, H=16, N=D=64, chunk 64",
         "kernel_source_sha256_16": kernel_source_hash(),
         "fetch_size_kib_per_dispatch": f_kib,
@@ -128,11 +128,13 @@ def cpu_baseline(layer0, batch_rows=32):
                       % (batch_rows - 1, A.shape[0], T, batch_rows * A.shape[0], el)}
 
 
-def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20):
+def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20, dtype=None):
     """The scan read straight from in_proj output rows (real x, B and C as
-    real/imaginary blocks; ssd_chunk_forward_proj) at the network layer shape,
-    layer 0's seed; median of `reps` event-timed calls."""
-    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev)
+    real/imaginary blocks; ssd_chunk_forward_proj, bfloat16 rows with
+    dtype=torch.bfloat16) at the network layer shape, layer 0's seed; median
+    of `reps` event-timed calls."""
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev, dtype=dtype)
+    elem = proj.element_size()
     y = torch.empty((B, T, H, D), device=dev)
     f = torch.empty((B, H, N, D), dtype=torch.complex64, device=dev)
     n = ssd.workspace_bytes(B, T, H, N, D, Q)
@@ -155,13 +157,14 @@ def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20):
     fl = th * ssd.proj_algorithmic_flops_per_token_head(N, D, Q)
     tf = fl / (ms * 1e-3) / 1e12
     del proj, y, f, wsp
-    return {"workload": "network layer in the in_proj layout (B=%d, T=%d, H=%d, N=D=%d, chunk %d)"
-                        % (B, T, H, N, Q),
+    return {"workload": "network layer in the in_proj layout, %s rows (B=%d, T=%d, H=%d, N=D=%d, "
+                        "chunk %d)" % ("bfloat16" if elem == 2 else "float32", B, T, H, N, Q),
             "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS,
                          "algorithmic_flops": fl,
-                         "algorithmic_bytes": th * ssd.proj_algorithmic_bytes_per_token_head(N, D, T)}}
+                         "algorithmic_bytes": th * ssd.proj_algorithmic_bytes_per_token_head(
+                             N, D, T, elem)}}
 
 
 def backward_leg(ssd, torch, g, reps=10, warmup=3):
@@ -337,7 +340,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
             "traffic": traffic,
-            "kernel": "scan_kernel<64,true> (one launch per layer)",
+            "kernel": "scan_kernel<64, true, 0> (complex layout; one launch per layer)",
             "avg_launch_ms": avg_launch_ms,
             "algorithmic_flops_per_launch": flops_launch,
             "algorithmic_bytes_per_launch": bytes_launch,
@@ -379,6 +382,8 @@ def main():
             del g, y, f, wsp
         out["single_layer"] = extra
         out["proj_layer"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev)
+        out["proj_layer_bf16"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev,
+                                          dtype=torch.bfloat16)
     if not args.no_backward:
         log("bench: timing the backward on layer 0")
         out["backward"] = backward_leg(ssd, torch, layers[0])

@@ -69,6 +69,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_forward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                                vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_forward_proj.restype = ctypes.c_int
+        lib.ssd_chunk_forward_proj_bf16.argtypes = lib.ssd_chunk_forward_proj.argtypes
+        lib.ssd_chunk_forward_proj_bf16.restype = ctypes.c_int
         lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
         lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_chunk_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
@@ -171,9 +173,10 @@ def proj_width(H: int, N: int, D: int) -> int:
 def chunk_forward_proj(proj, A, H: int, N: int, D: int, chunk_size: int = 64,
                        initial_state=None, want_final_state: bool = True, y=None,
                        final_state=None, workspace=None):
-    """The scan read from in_proj output rows: proj (B, T, S) float32, contiguous,
-    each token row [x (H*D) | Re B | Im B | Re C | Im C (H*N each) | dt (H) | ...]
-    with S >= H*(D + 4N + 1). Returns (y (B,T,H,D) float32, final_state or None)."""
+    """The scan read from in_proj output rows: proj (B, T, S) float32 or bfloat16,
+    contiguous, each token row [x (H*D) | Re B | Im B | Re C | Im C (H*N each) |
+    dt (H) | ...] with S >= H*(D + 4N + 1); bfloat16 rows are widened to float32
+    as they are loaded. Returns (y (B,T,H,D) float32, final_state or None)."""
     lib = load_library()
     if not isinstance(proj, torch.Tensor) or proj.dim() != 3:
         raise ValueError("proj must be a (B, T, S) tensor")
@@ -181,7 +184,8 @@ def chunk_forward_proj(proj, A, H: int, N: int, D: int, chunk_size: int = 64,
     dev = proj.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device, got %s" % dev)
-    _check(proj, "proj", torch.float32, (Bsz, T, S), dev)
+    bf16 = proj.dtype == torch.bfloat16
+    _check(proj, "proj", torch.bfloat16 if bf16 else torch.float32, (Bsz, T, S), dev)
     _check(A, "A", torch.complex64, (H,), dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
@@ -196,11 +200,11 @@ def chunk_forward_proj(proj, A, H: int, N: int, D: int, chunk_size: int = 64,
     if ws_n and workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ssd_chunk_forward_proj(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size),
-                                    _ptr(initial_state), _ptr(y), _ptr(final_state),
-                                    _ptr(workspace), ws_size, _stream(dev))
+    fn = lib.ssd_chunk_forward_proj_bf16 if bf16 else lib.ssd_chunk_forward_proj
+    st = fn(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size), _ptr(initial_state), _ptr(y),
+            _ptr(final_state), _ptr(workspace), ws_size, _stream(dev))
     if st != SSD_OK:
-        raise SSDError(st, "ssd_chunk_forward_proj")
+        raise SSDError(st, "ssd_chunk_forward_proj" + ("_bf16" if bf16 else ""))
     return y, final_state
 
 
@@ -307,9 +311,10 @@ def proj_algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
     return 8 * N * (Q + 1) / 2 + 2 * D * (Q + 1) / 2 + 8 * N * D + 8 * N * D / Q
 
 
-def proj_algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
-    """x (real), the four N-blocks and dt read, y written, final state amortised."""
-    return 4 * D + 16 * N + 4 + 4 * D + 8 * N * D / T
+def proj_algorithmic_bytes_per_token_head(N: int, D: int, T: int, elem: int = 4) -> float:
+    """x (real), the four N-blocks and dt read (elem bytes each: 4 for float32
+    rows, 2 for bfloat16), y written (float32), final state amortised."""
+    return elem * (D + 4 * N + 1) + 4 * D + 8 * N * D / T
 
 
 def algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:

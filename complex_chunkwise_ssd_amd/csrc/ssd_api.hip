@@ -35,33 +35,33 @@ int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64
     return SSD_OK;
 }
 
-template <int R, bool PROJ>
+template <int R, int LAYOUT>
 int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs, hipStream_t stream)
 {
     ssd::ScanParams prm = base;
     if (plan.P > 1) {
         prm.groups_per_seq = plan.P - 1;
         const int64_t grid = seqs * (plan.P - 1) * plan.ndb;
-        hipLaunchKernelGGL((ssd::scan_kernel<R, false, PROJ>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((ssd::scan_kernel<R, false, LAYOUT>), dim3((unsigned)grid),
                            dim3(ssd::kThreads), 0, stream, prm);
         if (int st = launch_status())
             return st;
     }
     prm.groups_per_seq = plan.P;
     const int64_t grid = seqs * plan.P * plan.ndb;
-    hipLaunchKernelGGL((ssd::scan_kernel<R, true, PROJ>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((ssd::scan_kernel<R, true, LAYOUT>), dim3((unsigned)grid),
                        dim3(ssd::kThreads), 0, stream, prm);
     return launch_status();
 }
 
-template <bool PROJ>
+template <int LAYOUT>
 int launch_forward(const ssd::ScanParams &prm, const ssd::Plan &plan, int64_t seqs,
                    hipStream_t stream)
 {
     switch (plan.R) {
-    case 16: return launch_scan<16, PROJ>(prm, plan, seqs, stream);
-    case 32: return launch_scan<32, PROJ>(prm, plan, seqs, stream);
-    default: return launch_scan<64, PROJ>(prm, plan, seqs, stream);
+    case 16: return launch_scan<16, LAYOUT>(prm, plan, seqs, stream);
+    case 32: return launch_scan<32, LAYOUT>(prm, plan, seqs, stream);
+    default: return launch_scan<64, LAYOUT>(prm, plan, seqs, stream);
     }
 }
 
@@ -94,6 +94,73 @@ int check_backward_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t
     if (D > 64)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
+}
+
+template <int LAYOUT, class E>
+int forward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t batch, int64_t T,
+                 int64_t H, int64_t N, int64_t D, int64_t chunk_size, const ssd_c64 *initial_state,
+                 float *y, ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                 ssd_stream_t stream)
+{
+    if (int st = check_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    if (token_stride < H * (D + 4 * N + 1))
+        return SSD_ERR_SHAPE;
+    // 32-bit byte offsets inside one chunk of token rows
+    if (token_stride > (1LL << 22))
+        return SSD_ERR_UNSUPPORTED;
+    if (batch == 0 || H == 0)
+        return SSD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (!final_state)
+            return SSD_OK;
+        if (!aligned(final_state, 8) || (initial_state && !aligned(initial_state, 8)))
+            return SSD_ERR_ALIGN;
+        const int64_t n = batch * H * N * D * 2;
+        hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                           (const float *)initial_state, (float *)final_state, n);
+        return launch_status();
+    }
+    if (!proj || !A || !y)
+        return SSD_ERR_NULL;
+    // B and C are read as pairs of elements: their blocks must start on a pair
+    if (!aligned(proj, 2 * sizeof(E)) || token_stride % 2 != 0 || (H * D) % 2 != 0 ||
+        !aligned(A, 8) ||
+        !aligned(y, 4) || (initial_state && !aligned(initial_state, 8)) ||
+        (final_state && !aligned(final_state, 8)))
+        return SSD_ERR_ALIGN;
+    const ssd::Plan plan = ssd::make_plan(batch, T, H, N, D, chunk_size);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes)
+            return SSD_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return SSD_ERR_ALIGN;
+    }
+    ssd::ScanParams prm{};
+    // element pointers of the row blocks (the kernel reads them as LAYOUT says)
+    prm.x = (const float *)proj;
+    prm.A = (const float *)A;
+    prm.Bt = (const float *)(proj + H * D);
+    prm.Ct = (const float *)(proj + H * D + 2 * H * N);
+    prm.dt = (const float *)(proj + H * D + 4 * H * N);
+    prm.tok_stride = token_stride;
+    prm.init_state = (const float *)initial_state;
+    prm.y = y;
+    prm.final_state = (float *)final_state;
+    prm.seg_state = plan.P > 1 ? (float *)workspace : nullptr;
+    prm.seg_logdecay = plan.P > 1 ? (float *)((char *)workspace + plan.seg_state_bytes) : nullptr;
+    prm.B = (int)batch;
+    prm.T = (int)T;
+    prm.H = (int)H;
+    prm.N = (int)N;
+    prm.D = (int)D;
+    prm.Q = (int)ssd::block_rows(chunk_size);
+    prm.nc = plan.nc;
+    prm.P = plan.P;
+    prm.spc = plan.spc;
+    prm.ndb = plan.ndb;
+    return launch_forward<LAYOUT>(prm, plan, batch * H, s);
 }
 
 }  // namespace
@@ -224,7 +291,7 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     prm.spc = plan.spc;
     prm.ndb = plan.ndb;
 
-    return launch_forward<false>(prm, plan, batch * H, s);
+    return launch_forward<ssd::kLayoutC64>(prm, plan, batch * H, s);
 }
 
 int ssd_chunk_forward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,
@@ -233,63 +300,20 @@ int ssd_chunk_forward_proj(const float *proj, int64_t token_stride, const ssd_c6
                            ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
                            ssd_stream_t stream)
 {
-    if (int st = check_sizes(batch, T, H, N, D, chunk_size))
-        return st;
-    if (token_stride < H * (D + 4 * N + 1))
-        return SSD_ERR_SHAPE;
-    // 32-bit byte offsets inside one chunk of token rows
-    if (token_stride > (1LL << 22))
-        return SSD_ERR_UNSUPPORTED;
-    if (batch == 0 || H == 0)
-        return SSD_OK;
-    hipStream_t s = (hipStream_t)stream;
-    if (T == 0) {
-        if (!final_state)
-            return SSD_OK;
-        if (!aligned(final_state, 8) || (initial_state && !aligned(initial_state, 8)))
-            return SSD_ERR_ALIGN;
-        const int64_t n = batch * H * N * D * 2;
-        hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
-                           (const float *)initial_state, (float *)final_state, n);
-        return launch_status();
-    }
-    if (!proj || !A || !y)
-        return SSD_ERR_NULL;
-    // B and C are read as pairs of floats: their blocks must start on 8 bytes
-    if (!aligned(proj, 8) || token_stride % 2 != 0 || (H * D) % 2 != 0 || !aligned(A, 8) ||
-        !aligned(y, 4) || (initial_state && !aligned(initial_state, 8)) ||
-        (final_state && !aligned(final_state, 8)))
-        return SSD_ERR_ALIGN;
-    const ssd::Plan plan = ssd::make_plan(batch, T, H, N, D, chunk_size);
-    if (plan.workspace_bytes > 0) {
-        if (!workspace || workspace_bytes < plan.workspace_bytes)
-            return SSD_ERR_WORKSPACE;
-        if (!aligned(workspace, 256))
-            return SSD_ERR_ALIGN;
-    }
-    ssd::ScanParams prm{};
-    prm.x = proj;
-    prm.A = (const float *)A;
-    prm.Bt = proj + H * D;
-    prm.Ct = proj + H * D + 2 * H * N;
-    prm.dt = proj + H * D + 4 * H * N;
-    prm.tok_stride = token_stride;
-    prm.init_state = (const float *)initial_state;
-    prm.y = y;
-    prm.final_state = (float *)final_state;
-    prm.seg_state = plan.P > 1 ? (float *)workspace : nullptr;
-    prm.seg_logdecay = plan.P > 1 ? (float *)((char *)workspace + plan.seg_state_bytes) : nullptr;
-    prm.B = (int)batch;
-    prm.T = (int)T;
-    prm.H = (int)H;
-    prm.N = (int)N;
-    prm.D = (int)D;
-    prm.Q = (int)ssd::block_rows(chunk_size);
-    prm.nc = plan.nc;
-    prm.P = plan.P;
-    prm.spc = plan.spc;
-    prm.ndb = plan.ndb;
-    return launch_forward<true>(prm, plan, batch * H, s);
+    return forward_proj<ssd::kLayoutProj>(proj, token_stride, A, batch, T, H, N, D, chunk_size,
+                                          initial_state, y, final_state, workspace,
+                                          workspace_bytes, stream);
+}
+
+int ssd_chunk_forward_proj_bf16(const uint16_t *proj, int64_t token_stride, const ssd_c64 *A,
+                                int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                                int64_t chunk_size, const ssd_c64 *initial_state, float *y,
+                                ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                                ssd_stream_t stream)
+{
+    return forward_proj<ssd::kLayoutProjBf16>(proj, token_stride, A, batch, T, H, N, D,
+                                              chunk_size, initial_state, y, final_state,
+                                              workspace, workspace_bytes, stream);
 }
 
 size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,

@@ -43,6 +43,14 @@ SSD_DEVICE float buf_load1(buf_t r, uint32_t off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+SSD_DEVICE uint32_t buf_load_u32(buf_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+SSD_DEVICE uint32_t buf_load_u16(buf_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
 SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);

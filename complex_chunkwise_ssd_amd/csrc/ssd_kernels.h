@@ -60,6 +60,10 @@ SSD_DEVICE void sincos_cw(float x, float *sp, float *cp)
     *cp = ((q + 1) & 2) ? -cv : cv;
 }
 
+// bfloat16 -> float32: the 16 bits are the high half of the float.
+SSD_DEVICE float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+SSD_DEVICE float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
 SSD_DEVICE v2f cexp_f(v2f z)
 {
     float s, c;
@@ -156,10 +160,13 @@ constexpr int tile_st(int k, int nr)
 // R: chunk rows held on chip (chunk_size rounded up to 16, 32 or 64; extra
 // rows are identity padding). FULL: produce y and the final state; otherwise
 // only the zero-start end state and total log-decay of each segment.
-// PROJ: the inputs are read from an in_proj output row per token, [x (H*D,
-// real) | Re B | Im B | Re C | Im C (H*N each) | dt (H)], p.tok_stride floats
-// apart: x is real, so Re(M X) needs only Re M and the state update only
-// (decay o B)^T x (half the MFMAs of the complex-x steps).
+// LAYOUT kLayoutC64: x, B_t, C_t complex64 (B, T, H, .), dt float32 (B, T, H).
+// kLayoutProj / kLayoutProjBf16: the inputs are read from an in_proj output row
+// per token, [x (H*D, real) | Re B | Im B | Re C | Im C (H*N each) | dt (H)],
+// p.tok_stride elements apart, float32 or bfloat16 (widened to float32 as they
+// are loaded; all arithmetic stays float32): x is real, so Re(M X) needs only
+// Re M and the state update only (decay o B)^T x (half the MFMAs of the
+// complex-x steps).
 //
 // Per chunk c (three barriers):
 //   stage   B_t, C_t rows (loaded during chunk c-1) copied into LDS as
@@ -177,9 +184,12 @@ constexpr int tile_st(int k, int nr)
 // walks down with L[l, s] = L[l, s+1] exp(a_{s+1}). Off the diagonal:
 // L[l, s] = W[l] K(st, lt) V[s] with W the decay from the start of l's tile,
 // V the decay from s to the end of its tile and K the whole tiles in between.
-template <int R, bool FULL, bool PROJ>
+template <int R, bool FULL, int LAYOUT>
 SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 {
+    constexpr bool PROJ = LAYOUT != kLayoutC64;
+    constexpr bool BF16 = LAYOUT == kLayoutProjBf16;
+    constexpr uint32_t ES = BF16 ? 2u : 4u;  // bytes per element of an in_proj row
     constexpr int NR = R / 16;               // 16-row tiles per chunk
     constexpr int NT = NR * (NR + 1) / 2;    // causal tile pairs
     constexpr int NWHOLE = NT < 8 ? NT : 8;  // tiles k < NWHOLE: produced whole by wave k
@@ -227,7 +237,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int64_t row0 = (int64_t)b * p.T * p.H + h;  // flat (b, t=0, h) index
     const int64_t bh = (int64_t)b * p.H + h;
     const v2f Ah = v2f{uniform(p.A[2 * h]), uniform(p.A[2 * h + 1])};
-    const uint32_t prow = (uint32_t)p.tok_stride * 4u;  // bytes between tokens: in_proj row
+    const uint32_t prow = (uint32_t)p.tok_stride * ES;  // bytes between tokens: in_proj row
     const uint32_t xrow = PROJ ? prow : (uint32_t)(p.H * p.D) * 8u;  //          x
     const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;                //          y
     const uint32_t brow = PROJ ? prow : (uint32_t)(p.H * p.N) * 8u;  //          B_t, C_t
@@ -240,8 +250,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
     // Loop-invariant lane offsets; masked lanes point past the buffer.
     const int ncol = (tid & 31) * 2;
-    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? 4u : 8u) : kOut;
-    const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * (PROJ ? 4u : 8u) : kOut;
+    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
+    const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * (PROJ ? ES : 8u) : kOut;
     const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
 
     // State rows n = 16 * (2 * nh + i) + 4 * Lk + r, column dcol.
@@ -294,7 +304,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     buf_t nbB, nbC, nbX;
     // PROJ: one buffer covers both planes of B (and of C); the imaginary plane of a
     // row starts H*N floats after its real plane
-    const uint32_t imoff = (uint32_t)(p.H * p.N) * 4u;
+    const uint32_t imoff = (uint32_t)(p.H * p.N) * ES;
+    // element e of an in_proj row array at base (float32 or bfloat16 elements)
+    auto at = [&](const float *base, int64_t e) { return (const void *)((const char *)base + e * ES); };
     // Chunk c's buffers; past the segment's last chunk they are empty, so the loads
     // still issue (keeping the wait counters exact) but read zero.
     auto fetch_begin = [&](int c) {
@@ -305,11 +317,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 const int64_t hn = (int64_t)h * p.N;
                 // rows past the chunk lie past this size (a token row is longer than
                 // both planes), so they still read zero
-                const uint32_t nb = (rows - 1) * brow + imoff + p.N * 4u;
-                nbB = make_buf(p.Bt + t0 + hn, nb);
-                nbC = make_buf(p.Ct + t0 + hn, nb);
-                nbX = make_buf(p.x + t0 + (int64_t)h * p.D + db * kDBlock,
-                               (rows - 1) * xrow + dsl * 4u);
+                const uint32_t nb = (rows - 1) * brow + imoff + p.N * ES;
+                nbB = make_buf(at(p.Bt, t0 + hn), nb);
+                nbC = make_buf(at(p.Ct, t0 + hn), nb);
+                nbX = make_buf(at(p.x, t0 + (int64_t)h * p.D + db * kDBlock),
+                               (rows - 1) * xrow + dsl * ES);
             } else {
                 const int64_t r0 = tok0(c);
                 nbB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
@@ -326,7 +338,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         constexpr int i = decltype(ic)::value;
         if constexpr (i < LOADS) {
             const uint32_t o = offB + (uint32_t)(16 * i) * brow;
-            if constexpr (PROJ) {  // two n of the real and of the imaginary plane
+            if constexpr (BF16) {  // two n of the real and of the imaginary plane
+                const uint32_t re = buf_load_u32(nbB, o), im = buf_load_u32(nbB, o + imoff);
+                pB[i] = v4f{bf16_lo(re), bf16_lo(im), bf16_hi(re), bf16_hi(im)};
+            } else if constexpr (PROJ) {
                 const v2f re = buf_load2(nbB, o), im = buf_load2(nbB, o + imoff);
                 pB[i] = v4f{re.x, im.x, re.y, im.y};
             } else {
@@ -334,7 +349,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             }
         } else if constexpr (FULL && i < 2 * LOADS) {
             const uint32_t o = offB + (uint32_t)(16 * (i - LOADS)) * brow;
-            if constexpr (PROJ) {
+            if constexpr (BF16) {
+                const uint32_t re = buf_load_u32(nbC, o), im = buf_load_u32(nbC, o + imoff);
+                pC[i - LOADS] = v4f{bf16_lo(re), bf16_lo(im), bf16_hi(re), bf16_hi(im)};
+            } else if constexpr (PROJ) {
                 const v2f re = buf_load2(nbC, o), im = buf_load2(nbC, o + imoff);
                 pC[i - LOADS] = v4f{re.x, im.x, re.y, im.y};
             } else {
@@ -342,7 +360,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             }
         } else if constexpr (i < NLOAD) {
             constexpr int x = i - (FULL ? 2 : 1) * LOADS, q = x >> 2, j = x & 3;
-            if constexpr (PROJ)
+            if constexpr (BF16)
+                pX[q][j] = bf16_lo(buf_load_u16(nbX, offX + (uint32_t)(16 * q + j) * xrow));
+            else if constexpr (PROJ)
                 pX[q][j] = buf_load1(nbX, offX + (uint32_t)(16 * q + j) * xrow);
             else
                 pX[q][j] = buf_load2(nbX, offX + (uint32_t)(16 * q + j) * xrow);
@@ -359,10 +379,14 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     constexpr int PER_S = (FULL ? NBC + 2 * NR - 1 : NLOAD + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
-        const float *dt0 = PROJ ? p.dt + prow0(c) + h : p.dt + tok0(c);
-        const buf_t bT = c < c_end ? make_buf(dt0, (uint32_t)(rows_of(c) - 1) * drow + 4u)
+        const void *dt0 = PROJ ? at(p.dt, prow0(c) + h) : (const void *)(p.dt + tok0(c));
+        const buf_t bT = c < c_end ? make_buf(dt0, (uint32_t)(rows_of(c) - 1) * drow + ES)
                                    : make_buf(p.dt, 0u);
-        pdt = buf_load1(bT, w == kScanWave ? (uint32_t)lane * drow : kOut);
+        const uint32_t od = w == kScanWave ? (uint32_t)lane * drow : kOut;
+        if constexpr (BF16)
+            pdt = bf16_lo(buf_load_u16(bT, od));
+        else
+            pdt = buf_load1(bT, od);
     };
 
     // One wave: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.

@@ -19,6 +19,10 @@ constexpr int kNPad = 64;         // state rows handled per workgroup (N padded)
 constexpr int kDBlock = 64;       // state columns (D) per workgroup
 constexpr int kTargetGroups = 256;  // one workgroup per compute unit of an MI355X
 constexpr int kMaxBlock = 256;
+// Input layouts of the forward scan.
+constexpr int kLayoutC64 = 0;       // x, B_t, C_t complex64; dt float32
+constexpr int kLayoutProj = 1;      // in_proj rows, float32
+constexpr int kLayoutProjBf16 = 2;  // in_proj rows, bfloat16
 
 // Kernel arguments. Complex arrays are interleaved (re, im) float pairs.
 struct ScanParams {

@@ -156,6 +156,23 @@ int ssd_chunk_forward_proj(const float *proj, int64_t token_stride, const ssd_c6
                            ssd_stream_t stream);
 
 /*
+ * ssd_chunk_forward_proj_bf16 -- ssd_chunk_forward_proj with the in_proj rows
+ * in bfloat16 ("AGENTS & System Architecture": the model trains in BF16
+ * (section 1, subagent notes) while the recurrent state stays complex64
+ * (section 3, numerical-stability rules)). proj holds bfloat16 bit patterns
+ * (uint16); each element is
+ * widened to float32 as it is loaded and every product, sum and the state
+ * stay float32, so the result equals ssd_chunk_forward_proj on the widened
+ * rows. Same arguments, constraints and workspace as ssd_chunk_forward_proj,
+ * except the alignment: proj 4 bytes (and token_stride, H*D even).
+ */
+int ssd_chunk_forward_proj_bf16(const uint16_t *proj, int64_t token_stride, const ssd_c64 *A,
+                                int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                                int64_t chunk_size, const ssd_c64 *initial_state, float *y,
+                                ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
+                                ssd_stream_t stream);
+
+/*
  * ssd_chunk_backward_workspace_bytes -- device workspace that
  * ssd_chunk_backward needs for these sizes (0 when T, batch or H is 0, or the
  * sizes are invalid). It holds the state entering and the adjoint leaving

@@ -146,12 +146,13 @@ def upstream_grads(batch, T, H, N, D, seed, device="cpu", with_final=True):
     return gy, gf
 
 
-def proj_case(batch, T, H, N, D, seed, device="cpu", dt_mean=0.0, extra=0):
+def proj_case(batch, T, H, N, D, seed, device="cpu", dt_mean=0.0, extra=0, dtype=None):
     """One layer's scan inputs in the in_proj layout: (proj, A) with proj of shape
     (batch, T, H*(D + 4N + 1) + extra) float32, each token row
     [x | Re B | Im B | Re C | Im C | dt | extra], x ~ N(0, 1) real, every B and C
     part ~ N(0, 1/(2N)) (complex variance 1/N as in layer_case), dt ~ N(dt_mean, 1),
-    A as in layer_case; the `extra` floats per row are NaN (they must never be read)."""
+    A as in layer_case; the `extra` floats per row are NaN (they must never be read).
+    dtype=torch.bfloat16 rounds the finished rows to bfloat16."""
     g = _gen(seed, device)
     a_re = -3.0 + 2.95 * torch.rand(H, generator=g, device=device)
     a_mag = 0.35 + 1.85 * torch.rand(H, generator=g, device=device)
@@ -165,6 +166,8 @@ def proj_case(batch, T, H, N, D, seed, device="cpu", dt_mean=0.0, extra=0):
     proj[..., H * (D + 4 * N):W] = dt_mean + torch.randn((batch, T, H), generator=g, device=device)
     if extra:
         proj[..., W:] = float("nan")
+    if dtype is not None:
+        proj = proj.to(dtype)
     return proj, A
 
 
@@ -172,6 +175,7 @@ def unpack_proj(proj, A, H, N, D):
     """The complex-layout ScanInputs that the in_proj rows stand for (layout
     marshalling only: x = x_real + 0i, B_t = Re B + i Im B, C_t likewise)."""
     Bsz, T = proj.shape[:2]
+    proj = proj.float()  # bfloat16 rows widen exactly
     HD, HN = H * D, H * N
     x = torch.complex(proj[..., :HD], torch.zeros_like(proj[..., :HD])).reshape(Bsz, T, H, D)
     blk = lambda k: proj[..., HD + k * HN:HD + (k + 1) * HN].reshape(Bsz, T, H, N)

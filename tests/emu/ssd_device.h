@@ -349,6 +349,20 @@ SSD_DEVICE float buf_load1(buf_t r, uint32_t off)
         memcpy(&v, r.base + off, 4);
     return v;
 }
+SSD_DEVICE uint32_t buf_load_u32(buf_t r, uint32_t off)
+{
+    uint32_t v = 0;
+    if (emu_buf_in(r, off, 4))
+        memcpy(&v, r.base + off, 4);
+    return v;
+}
+SSD_DEVICE uint32_t buf_load_u16(buf_t r, uint32_t off)
+{
+    uint16_t v = 0;
+    if (emu_buf_in(r, off, 2))
+        memcpy(&v, r.base + off, 2);
+    return v;
+}
 SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
 {
     if (emu_buf_in(r, off, 4))

@@ -73,6 +73,8 @@ def load(out_dir):
             lib.ssd_chunk_forward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p, p,
                                                    p, ctypes.c_size_t, p]
             lib.ssd_chunk_forward_proj.restype = ctypes.c_int
+            lib.ssd_chunk_forward_proj_bf16.argtypes = lib.ssd_chunk_forward_proj.argtypes
+            lib.ssd_chunk_forward_proj_bf16.restype = ctypes.c_int
             lib.emu_mfma_count.restype = ctypes.c_long
             lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
             lib.emu_sincos.restype = None
@@ -133,8 +135,14 @@ def chunk_backward(lib, inp, chunk, grad_y, grad_final=None, initial_state=None,
 
 
 def chunk_forward_proj(lib, proj, A, H, N, D, chunk, initial_state=None):
-    """proj (B, T, S) float32 in the in_proj layout; returns (status, y, final_state)."""
-    pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
+    """proj (B, T, S) float32 or bfloat16 (torch) in the in_proj layout; returns
+    (status, y, final_state)."""
+    import torch
+    bf16 = hasattr(proj, "dtype") and proj.dtype == torch.bfloat16
+    if bf16:
+        pr = np.ascontiguousarray(proj.contiguous().view(torch.int16).numpy())
+    else:
+        pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
     Av = _c64(A)
     Bsz, T, S = pr.shape
     y = np.full((Bsz, T, H, D), np.nan, np.float32)
@@ -144,7 +152,8 @@ def chunk_forward_proj(lib, proj, A, H, N, D, chunk, initial_state=None):
     ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
     ws_p = ws.ctypes.data
     ws_p = ws_p + (-ws_p) % 256
-    st = lib.ssd_chunk_forward_proj(pr.ctypes.data, S, Av.ctypes.data, Bsz, T, H, N, D, chunk,
+    fn = lib.ssd_chunk_forward_proj_bf16 if bf16 else lib.ssd_chunk_forward_proj
+    st = fn(pr.ctypes.data, S, Av.ctypes.data, Bsz, T, H, N, D, chunk,
                                     None if init is None else init.ctypes.data, y.ctypes.data,
                                     fs.ctypes.data, ws_p if ws_n else None, ws_n, None)
     return st, y, fs

@@ -192,3 +192,17 @@ def test_emulated_proj_layout_matches_oracle(emu, case):
     inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
     yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
     _check(y, fs, yo, fo)
+
+
+@pytest.mark.parametrize("case", PROJ_CASES[:3])
+def test_emulated_proj_bf16_matches_oracle(emu, case):
+    """bfloat16 rows: the oracle runs on the same rows widened to float32."""
+    import torch
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 3, dt_mean=0.3, extra=extra,
+                                   dtype=torch.bfloat16)
+    st, y, fs = emu_harness.chunk_forward_proj(emu, proj, A, H, N, D, Q)
+    assert st == 0
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y, fs, yo, fo)

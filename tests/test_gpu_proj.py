@@ -103,3 +103,36 @@ def test_proj_initial_state_and_zero_length():
                                     initial_state=torch.as_tensor(init).to(DEV))
     torch.cuda.synchronize()
     assert y0.numel() == 0 and np.array_equal(f0.cpu().numpy(), init)
+
+
+# bfloat16 rows (ssd_chunk_forward_proj_bf16): the oracle runs on the same rows
+# widened to float32, so the float32 bar applies unchanged.
+
+@pytest.mark.parametrize("case", CASES[:6])
+def test_proj_bf16_small_shapes(case):
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 50, dt_mean=0.3, extra=extra,
+                                   dtype=torch.bfloat16)
+    y, fs = ssd.chunk_forward_proj(proj.to(DEV), A.to(DEV), H, N, D, chunk_size=Q)
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    _check(y.cpu().numpy(), fs.cpu().numpy(), yo, fo, "bf16 " + str(case))
+
+
+def test_proj_bf16_network_layer_matches_float32_rows():
+    """The network layer shape (B=32) from bfloat16 rows equals the float32 entry
+    point on the widened rows (same arithmetic), and sampled sequences the oracle."""
+    proj, A = ssd_inputs.proj_case(32, 2048, 16, 64, 64, seed=0, device=DEV, dtype=torch.bfloat16)
+    y, fs = ssd.chunk_forward_proj(proj, A, 16, 64, 64, chunk_size=64)
+    y32, fs32 = ssd.chunk_forward_proj(proj.float(), A, 16, 64, 64, chunk_size=64)
+    torch.cuda.synchronize()
+    a = y.cpu().numpy()
+    assert np.array_equal(a, y32.cpu().numpy())
+    assert np.array_equal(fs.cpu().numpy(), fs32.cpu().numpy())
+    host = ssd_inputs.unpack_proj(proj.cpu(), A.cpu(), 16, 64, 64)
+    for b, h in [(3, 2), (30, 13)]:
+        one = host.select(b, h)
+        yo, fo = oracle.scan(one.x, one.A, one.B_t, one.C_t, one.dt)
+        _check(a[b:b + 1, :, h:h + 1], fs.cpu().numpy()[b:b + 1, h:h + 1], yo, fo,
+               "bf16 network (%d, %d)" % (b, h))
