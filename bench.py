@@ -167,6 +167,34 @@ def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20, dtype=None)
                              N, D, T, elem)}}
 
 
+def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10):
+    """ssd_chunk_backward_proj (gradients as in_proj gradient rows) at the network
+    layer shape; median of `reps` event-timed calls."""
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev)
+    gy, gf = ssd_inputs.upstream_grads(B, T, H, N, D, seed=0, device=dev)
+    ws = torch.empty(max(ssd.backward_workspace_bytes(B, T, H, N, D, 64), 1), dtype=torch.uint8,
+                     device=dev)
+    rows = torch.zeros_like(proj)
+    call = lambda: ssd.chunk_backward_proj(proj, A, H, N, D, gy, gf, chunk_size=64, grad_proj=rows,
+                                           workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del proj, gy, gf, ws, rows
+    return {"workload": "network layer backward from in_proj rows (B=%d, T=%d, H=%d, N=D=%d, "
+                        "chunk 64)" % (B, T, H, N),
+            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3)}
+
+
 def backward_leg(ssd, torch, g, reps=10, warmup=3):
     """ssd_chunk_backward on one network layer (B=32, T=2048, H=16, N=D=64,
     chunk 64) with seeded upstream gradients; median of `reps` calls, each
@@ -387,6 +415,8 @@ def main():
     if not args.no_backward:
         log("bench: timing the backward on layer 0")
         out["backward"] = backward_leg(ssd, torch, layers[0])
+        if not args.no_extra:
+            out["backward_proj"] = backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev)
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

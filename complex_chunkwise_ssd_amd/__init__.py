@@ -76,6 +76,9 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                            vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_backward.restype = ctypes.c_int
+        lib.ssd_chunk_backward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                                vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ssd_chunk_backward_proj.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.restype = ctypes.c_int
@@ -271,6 +274,49 @@ def chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None, chunk_size
     if st != SSD_OK:
         raise SSDError(st, "ssd_chunk_backward")
     return out
+
+
+def chunk_backward_proj(proj, A, H: int, N: int, D: int, grad_y, grad_final_state=None,
+                        chunk_size: int = 64, initial_state=None, grad_proj=None,
+                        want_initial_state_grad: bool = True, workspace=None):
+    """Gradients of the scan read from in_proj rows (chunk_forward_proj, float32
+    rows), as gradient rows of the same layout: returns (grad_proj (B, T, S)
+    float32, grad_A (H,) complex64, grad_initial_state or None). The x block
+    gets dl/dx (x is real), the B and C blocks the real and imaginary parts of
+    their gradients, the dt block dl/ddt; floats past the blocks are left as
+    they are (zero in a freshly allocated grad_proj)."""
+    lib = load_library()
+    if not isinstance(proj, torch.Tensor) or proj.dim() != 3:
+        raise ValueError("proj must be a (B, T, S) tensor")
+    Bsz, T, S = proj.shape
+    dev = proj.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(proj, "proj", torch.float32, (Bsz, T, S), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    _check(grad_y, "grad_y", torch.float32, (Bsz, T, H, D), dev)
+    if grad_final_state is not None:
+        _check(grad_final_state, "grad_final_state", torch.complex64, (Bsz, H, N, D), dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    if grad_proj is None:
+        grad_proj = torch.zeros((Bsz, T, S), dtype=torch.float32, device=dev)
+    _check(grad_proj, "grad_proj", torch.float32, (Bsz, T, S), dev)
+    gA = torch.empty((H,), dtype=torch.complex64, device=dev)
+    gi = None
+    if want_initial_state_grad:
+        gi = torch.empty((Bsz, H, N, D), dtype=torch.complex64, device=dev)
+    ws_n = int(lib.ssd_chunk_backward_workspace_bytes(Bsz, T, H, N, D, chunk_size))
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_backward_proj(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size),
+                                     _ptr(initial_state), _ptr(grad_y), _ptr(grad_final_state),
+                                     _ptr(grad_proj), _ptr(gA), _ptr(gi), _ptr(workspace), ws_size,
+                                     _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_backward_proj")
+    return grad_proj, gA, gi
 
 
 def discretise(dt, A, chunk_size: int = 0, want_abar: bool = True):

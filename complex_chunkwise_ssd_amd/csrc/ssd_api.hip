@@ -65,20 +65,20 @@ int launch_forward(const ssd::ScanParams &prm, const ssd::Plan &plan, int64_t se
     }
 }
 
-template <int R>
+template <int R, bool PROJ>
 int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false>), dim3((unsigned)seqs), dim3(512), 0,
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false, PROJ>), dim3((unsigned)seqs), dim3(512), 0,
                        stream, prm);
     if (int st = launch_status())
         return st;
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true>), dim3((unsigned)seqs), dim3(512), 0,
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, PROJ>), dim3((unsigned)seqs), dim3(512), 0,
                        stream, prm);
     if (int st = launch_status())
         return st;
     const int64_t chunks = seqs * prm.nc;
     const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
-    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R>), dim3((unsigned)groups), dim3(512), 0, stream,
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, PROJ>), dim3((unsigned)groups), dim3(512), 0, stream,
                        prm);
     if (int st = launch_status())
         return st;
@@ -395,7 +395,82 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
     prm.Q = plan.Q;
     prm.nc = plan.nc;
     const int64_t seqs = batch * H;
-    return plan.R == 16 ? launch_backward<16>(prm, seqs, s) : launch_backward<32>(prm, seqs, s);
+    return plan.R == 16 ? launch_backward<16, false>(prm, seqs, s)
+                        : launch_backward<32, false>(prm, seqs, s);
+}
+
+int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,
+                            int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                            int64_t chunk_size, const ssd_c64 *initial_state, const float *grad_y,
+                            const ssd_c64 *grad_final_state, float *grad_proj, ssd_c64 *grad_A,
+                            ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
+                            ssd_stream_t stream)
+{
+    if (int st = check_backward_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    if (token_stride < H * (D + 4 * N + 1))
+        return SSD_ERR_SHAPE;
+    if (batch == 0 || H == 0)
+        return SSD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (!grad_A)
+        return SSD_ERR_NULL;
+    if (!aligned(grad_A, 8) || (grad_final_state && !aligned(grad_final_state, 8)) ||
+        (grad_initial_state && !aligned(grad_initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    if (T == 0) {
+        if (grad_initial_state) {
+            const int64_t n = batch * H * N * D * 2;
+            hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                               (const float *)grad_final_state, (float *)grad_initial_state, n);
+            if (int st = launch_status())
+                return st;
+        }
+        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)H), dim3(256), 0, s,
+                           (const float *)nullptr, (int)batch, (int)H, 0, (float *)grad_A);
+        return launch_status();
+    }
+    if (!proj || !A || !grad_y || !grad_proj)
+        return SSD_ERR_NULL;
+    if (!aligned(proj, 4) || !aligned(grad_proj, 4) || !aligned(A, 8) || !aligned(grad_y, 4) ||
+        (initial_state && !aligned(initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+        return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return SSD_ERR_ALIGN;
+
+    const int64_t HD = H * D, HN = H * N;
+    ssd::BwdParams prm{};
+    prm.x = proj;
+    prm.A = (const float *)A;
+    prm.Bt = proj + HD;
+    prm.Ct = proj + HD + 2 * HN;
+    prm.dt = proj + HD + 4 * HN;
+    prm.init = (const float *)initial_state;
+    prm.gy = grad_y;
+    prm.gfinal = (const float *)grad_final_state;
+    prm.gx = grad_proj;
+    prm.gA = (float *)grad_A;
+    prm.gB = grad_proj + HD;
+    prm.gC = grad_proj + HD + 2 * HN;
+    prm.gdt = grad_proj + HD + 4 * HN;
+    prm.ginit = (float *)grad_initial_state;
+    prm.fwd_states = (float *)workspace;
+    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
+    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
+    prm.B = (int)batch;
+    prm.T = (int)T;
+    prm.H = (int)H;
+    prm.N = (int)N;
+    prm.D = (int)D;
+    prm.Q = plan.Q;
+    prm.nc = plan.nc;
+    prm.tok_stride = token_stride;
+    const int64_t seqs = batch * H;
+    return plan.R == 16 ? launch_backward<16, true>(prm, seqs, s)
+                        : launch_backward<32, true>(prm, seqs, s);
 }
 
 }  // extern "C"

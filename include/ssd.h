@@ -218,6 +218,28 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
                        ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
                        ssd_stream_t stream);
 
+/*
+ * ssd_chunk_backward_proj -- ssd_chunk_backward for the scan read from in_proj
+ * rows (ssd_chunk_forward_proj, float32 rows): the gradients are written as
+ * gradient rows of the same layout.
+ *   proj, token_stride, A, chunk_size, initial_state, grad_y, grad_final_state,
+ *                as for ssd_chunk_forward_proj and ssd_chunk_backward.
+ *   grad_proj    out: (batch, T, token_stride) float32; in each token row the x
+ *                block receives dl/dx (x is real), the Re/Im B and C blocks the
+ *                real and imaginary parts of the B_t and C_t gradients, the dt
+ *                block dl/ddt. Floats past the blocks are not written.
+ *   grad_A, grad_initial_state, workspace: as for ssd_chunk_backward (same
+ *                workspace size).
+ * Constraints: as ssd_chunk_backward (D <= 64 among them).
+ * Alignment: proj, grad_proj, grad_y 4 bytes; A and the states 8 bytes.
+ */
+int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,
+                            int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                            int64_t chunk_size, const ssd_c64 *initial_state, const float *grad_y,
+                            const ssd_c64 *grad_final_state, float *grad_proj, ssd_c64 *grad_A,
+                            ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
+                            ssd_stream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 

@@ -183,3 +183,23 @@ def unpack_proj(proj, A, H, N, D):
     C_t = torch.complex(blk(2), blk(3))
     dt = proj[..., HD + 4 * HN:HD + 4 * HN + H]
     return ScanInputs(x.contiguous(), A, B_t.contiguous(), C_t.contiguous(), dt.contiguous())
+
+
+def pack_proj_grads(gx, gB, gC, gdt, S):
+    """Gradient rows in the in_proj layout from the complex-layout gradients of the
+    inputs the rows stand for (layout marshalling only): the x block takes the
+    real part of x's gradient (x is real), the B and C blocks the real and
+    imaginary parts, the dt block dt's gradient; floats past the blocks are 0."""
+    import numpy as np
+    gx, gB, gC, gdt = (np.asarray(v) for v in (gx, gB, gC, gdt))
+    Bsz, T, H, D = gx.shape
+    N = gB.shape[-1]
+    HD, HN = H * D, H * N
+    rows = np.zeros((Bsz, T, S), np.float64)
+    rows[..., :HD] = gx.real.reshape(Bsz, T, HD)
+    rows[..., HD:HD + HN] = gB.real.reshape(Bsz, T, HN)
+    rows[..., HD + HN:HD + 2 * HN] = gB.imag.reshape(Bsz, T, HN)
+    rows[..., HD + 2 * HN:HD + 3 * HN] = gC.real.reshape(Bsz, T, HN)
+    rows[..., HD + 3 * HN:HD + 4 * HN] = gC.imag.reshape(Bsz, T, HN)
+    rows[..., HD + 4 * HN:HD + 4 * HN + H] = gdt.reshape(Bsz, T, H)
+    return rows

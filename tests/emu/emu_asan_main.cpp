@@ -106,6 +106,32 @@ static int run_proj(int B, int T, int H, int N, int D, int Q, int extra)
     return st != 0 || bad != 0;
 }
 
+static int run_bwd_proj(int B, int T, int H, int N, int D, int Q, int extra)
+{
+    unsigned seed = 4242u + B * 7 + T * 13 + H * 17 + N * 19 + D * 23 + Q * 29;
+    const int64_t S = (int64_t)H * (D + 4 * N + 1) + extra;
+    float *proj = alloc_fill((size_t)B * T * S, seed);
+    float *A = alloc_fill((size_t)H * 2, seed);
+    for (int h = 0; h < H; ++h)
+        A[2 * h] = -0.05f - 2.9f * (A[2 * h] + 0.5f);
+    float *gy = alloc_fill((size_t)B * T * H * D, seed);
+    float *gp = (float *)malloc((size_t)B * T * S * sizeof(float));
+    for (size_t i = 0; i < (size_t)B * T * S; ++i)
+        gp[i] = 0.f;
+    float *gA = (float *)malloc((size_t)H * 2 * sizeof(float));
+    size_t ws = ssd_chunk_backward_workspace_bytes(B, T, H, N, D, Q);
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
+    int st = ssd_chunk_backward_proj(proj, S, (ssd_c64 *)A, B, T, H, N, D, Q, nullptr, gy, nullptr,
+                                     gp, (ssd_c64 *)gA, nullptr, w, ws, nullptr);
+    int bad = 0;
+    for (size_t i = 0; i < (size_t)B * T * S; ++i)
+        bad += !isfinite(gp[i]);
+    printf("backward proj B=%d T=%d H=%d N=%d D=%d Q=%d ws=%zu status=%d nonfinite=%d\n", B, T, H,
+           N, D, Q, ws, st, bad);
+    free(proj); free(A); free(gy); free(gp); free(gA); free(w);
+    return st != 0 || bad != 0;
+}
+
 int main()
 {
     int fails = 0;
@@ -122,6 +148,8 @@ int main()
     fails += run_proj(1, 40, 2, 4, 6, 16, 0);    // the last row's dt is the last float read
     fails += run_proj(1, 150, 1, 64, 64, 64, 1); // full tiles, segments (stride made even)
     fails += run_proj(2, 9, 1, 2, 4, 4, 1);      // Q < 16
+    fails += run_bwd_proj(1, 40, 2, 4, 6, 16, 1);   // gradient rows with a spare float
+    fails += run_bwd_proj(1, 70, 1, 64, 64, 64, 0); // full tiles
     printf("%s\n", fails ? "FAIL" : "OK");
     return fails;
 }

@@ -68,6 +68,9 @@ def load(out_dir):
             lib.ssd_chunk_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p,
                                                p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
             lib.ssd_chunk_backward.restype = ctypes.c_int
+            lib.ssd_chunk_backward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p,
+                                                    p, p, p, p, p, ctypes.c_size_t, p]
+            lib.ssd_chunk_backward_proj.restype = ctypes.c_int
             lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
             lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
             lib.ssd_chunk_forward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p, p,
@@ -157,3 +160,26 @@ def chunk_forward_proj(lib, proj, A, H, N, D, chunk, initial_state=None):
                                     None if init is None else init.ctypes.data, y.ctypes.data,
                                     fs.ctypes.data, ws_p if ws_n else None, ws_n, None)
     return st, y, fs
+
+
+def chunk_backward_proj(lib, proj, A, H, N, D, chunk, grad_y, grad_final=None):
+    """Returns (status, grad_proj rows (B, T, S) float32 with NaN past the blocks,
+    grad_A, grad_initial_state)."""
+    pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
+    Av = _c64(A)
+    Bsz, T, S = pr.shape
+    gy = np.ascontiguousarray(grad_y, np.float32)
+    gf = None if grad_final is None else np.ascontiguousarray(grad_final, np.complex64)
+    grows = np.full((Bsz, T, S), np.nan, np.float32)
+    W = H * (D + 4 * N + 1)
+    gA = np.full((H,), np.nan + 0j, np.complex64)
+    gi = np.full((Bsz, H, N, D), np.nan + 0j, np.complex64)
+    ws_n = lib.ssd_chunk_backward_workspace_bytes(Bsz, T, H, N, D, chunk)
+    ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
+    ws_p = ws.ctypes.data
+    ws_p = ws_p + (-ws_p) % 256
+    ptr = lambda a: None if a is None else a.ctypes.data
+    st = lib.ssd_chunk_backward_proj(ptr(pr), S, ptr(Av), Bsz, T, H, N, D, chunk, None, ptr(gy),
+                                     ptr(gf), ptr(grows), ptr(gA), ptr(gi),
+                                     ws_p if ws_n else None, ws_n, None)
+    return st, grows, gA, gi, W

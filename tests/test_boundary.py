@@ -211,3 +211,23 @@ def test_proj_argument_checks(lib):
         ssd.SSD_ERR_WORKSPACE
     assert lib.ssd_chunk_forward_proj(None, 42, None, 0, 16, 2, 4, 4, 4, None, None, None, None,
                                       0, None) == ssd.SSD_OK
+
+
+
+def test_backward_proj_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    S = 2 * (4 + 16 + 1)
+    need = lib.ssd_chunk_backward_workspace_bytes(1, 16, 2, 4, 4, 4)
+    f = lib.ssd_chunk_backward_proj
+    assert f(p, S - 1, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, p, need, None) == \
+        ssd.SSD_ERR_SHAPE
+    assert f(p, 1000, p, 1, 16, 2, 4, 65, 4, None, p, None, p, p, None, p, need, None) == \
+        ssd.SSD_ERR_UNSUPPORTED  # the backward's D <= 64
+    assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, None, p, None, p, need, None) == \
+        ssd.SSD_ERR_NULL
+    assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, None, None, p, need, None) == \
+        ssd.SSD_ERR_NULL
+    assert f(ctypes.c_void_p(0x100002), S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, p,
+             need, None) == ssd.SSD_ERR_ALIGN
+    assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, None, need, None) == \
+        ssd.SSD_ERR_WORKSPACE

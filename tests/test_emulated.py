@@ -206,3 +206,28 @@ def test_emulated_proj_bf16_matches_oracle(emu, case):
     inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
     yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
     _check(y, fs, yo, fo)
+
+
+@pytest.mark.parametrize("case", [(2, 16, 2, 4, 4, 4, 0), (1, 97, 2, 8, 6, 32, 6),
+                                  (2, 50, 2, 6, 10, 16, 4)])
+def test_emulated_backward_proj_matches_oracle(emu, case):
+    """Gradient rows of the in_proj layout: every block against the oracle's
+    gradients of the complex inputs the rows stand for; floats past the blocks
+    are not written."""
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 9, dt_mean=0.3, extra=extra)
+    rng = np.random.default_rng(sum(case))
+    gy = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+    st, rows, gA, gi, W = emu_harness.chunk_backward_proj(emu, proj, A, H, N, D, Q, gy, gf)
+    assert st == 0
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf)
+    want = ssd_inputs.pack_proj_grads(ref.x, ref.B_t, ref.C_t, ref.dt, proj.shape[-1])
+    got = rows[..., :W]
+    assert np.isfinite(got).all()
+    err = np.abs(got - want[..., :W])
+    assert (err <= 1e-4 + 1e-4 * np.abs(want[..., :W])).all(), err.max()
+    assert np.isnan(rows[..., W:]).all()
+    assert (np.abs(gA - ref.A) <= 1e-4 + 1e-6 * B * T + 1e-4 * np.abs(ref.A)).all()
+    assert (np.abs(gi - ref.initial_state) <= 1e-4 + 1e-4 * np.abs(ref.initial_state)).all()

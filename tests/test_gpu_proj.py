@@ -136,3 +136,70 @@ def test_proj_bf16_network_layer_matches_float32_rows():
         yo, fo = oracle.scan(one.x, one.A, one.B_t, one.C_t, one.dt)
         _check(a[b:b + 1, :, h:h + 1], fs.cpu().numpy()[b:b + 1, h:h + 1], yo, fo,
                "bf16 network (%d, %d)" % (b, h))
+
+
+# Gradients from in_proj rows (ssd_chunk_backward_proj): every block of the
+# gradient rows against the oracle's gradients of the complex inputs the rows
+# stand for, with the gradient bar (grad_A's absolute term grows 1e-6 per
+# token summed); floats past the blocks stay untouched.
+
+def _check_grad_rows(rows, gA, gi, ref, S, W, what, tokens):
+    want = ssd_inputs.pack_proj_grads(ref.x, ref.B_t, ref.C_t, ref.dt, S)
+    got = rows[..., :W]
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - want[..., :W])
+    bad = err > 1e-4 + 1e-4 * np.abs(want[..., :W])
+    assert not bad.any(), "%s: %d violations, max %.3e" % (what, int(bad.sum()), err.max())
+    assert (rows[..., W:] == 0).all(), what
+    for comp in (np.real, np.imag):
+        assert (np.abs(comp(gA) - comp(ref.A)) <= 1e-4 + 1e-6 * tokens
+                + 1e-4 * np.abs(comp(ref.A))).all(), what
+        d = np.abs(comp(gi) - comp(ref.initial_state))
+        assert (d <= 1e-4 + 1e-4 * np.abs(comp(ref.initial_state))).all(), what
+
+
+@pytest.mark.parametrize("case", CASES[:8])
+def test_backward_proj_small_shapes(case):
+    B, T, H, N, D, Q, extra = case
+    if D > 64:
+        pytest.skip("the backward covers D <= 64")
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 70, dt_mean=0.3, extra=extra)
+    gy, gf = ssd_inputs.upstream_grads(B, T, H, N, D, seed=sum(case))
+    rows, gA, gi = ssd.chunk_backward_proj(proj.to(DEV), A.to(DEV), H, N, D, gy.to(DEV),
+                                           gf.to(DEV), chunk_size=Q)
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf)
+    _check_grad_rows(rows.cpu().numpy(), gA.cpu().numpy(), gi.cpu().numpy(), ref, proj.shape[-1],
+                     H * (D + 4 * N + 1), "bwd proj " + str(case), B * T)
+
+
+def test_backward_proj_network_layer_sampled():
+    """Network layer shape (B=32): sampled sequences' gradient rows, and the x,
+    B and C blocks against the complex-layout backward on the unpacked inputs."""
+    H, N, D = 16, 64, 64
+    proj, A = ssd_inputs.proj_case(32, 2048, H, N, D, seed=0, device=DEV)
+    gy, gf = ssd_inputs.upstream_grads(32, 2048, H, N, D, seed=0, device=DEV)
+    rows, gA, gi = ssd.chunk_backward_proj(proj, A, H, N, D, gy, gf, chunk_size=64)
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    g = ssd.chunk_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf, chunk_size=64)
+    torch.cuda.synchronize()
+    want = ssd_inputs.pack_proj_grads(g.x.cpu().numpy(), g.B_t.cpu().numpy(), g.C_t.cpu().numpy(),
+                                      g.dt.cpu().numpy(), proj.shape[-1])
+    r = rows.cpu().numpy()
+    assert (np.abs(r - want) <= 2e-4 + 2e-4 * np.abs(want)).all()
+    host, hgy, hgf = inp.to("cpu"), gy.cpu(), gf.cpu()
+    for b, h in [(2, 5), (29, 14)]:
+        one = host.select(b, h)
+        ref = oracle.scan_backward(one.x, one.A, one.B_t, one.C_t, one.dt,
+                                   hgy[b:b + 1, :, h:h + 1], hgf[b:b + 1, h:h + 1])
+        want1 = ssd_inputs.pack_proj_grads(ref.x, ref.B_t, ref.C_t, ref.dt, 1 * (D + 4 * N + 1))
+        got1 = np.concatenate([
+            r[b, :, h * D:(h + 1) * D],
+            r[b, :, H * D + h * N:H * D + (h + 1) * N],
+            r[b, :, H * D + H * N + h * N:H * D + H * N + (h + 1) * N],
+            r[b, :, H * D + 2 * H * N + h * N:H * D + 2 * H * N + (h + 1) * N],
+            r[b, :, H * D + 3 * H * N + h * N:H * D + 3 * H * N + (h + 1) * N],
+            r[b, :, H * D + 4 * H * N + h:H * D + 4 * H * N + h + 1]], axis=-1)[None]
+        e = np.abs(got1 - want1)
+        assert (e <= 1e-4 + 1e-4 * np.abs(want1)).all(), ((b, h), e.max())
