@@ -17,6 +17,9 @@ scan_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None,
     -> Grads(x, A, B_t, C_t, dt, initial_state): the gradients of
        sum(grad_y * y.real) + sum(Re(conj(grad_final_state) * final_state)),
        complex ones as dl/dRe + i dl/dIm (torch's convention), in float64
+head_mix(y, W, lib=None) -> z float64, same shape as y (..., H, D):
+    z[..., i, :] = sum_j W[i, j] y[..., j, :]   (the MIMO head mixer)
+head_mix_backward(y, W, grad_z, lib=None) -> (grad_y, grad_W) float64
 """
 
 from __future__ import annotations
@@ -60,6 +63,10 @@ def _bind(lib):
     lib.oracle_scan_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p, p, p,
                                          p, p, p, p, p, p, ctypes.c_int]
     lib.oracle_scan_backward.restype = ctypes.c_int
+    lib.oracle_head_mix.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_head_mix.restype = ctypes.c_int
+    lib.oracle_head_mix_backward.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.oracle_head_mix_backward.restype = ctypes.c_int
     return lib
 
 
@@ -192,3 +199,42 @@ def scan_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None, initial_sta
         raise RuntimeError("oracle_scan_backward failed with %d" % rc)
     c = lambda v: v[..., 0] + 1j * v[..., 1]
     return Grads(c(gx), c(gA), c(gB), c(gC), gdt, c(gi))
+
+
+def _mix_operands(y, W):
+    yf = _as_f32(y)
+    Wf = _as_f32(W)
+    if yf.ndim < 2:
+        raise ValueError("y must be (..., H, D)")
+    H, D = yf.shape[-2:]
+    if Wf.shape != (H, H):
+        raise ValueError("W must be (H, H) = (%d, %d)" % (H, H))
+    M = int(np.prod(yf.shape[:-2], dtype=np.int64))
+    return yf, Wf, M, H, D
+
+
+def head_mix(y, W, lib=None):
+    """z[..., i, :] = sum_j W[i, j] y[..., j, :] in double, from float32 inputs."""
+    lib = lib or load()
+    yf, Wf, M, H, D = _mix_operands(y, W)
+    z = np.zeros(yf.shape, np.float64)
+    rc = lib.oracle_head_mix(yf.ctypes.data, Wf.ctypes.data, M, H, D, z.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_head_mix failed with %d" % rc)
+    return z
+
+
+def head_mix_backward(y, W, grad_z, lib=None):
+    """Gradients of sum(grad_z * head_mix(y, W)) for y and W, in double."""
+    lib = lib or load()
+    yf, Wf, M, H, D = _mix_operands(y, W)
+    gzf = _as_f32(grad_z)
+    if gzf.shape != yf.shape:
+        raise ValueError("grad_z must have the shape of y")
+    gy = np.zeros(yf.shape, np.float64)
+    gW = np.zeros((H, H), np.float64)
+    rc = lib.oracle_head_mix_backward(yf.ctypes.data, Wf.ctypes.data, gzf.ctypes.data, M, H, D,
+                                      gy.ctypes.data, gW.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_head_mix_backward failed with %d" % rc)
+    return gy, gW

@@ -78,7 +78,7 @@ static void store_c(double *p, int64_t i, cplx v)
     p[2 * i + 1] = cimag(v);
 }
 
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
@@ -283,6 +283,60 @@ int oracle_scan_backward(const float *x, const float *A, const float *Bt, const 
     }
     free(gA_seq);
     return failed ? -2 : 0;
+}
+
+/* MIMO head mixer after the scan -- index.html lab 02 "MIMO MIXER" (a 16 x 16
+ * fully connected mixer across the SSM heads, 1024 -> 1024 as 16 heads of 64,
+ * identity at initialisation), the AGENTS page "Knows cold" item 2, and the
+ * in_proj -> scan -> MIMO -> out_proj order of the "Extending" guide, Path A.
+ * Read as one H x H real matrix shared by every token and every head-dim
+ * channel:
+ *     z[m, i, d] = sum_j W[i, j] y[m, j, d]
+ * y, z (M, H, D) with M = batch * T tokens; W (H, H) row-major. */
+int oracle_head_mix(const float *y, const float *W, int64_t M, int64_t H, int64_t D, double *z)
+{
+    if (!y || !W || !z || M < 0 || H <= 0 || D <= 0)
+        return -1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < H; ++i)
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < H; ++j)
+                    acc += (double)W[i * H + j] * (double)y[(m * H + j) * D + d];
+                z[(m * H + i) * D + d] = acc;
+            }
+    return 0;
+}
+
+/* Gradients of l = sum gz * z for the mixer above, by the chain rule on its
+ * definition:
+ *     gy[m, j, d] = sum_i W[i, j] gz[m, i, d]
+ *     gW[i, j]    = sum_{m, d} gz[m, i, d] y[m, j, d]
+ * Either output may be NULL. */
+int oracle_head_mix_backward(const float *y, const float *W, const float *gz, int64_t M,
+                             int64_t H, int64_t D, double *gy, double *gW)
+{
+    if (!y || !W || !gz || M < 0 || H <= 0 || D <= 0)
+        return -1;
+    if (gy)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t j = 0; j < H; ++j)
+                for (int64_t d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < H; ++i)
+                        acc += (double)W[i * H + j] * (double)gz[(m * H + i) * D + d];
+                    gy[(m * H + j) * D + d] = acc;
+                }
+    if (gW)
+        for (int64_t i = 0; i < H; ++i)
+            for (int64_t j = 0; j < H; ++j) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m)
+                    for (int64_t d = 0; d < D; ++d)
+                        acc += (double)gz[(m * H + i) * D + d] * (double)y[(m * H + j) * D + d];
+                gW[i * H + j] = acc;
+            }
+    return 0;
 }
 
 int oracle_max_threads(void)
