@@ -167,6 +167,46 @@ def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20, dtype=None)
                              N, D, T, elem)}}
 
 
+def mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev, reps=20):
+    """The MIMO head mixer after the scan (ssd_head_mix) and its gradients
+    (ssd_head_mix_backward) at the network layer shape; median of `reps`
+    event-timed calls each. Both are bound by HBM: the forward reads y and
+    writes z once (8 bytes per element), the backward reads y and grad_z and
+    writes grad_y (12 bytes per element; W, grad_W and the partial gW tiles
+    are a few KB)."""
+    y, W, gz = ssd_inputs.mix_case((B, T, H, D), seed=0, device=dev)
+    z = torch.empty_like(y)
+    gy = torch.empty_like(y)
+    gW = torch.empty((H, H), device=dev)
+    ws = torch.empty(max(ssd.head_mix_workspace_bytes(B * T, H, D), 1), dtype=torch.uint8,
+                     device=dev)
+    out = {"workload": "network layer y (B=%d, T=%d, H=%d, D=%d), W (%d, %d)" % (B, T, H, D, H, H)}
+    elems = B * T * H * D
+    for name, call, nbytes in (
+            ("forward", lambda: ssd.head_mix(y, W, z=z), 8 * elems),
+            ("backward", lambda: ssd.head_mix_backward(y, W, gz, grad_y=gy, grad_W=gW,
+                                                       workspace=ws), 12 * elems)):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                  "algorithmic_bytes": nbytes}}
+    del y, W, gz, z, gy, gW, ws
+    return out
+
+
 def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10):
     """ssd_chunk_backward_proj (gradients as in_proj gradient rows) at the network
     layer shape; median of `reps` event-timed calls."""
@@ -251,6 +291,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward side figure")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward on layer 0 of the workload and print it")
+    ap.add_argument("--mix-only", action="store_true",
+                    help="time only the MIMO head mixer (forward and gradients) and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR", default=None,
                     help="read the four rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scan and a "
                          "1 GiB copy) under DIR and write the committed traffic summary")
@@ -283,6 +325,10 @@ def main():
         return 0
     wl = dict(ssd_inputs.WORKLOADS[args.workload])
     B, T, H, N, D = wl["batch"], wl["T"], wl["H"], wl["N"], wl["D"]
+    if args.mix_only:
+        print(json.dumps({"head_mix": mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev,
+                                              reps=max(args.steps, 1))}), flush=True)
+        return 0
     if args.backward_only:
         g = ssd_inputs.layer_case(B, T, H, N, D, seed=0 if wl["seed"] is None else wl["seed"],
                                   dt_mean=wl["dt_mean"], device=dev)
@@ -412,6 +458,7 @@ def main():
         out["proj_layer"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev)
         out["proj_layer_bf16"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev,
                                           dtype=torch.bfloat16)
+        out["head_mix"] = mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev)
     if not args.no_backward:
         log("bench: timing the backward on layer 0")
         out["backward"] = backward_leg(ssd, torch, layers[0])

@@ -9,6 +9,8 @@ and a visible GPU, and fails loudly otherwise (there is no fallback path).
     y, final_state = chunk_forward_proj(proj, A, H, N, D, chunk_size=64)
     grads = chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None)
     A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
+    z = head_mix(y, W)                       # MIMO head mixer after the scan
+    grad_y, grad_W = head_mix_backward(y, W, grad_z)
 """
 
 from __future__ import annotations
@@ -79,6 +81,13 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_backward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                                 vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_backward_proj.restype = ctypes.c_int
+        lib.ssd_head_mix.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        lib.ssd_head_mix.restype = ctypes.c_int
+        lib.ssd_head_mix_backward_workspace_bytes.argtypes = [i64] * 3
+        lib.ssd_head_mix_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_head_mix_backward.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp,
+                                              ctypes.c_size_t, vp]
+        lib.ssd_head_mix_backward.restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_version.restype = ctypes.c_int
@@ -388,3 +397,59 @@ def backward_algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
     """Bytes the gradients must move per (token, head): x, B_t, C_t, dt, grad_y
     in; grad_x, grad_B_t, grad_C_t, grad_dt out; the state gradients amortised."""
     return (8 * D + 16 * N + 4 + 4 * D) + (8 * D + 16 * N + 4) + 16 * N * D / T
+
+
+def _mix_shape(y, W):
+    if not isinstance(y, torch.Tensor) or y.dim() < 2:
+        raise ValueError("y must be a (..., H, D) tensor")
+    H, D = y.shape[-2], y.shape[-1]
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(y, "y", torch.float32, tuple(y.shape), dev)
+    _check(W, "W", torch.float32, (H, H), dev)
+    tokens = 1
+    for n in y.shape[:-2]:
+        tokens *= int(n)
+    return tokens, H, D, dev
+
+
+def head_mix(y, W, z=None):
+    """MIMO head mixer after the scan: z[..., i, :] = sum_j W[i, j] y[..., j, :].
+    y (..., H, D) float32 (e.g. the scan's (B, T, H, D) output), W (H, H)
+    float32; z may be passed in (it may be y itself)."""
+    lib = load_library()
+    tokens, H, D, dev = _mix_shape(y, W)
+    if z is None:
+        z = torch.empty_like(y)
+    _check(z, "z", torch.float32, tuple(y.shape), dev)
+    st = lib.ssd_head_mix(_ptr(y), _ptr(W), tokens, H, D, _ptr(z), _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_head_mix")
+    return z
+
+
+def head_mix_workspace_bytes(tokens: int, H: int, D: int) -> int:
+    return int(load_library().ssd_head_mix_backward_workspace_bytes(tokens, H, D))
+
+
+def head_mix_backward(y, W, grad_z, grad_y=None, grad_W=None, workspace=None):
+    """Gradients of sum(grad_z * head_mix(y, W)): returns (grad_y, grad_W)."""
+    lib = load_library()
+    tokens, H, D, dev = _mix_shape(y, W)
+    _check(grad_z, "grad_z", torch.float32, tuple(y.shape), dev)
+    if grad_y is None:
+        grad_y = torch.empty_like(y)
+    _check(grad_y, "grad_y", torch.float32, tuple(y.shape), dev)
+    if grad_W is None:
+        grad_W = torch.empty((H, H), dtype=torch.float32, device=dev)
+    _check(grad_W, "grad_W", torch.float32, (H, H), dev)
+    ws_n = int(lib.ssd_head_mix_backward_workspace_bytes(tokens, H, D))
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_head_mix_backward(_ptr(y), _ptr(W), _ptr(grad_z), tokens, H, D, _ptr(grad_y),
+                                   _ptr(grad_W), _ptr(workspace), ws_size, _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_head_mix_backward")
+    return grad_y, grad_W

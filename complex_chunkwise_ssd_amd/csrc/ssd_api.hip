@@ -4,6 +4,7 @@
 #include "ssd.h"
 
 #include <ssd_bwd_kernels.h>
+#include <ssd_mix_kernels.h>
 
 namespace {
 
@@ -163,6 +164,59 @@ int forward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t 
     return launch_forward<LAYOUT>(prm, plan, batch * H, s);
 }
 
+int check_mix(int64_t tokens, int64_t H, int64_t D)
+{
+    if (tokens < 0 || H < 1 || D < 1)
+        return SSD_ERR_SHAPE;
+    if (D > SSD_MAX_BLOCK)
+        return SSD_ERR_BLOCK_DIMS;
+    if (H > ssd::kMixMaxH)
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+// Workgroups of the gW pass: four tokens per workgroup at most, 1024 at most.
+int64_t mix_gw_groups(int64_t tokens)
+{
+    const int64_t g = (tokens + 3) / 4;
+    return g < ssd::kMixGwGroups ? g : ssd::kMixGwGroups;
+}
+
+template <int HMAX>
+int launch_mix_h(const ssd::MixParams &p, bool vec, hipStream_t stream)
+{
+    const int64_t cols = p.M * (vec ? p.D / 4 : p.D);
+    int64_t blocks = (cols + ssd::kMixThreads - 1) / ssd::kMixThreads;
+    if (blocks > 16384)
+        blocks = 16384;  // the kernel strides over the rest
+    if (blocks == 0)
+        return SSD_OK;
+    if (vec)
+        hipLaunchKernelGGL((ssd::mix_kernel<HMAX, 4>), dim3((unsigned)blocks),
+                           dim3(ssd::kMixThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((ssd::mix_kernel<HMAX, 1>), dim3((unsigned)blocks),
+                           dim3(ssd::kMixThreads), 0, stream, p);
+    return launch_status();
+}
+
+int launch_mix(const ssd::MixParams &p, bool vec, hipStream_t stream)
+{
+    return p.H <= 16 ? launch_mix_h<16>(p, vec, stream) : launch_mix_h<32>(p, vec, stream);
+}
+
+template <int HT>
+int launch_mix_gw(const ssd::MixGradParams &p, int64_t groups, bool vec, hipStream_t stream)
+{
+    if (vec)
+        hipLaunchKernelGGL((ssd::mix_gw_kernel<HT, 4>), dim3((unsigned)groups),
+                           dim3(ssd::kMixThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((ssd::mix_gw_kernel<HT, 1>), dim3((unsigned)groups),
+                           dim3(ssd::kMixThreads), 0, stream, p);
+    return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,7 +235,8 @@ const char *ssd_status_string(int status)
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
     case SSD_ERR_UNSUPPORTED:
-        return "size not covered by this build (N <= 64; for gradients also D <= 64)";
+        return "size not covered by this build (N <= 64; for gradients also D <= 64; "
+               "mixer H <= 32)";
     default: return "unknown status";
     }
 }
@@ -471,6 +526,89 @@ int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c
     const int64_t seqs = batch * H;
     return plan.R == 16 ? launch_backward<16, true>(prm, seqs, s)
                         : launch_backward<32, true>(prm, seqs, s);
+}
+
+int ssd_head_mix(const float *y, const float *W, int64_t tokens, int64_t H, int64_t D, float *z,
+                 ssd_stream_t stream)
+{
+    if (int st = check_mix(tokens, H, D))
+        return st;
+    if (tokens == 0)
+        return SSD_OK;
+    if (!y || !W || !z)
+        return SSD_ERR_NULL;
+    if (!aligned(y, 4) || !aligned(W, 4) || !aligned(z, 4))
+        return SSD_ERR_ALIGN;
+    ssd::MixParams p{};
+    p.in = y;
+    p.W = W;
+    p.out = z;
+    p.M = tokens;
+    p.H = (int)H;
+    p.D = (int)D;
+    p.transpose = 0;
+    const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(z, 16);
+    return launch_mix(p, vec, (hipStream_t)stream);
+}
+
+size_t ssd_head_mix_backward_workspace_bytes(int64_t tokens, int64_t H, int64_t D)
+{
+    if (check_mix(tokens, H, D))
+        return 0;
+    return ssd::align_up((size_t)mix_gw_groups(tokens) * (size_t)(H * H) * 4, 256);
+}
+
+int ssd_head_mix_backward(const float *y, const float *W, const float *grad_z, int64_t tokens,
+                          int64_t H, int64_t D, float *grad_y, float *grad_W, void *workspace,
+                          size_t workspace_bytes, ssd_stream_t stream)
+{
+    if (int st = check_mix(tokens, H, D))
+        return st;
+    if (!grad_W || (tokens > 0 && (!y || !W || !grad_z || !grad_y)))
+        return SSD_ERR_NULL;
+    if (!aligned(y, 4) || !aligned(W, 4) || !aligned(grad_z, 4) || !aligned(grad_y, 4) ||
+        !aligned(grad_W, 4))
+        return SSD_ERR_ALIGN;
+    const size_t need = ssd_head_mix_backward_workspace_bytes(tokens, H, D);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return SSD_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 4))
+        return SSD_ERR_ALIGN;
+    const hipStream_t s = (hipStream_t)stream;
+    if (tokens == 0) {  // grad_W = 0
+        hipLaunchKernelGGL(ssd::mix_gw_reduce_kernel, dim3((unsigned)(H * H)), dim3(64), 0, s,
+                           (const float *)nullptr, 0, (int)(H * H), grad_W);
+        return launch_status();
+    }
+
+    ssd::MixParams p{};
+    p.in = grad_z;
+    p.W = W;
+    p.out = grad_y;
+    p.M = tokens;
+    p.H = (int)H;
+    p.D = (int)D;
+    p.transpose = 1;
+    if (int st = launch_mix(p, D % 4 == 0 && aligned(grad_z, 16) && aligned(grad_y, 16), s))
+        return st;
+
+    const int64_t groups = mix_gw_groups(tokens);
+    {
+        ssd::MixGradParams g{};
+        g.y = y;
+        g.gz = grad_z;
+        g.partial = (float *)workspace;
+        g.M = tokens;
+        g.H = (int)H;
+        g.D = (int)D;
+        const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16);
+        const int st = H <= 16 ? launch_mix_gw<1>(g, groups, vec, s) : launch_mix_gw<2>(g, groups, vec, s);
+        if (st)
+            return st;
+    }
+    hipLaunchKernelGGL(ssd::mix_gw_reduce_kernel, dim3((unsigned)(H * H)), dim3(64), 0, s,
+                       (const float *)workspace, (int)groups, (int)(H * H), grad_W);
+    return launch_status();
 }
 
 }  // extern "C"

@@ -240,6 +240,55 @@ int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c
                             ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
                             ssd_stream_t stream);
 
+/*
+ * ssd_head_mix -- the MIMO head mixer that follows the scan (index.html lab 02
+ * "MIMO MIXER": a fully connected mixer across the SSM heads, 16 x 16 for the
+ * 16 heads of 64 channels, identity at initialisation; "Knows cold" item 2 of
+ * the AGENTS page; the in_proj -> scan -> MIMO -> out_proj order of
+ * "Extending", Path A). One H x H real matrix mixes the heads of each token,
+ * the same for every head-dim channel:
+ *
+ *   z[m, i, d] = sum_j W[i, j] * y[m, j, d]
+ *
+ *   y        (tokens, H, D) float32: the scan output, tokens = batch * T.
+ *   W        (H, H) float32, row-major (row i = weights of output head i).
+ *   z        out: (tokens, H, D) float32. z may be y itself (in place); any
+ *            other overlap of z with y or W gives undefined results.
+ *   tokens   >= 0; with 0 nothing is launched and y, W, z may be NULL.
+ *            1 <= H <= 32; 1 <= D <= 256.
+ * Alignment: 4 bytes (16-byte aligned y, z with D % 4 == 0 take the vector path).
+ * Status: SSD_ERR_SHAPE for sizes out of range, SSD_ERR_BLOCK_DIMS for D > 256,
+ * SSD_ERR_UNSUPPORTED for H > 32.
+ */
+int ssd_head_mix(const float *y, const float *W, int64_t tokens, int64_t H, int64_t D, float *z,
+                 ssd_stream_t stream);
+
+/* Workspace bytes that ssd_head_mix_backward needs (0 for invalid sizes or
+ * tokens == 0). At most 1024 * H * H * 4 bytes. */
+size_t ssd_head_mix_backward_workspace_bytes(int64_t tokens, int64_t H, int64_t D);
+
+/*
+ * ssd_head_mix_backward -- gradients of l = sum grad_z * z for ssd_head_mix,
+ * by the chain rule on its definition:
+ *
+ *   grad_y[m, j, d] = sum_i W[i, j] * grad_z[m, i, d]
+ *   grad_W[i, j]    = sum_{m, d} grad_z[m, i, d] * y[m, j, d]
+ *
+ *   y, W, tokens, H, D  as for ssd_head_mix (y is the forward's input).
+ *   grad_z    (tokens, H, D) float32.
+ *   grad_y    out: (tokens, H, D) float32; may be grad_z itself (in place).
+ *   grad_W    out: (H, H) float32, overwritten. The sum runs in a fixed
+ *             order: repeated calls give identical bits. With tokens == 0 it is
+ *             set to zero and every other pointer may be NULL.
+ *   workspace device memory of ssd_head_mix_backward_workspace_bytes bytes
+ *             (NULL allowed when that is 0), 4-byte aligned.
+ * Alignment and status codes as ssd_head_mix; SSD_ERR_WORKSPACE when the
+ * workspace is missing or too small.
+ */
+int ssd_head_mix_backward(const float *y, const float *W, const float *grad_z, int64_t tokens,
+                          int64_t H, int64_t D, float *grad_y, float *grad_W, void *workspace,
+                          size_t workspace_bytes, ssd_stream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 

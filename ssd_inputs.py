@@ -203,3 +203,17 @@ def pack_proj_grads(gx, gB, gC, gdt, S):
     rows[..., HD + 3 * HN:HD + 4 * HN] = gC.imag.reshape(Bsz, T, HN)
     rows[..., HD + 4 * HN:HD + 4 * HN + H] = gdt.reshape(Bsz, T, H)
     return rows
+
+
+def mix_case(shape, seed, device="cpu", spread=0.1):
+    """Inputs of the MIMO head mixer: y and the upstream gradient gz of the
+    given (..., H, D) shape, standard normal float32, and W = identity plus
+    spread * N(0, 1) per entry (the pages start the mixer at the identity and
+    let training grow cross-head links; the perturbation stands in for a
+    trained mixer). Draw order: W noise, y, gz."""
+    g = _gen(seed, device)
+    H = shape[-2]
+    W = torch.eye(H, device=device) + spread * torch.randn(H, H, generator=g, device=device)
+    y = torch.randn(*shape, generator=g, device=device)
+    gz = torch.randn(*shape, generator=g, device=device)
+    return y, W.contiguous(), gz

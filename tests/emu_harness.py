@@ -78,6 +78,13 @@ def load(out_dir):
             lib.ssd_chunk_forward_proj.restype = ctypes.c_int
             lib.ssd_chunk_forward_proj_bf16.argtypes = lib.ssd_chunk_forward_proj.argtypes
             lib.ssd_chunk_forward_proj_bf16.restype = ctypes.c_int
+            lib.ssd_head_mix.argtypes = [p, p, i64, i64, i64, p, p]
+            lib.ssd_head_mix.restype = ctypes.c_int
+            lib.ssd_head_mix_backward_workspace_bytes.argtypes = [i64] * 3
+            lib.ssd_head_mix_backward_workspace_bytes.restype = ctypes.c_size_t
+            lib.ssd_head_mix_backward.argtypes = [p, p, p, i64, i64, i64, p, p, p, ctypes.c_size_t,
+                                                  p]
+            lib.ssd_head_mix_backward.restype = ctypes.c_int
             lib.emu_mfma_count.restype = ctypes.c_long
             lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
             lib.emu_sincos.restype = None
@@ -183,3 +190,37 @@ def chunk_backward_proj(lib, proj, A, H, N, D, chunk, grad_y, grad_final=None):
                                      ptr(gf), ptr(grows), ptr(gA), ptr(gi),
                                      ws_p if ws_n else None, ws_n, None)
     return st, grows, gA, gi, W
+
+
+def head_mix(lib, y, W, offset=0):
+    """y (..., H, D) float32 numpy, W (H, H); returns (status, z). `offset`
+    floats shift y and z off 16-byte alignment (the scalar path)."""
+    y = np.asarray(y, np.float32)
+    H, D = y.shape[-2:]
+    M = int(np.prod(y.shape[:-2], dtype=np.int64))
+    yb = np.zeros(y.size + 8, np.float32)
+    zb = np.full(y.size + 8, np.nan, np.float32)
+    yb[offset:offset + y.size] = y.ravel()
+    Wv = np.ascontiguousarray(W, np.float32)
+    st = lib.ssd_head_mix(yb.ctypes.data + 4 * offset, Wv.ctypes.data, M, H, D,
+                          zb.ctypes.data + 4 * offset, None)
+    return st, zb[offset:offset + y.size].reshape(y.shape)
+
+
+def head_mix_backward(lib, y, W, gz):
+    """Returns (status, grad_y, grad_W) from the emulated library."""
+    y = np.ascontiguousarray(y, np.float32)
+    gz = np.ascontiguousarray(gz, np.float32)
+    H, D = y.shape[-2:]
+    M = int(np.prod(y.shape[:-2], dtype=np.int64))
+    Wv = np.ascontiguousarray(W, np.float32)
+    gy = np.full(y.shape, np.nan, np.float32)
+    gW = np.full((H, H), np.nan, np.float32)
+    ws_n = lib.ssd_head_mix_backward_workspace_bytes(M, H, D)
+    ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
+    ws_p = ws.ctypes.data
+    ws_p = ws_p + (-ws_p) % 256
+    st = lib.ssd_head_mix_backward(y.ctypes.data, Wv.ctypes.data, gz.ctypes.data, M, H, D,
+                                   gy.ctypes.data, gW.ctypes.data, ws_p if ws_n else None, ws_n,
+                                   None)
+    return st, gy, gW

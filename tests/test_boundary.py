@@ -231,3 +231,44 @@ def test_backward_proj_argument_checks(lib):
              need, None) == ssd.SSD_ERR_ALIGN
     assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, None, need, None) == \
         ssd.SSD_ERR_WORKSPACE
+
+
+def test_head_mix_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    f = lib.ssd_head_mix
+    assert f(None, p, 4, 16, 64, p, None) == ssd.SSD_ERR_NULL
+    assert f(p, None, 4, 16, 64, p, None) == ssd.SSD_ERR_NULL
+    assert f(p, p, 4, 16, 64, None, None) == ssd.SSD_ERR_NULL
+    assert f(p, p, -1, 16, 64, p, None) == ssd.SSD_ERR_SHAPE
+    assert f(p, p, 4, 0, 64, p, None) == ssd.SSD_ERR_SHAPE
+    assert f(p, p, 4, 16, 0, p, None) == ssd.SSD_ERR_SHAPE
+    assert f(p, p, 4, 16, 257, p, None) == ssd.SSD_ERR_BLOCK_DIMS
+    assert f(p, p, 4, 33, 64, p, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert f(ctypes.c_void_p(0x100002), p, 4, 16, 64, p, None) == ssd.SSD_ERR_ALIGN
+    assert f(p, p, 0, 16, 64, p, None) == ssd.SSD_OK  # no tokens: nothing launched
+
+
+def test_head_mix_backward_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    f = lib.ssd_head_mix_backward
+    need = lib.ssd_head_mix_backward_workspace_bytes(65536, 16, 64)
+    assert need == 1024 * 16 * 16 * 4
+    assert lib.ssd_head_mix_backward_workspace_bytes(5, 16, 64) == 256 * ((2 * 1024 + 255) // 256)
+    assert lib.ssd_head_mix_backward_workspace_bytes(0, 16, 64) == 0
+    assert lib.ssd_head_mix_backward_workspace_bytes(4, 33, 64) == 0
+    assert f(p, p, p, 8, 16, 64, p, None, p, need, None) == ssd.SSD_ERR_NULL
+    assert f(p, p, None, 8, 16, 64, p, p, p, need, None) == ssd.SSD_ERR_NULL
+    assert f(p, p, p, 8, 40, 64, p, p, p, need, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert f(p, p, p, 8, 16, 64, p, p, None, need, None) == ssd.SSD_ERR_WORKSPACE
+    assert f(p, p, p, 8, 16, 64, p, p, p, 16, None) == ssd.SSD_ERR_WORKSPACE
+    assert f(p, p, p, 8, 16, 64, ctypes.c_void_p(0x100001), p, p, need, None) == \
+        ssd.SSD_ERR_ALIGN
+
+
+def test_python_head_mix_rejects_bad_tensors():
+    import torch
+    y = torch.zeros(2, 3, 4, 8)
+    with pytest.raises(ValueError):
+        ssd.head_mix(y, torch.eye(4))  # CPU tensors
+    with pytest.raises(ValueError):
+        ssd.head_mix_backward(y, torch.eye(4), y)

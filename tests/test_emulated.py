@@ -12,6 +12,7 @@ import pytest
 import emu_harness
 import oracle
 import ssd_inputs
+import tolerances
 
 
 @pytest.fixture(scope="module")
@@ -231,3 +232,48 @@ def test_emulated_backward_proj_matches_oracle(emu, case):
     assert np.isnan(rows[..., W:]).all()
     assert (np.abs(gA - ref.A) <= 1e-4 + 1e-6 * B * T + 1e-4 * np.abs(ref.A)).all()
     assert (np.abs(gi - ref.initial_state) <= 1e-4 + 1e-4 * np.abs(ref.initial_state)).all()
+
+
+MIX_CASES = [
+    # tokens shape, H, D, float offset (1 = off 16-byte alignment)
+    ((5,), 16, 64, 0),      # vector path, the pages' 16 heads of 64
+    ((2, 3), 7, 10, 0),     # D % 4 != 0: scalar path; H < 16 padded
+    ((9,), 20, 8, 0),       # H > 16: two head blocks
+    ((1,), 1, 1, 0),
+    ((4,), 16, 64, 1),      # misaligned rows take the scalar path
+    ((3,), 32, 12, 0),
+]
+
+
+@pytest.mark.parametrize("case", MIX_CASES)
+def test_emulated_head_mix_matches_oracle(emu, case):
+    lead, H, D, off = case
+    y, W, gz = ssd_inputs.mix_case(lead + (H, D), seed=H * 100 + D)
+    st, z = emu_harness.head_mix(emu, y.numpy(), W.numpy(), offset=off)
+    assert st == 0
+    ref = oracle.head_mix(y, W)
+    assert np.isfinite(z).all()
+    err = np.abs(z - ref)
+    assert (err <= 1e-4 + 1e-4 * np.abs(ref)).all(), err.max()
+
+
+@pytest.mark.parametrize("case", MIX_CASES[:3] + [((70,), 16, 64, 0), ((2100,), 4, 4, 0)])
+def test_emulated_head_mix_backward_matches_oracle(emu, case):
+    lead, H, D, _ = case
+    y, W, gz = ssd_inputs.mix_case(lead + (H, D), seed=H * 100 + D + 1)
+    st, gy, gW = emu_harness.head_mix_backward(emu, y.numpy(), W.numpy(), gz.numpy())
+    assert st == 0
+    ry, rW = oracle.head_mix_backward(y, W, gz)
+    assert np.isfinite(gy).all() and np.isfinite(gW).all()
+    assert (np.abs(gy - ry) <= 1e-4 + 1e-4 * np.abs(ry)).all()
+    tol = 1e-4 * (1 + np.abs(rW)) + tolerances.grad_w_extra(gz.numpy(), y.numpy())
+    assert (np.abs(gW - rW) <= tol).all(), np.abs(gW - rW).max()
+
+
+def test_emulated_head_mix_zero_tokens(emu):
+    y = np.zeros((0, 4, 8), np.float32)
+    W = np.eye(4, dtype=np.float32)
+    st, z = emu_harness.head_mix(emu, y, W)
+    assert st == 0 and z.shape == (0, 4, 8)
+    st, gy, gW = emu_harness.head_mix_backward(emu, y, W, y)
+    assert st == 0 and np.array_equal(gW, np.zeros((4, 4), np.float32))
