@@ -76,8 +76,8 @@ def write_traffic_profile(root):
             raise SystemExit("no %s records for %s under %s" % (name, kernel_part, sub))
         return vals
 
-    fetch = counter("pmc_fetch", "FETCH_SIZE", "scan_kernel<64, true, 0>")
-    write = counter("pmc_write", "WRITE_SIZE", "scan_kernel<64, true, 0>")
+    fetch = counter("pmc_fetch", "FETCH_SIZE", "scan_kernel<64, 0>")
+    write = counter("pmc_write", "WRITE_SIZE", "scan_kernel<64, 0>")
     cf = max(counter("pmc_fetch_copy", "FETCH_SIZE", "copyBuffer"))
     cw = max(counter("pmc_write_copy", "WRITE_SIZE", "copyBuffer"))
     copied = 1 << 30
@@ -87,7 +87,7 @@ def write_traffic_profile(root):
     import complex_chunkwise_ssd_amd as ssd
     th = 32 * 2048 * 16
     rec = {
-        "kernel": "ssd::scan_kernel<64, true, 0>",
+        "kernel": "ssd::scan_kernel<64, 0>",
         "workload": "one layer of the 28-layer network load: B=32, T=2048, H=16, N=D=64, chunk 64",
         "kernel_source_sha256_16": kernel_source_hash(),
         "fetch_size_kib_per_dispatch": f_kib,
@@ -207,6 +207,51 @@ def mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev, reps=20):
     return out
 
 
+def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
+    """The long-context chunk-size sweep: B=4, T=8192, H=16, N=D=64, dt ~ N(0.5, 1),
+    one input set for chunk 32, 64, 128 and 256; median of `reps` event-timed
+    ssd_chunk_forward calls per chunk size. A chunk above 64 tokens is evaluated
+    as 64-token sub-chunks (the same sums re-associated), so the executed work is
+    that of chunk 64; both fractions are given: against the algorithmic count at
+    the executed block size and at the nominal chunk size."""
+    w = ssd_inputs.WORKLOADS["sweep_b4_t8192"]
+    B, T, H, N, D = w["batch"], w["T"], w["H"], w["N"], w["D"]
+    g = ssd_inputs.layer_case(B, T, H, N, D, seed=w["seed"], dt_mean=w["dt_mean"], device=dev)
+    y = torch.empty((B, T, H, D), device=dev)
+    f = torch.empty((B, H, N, D), dtype=torch.complex64, device=dev)
+    out = {"workload": "B=%d, T=%d, H=%d, N=D=%d, dt ~ N(%.1f, 1), one input set" % (
+        B, T, H, N, w["dt_mean"])}
+    th = B * T * H
+    for q in w["chunks"]:
+        n = ssd.workspace_bytes(B, T, H, N, D, q)
+        wsp = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        call = lambda: ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=q, y=y,
+                                         final_state=f, workspace=wsp)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        qe = ssd.block_rows(q)
+        fe = th * ssd.algorithmic_flops_per_token_head(N, D, qe)
+        fn = th * ssd.algorithmic_flops_per_token_head(N, D, q)
+        out["chunk_%d" % q] = {
+            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "token_heads_per_s": th / (ms * 1e-3), "evaluated_block_rows": qe,
+            "roofline_frac_mfma": fe / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+            "roofline_frac_mfma_nominal_chunk": fn / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+        del wsp
+    del g, y, f
+    return out
+
+
 def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10):
     """ssd_chunk_backward_proj (gradients as in_proj gradient rows) at the network
     layer shape; median of `reps` event-timed calls."""
@@ -291,6 +336,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward side figure")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward on layer 0 of the workload and print it")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="time only the T=8192 chunk-size sweep and exit")
     ap.add_argument("--mix-only", action="store_true",
                     help="time only the MIMO head mixer (forward and gradients) and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR", default=None,
@@ -325,6 +372,10 @@ def main():
         return 0
     wl = dict(ssd_inputs.WORKLOADS[args.workload])
     B, T, H, N, D = wl["batch"], wl["T"], wl["H"], wl["N"], wl["D"]
+    if args.sweep_only:
+        print(json.dumps({"chunk_sweep": sweep_leg(ssd, torch, ssd_inputs, dev,
+                                                   reps=max(args.steps, 1))}), flush=True)
+        return 0
     if args.mix_only:
         print(json.dumps({"head_mix": mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev,
                                               reps=max(args.steps, 1))}), flush=True)
@@ -414,7 +465,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
             "traffic": traffic,
-            "kernel": "scan_kernel<64, true, 0> (complex layout; one launch per layer)",
+            "kernel": "scan_kernel<64, 0> (complex layout; one launch per layer)",
             "avg_launch_ms": avg_launch_ms,
             "algorithmic_flops_per_launch": flops_launch,
             "algorithmic_bytes_per_launch": bytes_launch,
@@ -459,6 +510,7 @@ def main():
         out["proj_layer_bf16"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev,
                                           dtype=torch.bfloat16)
         out["head_mix"] = mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev)
+        out["chunk_sweep"] = sweep_leg(ssd, torch, ssd_inputs, dev)
     if not args.no_backward:
         log("bench: timing the backward on layer 0")
         out["backward"] = backward_leg(ssd, torch, layers[0])

@@ -378,6 +378,12 @@ def algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
     return 8 * D + 16 * N + 4 + 4 * D + 8 * N * D / T
 
 
+def block_rows(chunk_size: int) -> int:
+    """Tokens the forward evaluates per chunk: chunk_size up to 64; a longer chunk
+    runs as 64-token sub-chunks with the state passed between them."""
+    return min(int(chunk_size), 64)
+
+
 def backward_block_rows(chunk_size: int) -> int:
     """Tokens the backward evaluates per chunk (the state spacing it stores)."""
     return min(int(chunk_size), 32)

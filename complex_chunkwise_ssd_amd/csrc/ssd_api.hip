@@ -4,6 +4,7 @@
 #include "ssd.h"
 
 #include <ssd_bwd_kernels.h>
+#include <ssd_segment_kernels.h>
 #include <ssd_mix_kernels.h>
 
 namespace {
@@ -36,23 +37,41 @@ int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64
     return SSD_OK;
 }
 
+// The scan over every (sequence, segment, D slice); with several segments, the
+// prefix pass (entering states, final state) and the fix-up of the later
+// segments' outputs follow on the same stream.
 template <int R, int LAYOUT>
 int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs, hipStream_t stream)
 {
     ssd::ScanParams prm = base;
-    if (plan.P > 1) {
-        prm.groups_per_seq = plan.P - 1;
-        const int64_t grid = seqs * (plan.P - 1) * plan.ndb;
-        hipLaunchKernelGGL((ssd::scan_kernel<R, false, LAYOUT>), dim3((unsigned)grid),
-                           dim3(ssd::kThreads), 0, stream, prm);
-        if (int st = launch_status())
-            return st;
-    }
     prm.groups_per_seq = plan.P;
     const int64_t grid = seqs * plan.P * plan.ndb;
-    hipLaunchKernelGGL((ssd::scan_kernel<R, true, LAYOUT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((ssd::scan_kernel<R, LAYOUT>), dim3((unsigned)grid),
                        dim3(ssd::kThreads), 0, stream, prm);
+    if (int st = launch_status())
+        return st;
+    if (plan.P == 1)
+        return SSD_OK;
+    const int64_t elems = seqs * (int64_t)prm.N * prm.D;
+    hipLaunchKernelGGL(ssd::segment_prefix_kernel, dim3(grid_1d(elems, 256)), dim3(256), 0, stream,
+                       prm);
+    if (int st = launch_status())
+        return st;
+    const int64_t fix = seqs * (plan.P - 1) * plan.ndb * plan.fix_groups;
+    hipLaunchKernelGGL((ssd::segment_fixup_kernel<R, LAYOUT>), dim3((unsigned)fix),
+                       dim3(ssd::kFixThreads), 0, stream, prm);
     return launch_status();
+}
+
+// Segment workspace: end states, segment log-decays, chunk-start log-decays.
+void set_segment_workspace(ssd::ScanParams &prm, const ssd::Plan &plan, void *workspace)
+{
+    if (plan.P == 1)
+        return;
+    char *w = (char *)workspace;
+    prm.seg_state = (float *)w;
+    prm.seg_logdecay = (float *)(w + plan.seg_state_bytes);
+    prm.chunk_log = (float *)(w + plan.seg_state_bytes + plan.seg_decay_bytes);
 }
 
 template <int LAYOUT>
@@ -149,8 +168,7 @@ int forward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t 
     prm.init_state = (const float *)initial_state;
     prm.y = y;
     prm.final_state = (float *)final_state;
-    prm.seg_state = plan.P > 1 ? (float *)workspace : nullptr;
-    prm.seg_logdecay = plan.P > 1 ? (float *)((char *)workspace + plan.seg_state_bytes) : nullptr;
+    set_segment_workspace(prm, plan, workspace);
     prm.B = (int)batch;
     prm.T = (int)T;
     prm.H = (int)H;
@@ -161,6 +179,7 @@ int forward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t 
     prm.P = plan.P;
     prm.spc = plan.spc;
     prm.ndb = plan.ndb;
+    prm.fix_groups = plan.fix_groups;
     return launch_forward<LAYOUT>(prm, plan, batch * H, s);
 }
 
@@ -333,8 +352,7 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     prm.init_state = (const float *)initial_state;
     prm.y = y;
     prm.final_state = (float *)final_state;
-    prm.seg_state = plan.P > 1 ? (float *)workspace : nullptr;
-    prm.seg_logdecay = plan.P > 1 ? (float *)((char *)workspace + plan.seg_state_bytes) : nullptr;
+    set_segment_workspace(prm, plan, workspace);
     prm.B = (int)batch;
     prm.T = (int)T;
     prm.H = (int)H;
@@ -345,6 +363,7 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     prm.P = plan.P;
     prm.spc = plan.spc;
     prm.ndb = plan.ndb;
+    prm.fix_groups = plan.fix_groups;
 
     return launch_forward<ssd::kLayoutC64>(prm, plan, batch * H, s);
 }

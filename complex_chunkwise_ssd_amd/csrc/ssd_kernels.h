@@ -158,8 +158,8 @@ constexpr int tile_st(int k, int nr)
 }
 
 // R: chunk rows held on chip (chunk_size rounded up to 16, 32 or 64; extra
-// rows are identity padding). FULL: produce y and the final state; otherwise
-// only the zero-start end state and total log-decay of each segment.
+// rows are identity padding). One segment of one sequence per workgroup: y for
+// its tokens and its end state (the final state when there is one segment).
 // LAYOUT kLayoutC64: x, B_t, C_t complex64 (B, T, H, .), dt float32 (B, T, H).
 // kLayoutProj / kLayoutProjBf16: the inputs are read from an in_proj output row
 // per token, [x (H*D, real) | Re B | Im B | Re C | Im C (H*N each) | dt (H)],
@@ -184,7 +184,7 @@ constexpr int tile_st(int k, int nr)
 // walks down with L[l, s] = L[l, s+1] exp(a_{s+1}). Off the diagonal:
 // L[l, s] = W[l] K(st, lt) V[s] with W the decay from the start of l's tile,
 // V the decay from s to the end of its tile and K the whole tiles in between.
-template <int R, bool FULL, int LAYOUT>
+template <int R, int LAYOUT>
 SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 {
     constexpr bool PROJ = LAYOUT != kLayoutC64;
@@ -202,11 +202,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     constexpr int kScanWave = 0;             // the wave that scans each chunk's log-decay
 
     SSD_LDS float sB[R * LDI];                // B[s][n] interleaved (re, im)
-    SSD_LDS float sC[FULL ? R * LDI : 1];     // C[l][n]
-    SSD_LDS float sP[FULL ? R * LDI : 1];     // exp(Lam[l]) C[l][n] as (re, -im)
-    SSD_LDS v4f sMre[FULL ? NT * 64 : 1], sMim[FULL ? NT * 64 : 1];    // M tiles (re, -im), lane-major
-    SSD_LDS v4f sYx[FULL ? 4 * NR * 64 : 1];                           // partial-y exchange
-    SSD_LDS v4f sLdre[FULL ? NR * 64 : 1], sLdim[FULL ? NR * 64 : 1];  // L on diagonal tiles, lane-major
+    SSD_LDS float sC[R * LDI];                // C[l][n]
+    SSD_LDS float sP[R * LDI];                // exp(Lam[l]) C[l][n] as (re, -im)
+    SSD_LDS v4f sMre[NT * 64], sMim[NT * 64]; // M tiles (re, -im), lane-major
+    SSD_LDS v4f sYx[4 * NR * 64];             // partial-y exchange
+    SSD_LDS v4f sLdre[NR * 64], sLdim[NR * 64];  // L on diagonal tiles, lane-major
     SSD_LDS v2f sDout[R];      // exp(sum of a over rows s+1 .. chunk end)
     SSD_LDS v2f sW[R];         // exp(sum of a over rows tile start .. l)
     SSD_LDS v2f sV[R];         // exp(sum of a over rows s+1 .. end of its tile)
@@ -273,15 +273,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 Him[i][r] = hv.y + e.y;
             }
     };
-    if (FULL) {
-        if (p.init_state)
-            add_state(p.init_state + bh * p.N * p.D * 2, v2f{0.f, 0.f});
-        for (int q = 0; q < seg; ++q) {
-            const int64_t sidx = bh * (p.P - 1) + q;
-            const v2f lg = *(const v2f *)&p.seg_logdecay[sidx * 2];
-            add_state(p.seg_state + sidx * p.N * p.D * 2, cexp_f(lg));
-        }
-    }
+    // Segment 0 starts from the initial state, the others from zero (the fix-up
+    // pass adds what the state entering them contributes).
+    if (seg == 0 && p.init_state)
+        add_state(p.init_state + bh * p.N * p.D * 2, v2f{0.f, 0.f});
 
     const int c_begin = seg * p.spc;
     const int c_end = c_begin + p.spc < p.nc ? c_begin + p.spc : p.nc;
@@ -299,8 +294,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     XT pX[NR][4];
     // The next chunk's loads are spread over the MFMA steps of phase 1 (a burst of
     // them would hold each wave's in-order issue). Item i < LOADS: a B_t block;
-    // then (FULL) the C_t blocks; then x at (q, j).
-    constexpr int NLOAD = (FULL ? 2 : 1) * LOADS + 4 * NR;
+    // then the C_t blocks; then x at (q, j).
+    constexpr int NLOAD = 2 * LOADS + 4 * NR;
     buf_t nbB, nbC, nbX;
     // PROJ: one buffer covers both planes of B (and of C); the imaginary plane of a
     // row starts H*N floats after its real plane
@@ -347,7 +342,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             } else {
                 pB[i] = buf_load4(nbB, o);
             }
-        } else if constexpr (FULL && i < 2 * LOADS) {
+        } else if constexpr (i < 2 * LOADS) {
             const uint32_t o = offB + (uint32_t)(16 * (i - LOADS)) * brow;
             if constexpr (BF16) {
                 const uint32_t re = buf_load_u32(nbC, o), im = buf_load_u32(nbC, o + imoff);
@@ -359,7 +354,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 pC[i - LOADS] = buf_load4(nbC, o);
             }
         } else if constexpr (i < NLOAD) {
-            constexpr int x = i - (FULL ? 2 : 1) * LOADS, q = x >> 2, j = x & 3;
+            constexpr int x = i - 2 * LOADS, q = x >> 2, j = x & 3;
             if constexpr (BF16)
                 pX[q][j] = bf16_lo(buf_load_u16(nbX, offX + (uint32_t)(16 * q + j) * xrow));
             else if constexpr (PROJ)
@@ -372,11 +367,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         fetch_begin(c);
         static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
     };
-    // FULL: the B_t and C_t items go out with the state steps of phase 1 and the x
-    // items with the Re(M X) steps of phase 2 (x of the next chunk then shares no
-    // registers' lifetime with phase 1). State-only: everything with the state steps.
-    constexpr int NBC = (FULL ? 2 : 1) * LOADS;
-    constexpr int PER_S = (FULL ? NBC + 2 * NR - 1 : NLOAD + 2 * NR - 1) / (2 * NR);
+    // The B_t and C_t items go out with the state steps of phase 1 and the x items
+    // with the Re(M X) steps of phase 2 (x of the next chunk then shares no
+    // registers' lifetime with phase 1).
+    constexpr int NBC = 2 * LOADS;
+    constexpr int PER_S = (NBC + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
         const void *dt0 = PROJ ? at(p.dt, prow0(c) + h) : (const void *)(p.dt + tok0(c));
@@ -388,6 +383,12 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         else
             pdt = buf_load1(bT, od);
     };
+
+    // The segment's log-decay at each chunk start, for the fix-up pass (one slice of
+    // D writes it).
+    const buf_t bLog = make_buf(p.chunk_log ? (const void *)(p.chunk_log + bh * p.nc * 2)
+                                            : (const void *)p.dt,
+                                p.chunk_log && db == 0 ? (uint32_t)p.nc * 8u : 0u);
 
     // One wave: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
     auto scan = [&](int c) {
@@ -414,14 +415,16 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         if (lane < R) {
             sLam[lane] = lam;
             sSig[lane] = sig;
-            if (FULL)
-                sAbar[lane] = cexp_f(a);
+            sAbar[lane] = cexp_f(a);
         }
         if (lane == 0) {
             for (int t = 0; t < NR; ++t)
                 sTau[t] = tau[t];
             sTau[NR] = tot;
         }
+        const uint32_t olog = lane == 0 ? (uint32_t)c * 8u : kOut;
+        buf_store1(bLog, olog, seg_log.x);
+        buf_store1(bLog, olog + 4u, seg_log.y);
         seg_log += tot;
     };
 
@@ -431,7 +434,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     // to the chunk end; wave 7: V.
     auto factors = [&]() {
         if (tid < 256) {
-            if (FULL && tid < NR * 64) {
+            if (tid < NR * 64) {
                 const int tile = tid >> 6, ln = tid & 63;
                 const int l = ln & 15, g = 4 * (ln >> 4);
                 const v2f *lam = sLam + 16 * tile;
@@ -454,13 +457,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         }
         const int role = (tid >> 6) - 4, ri = tid & 63;
         if (role == 0) {
-            if (FULL && ri < R)
+            if (ri < R)
                 sW[ri] = cexp_f(sLam[ri]);
         } else if (role == 1) {
             // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before
             // lt; slot NR * NR: the whole chunk (the decay of the state).
             const int st = ri / NR, lt = ri % NR;
-            if (ri <= NR * NR && (ri == NR * NR || (FULL && st <= lt))) {
+            if (ri <= NR * NR && (ri == NR * NR || st <= lt)) {
                 v2f z = v2f{0.f, 0.f};
                 for (int t = 0; t < NR; ++t)
                     if (ri == NR * NR || (st < lt ? (t > st && t < lt) : t < lt))
@@ -480,7 +483,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 sDout[ri] = cexp_f(z);
             }
         } else {
-            if (FULL && ri < R)
+            if (ri < R)
                 sV[ri] = cexp_f(sSig[ri]);
         }
     };
@@ -504,19 +507,17 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         for (int i = 0; i < LOADS; ++i) {
             const int row = 16 * i + (tid >> 5);
             *(v4f *)&sB[row * LDI + 2 * ncol] = pB[i];
-            if (FULL) {
-                const v4f vc = pC[i];
-                *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
-                const v2f e = cmul(sW[row], sK[(row >> 4) * (NR + 1)]);  // exp(Lam[row])
-                const v2f c0 = cmul(e, v2f{vc.x, vc.y}), c1 = cmul(e, v2f{vc.z, vc.w});
-                *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
-            }
+            const v4f vc = pC[i];
+            *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
+            const v2f e = cmul(sW[row], sK[(row >> 4) * (NR + 1)]);  // exp(Lam[row])
+            const v2f c0 = cmul(e, v2f{vc.x, vc.y}), c1 = cmul(e, v2f{vc.z, vc.w});
+            *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
         }
         XT X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
                 X[q][j] = pX[q][j];
-        if (FULL && NSPLIT > 0 && tid < NSPLIT * 64 * 2) {
+        if (NSPLIT > 0 && tid < NSPLIT * 64 * 2) {
             const int slot = NWHOLE * 64 + (tid & (NSPLIT * 64 - 1));
             if (tid < NSPLIT * 64)
                 sMre[slot] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -531,9 +532,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         v4f Y[NR];
         for (int lt = 0; lt < NR; ++lt)
             Y[lt] = v4f{0.f, 0.f, 0.f, 0.f};
-        if (FULL) {
-            // ---- phase 1a: M tiles. Whole tiles k < NWHOLE by wave k; the others as
-            // two K halves accumulated into LDS (two adds onto zero: order-free).
+        // ---- phase 1a: M tiles. Whole tiles k < NWHOLE by wave k; the others as
+        // two K halves accumulated into LDS (two adds onto zero: order-free).
+        {
             auto produce = [&](auto kc, auto q0c, auto q1c) {
                 constexpr int k = decltype(kc)::value;
                 constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
@@ -668,7 +669,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 constexpr int g = decltype(gc)::value, q = g >> 1, i = g & 1, cur = g & 1;
                 if constexpr (g + 1 < 2 * NR)
                     load(g + 1, ob[cur ^ 1], od[q & 1 ^ (i == 1 ? 1 : 0)]);
-                constexpr int SL = FULL ? NBC : NLOAD;  // items the state steps issue
+                constexpr int SL = NBC;  // items the state steps issue
                 static_for<g * PER_S, ((g + 1) * PER_S < SL ? (g + 1) * PER_S : SL)>(
                     [&](auto ic) { fetch_item(ic); });
                 sched_fence();
@@ -701,7 +702,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         // ---- phase 2: intra-chunk term Re(M X) = Mre Xre + (-Mim) Xim; the tiles of a
         // column tile are split between its two waves by parity. Then the next
         // chunk's decay factors.
-        if (FULL) {
+        {
             auto ydiag = [&](auto nhc) {
                 constexpr int NH = decltype(nhc)::value;
                 constexpr int NK = (NT + 1 - NH) / 2;  // tiles k = NH, NH + 2, ...
@@ -754,9 +755,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             factors();
         block_sync();
 
-        if (FULL) {
-            // Straight-line stores (a tile this wave does not own is aimed past the
-            // buffer), so the wait counters stay exact across the loop.
+        // ---- store y. Straight-line stores (a tile this wave does not own is aimed
+        // past the buffer), so the wait counters stay exact across the loop.
+        {
             const buf_t bY = make_buf(p.y + r0 * p.D + db * kDBlock,
                                       (uint32_t)(rows - 1) * yrow + dsl * 4u);
             for (int j = 0; j < (NR + 1) / 2; ++j) {
@@ -773,11 +774,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
     // ---- results of the segment.
     float *out = nullptr;
-    if (FULL) {
-        if (seg == p.P - 1 && p.final_state)
-            out = p.final_state + bh * p.N * p.D * 2;
+    if (p.P == 1) {
+        out = p.final_state ? p.final_state + bh * p.N * p.D * 2 : nullptr;
     } else {
-        const int64_t sidx = bh * (p.P - 1) + seg;
+        const int64_t sidx = bh * p.P + seg;
         out = p.seg_state + sidx * p.N * p.D * 2;
         if (db == 0 && tid == kScanWave * 64)  // the scan wave holds the segment total
             *(v2f *)&p.seg_logdecay[sidx * 2] = seg_log;

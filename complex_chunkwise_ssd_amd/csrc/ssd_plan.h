@@ -4,9 +4,12 @@
 // One workgroup walks the chunks of one (batch row, head, sequence segment,
 // 64-wide slice of D) in order, keeping the N x 64 state on chip. When there
 // are too few (batch, head) sequences to fill the GPU, each sequence is cut
-// into P segments: a first pass computes every segment's end state from a
-// zero start (and its total log-decay), and the full pass then starts segment
-// p from the composition of the earlier segments' results.
+// into P segments that the scan runs side by side, segment 0 from the initial
+// state and the others from zero; each records its end state, its total
+// log-decay and the log-decay at each of its chunk starts. A prefix pass then
+// composes the states entering every segment (and the final state), and a
+// fix-up pass adds each later segment's missing term, the entering state seen
+// through the decay, Re(exp(Lambda_t) C_t H_in), to its outputs.
 #pragma once
 
 #include <stddef.h>
@@ -34,14 +37,19 @@ struct ScanParams {
     const float *init_state;  // (B, H, N, D) complex or null
     float *y;                 // (B, T, H, D)
     float *final_state;       // (B, H, N, D) complex or null
-    float *seg_state;         // (B, H, P-1, N, D) complex, zero-start segment end states
-    float *seg_logdecay;      // (B, H, P-1) complex, sum of softplus(dt)*A over a segment
+    float *seg_state;         // (B, H, P, N, D) complex: segment end states (from the segment's
+                              // own start); after the prefix pass slot p-1 holds the state
+                              // entering segment p
+    float *seg_logdecay;      // (B, H, P) complex, sum of softplus(dt)*A over a segment
+    float *chunk_log;         // (B, H, nc) complex, that sum from the segment start to each
+                              // chunk start
     int B, T, H, N, D, Q;
     int nc;    // chunks per sequence
     int P;     // segments per sequence
     int spc;   // chunks per segment
     int ndb;   // 64-wide D slices
-    int groups_per_seq;  // P (full pass) or P - 1 (state pass)
+    int groups_per_seq;  // workgroups per sequence and D slice: the P segments
+    int fix_groups;      // fix-up workgroups per (sequence, later segment, D slice)
     int64_t tok_stride;  // in_proj layout: floats between consecutive tokens' rows
 };
 
@@ -51,10 +59,15 @@ struct Plan {
     int P = 1;
     int spc = 0;
     int ndb = 0;
+    int fix_groups = 0;
     size_t seg_state_bytes = 0;
     size_t seg_decay_bytes = 0;
+    size_t chunk_log_bytes = 0;
     size_t workspace_bytes = 0;
 };
+
+constexpr int kFixThreads = 256;        // four wave64s, one 16-column tile of D each
+constexpr int kFixTargetGroups = 1024;  // fix-up workgroups to aim for (four per CU)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -87,10 +100,14 @@ inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int
     p.spc = (int)((p.nc + want - 1) / want);
     p.P = (p.nc + p.spc - 1) / p.spc;
     if (p.P > 1) {
-        p.seg_state_bytes = align_up((size_t)B * H * (p.P - 1) * N * D * 8, 256);
-        p.seg_decay_bytes = align_up((size_t)B * H * (p.P - 1) * 8, 256);
+        p.seg_state_bytes = align_up((size_t)B * H * p.P * N * D * 8, 256);
+        p.seg_decay_bytes = align_up((size_t)B * H * p.P * 8, 256);
+        p.chunk_log_bytes = align_up((size_t)B * H * p.nc * 8, 256);
+        const int64_t units = B * H * (p.P - 1) * p.ndb;
+        int64_t g = (kFixTargetGroups + units - 1) / units;
+        p.fix_groups = (int)(g < p.spc ? g : p.spc);
     }
-    p.workspace_bytes = p.seg_state_bytes + p.seg_decay_bytes;
+    p.workspace_bytes = p.seg_state_bytes + p.seg_decay_bytes + p.chunk_log_bytes;
     return p;
 }
 
