@@ -252,10 +252,11 @@ def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
     return out
 
 
-def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10):
-    """ssd_chunk_backward_proj (gradients as in_proj gradient rows) at the network
-    layer shape; median of `reps` event-timed calls."""
-    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev)
+def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10, dtype=None):
+    """ssd_chunk_backward_proj (gradients as in_proj gradient rows; bfloat16 rows
+    and gradient rows with dtype=torch.bfloat16) at the network layer shape;
+    median of `reps` event-timed calls."""
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=0, device=dev, dtype=dtype)
     gy, gf = ssd_inputs.upstream_grads(B, T, H, N, D, seed=0, device=dev)
     ws = torch.empty(max(ssd.backward_workspace_bytes(B, T, H, N, D, 64), 1), dtype=torch.uint8,
                      device=dev)
@@ -275,8 +276,9 @@ def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
     del proj, gy, gf, ws, rows
-    return {"workload": "network layer backward from in_proj rows (B=%d, T=%d, H=%d, N=D=%d, "
-                        "chunk 64)" % (B, T, H, N),
+    return {"workload": "network layer backward from %s in_proj rows (B=%d, T=%d, H=%d, "
+                        "N=D=%d, chunk 64)" % ("bfloat16" if dtype == torch.bfloat16 else
+                                              "float32", B, T, H, N),
             "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3)}
 
 
@@ -516,6 +518,8 @@ def main():
         out["backward"] = backward_leg(ssd, torch, layers[0])
         if not args.no_extra:
             out["backward_proj"] = backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev)
+            out["backward_proj_bf16"] = backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D,
+                                                          dev, dtype=torch.bfloat16)
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

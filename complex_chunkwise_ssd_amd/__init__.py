@@ -81,6 +81,8 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_backward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                                 vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_backward_proj.restype = ctypes.c_int
+        lib.ssd_chunk_backward_proj_bf16.argtypes = lib.ssd_chunk_backward_proj.argtypes
+        lib.ssd_chunk_backward_proj_bf16.restype = ctypes.c_int
         lib.ssd_head_mix.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         lib.ssd_head_mix.restype = ctypes.c_int
         lib.ssd_head_mix_backward_workspace_bytes.argtypes = [i64] * 3
@@ -288,12 +290,13 @@ def chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None, chunk_size
 def chunk_backward_proj(proj, A, H: int, N: int, D: int, grad_y, grad_final_state=None,
                         chunk_size: int = 64, initial_state=None, grad_proj=None,
                         want_initial_state_grad: bool = True, workspace=None):
-    """Gradients of the scan read from in_proj rows (chunk_forward_proj, float32
-    rows), as gradient rows of the same layout: returns (grad_proj (B, T, S)
-    float32, grad_A (H,) complex64, grad_initial_state or None). The x block
-    gets dl/dx (x is real), the B and C blocks the real and imaginary parts of
-    their gradients, the dt block dl/ddt; floats past the blocks are left as
-    they are (zero in a freshly allocated grad_proj)."""
+    """Gradients of the scan read from in_proj rows (chunk_forward_proj), as
+    gradient rows of the same layout and dtype (float32, or bfloat16 rounded
+    from float32 results): returns (grad_proj (B, T, S), grad_A (H,) complex64,
+    grad_initial_state or None). The x block gets dl/dx (x is real), the B and
+    C blocks the real and imaginary parts of their gradients, the dt block
+    dl/ddt; elements past the blocks are left as they are (zero in a freshly
+    allocated grad_proj)."""
     lib = load_library()
     if not isinstance(proj, torch.Tensor) or proj.dim() != 3:
         raise ValueError("proj must be a (B, T, S) tensor")
@@ -301,7 +304,9 @@ def chunk_backward_proj(proj, A, H: int, N: int, D: int, grad_y, grad_final_stat
     dev = proj.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device, got %s" % dev)
-    _check(proj, "proj", torch.float32, (Bsz, T, S), dev)
+    bf16 = proj.dtype == torch.bfloat16
+    rdt = torch.bfloat16 if bf16 else torch.float32
+    _check(proj, "proj", rdt, (Bsz, T, S), dev)
     _check(A, "A", torch.complex64, (H,), dev)
     _check(grad_y, "grad_y", torch.float32, (Bsz, T, H, D), dev)
     if grad_final_state is not None:
@@ -309,8 +314,8 @@ def chunk_backward_proj(proj, A, H: int, N: int, D: int, grad_y, grad_final_stat
     if initial_state is not None:
         _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
     if grad_proj is None:
-        grad_proj = torch.zeros((Bsz, T, S), dtype=torch.float32, device=dev)
-    _check(grad_proj, "grad_proj", torch.float32, (Bsz, T, S), dev)
+        grad_proj = torch.zeros((Bsz, T, S), dtype=rdt, device=dev)
+    _check(grad_proj, "grad_proj", rdt, (Bsz, T, S), dev)
     gA = torch.empty((H,), dtype=torch.complex64, device=dev)
     gi = None
     if want_initial_state_grad:
@@ -319,12 +324,12 @@ def chunk_backward_proj(proj, A, H: int, N: int, D: int, grad_y, grad_final_stat
     if ws_n and workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ssd_chunk_backward_proj(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size),
-                                     _ptr(initial_state), _ptr(grad_y), _ptr(grad_final_state),
-                                     _ptr(grad_proj), _ptr(gA), _ptr(gi), _ptr(workspace), ws_size,
-                                     _stream(dev))
+    fn = lib.ssd_chunk_backward_proj_bf16 if bf16 else lib.ssd_chunk_backward_proj
+    st = fn(_ptr(proj), S, _ptr(A), Bsz, T, H, N, D, int(chunk_size), _ptr(initial_state),
+            _ptr(grad_y), _ptr(grad_final_state), _ptr(grad_proj), _ptr(gA), _ptr(gi),
+            _ptr(workspace), ws_size, _stream(dev))
     if st != SSD_OK:
-        raise SSDError(st, "ssd_chunk_backward_proj")
+        raise SSDError(st, "ssd_chunk_backward_proj" + ("_bf16" if bf16 else ""))
     return grad_proj, gA, gi
 
 

@@ -85,20 +85,20 @@ int launch_forward(const ssd::ScanParams &prm, const ssd::Plan &plan, int64_t se
     }
 }
 
-template <int R, bool PROJ>
+template <int R, int LAYOUT>
 int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false, PROJ>), dim3((unsigned)seqs), dim3(512), 0,
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false, LAYOUT>), dim3((unsigned)seqs), dim3(512), 0,
                        stream, prm);
     if (int st = launch_status())
         return st;
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, PROJ>), dim3((unsigned)seqs), dim3(512), 0,
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, LAYOUT>), dim3((unsigned)seqs), dim3(512), 0,
                        stream, prm);
     if (int st = launch_status())
         return st;
     const int64_t chunks = seqs * prm.nc;
     const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
-    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, PROJ>), dim3((unsigned)groups), dim3(512), 0, stream,
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, LAYOUT>), dim3((unsigned)groups), dim3(512), 0, stream,
                        prm);
     if (int st = launch_status())
         return st;
@@ -181,6 +181,85 @@ int forward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t 
     prm.ndb = plan.ndb;
     prm.fix_groups = plan.fix_groups;
     return launch_forward<LAYOUT>(prm, plan, batch * H, s);
+}
+
+// The backward of the in_proj-row scan; E is the row element (float or the bits
+// of a bfloat16), LAYOUT the matching kernel layout.
+template <int LAYOUT, class E>
+int backward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t batch, int64_t T,
+                  int64_t H, int64_t N, int64_t D, int64_t chunk_size,
+                  const ssd_c64 *initial_state, const float *grad_y,
+                  const ssd_c64 *grad_final_state, E *grad_proj, ssd_c64 *grad_A,
+                  ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
+                  ssd_stream_t stream)
+{
+    if (int st = check_backward_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    if (token_stride < H * (D + 4 * N + 1))
+        return SSD_ERR_SHAPE;
+    if (batch == 0 || H == 0)
+        return SSD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (!grad_A)
+        return SSD_ERR_NULL;
+    if (!aligned(grad_A, 8) || (grad_final_state && !aligned(grad_final_state, 8)) ||
+        (grad_initial_state && !aligned(grad_initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    if (T == 0) {
+        if (grad_initial_state) {
+            const int64_t n = batch * H * N * D * 2;
+            hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
+                               (const float *)grad_final_state, (float *)grad_initial_state, n);
+            if (int st = launch_status())
+                return st;
+        }
+        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)H), dim3(256), 0, s,
+                           (const float *)nullptr, (int)batch, (int)H, 0, (float *)grad_A);
+        return launch_status();
+    }
+    if (!proj || !A || !grad_y || !grad_proj)
+        return SSD_ERR_NULL;
+    if (!aligned(proj, sizeof(E)) || !aligned(grad_proj, sizeof(E)) || !aligned(A, 8) ||
+        !aligned(grad_y, 4) ||
+        (initial_state && !aligned(initial_state, 8)))
+        return SSD_ERR_ALIGN;
+    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+        return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return SSD_ERR_ALIGN;
+
+    const int64_t HD = H * D, HN = H * N;
+    // element pointers of the row blocks (the kernels read them as LAYOUT says)
+    ssd::BwdParams prm{};
+    prm.x = (const float *)proj;
+    prm.A = (const float *)A;
+    prm.Bt = (const float *)(proj + HD);
+    prm.Ct = (const float *)(proj + HD + 2 * HN);
+    prm.dt = (const float *)(proj + HD + 4 * HN);
+    prm.init = (const float *)initial_state;
+    prm.gy = grad_y;
+    prm.gfinal = (const float *)grad_final_state;
+    prm.gx = (float *)grad_proj;
+    prm.gA = (float *)grad_A;
+    prm.gB = (float *)(grad_proj + HD);
+    prm.gC = (float *)(grad_proj + HD + 2 * HN);
+    prm.gdt = (float *)(grad_proj + HD + 4 * HN);
+    prm.ginit = (float *)grad_initial_state;
+    prm.fwd_states = (float *)workspace;
+    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
+    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
+    prm.B = (int)batch;
+    prm.T = (int)T;
+    prm.H = (int)H;
+    prm.N = (int)N;
+    prm.D = (int)D;
+    prm.Q = plan.Q;
+    prm.nc = plan.nc;
+    prm.tok_stride = token_stride;
+    const int64_t seqs = batch * H;
+    return plan.R == 16 ? launch_backward<16, LAYOUT>(prm, seqs, s)
+                        : launch_backward<32, LAYOUT>(prm, seqs, s);
 }
 
 int check_mix(int64_t tokens, int64_t H, int64_t D)
@@ -469,8 +548,8 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
     prm.Q = plan.Q;
     prm.nc = plan.nc;
     const int64_t seqs = batch * H;
-    return plan.R == 16 ? launch_backward<16, false>(prm, seqs, s)
-                        : launch_backward<32, false>(prm, seqs, s);
+    return plan.R == 16 ? launch_backward<16, ssd::kLayoutC64>(prm, seqs, s)
+                        : launch_backward<32, ssd::kLayoutC64>(prm, seqs, s);
 }
 
 int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,
@@ -480,71 +559,25 @@ int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c
                             ssd_c64 *grad_initial_state, void *workspace, size_t workspace_bytes,
                             ssd_stream_t stream)
 {
-    if (int st = check_backward_sizes(batch, T, H, N, D, chunk_size))
-        return st;
-    if (token_stride < H * (D + 4 * N + 1))
-        return SSD_ERR_SHAPE;
-    if (batch == 0 || H == 0)
-        return SSD_OK;
-    hipStream_t s = (hipStream_t)stream;
-    if (!grad_A)
-        return SSD_ERR_NULL;
-    if (!aligned(grad_A, 8) || (grad_final_state && !aligned(grad_final_state, 8)) ||
-        (grad_initial_state && !aligned(grad_initial_state, 8)))
-        return SSD_ERR_ALIGN;
-    if (T == 0) {
-        if (grad_initial_state) {
-            const int64_t n = batch * H * N * D * 2;
-            hipLaunchKernelGGL(ssd::copy_state_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, s,
-                               (const float *)grad_final_state, (float *)grad_initial_state, n);
-            if (int st = launch_status())
-                return st;
-        }
-        hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)H), dim3(256), 0, s,
-                           (const float *)nullptr, (int)batch, (int)H, 0, (float *)grad_A);
-        return launch_status();
-    }
-    if (!proj || !A || !grad_y || !grad_proj)
-        return SSD_ERR_NULL;
-    if (!aligned(proj, 4) || !aligned(grad_proj, 4) || !aligned(A, 8) || !aligned(grad_y, 4) ||
-        (initial_state && !aligned(initial_state, 8)))
-        return SSD_ERR_ALIGN;
-    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
-    if (!workspace || workspace_bytes < plan.workspace_bytes)
-        return SSD_ERR_WORKSPACE;
-    if (!aligned(workspace, 256))
-        return SSD_ERR_ALIGN;
+    return backward_proj<ssd::kLayoutProj>(proj, token_stride, A, batch, T, H, N, D, chunk_size,
+                                           initial_state, grad_y, grad_final_state, grad_proj,
+                                           grad_A, grad_initial_state, workspace, workspace_bytes,
+                                           stream);
+}
 
-    const int64_t HD = H * D, HN = H * N;
-    ssd::BwdParams prm{};
-    prm.x = proj;
-    prm.A = (const float *)A;
-    prm.Bt = proj + HD;
-    prm.Ct = proj + HD + 2 * HN;
-    prm.dt = proj + HD + 4 * HN;
-    prm.init = (const float *)initial_state;
-    prm.gy = grad_y;
-    prm.gfinal = (const float *)grad_final_state;
-    prm.gx = grad_proj;
-    prm.gA = (float *)grad_A;
-    prm.gB = grad_proj + HD;
-    prm.gC = grad_proj + HD + 2 * HN;
-    prm.gdt = grad_proj + HD + 4 * HN;
-    prm.ginit = (float *)grad_initial_state;
-    prm.fwd_states = (float *)workspace;
-    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
-    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
-    prm.B = (int)batch;
-    prm.T = (int)T;
-    prm.H = (int)H;
-    prm.N = (int)N;
-    prm.D = (int)D;
-    prm.Q = plan.Q;
-    prm.nc = plan.nc;
-    prm.tok_stride = token_stride;
-    const int64_t seqs = batch * H;
-    return plan.R == 16 ? launch_backward<16, true>(prm, seqs, s)
-                        : launch_backward<32, true>(prm, seqs, s);
+int ssd_chunk_backward_proj_bf16(const uint16_t *proj, int64_t token_stride, const ssd_c64 *A,
+                                 int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                                 int64_t chunk_size, const ssd_c64 *initial_state,
+                                 const float *grad_y, const ssd_c64 *grad_final_state,
+                                 uint16_t *grad_proj, ssd_c64 *grad_A,
+                                 ssd_c64 *grad_initial_state, void *workspace,
+                                 size_t workspace_bytes, ssd_stream_t stream)
+{
+    return backward_proj<ssd::kLayoutProjBf16>(proj, token_stride, A, batch, T, H, N, D,
+                                               chunk_size, initial_state, grad_y,
+                                               grad_final_state, grad_proj, grad_A,
+                                               grad_initial_state, workspace, workspace_bytes,
+                                               stream);
 }
 
 int ssd_head_mix(const float *y, const float *W, int64_t tokens, int64_t H, int64_t D, float *z,

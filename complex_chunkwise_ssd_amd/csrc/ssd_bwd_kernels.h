@@ -60,10 +60,12 @@ struct BwdParams {
     float *adj_states;      // (B, H, nc, 64, 64) complex: adjoint leaving each chunk, conjugated
     float *gA_part;         // (B, H, nc) complex: each chunk's share of gA
     int B, T, H, N, D, Q, nc;
-    // In_proj rows (the PROJ kernels): x, Bt, Ct, dt point at the x, Re B, Re C and
-    // dt blocks of token (0, 0)'s row and gx, gB, gC, gdt at the same blocks of
-    // the gradient rows; rows are tok_stride floats apart, an imaginary block
-    // starts H*N floats after its real block, and x (so its gradient) is real.
+    // In_proj rows (the in_proj layouts): x, Bt, Ct, dt point at the x, Re B, Re C
+    // and dt blocks of token (0, 0)'s row and gx, gB, gC, gdt at the same blocks of
+    // the gradient rows; rows are tok_stride elements apart (float32, or bfloat16
+    // in kLayoutProjBf16, where the pointers hold 16-bit elements), an imaginary
+    // block starts H*N elements after its real block, and x (so its gradient) is
+    // real.
     int64_t tok_stride;
 };
 
@@ -90,45 +92,76 @@ SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i];
 SSD_DEVICE v2f cmul_d(v2f a, v2f b) { return cmul(a, b); }
 
 // Flat element index of (b, t, h, col) in a (B, T, H, width) tensor, or in
-// the block of an in_proj row (PROJ).
-template <bool PROJ>
+// the block of an in_proj row (the in_proj layouts).
+template <int LAYOUT>
 SSD_DEVICE int64_t bwd_elem(const BwdParams &p, int b, int t, int h, int width, int col)
 {
-    if constexpr (PROJ)
+    if constexpr (LAYOUT != kLayoutC64)
         return ((int64_t)b * p.T + t) * p.tok_stride + (int64_t)h * width + col;
     else
         return (((int64_t)b * p.T + t) * p.H + h) * width + col;
 }
 
+// Element e of an in_proj row array: float32, or bfloat16 widened to float32.
+template <int LAYOUT>
+SSD_DEVICE float bwd_row_load(const float *base, int64_t e)
+{
+    if constexpr (LAYOUT == kLayoutProjBf16)
+        return bf16_lo(((const uint16_t *)base)[e]);
+    else
+        return base[e];
+}
+
+// float32 -> bfloat16, rounded to nearest with ties to even (NaN stays a quiet NaN).
+SSD_DEVICE uint16_t f32_to_bf16(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Stores element e of an in_proj gradient row array (bfloat16 rounds).
+template <int LAYOUT>
+SSD_DEVICE void bwd_row_store(float *base, int64_t e, float v)
+{
+    if constexpr (LAYOUT == kLayoutProjBf16)
+        ((uint16_t *)base)[e] = f32_to_bf16(v);
+    else
+        base[e] = v;
+}
+
 // Complex B_t or C_t element (base = p.Bt or p.Ct).
-template <bool PROJ>
+template <int LAYOUT>
 SSD_DEVICE v2f bwd_load_bc(const BwdParams &p, const float *base, int b, int t, int h, int col)
 {
-    const int64_t e = bwd_elem<PROJ>(p, b, t, h, p.N, col);
-    if constexpr (PROJ)
-        return v2f{base[e], base[e + (int64_t)p.H * p.N]};
+    const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, p.N, col);
+    if constexpr (LAYOUT != kLayoutC64)
+        return v2f{bwd_row_load<LAYOUT>(base, e), bwd_row_load<LAYOUT>(base, e + (int64_t)p.H * p.N)};
     else
         return ld_c(base, e);
 }
 
 // x element (real in the in_proj rows).
-template <bool PROJ>
+template <int LAYOUT>
 SSD_DEVICE v2f bwd_load_x(const BwdParams &p, int b, int t, int h, int col)
 {
-    const int64_t e = bwd_elem<PROJ>(p, b, t, h, p.D, col);
-    if constexpr (PROJ)
-        return v2f{p.x[e], 0.f};
+    const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, p.D, col);
+    if constexpr (LAYOUT != kLayoutC64)
+        return v2f{bwd_row_load<LAYOUT>(p.x, e), 0.f};
     else
         return ld_c(p.x, e);
 }
 
 // dt of chunk row tid (tid < R), or 0 past the chunk or past T.
-template <int R, bool PROJ>
+template <int R, int LAYOUT>
 SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
 {
     const int tid = thread_id();
     const int t = c * p.Q + tid;
-    return (tid < R && tid < p.Q && t < p.T) ? p.dt[bwd_elem<PROJ>(p, b, t, h, 1, 0)] : 0.f;
+    return (tid < R && tid < p.Q && t < p.T)
+               ? bwd_row_load<LAYOUT>(p.dt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0))
+               : 0.f;
 }
 
 // Double-precision lane moves (two 32-bit DPP / readlane moves).
@@ -192,7 +225,7 @@ SSD_DEVICE v2f cexp_diff(const double *sLam, int l, int s)
 // leaves (adjoint) each chunk before folding the chunk in. The 64 x 64 value
 // lives in MFMA accumulators: wave w holds tiles w and w + 8 of the 4 x 4 grid
 // (rows n, columns d).
-template <int R, bool REV, bool PROJ>
+template <int R, bool REV, int LAYOUT>
 SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
 {
     constexpr int LD = kBwdLd;
@@ -233,18 +266,18 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
     v2f pa[PER], px[PER];
     float pdt = 0.f;
     auto fetch = [&](int c) {
-        pdt = bwd_load_dt<R, PROJ>(p, b, h, c);
+        pdt = bwd_load_dt<R, LAYOUT>(p, b, h, c);
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
             const int t = c * p.Q + l;
             const bool valid = l < p.Q && t < p.T;
             const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
-            pa[j] = (valid && col < N) ? bwd_load_bc<PROJ>(p, REV ? p.Ct : p.Bt, b, t, h, col)
+            pa[j] = (valid && col < N) ? bwd_load_bc<LAYOUT>(p, REV ? p.Ct : p.Bt, b, t, h, col)
                                        : v2f{0.f, 0.f};
             if (REV)
                 px[j] = v2f{(valid && col < D) ? p.gy[row * D + col] : 0.f, 0.f};
             else
-                px[j] = (valid && col < D) ? bwd_load_x<PROJ>(p, b, t, h, col) : v2f{0.f, 0.f};
+                px[j] = (valid && col < D) ? bwd_load_x<LAYOUT>(p, b, t, h, col) : v2f{0.f, 0.f};
         }
     };
     fetch(REV ? p.nc - 1 : 0);
@@ -383,7 +416,7 @@ SSD_DEVICE v4f row_total(v4f v)
 // adjoints. A fixed number of workgroups (about one per compute unit) take the
 // chunks in a strided loop, loading the next chunk's inputs into registers
 // while the current one is evaluated.
-template <int R, bool PROJ>
+template <int R, int LAYOUT>
 SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
 {
     constexpr int LD = kBwdLd;
@@ -442,7 +475,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         const int cc = (int)(k % p.nc);
         const int bb = (int)(sq / p.H), hh = (int)(sq % p.H);
         if constexpr (part == 0)
-            pdt = bwd_load_dt<R, PROJ>(p, bb, hh, cc);
+            pdt = bwd_load_dt<R, LAYOUT>(p, bb, hh, cc);
         if constexpr (part <= 1) {
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + 512 * j, l = i >> 6, col = i & 63;
@@ -451,10 +484,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const int64_t row = ((int64_t)bb * p.T + t) * p.H + hh;
                 const bool vn = valid && col < N, vd = valid && col < D;
                 if constexpr (part == 0) {
-                    pb[j] = vn ? bwd_load_bc<PROJ>(p, p.Bt, bb, t, hh, col) : v2f{0.f, 0.f};
-                    pc[j] = vn ? bwd_load_bc<PROJ>(p, p.Ct, bb, t, hh, col) : v2f{0.f, 0.f};
+                    pb[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Bt, bb, t, hh, col) : v2f{0.f, 0.f};
+                    pc[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Ct, bb, t, hh, col) : v2f{0.f, 0.f};
                 } else {
-                    px[j] = vd ? bwd_load_x<PROJ>(p, bb, t, hh, col) : v2f{0.f, 0.f};
+                    px[j] = vd ? bwd_load_x<LAYOUT>(p, bb, t, hh, col) : v2f{0.f, 0.f};
                     pgy[j] = vd ? p.gy[row * D + col] : 0.f;
                 }
             }
@@ -691,11 +724,11 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
                 const int t = c * p.Q + row;
                 if (row < p.Q && t < p.T && col < width) {
-                    if constexpr (PROJ) {  // real x: its gradient is the real part
-                        const int64_t e = bwd_elem<true>(p, b, t, h, width, col);
-                        dst[e] = outr[r];
+                    if constexpr (LAYOUT != kLayoutC64) {  // real x: its gradient is the real part
+                        const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, width, col);
+                        bwd_row_store<LAYOUT>(dst, e, outr[r]);
                         if (kind != 0)
-                            dst[e + (int64_t)p.H * p.N] = -outi[r];
+                            bwd_row_store<LAYOUT>(dst, e + (int64_t)p.H * p.N, -outi[r]);
                     } else {
                         const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
                         *(v2f *)&dst[2 * (g * width + col)] = v2f{outr[r], -outi[r]};
@@ -770,7 +803,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const float gar = fr, gai = -fi;
                 const float dtv = sDt[t0];
                 const float sig = 1.f / (1.f + expf(-dtv));
-                p.gdt[bwd_elem<PROJ>(p, b, t, h, 1, 0)] = (Ar * gar + Ai * gai) * sig;
+                bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0),
+                                      (Ar * gar + Ai * gai) * sig);
                 const float sp = softplus_f(dtv);
                 gAr = sp * gar;
                 gAi = sp * gai;

@@ -241,6 +241,26 @@ int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c
                             ssd_stream_t stream);
 
 /*
+ * ssd_chunk_backward_proj_bf16 -- ssd_chunk_backward_proj for bfloat16 rows (the
+ * training precision of AGENTS & System Architecture: BF16 activations, the
+ * recurrent state complex64): proj and grad_proj hold bfloat16 values as their
+ * 16-bit patterns. Rows are widened to float32 as they are loaded; every
+ * product, sum and stored state stays float32 (as in ssd_chunk_forward_proj_bf16),
+ * and each gradient is rounded to bfloat16 (nearest, ties to even) as it is
+ * stored. grad_y, grad_final_state, grad_A and grad_initial_state stay float32
+ * / complex64.
+ * Arguments, constraints and workspace: as ssd_chunk_backward_proj.
+ * Alignment: proj, grad_proj 2 bytes; grad_y 4 bytes; A and the states 8 bytes.
+ */
+int ssd_chunk_backward_proj_bf16(const uint16_t *proj, int64_t token_stride, const ssd_c64 *A,
+                                 int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D,
+                                 int64_t chunk_size, const ssd_c64 *initial_state,
+                                 const float *grad_y, const ssd_c64 *grad_final_state,
+                                 uint16_t *grad_proj, ssd_c64 *grad_A,
+                                 ssd_c64 *grad_initial_state, void *workspace,
+                                 size_t workspace_bytes, ssd_stream_t stream);
+
+/*
  * ssd_head_mix -- the MIMO head mixer that follows the scan (index.html lab 02
  * "MIMO MIXER": a fully connected mixer across the SSM heads, 16 x 16 for the
  * 16 heads of 64 channels, identity at initialisation; "Knows cold" item 2 of

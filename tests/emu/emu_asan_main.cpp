@@ -132,6 +132,36 @@ static int run_bwd_proj(int B, int T, int H, int N, int D, int Q, int extra)
     return st != 0 || bad != 0;
 }
 
+static int run_bwd_proj_bf16(int B, int T, int H, int N, int D, int Q, int extra)
+{
+    unsigned seed = 5151u + B * 7 + T * 13 + H * 17 + N * 19 + D * 23 + Q * 29;
+    const int64_t S = (int64_t)H * (D + 4 * N + 1) + extra;
+    float *src = alloc_fill((size_t)B * T * S, seed);
+    uint16_t *proj = (uint16_t *)malloc((size_t)B * T * S * sizeof(uint16_t));
+    for (size_t i = 0; i < (size_t)B * T * S; ++i) {
+        uint32_t u;
+        memcpy(&u, &src[i], 4);
+        proj[i] = (uint16_t)(u >> 16);
+    }
+    float *A = alloc_fill((size_t)H * 2, seed);
+    for (int h = 0; h < H; ++h)
+        A[2 * h] = -0.05f - 2.9f * (A[2 * h] + 0.5f);
+    float *gy = alloc_fill((size_t)B * T * H * D, seed);
+    uint16_t *gp = (uint16_t *)calloc((size_t)B * T * S, sizeof(uint16_t));
+    float *gA = (float *)malloc((size_t)H * 2 * sizeof(float));
+    size_t ws = ssd_chunk_backward_workspace_bytes(B, T, H, N, D, Q);
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
+    int st = ssd_chunk_backward_proj_bf16(proj, S, (ssd_c64 *)A, B, T, H, N, D, Q, nullptr, gy,
+                                          nullptr, gp, (ssd_c64 *)gA, nullptr, w, ws, nullptr);
+    int bad = 0;
+    for (size_t i = 0; i < (size_t)B * T * S; ++i)
+        bad += (gp[i] & 0x7f80u) == 0x7f80u;  // Inf or NaN
+    printf("backward proj bf16 B=%d T=%d H=%d N=%d D=%d Q=%d ws=%zu status=%d nonfinite=%d\n", B,
+           T, H, N, D, Q, ws, st, bad);
+    free(src); free(proj); free(A); free(gy); free(gp); free(gA); free(w);
+    return st != 0 || bad != 0;
+}
+
 static int run_mix(int64_t M, int H, int D)
 {
     unsigned seed = 31u + (unsigned)M * 7 + H * 17 + D * 23;
@@ -175,6 +205,7 @@ int main()
     fails += run_proj(2, 9, 1, 2, 4, 4, 1);      // Q < 16
     fails += run_bwd_proj(1, 40, 2, 4, 6, 16, 1);   // gradient rows with a spare float
     fails += run_bwd_proj(1, 70, 1, 64, 64, 64, 0); // full tiles
+    fails += run_bwd_proj_bf16(1, 40, 2, 4, 6, 16, 1);  // bfloat16 rows, odd row length
     fails += run_mix(5, 16, 64);    // vector path
     fails += run_mix(3, 7, 10);     // scalar path, padded heads
     fails += run_mix(9, 20, 8);     // two head blocks

@@ -71,6 +71,8 @@ def load(out_dir):
             lib.ssd_chunk_backward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p,
                                                     p, p, p, p, p, ctypes.c_size_t, p]
             lib.ssd_chunk_backward_proj.restype = ctypes.c_int
+            lib.ssd_chunk_backward_proj_bf16.argtypes = lib.ssd_chunk_backward_proj.argtypes
+            lib.ssd_chunk_backward_proj_bf16.restype = ctypes.c_int
             lib.ssd_chunk_backward_workspace_bytes.argtypes = [i64] * 6
             lib.ssd_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
             lib.ssd_chunk_forward_proj.argtypes = [p, i64, p, i64, i64, i64, i64, i64, i64, p, p, p,
@@ -170,14 +172,22 @@ def chunk_forward_proj(lib, proj, A, H, N, D, chunk, initial_state=None):
 
 
 def chunk_backward_proj(lib, proj, A, H, N, D, chunk, grad_y, grad_final=None):
-    """Returns (status, grad_proj rows (B, T, S) float32 with NaN past the blocks,
-    grad_A, grad_initial_state)."""
-    pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
+    """Returns (status, grad_proj rows (B, T, S) with NaN past the blocks,
+    grad_A, grad_initial_state). proj float32 numpy/torch, or a bfloat16 torch
+    tensor; bfloat16 gradient rows come back widened to float32."""
+    import torch
+    bf16 = hasattr(proj, "dtype") and proj.dtype == torch.bfloat16
+    if bf16:
+        pr = np.ascontiguousarray(proj.contiguous().view(torch.int16).numpy())
+    else:
+        pr = np.ascontiguousarray(proj.numpy() if hasattr(proj, "numpy") else proj, np.float32)
     Av = _c64(A)
     Bsz, T, S = pr.shape
     gy = np.ascontiguousarray(grad_y, np.float32)
     gf = None if grad_final is None else np.ascontiguousarray(grad_final, np.complex64)
-    grows = np.full((Bsz, T, S), np.nan, np.float32)
+    # NaN (as bfloat16 bits 0x7fc0 or float32) past the blocks
+    grows = np.full((Bsz, T, S), 0x7fc0, np.uint16) if bf16 else np.full((Bsz, T, S), np.nan,
+                                                                          np.float32)
     W = H * (D + 4 * N + 1)
     gA = np.full((H,), np.nan + 0j, np.complex64)
     gi = np.full((Bsz, H, N, D), np.nan + 0j, np.complex64)
@@ -186,9 +196,11 @@ def chunk_backward_proj(lib, proj, A, H, N, D, chunk, grad_y, grad_final=None):
     ws_p = ws.ctypes.data
     ws_p = ws_p + (-ws_p) % 256
     ptr = lambda a: None if a is None else a.ctypes.data
-    st = lib.ssd_chunk_backward_proj(ptr(pr), S, ptr(Av), Bsz, T, H, N, D, chunk, None, ptr(gy),
-                                     ptr(gf), ptr(grows), ptr(gA), ptr(gi),
-                                     ws_p if ws_n else None, ws_n, None)
+    fn = lib.ssd_chunk_backward_proj_bf16 if bf16 else lib.ssd_chunk_backward_proj
+    st = fn(ptr(pr), S, ptr(Av), Bsz, T, H, N, D, chunk, None, ptr(gy), ptr(gf), ptr(grows),
+            ptr(gA), ptr(gi), ws_p if ws_n else None, ws_n, None)
+    if bf16:
+        grows = (grows.astype(np.uint32) << 16).view(np.float32)
     return st, grows, gA, gi, W
 
 

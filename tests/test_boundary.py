@@ -272,3 +272,18 @@ def test_python_head_mix_rejects_bad_tensors():
         ssd.head_mix(y, torch.eye(4))  # CPU tensors
     with pytest.raises(ValueError):
         ssd.head_mix_backward(y, torch.eye(4), y)
+
+
+def test_backward_proj_bf16_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    S = 2 * (4 + 16 + 1)
+    need = lib.ssd_chunk_backward_workspace_bytes(1, 16, 2, 4, 4, 4)
+    f = lib.ssd_chunk_backward_proj_bf16
+    assert f(p, S - 1, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, p, need, None) == \
+        ssd.SSD_ERR_SHAPE
+    assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, None, p, None, p, need, None) == \
+        ssd.SSD_ERR_NULL
+    assert f(ctypes.c_void_p(0x100001), S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, p,
+             need, None) == ssd.SSD_ERR_ALIGN     # bfloat16 rows need 2 bytes
+    assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, None, need, None) == \
+        ssd.SSD_ERR_WORKSPACE

@@ -277,3 +277,27 @@ def test_emulated_head_mix_zero_tokens(emu):
     assert st == 0 and z.shape == (0, 4, 8)
     st, gy, gW = emu_harness.head_mix_backward(emu, y, W, y)
     assert st == 0 and np.array_equal(gW, np.zeros((4, 4), np.float32))
+
+
+@pytest.mark.parametrize("case", [(2, 16, 2, 4, 4, 4, 0), (1, 97, 2, 8, 6, 32, 6)])
+def test_emulated_backward_proj_bf16_matches_oracle(emu, case):
+    """bfloat16 rows and gradient rows: the oracle runs on the widened rows; the
+    bar adds the bfloat16 rounding of the result (2^-8 of it)."""
+    import torch
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 19, dt_mean=0.3, extra=extra,
+                                   dtype=torch.bfloat16)
+    rng = np.random.default_rng(sum(case) + 1)
+    gy = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+    st, rows, gA, gi, W = emu_harness.chunk_backward_proj(emu, proj, A, H, N, D, Q, gy, gf)
+    assert st == 0
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf)
+    want = ssd_inputs.pack_proj_grads(ref.x, ref.B_t, ref.C_t, ref.dt, proj.shape[-1])
+    got = rows[..., :W]
+    assert np.isfinite(got).all()
+    err = np.abs(got - want[..., :W])
+    assert (err <= 1e-4 + (1e-4 + 2.0 ** -8) * np.abs(want[..., :W])).all(), err.max()
+    assert np.isnan(rows[..., W:]).all()
+    assert (np.abs(gA - ref.A) <= 1e-4 + 1e-6 * B * T + 1e-4 * np.abs(ref.A)).all()

@@ -143,12 +143,17 @@ def test_proj_bf16_network_layer_matches_float32_rows():
 # stand for, with the gradient bar (grad_A's absolute term grows 1e-6 per
 # token summed); floats past the blocks stay untouched.
 
-def _check_grad_rows(rows, gA, gi, ref, S, W, what, tokens):
+# bfloat16 gradient rows: the float32 result is rounded to nearest bfloat16
+# (8 significant bits), which adds at most 2^-8 of the value to the float32 bar.
+BF16_REL = 1e-4 + 2.0 ** -8
+
+
+def _check_grad_rows(rows, gA, gi, ref, S, W, what, tokens, rel=1e-4):
     want = ssd_inputs.pack_proj_grads(ref.x, ref.B_t, ref.C_t, ref.dt, S)
     got = rows[..., :W]
     assert np.isfinite(got).all(), what
     err = np.abs(got - want[..., :W])
-    bad = err > 1e-4 + 1e-4 * np.abs(want[..., :W])
+    bad = err > 1e-4 + rel * np.abs(want[..., :W])
     assert not bad.any(), "%s: %d violations, max %.3e" % (what, int(bad.sum()), err.max())
     assert (rows[..., W:] == 0).all(), what
     for comp in (np.real, np.imag):
@@ -203,3 +208,41 @@ def test_backward_proj_network_layer_sampled():
             r[b, :, H * D + 4 * H * N + h:H * D + 4 * H * N + h + 1]], axis=-1)[None]
         e = np.abs(got1 - want1)
         assert (e <= 1e-4 + 1e-4 * np.abs(want1)).all(), ((b, h), e.max())
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[2], CASES[6], CASES[7]])
+def test_backward_proj_bf16_small_shapes(case):
+    """bfloat16 rows in, bfloat16 gradient rows out: against the oracle run on
+    the rows widened to float32, with the bfloat16 bar."""
+    B, T, H, N, D, Q, extra = case
+    proj, A = ssd_inputs.proj_case(B, T, H, N, D, seed=sum(case) + 90, dt_mean=0.3, extra=extra,
+                                   dtype=torch.bfloat16)
+    gy, gf = ssd_inputs.upstream_grads(B, T, H, N, D, seed=sum(case) + 1)
+    rows, gA, gi = ssd.chunk_backward_proj(proj.to(DEV), A.to(DEV), H, N, D, gy.to(DEV),
+                                           gf.to(DEV), chunk_size=Q)
+    torch.cuda.synchronize()
+    assert rows.dtype == torch.bfloat16
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy, gf)
+    _check_grad_rows(rows.float().cpu().numpy(), gA.cpu().numpy(), gi.cpu().numpy(), ref,
+                     proj.shape[-1], H * (D + 4 * N + 1), "bwd proj bf16 " + str(case), B * T,
+                     rel=BF16_REL)
+
+
+def test_backward_proj_bf16_network_layer_rounds_the_float32_rows():
+    """Network layer shape: the bfloat16 gradient rows are the float32 path's
+    gradient rows (same widened inputs) rounded to nearest bfloat16, to within
+    one bfloat16 step where the two float32 results straddle a rounding boundary."""
+    H, N, D = 16, 64, 64
+    proj, A = ssd_inputs.proj_case(32, 2048, H, N, D, seed=0, device=DEV, dtype=torch.bfloat16)
+    gy, gf = ssd_inputs.upstream_grads(32, 2048, H, N, D, seed=0, device=DEV)
+    rows16, gA16, gi16 = ssd.chunk_backward_proj(proj, A, H, N, D, gy, gf, chunk_size=64)
+    rows32, gA32, gi32 = ssd.chunk_backward_proj(proj.float(), A, H, N, D, gy, gf, chunk_size=64)
+    torch.cuda.synchronize()
+    W = H * (D + 4 * N + 1)
+    a = rows16.float()[..., :W]
+    r = rows32[..., :W].to(torch.bfloat16).float()
+    step = torch.abs(r) * 2.0 ** -7 + 1e-30
+    assert bool((torch.abs(a - r) <= step).all())
+    assert float((a != r).float().mean()) < 0.01  # nearly all identical
+    assert torch.equal(gA16, gA32) and torch.equal(gi16, gi32)
