@@ -102,14 +102,30 @@ SSD_DEVICE int64_t bwd_elem(const BwdParams &p, int b, int t, int h, int width, 
         return (((int64_t)b * p.T + t) * p.H + h) * width + col;
 }
 
-// Element e of an in_proj row array: float32, or bfloat16 widened to float32.
+// Element e of an in_proj row array as loaded: a float32 value, or the 16 bits
+// of a bfloat16 value held in a float register. The prefetch registers keep
+// what was loaded; bwd_widen turns it into float32 where it is used, so that no
+// conversion right behind a load makes the wave wait for that load.
 template <int LAYOUT>
 SSD_DEVICE float bwd_row_load(const float *base, int64_t e)
 {
     if constexpr (LAYOUT == kLayoutProjBf16)
-        return bf16_lo(((const uint16_t *)base)[e]);
+        return __builtin_bit_cast(float, (uint32_t)((const uint16_t *)base)[e]);
     else
         return base[e];
+}
+template <int LAYOUT>
+SSD_DEVICE float bwd_widen(float v)
+{
+    if constexpr (LAYOUT == kLayoutProjBf16)
+        return bf16_lo(__builtin_bit_cast(uint32_t, v));
+    else
+        return v;
+}
+template <int LAYOUT>
+SSD_DEVICE v2f bwd_widen2(v2f v)
+{
+    return v2f{bwd_widen<LAYOUT>(v.x), bwd_widen<LAYOUT>(v.y)};
 }
 
 // float32 -> bfloat16, rounded to nearest with ties to even (NaN stays a quiet NaN).
@@ -153,7 +169,8 @@ SSD_DEVICE v2f bwd_load_x(const BwdParams &p, int b, int t, int h, int col)
         return ld_c(p.x, e);
 }
 
-// dt of chunk row tid (tid < R), or 0 past the chunk or past T.
+// dt of chunk row tid (tid < R), or 0 past the chunk or past T (as loaded:
+// bwd_widen gives the value).
 template <int R, int LAYOUT>
 SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
 {
@@ -270,14 +287,15 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
             const int t = c * p.Q + l;
-            const bool valid = l < p.Q && t < p.T;
-            const int64_t row = ((int64_t)b * p.T + t) * p.H + h;
-            pa[j] = (valid && col < N) ? bwd_load_bc<LAYOUT>(p, REV ? p.Ct : p.Bt, b, t, h, col)
-                                       : v2f{0.f, 0.f};
+            // every lane loads (from a clamped element); the stage zeroes the lanes
+            // outside the chunk, so no branch or select waits behind the loads
+            const int tc = t < p.T ? t : p.T - 1;
+            pa[j] = bwd_load_bc<LAYOUT>(p, REV ? p.Ct : p.Bt, b, tc, h, col < N ? col : N - 1);
             if (REV)
-                px[j] = v2f{(valid && col < D) ? p.gy[row * D + col] : 0.f, 0.f};
+                px[j] = v2f{p.gy[(((int64_t)b * p.T + tc) * p.H + h) * D + (col < D ? col : D - 1)],
+                            0.f};
             else
-                px[j] = (valid && col < D) ? bwd_load_x<LAYOUT>(p, b, t, h, col) : v2f{0.f, 0.f};
+                px[j] = bwd_load_x<LAYOUT>(p, b, tc, h, col < D ? col : D - 1);
         }
     };
     fetch(REV ? p.nc - 1 : 0);
@@ -296,7 +314,7 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
         if (w == 0) {
             // REV: e_in = exp(Lam[l]); forward: e_end = exp(Lam[R-1] - Lam[l])
             double lr, li, er, ei;
-            wave_decays<R>(p, c, pdt, Ar, Ai, lr, li, er, ei);
+            wave_decays<R>(p, c, bwd_widen<LAYOUT>(pdt), Ar, Ai, lr, li, er, ei);
             if (lane < R)
                 *(v2f *)&sF[2 * lane] = REV ? cexp_f(v2f{(float)lr, (float)li})
                                             : cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
@@ -306,13 +324,20 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
         block_sync();
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
-            const v2f a = cmul(pa[j], *(const v2f *)&sF[2 * l]);
+            // REV: grad_y, always float32; otherwise x as loaded. Lanes outside the
+            // chunk (or past N, D) are zeroed here.
+            const int t = c * p.Q + l;
+            const bool valid = l < p.Q && t < p.T;
+            const v2f av = valid && col < N ? bwd_widen2<LAYOUT>(pa[j]) : v2f{0.f, 0.f};
+            const v2f xv = !(valid && col < D) ? v2f{0.f, 0.f}
+                                               : (REV ? px[j] : bwd_widen2<LAYOUT>(px[j]));
+            const v2f a = cmul(av, *(const v2f *)&sF[2 * l]);
             sAre[l * LD + col] = a.x;
             sAim[l * LD + col] = a.y;
             sAimN[l * LD + col] = -a.y;
-            sXre[l * LD + col] = px[j].x;
+            sXre[l * LD + col] = xv.x;
             if (!REV)
-                sXim[l * LD + col] = px[j].y;
+                sXim[l * LD + col] = xv.y;
         }
         block_sync();
         if (ci + 1 < p.nc)
@@ -508,12 +533,14 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     auto stage = [&]() {
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
-            sBre[l * LD + col] = pb[j].x;
-            sBim[l * LD + col] = pb[j].y;
-            sCre[l * LD + col] = pc[j].x;
-            sCim[l * LD + col] = pc[j].y;
-            sXre[l * LD + col] = px[j].x;
-            sXim[l * LD + col] = px[j].y;
+            const v2f bv = bwd_widen2<LAYOUT>(pb[j]), cv = bwd_widen2<LAYOUT>(pc[j]);
+            const v2f xv = bwd_widen2<LAYOUT>(px[j]);
+            sBre[l * LD + col] = bv.x;
+            sBim[l * LD + col] = bv.y;
+            sCre[l * LD + col] = cv.x;
+            sCim[l * LD + col] = cv.y;
+            sXre[l * LD + col] = xv.x;
+            sXim[l * LD + col] = xv.y;
             sGy[l * LD + col] = pgy[j];
         }
         for (int j = 0; j < PS; ++j) {
@@ -542,12 +569,13 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         if (w == 0) {
             // running sums and row factors of this chunk; read after the next barrier
             double lr, li, er, ei;
-            wave_decays<R>(p, c, pdt, Ar, Ai, lr, li, er, ei);
+            const float dtv = bwd_widen<LAYOUT>(pdt);
+            wave_decays<R>(p, c, dtv, Ar, Ai, lr, li, er, ei);
             if (lane < R) {
                 const int t = c * p.Q + lane;
                 sLam[2 * lane] = lr;
                 sLam[2 * lane + 1] = li;
-                sDt[lane] = (lane < p.Q && t < p.T) ? pdt : 0.f;
+                sDt[lane] = (lane < p.Q && t < p.T) ? dtv : 0.f;
                 *(v2f *)&sEin[2 * lane] = cexp_f(v2f{(float)lr, (float)li});
                 *(v2f *)&sEend[2 * lane] = cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
             }
