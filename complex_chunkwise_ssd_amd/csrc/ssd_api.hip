@@ -633,28 +633,36 @@ int ssd_head_mix_backward(const float *y, const float *W, const float *grad_z, i
         return launch_status();
     }
 
-    ssd::MixParams p{};
-    p.in = grad_z;
-    p.W = W;
-    p.out = grad_y;
-    p.M = tokens;
-    p.H = (int)H;
-    p.D = (int)D;
-    p.transpose = 1;
-    if (int st = launch_mix(p, D % 4 == 0 && aligned(grad_z, 16) && aligned(grad_y, 16), s))
-        return st;
-
     const int64_t groups = mix_gw_groups(tokens);
-    {
-        ssd::MixGradParams g{};
-        g.y = y;
-        g.gz = grad_z;
-        g.partial = (float *)workspace;
-        g.M = tokens;
-        g.H = (int)H;
-        g.D = (int)D;
-        const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16);
-        const int st = H <= 16 ? launch_mix_gw<1>(g, groups, vec, s) : launch_mix_gw<2>(g, groups, vec, s);
+    ssd::MixGradParams g{};
+    g.y = y;
+    g.gz = grad_z;
+    g.partial = (float *)workspace;
+    g.M = tokens;
+    g.H = (int)H;
+    g.D = (int)D;
+    g.W = W;
+    g.gy = grad_y;
+    const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16) && aligned(grad_y, 16);
+    if (H <= 16 && vec) {
+        // one pass: grad_y and the gW tiles
+        hipLaunchKernelGGL(ssd::mix_bwd_fused_kernel, dim3((unsigned)groups),
+                           dim3(ssd::kMixThreads), 0, s, g);
+        if (int st = launch_status())
+            return st;
+    } else {
+        ssd::MixParams p{};
+        p.in = grad_z;
+        p.W = W;
+        p.out = grad_y;
+        p.M = tokens;
+        p.H = (int)H;
+        p.D = (int)D;
+        p.transpose = 1;
+        if (int st = launch_mix(p, D % 4 == 0 && aligned(grad_z, 16) && aligned(grad_y, 16), s))
+            return st;
+        const bool gvec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16);
+        const int st = H <= 16 ? launch_mix_gw<1>(g, groups, gvec, s) : launch_mix_gw<2>(g, groups, gvec, s);
         if (st)
             return st;
     }

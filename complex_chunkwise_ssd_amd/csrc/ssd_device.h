@@ -23,6 +23,16 @@ SSD_DEVICE v4f mfma_16x16x4(float a, float b, v4f c)
 
 SSD_DEVICE void block_sync() { __syncthreads(); }
 
+// Orders one wave's shared-memory accesses around this point: the wave's LDS
+// instructions complete in the order they issue, so its earlier writes are
+// seen by its later reads; this only keeps the compiler from moving memory
+// accesses across the point.
+SSD_DEVICE void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Buffer resources: 32-bit byte offsets from a wave-uniform base. An access
 // at or past `bytes` reads zero and a store there is dropped, which is how the
 // kernels mask padded rows and columns.

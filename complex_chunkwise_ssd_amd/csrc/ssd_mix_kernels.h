@@ -40,7 +40,12 @@ struct MixGradParams {
     float *partial;    // (gridDim.x, H, H) one gW tile set per workgroup
     int64_t M;
     int H, D;
+    const float *W;    // (H, H): the fused pass also forms grad_y
+    float *gy;         // (M, H, D)
 };
+
+constexpr int kMixCB = 64;            // channels of one staged token tile in the fused pass
+constexpr int kMixLd = kMixCB + 4;    // its row stride (floats) in shared memory
 
 template <int DV>
 struct MixVec;
@@ -182,6 +187,129 @@ SSD_KERNEL(kMixThreads) void mix_gw_kernel(MixGradParams p)
     for (int e = tid; e < p.H * p.H; e += kMixThreads) {
         const int i = e / p.H, j = e % p.H;
         const int o = i * HP + j;
+        dst[e] = ((sPart[0][o] + sPart[1][o]) + sPart[2][o]) + sPart[3][o];
+    }
+}
+
+// The fused backward for H <= 16 and D % 4 == 0 (16-byte aligned rows): one
+// pass over grad_z and y forms both grad_y and the gW partial tiles, so grad_z
+// is read once. Each wave takes whole tokens (4b + w, then every 4*grid); per
+// token and 64-channel block it loads the 16 x 64 tiles of grad_z and y with
+// row-contiguous 16-byte loads (lane l covers floats 4l + 256k of the tile),
+// issued one token ahead, and stages them in its own shared-memory tiles. From
+// there: the gW tile on MFMA exactly as in mix_gw_kernel (lane (r, q) reads
+// head r, channels 16u + 4q ..), and grad_y on the vector ALUs: lane (g, s)
+// forms output heads 4s .. 4s+3 at channels 4g .. 4g+3 from all 16 input
+// heads, reading W[i][4s .. 4s+3] from shared memory (a broadcast read).
+SSD_KERNEL(kMixThreads) void mix_bwd_fused_kernel(MixGradParams p)
+{
+    SSD_LDS float sG[4][16 * kMixLd];
+    SSD_LDS float sY[4][16 * kMixLd];
+    SSD_LDS float sPart[4][16 * 16];
+    SSD_LDS float sW[16 * 16];  // sW[i * 16 + j] = W[i][j], zero past H
+    const int tid = thread_id();
+    const int wave = wave_id();
+    const int lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;  // MFMA roles; also (g, s) of grad_y
+    const int64_t HD = (int64_t)p.H * p.D;
+    const uint32_t row_bytes = (uint32_t)(HD * 4);
+    const int nblk = (p.D + kMixCB - 1) / kMixCB;
+
+    static_assert(kMixThreads == 16 * 16, "one thread per weight");
+    {
+        const int i = tid >> 4, j = tid & 15;
+        sW[tid] = i < p.H && j < p.H ? p.W[i * p.H + j] : 0.f;
+    }
+    block_sync();
+
+    // tile element f = 4 lane + 256 k (k < 4): head f / 64, channel f % 64 of the
+    // block; heads past H and channels past D read zero
+    auto tile_off = [&](int cb, int k) {
+        const int f = 4 * lane + 256 * k, i = f >> 6, c = f & 63;
+        const int d = kMixCB * cb + c;
+        return i < p.H && d < p.D ? (uint32_t)(i * p.D + d) * 4 : row_bytes;
+    };
+    struct Tiles {
+        v4f g[4], v[4];
+    };
+    auto fetch = [&](int64_t m, int cb, Tiles &t) {
+        const bool live = m < p.M;
+        const buf_t bg = make_buf(p.gz + (live ? m : 0) * HD, live ? row_bytes : 0u);
+        const buf_t by = make_buf(p.y + (live ? m : 0) * HD, live ? row_bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t o = tile_off(cb, k);
+            t.g[k] = buf_load4(bg, o);
+            t.v[k] = buf_load4(by, o);
+        }
+    };
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    const int64_t wstride = grid_blocks() * 4;
+    int64_t m = block_id() * 4 + wave;
+    int cb = 0;
+    Tiles nx;
+    fetch(m, cb, nx);
+    float *tg = sG[wave];
+    float *ty = sY[wave];
+    while (m < p.M) {
+        const Tiles cur = nx;
+        const int64_t mc = m;
+        const int cbc = cb;
+        if (++cb == nblk) {
+            cb = 0;
+            m += wstride;
+        }
+        fetch(m, cb, nx);  // the next tile is in flight while this one is used
+        wave_lds_sync();   // the previous tile's reads are done
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int f = 4 * lane + 256 * k, i = f >> 6, c = f & 63;
+            *(v4f *)&tg[i * kMixLd + c] = cur.g[k];
+            *(v4f *)&ty[i * kMixLd + c] = cur.v[k];
+        }
+        wave_lds_sync();
+        // gW: head r of grad_z against head r of y at channels 16u + 4q + 0..3
+#pragma unroll
+        for (int u = 0; u < kMixCB / 16; ++u) {
+            const v4f a4 = *(const v4f *)&tg[r * kMixLd + 16 * u + 4 * q];
+            const v4f b4 = *(const v4f *)&ty[r * kMixLd + 16 * u + 4 * q];
+            acc = mfma_16x16x4(a4.x, b4.x, acc);
+            acc = mfma_16x16x4(a4.y, b4.y, acc);
+            acc = mfma_16x16x4(a4.z, b4.z, acc);
+            acc = mfma_16x16x4(a4.w, b4.w, acc);
+        }
+        // grad_y at output heads 4q + jj, channels 4r .. 4r + 3 of the block
+        v4f o[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            o[jj] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const v4f gv = *(const v4f *)&tg[i * kMixLd + 4 * r];
+            const v4f w4 = *(const v4f *)&sW[i * 16 + 4 * q];
+            o[0] += w4.x * gv;
+            o[1] += w4.y * gv;
+            o[2] += w4.z * gv;
+            o[3] += w4.w * gv;
+        }
+        const int d = kMixCB * cbc + 4 * r;
+        float *gyrow = p.gy + mc * HD + d;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * q + jj;
+            if (j < p.H && d < p.D)
+                *(v4f *)(gyrow + (int64_t)j * p.D) = o[jj];
+        }
+    }
+    // lane L holds rows 4q..4q+3 of column r of the wave's tile
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        sPart[wave][(4 * q + k) * 16 + r] = acc[k];
+    block_sync();
+    float *dst = p.partial + block_id() * (int64_t)p.H * p.H;
+    for (int e = tid; e < p.H * p.H; e += kMixThreads) {
+        const int o = (e / p.H) * 16 + e % p.H;
         dst[e] = ((sPart[0][o] + sPart[1][o]) + sPart[2][o]) + sPart[3][o];
     }
 }

@@ -309,6 +309,8 @@ SSD_DEVICE int lane_read_i(int v, int src)
     return __builtin_bit_cast(int, emu_shfl(__builtin_bit_cast(float, v), emu::SH_READ, src));
 }
 SSD_DEVICE float uniform(float v) { return v; }
+// A wave-level meeting point: every lane of the wave arrives before any goes on.
+SSD_DEVICE void wave_lds_sync() { (void)emu_shfl(0.f, emu::SH_READ, 0); }
 
 // Buffer resources: an access must lie wholly inside [0, bytes) or wholly
 // outside it (outside reads zero, outside stores are dropped); a straddling

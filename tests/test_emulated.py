@@ -257,7 +257,8 @@ def test_emulated_head_mix_matches_oracle(emu, case):
     assert (err <= 1e-4 + 1e-4 * np.abs(ref)).all(), err.max()
 
 
-@pytest.mark.parametrize("case", MIX_CASES[:3] + [((70,), 16, 64, 0), ((2100,), 4, 4, 0)])
+@pytest.mark.parametrize("case", MIX_CASES[:3] + [((70,), 16, 64, 0), ((2100,), 4, 4, 0),
+                                  ((3,), 16, 100, 0), ((5,), 12, 132, 0)])
 def test_emulated_head_mix_backward_matches_oracle(emu, case):
     lead, H, D, _ = case
     y, W, gz = ssd_inputs.mix_case(lead + (H, D), seed=H * 100 + D + 1)

@@ -30,6 +30,9 @@ CASES = [
     ((2, 300), 16, 64),
     ((4, 33), 5, 36),
     ((1, 2048), 16, 64),      # one sequence of the single-layer shape
+    ((3, 7), 16, 100),        # the fused backward over two channel blocks
+    ((9,), 12, 132),          # fewer heads than a block, three channel blocks
+    ((2, 5), 20, 64),         # more than 16 heads: the two-pass backward
 ]
 
 
@@ -128,3 +131,15 @@ def test_head_mix_zero_tokens():
     gy, gW = ssd.head_mix_backward(y, W, y)
     torch.cuda.synchronize()
     assert z.shape == (0, 16, 64) and torch.equal(gW.cpu(), torch.zeros(16, 16))
+
+
+def test_head_mix_backward_in_place():
+    """grad_y may be grad_z itself: each token's grad_z is read before its grad_y
+    is written."""
+    y, W, gz = ssd_inputs.mix_case((6, 50, 16, 64), seed=14)
+    yd, Wd = y.to(DEV), W.to(DEV)
+    g = gz.to(DEV).clone()
+    ref_y, ref_W = ssd.head_mix_backward(yd, Wd, gz.to(DEV))
+    gy, gW = ssd.head_mix_backward(yd, Wd, g, grad_y=g)
+    torch.cuda.synchronize()
+    assert torch.equal(gy, ref_y) and torch.equal(gW, ref_W)
