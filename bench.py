@@ -49,11 +49,13 @@ def measured_traffic(launch_tokens_heads):
     return rec.get("hbm_bytes_per_launch")
 
 
+# The four counter runs behind the traffic record (<dir> is any output directory;
+# `bench.py --write-traffic-profile <dir>` then reads them).
 TRAFFIC_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_fetch -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write -o scan -- python -u bench.py --steps 1 --warmup 0 --layers 2 --no-extra --no-cpu-baseline --no-backward",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_fetch_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_copy -o copy -- python -u bench.py --copy-calibration-mib 1024",
 ]
 
 
@@ -351,8 +353,8 @@ def main():
     if args.write_traffic_profile:
         return write_traffic_profile(args.write_traffic_profile)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences are independent; see the sharding note in the design document)",
+        print("bench.py measures one GPU only: there is no multi-GPU path (the (batch, head) "
+              "sequences are independent, so they would shard over GPUs with no communication)",
               file=sys.stderr)
         return 2
 
