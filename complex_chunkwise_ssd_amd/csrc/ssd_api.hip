@@ -27,8 +27,6 @@ int check_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64
         return SSD_ERR_ODD_N;
     if (N > SSD_MAX_BLOCK || D > SSD_MAX_BLOCK || chunk > SSD_MAX_BLOCK)
         return SSD_ERR_BLOCK_DIMS;
-    if (N > ssd::kNPad)
-        return SSD_ERR_UNSUPPORTED;
     // 32-bit token indices, and 32-bit byte offsets inside one chunk of one sequence
     if (T > (1LL << 30) || batch * H > (1LL << 30))
         return SSD_ERR_UNSUPPORTED;
@@ -45,11 +43,19 @@ int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs
 {
     ssd::ScanParams prm = base;
     prm.groups_per_seq = plan.P;
-    const int64_t grid = seqs * plan.P * plan.ndb;
+    const int64_t grid = seqs * plan.P * plan.ndb * plan.nnb;
     hipLaunchKernelGGL((ssd::scan_kernel<R, LAYOUT>), dim3((unsigned)grid),
                        dim3(ssd::kThreads), 0, stream, prm);
     if (int st = launch_status())
         return st;
+    if (plan.nnb > 1) {  // add up the N slices' partial outputs
+        const int64_t n = (int64_t)prm.B * prm.T * prm.H * prm.D;
+        const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+        hipLaunchKernelGGL(ssd::slice_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const float *)prm.y_part, plan.nnb, n, prm.y);
+        if (int st = launch_status())
+            return st;
+    }
     if (plan.P == 1)
         return SSD_OK;
     const int64_t elems = seqs * (int64_t)prm.N * prm.D;
@@ -63,15 +69,20 @@ int launch_scan(const ssd::ScanParams &base, const ssd::Plan &plan, int64_t seqs
     return launch_status();
 }
 
-// Segment workspace: end states, segment log-decays, chunk-start log-decays.
+// Workspace: segment end states, segment log-decays, chunk-start log-decays (with
+// several segments) and the N slices' partial outputs (N above 64).
 void set_segment_workspace(ssd::ScanParams &prm, const ssd::Plan &plan, void *workspace)
 {
-    if (plan.P == 1)
-        return;
     char *w = (char *)workspace;
-    prm.seg_state = (float *)w;
-    prm.seg_logdecay = (float *)(w + plan.seg_state_bytes);
-    prm.chunk_log = (float *)(w + plan.seg_state_bytes + plan.seg_decay_bytes);
+    if (plan.P > 1) {
+        prm.seg_state = (float *)w;
+        prm.seg_logdecay = (float *)(w + plan.seg_state_bytes);
+        prm.chunk_log = (float *)(w + plan.seg_state_bytes + plan.seg_decay_bytes);
+    }
+    if (plan.nnb > 1)
+        prm.y_part = (float *)(w + plan.seg_state_bytes + plan.seg_decay_bytes +
+                               plan.chunk_log_bytes);
+    prm.nnb = plan.nnb;
 }
 
 template <int LAYOUT>
@@ -111,7 +122,7 @@ int check_backward_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t
 {
     if (int st = check_sizes(batch, T, H, N, D, chunk))
         return st;
-    if (D > 64)
+    if (N > ssd::kNPad || D > 64)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
@@ -333,8 +344,7 @@ const char *ssd_status_string(int status)
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
     case SSD_ERR_UNSUPPORTED:
-        return "size not covered by this build (N <= 64; for gradients also D <= 64; "
-               "mixer H <= 32)";
+        return "size not covered by this build (gradients: N <= 64 and D <= 64; mixer: H <= 32)";
     default: return "unknown status";
     }
 }

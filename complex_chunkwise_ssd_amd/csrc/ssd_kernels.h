@@ -227,6 +227,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int Lk = lane >> 4;
 
     int64_t blk = block_id();
+    const int ns = (int)(blk % p.nnb);  // 64-row slice of the state (N)
+    blk /= p.nnb;
     const int db = (int)(blk % p.ndb);
     blk /= p.ndb;
     const int seg = (int)(blk % p.groups_per_seq);
@@ -247,10 +249,16 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     const int dl = 16 * dtl + Lr;                      // this lane's column in the slice
     const bool dvalid = dl < dsl;
     const int dcol = db * kDBlock + dl;
+    // With N above 64 each workgroup holds 64 state rows, n0 .. n0 + 63: the
+    // state update stays within them, and its y (a sum over n) is a partial sum
+    // that a later pass adds up over the slices.
+    const int n0 = ns * kNPad;
+    const int nsl = p.N - n0 < kNPad ? p.N - n0 : kNPad;  // rows of this slice
+    float *const yout = p.nnb > 1 ? p.y_part + (int64_t)ns * p.B * p.T * p.H * p.D : p.y;
 
     // Loop-invariant lane offsets; masked lanes point past the buffer.
     const int ncol = (tid & 31) * 2;
-    const uint32_t offB = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
+    const uint32_t offB = ncol < nsl ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
     const uint32_t offX = dvalid ? (uint32_t)(4 * Lk) * xrow + dl * (PROJ ? ES : 8u) : kOut;
     const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
 
@@ -266,8 +274,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             for (int r = 0; r < 4; ++r) {
                 const int n = 16 * (2 * nh + i) + 4 * Lk + r;
                 v2f e = v2f{0.f, 0.f};
-                if (n < p.N && dvalid)
-                    e = *(const v2f *)&base[((int64_t)n * p.D + dcol) * 2];
+                if (n < nsl && dvalid)
+                    e = *(const v2f *)&base[((int64_t)(n0 + n) * p.D + dcol) * 2];
                 const v2f hv = cmul(scale, v2f{Hre[i][r], Him[i][r]});
                 Hre[i][r] = hv.x + e.x;
                 Him[i][r] = hv.y + e.y;
@@ -309,18 +317,18 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             const uint32_t rows = (uint32_t)rows_of(c);
             if constexpr (PROJ) {
                 const int64_t t0 = prow0(c);
-                const int64_t hn = (int64_t)h * p.N;
+                const int64_t hn = (int64_t)h * p.N + n0;
                 // rows past the chunk lie past this size (a token row is longer than
                 // both planes), so they still read zero
-                const uint32_t nb = (rows - 1) * brow + imoff + p.N * ES;
+                const uint32_t nb = (rows - 1) * brow + imoff + nsl * ES;
                 nbB = make_buf(at(p.Bt, t0 + hn), nb);
                 nbC = make_buf(at(p.Ct, t0 + hn), nb);
                 nbX = make_buf(at(p.x, t0 + (int64_t)h * p.D + db * kDBlock),
                                (rows - 1) * xrow + dsl * ES);
             } else {
                 const int64_t r0 = tok0(c);
-                nbB = make_buf(p.Bt + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
-                nbC = make_buf(p.Ct + r0 * p.N * 2, (rows - 1) * brow + p.N * 8u);
+                nbB = make_buf(p.Bt + (r0 * p.N + n0) * 2, (rows - 1) * brow + nsl * 8u);
+                nbC = make_buf(p.Ct + (r0 * p.N + n0) * 2, (rows - 1) * brow + nsl * 8u);
                 nbX = make_buf(p.x + (r0 * p.D + db * kDBlock) * 2, (rows - 1) * xrow + dsl * 8u);
             }
         } else {
@@ -388,7 +396,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     // D writes it).
     const buf_t bLog = make_buf(p.chunk_log ? (const void *)(p.chunk_log + bh * p.nc * 2)
                                             : (const void *)p.dt,
-                                p.chunk_log && db == 0 ? (uint32_t)p.nc * 8u : 0u);
+                                p.chunk_log && db == 0 && ns == 0 ? (uint32_t)p.nc * 8u : 0u);
 
     // One wave: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
     auto scan = [&](int c) {
@@ -758,7 +766,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         // ---- store y. Straight-line stores (a tile this wave does not own is aimed
         // past the buffer), so the wait counters stay exact across the loop.
         {
-            const buf_t bY = make_buf(p.y + r0 * p.D + db * kDBlock,
+            const buf_t bY = make_buf(yout + r0 * p.D + db * kDBlock,
                                       (uint32_t)(rows - 1) * yrow + dsl * 4u);
             for (int j = 0; j < (NR + 1) / 2; ++j) {
                 const int lt = 2 * j + nh;
@@ -779,15 +787,15 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     } else {
         const int64_t sidx = bh * p.P + seg;
         out = p.seg_state + sidx * p.N * p.D * 2;
-        if (db == 0 && tid == kScanWave * 64)  // the scan wave holds the segment total
+        if (db == 0 && ns == 0 && tid == kScanWave * 64)  // the scan wave holds the total
             *(v2f *)&p.seg_logdecay[sidx * 2] = seg_log;
     }
     if (out) {
         for (int i = 0; i < 2; ++i)
             for (int r = 0; r < 4; ++r) {
                 const int n = 16 * (2 * nh + i) + 4 * Lk + r;
-                if (n < p.N && dvalid)
-                    *(v2f *)&out[((int64_t)n * p.D + dcol) * 2] = v2f{Hre[i][r], Him[i][r]};
+                if (n < nsl && dvalid)
+                    *(v2f *)&out[((int64_t)(n0 + n) * p.D + dcol) * 2] = v2f{Hre[i][r], Him[i][r]};
             }
     }
 }

@@ -2,7 +2,9 @@
 // C ABI and its tests. Plain C++: no HIP calls.
 //
 // One workgroup walks the chunks of one (batch row, head, sequence segment,
-// 64-wide slice of D) in order, keeping the N x 64 state on chip. When there
+// 64-wide slice of D, 64-row slice of N) in order, keeping its 64 x 64 block of
+// the state on chip. With more than one N slice, each writes a partial y (the
+// output sums over n) and a pass adds the slices up. When there
 // are too few (batch, head) sequences to fill the GPU, each sequence is cut
 // into P segments that the scan runs side by side, segment 0 from the initial
 // state and the others from zero; each records its end state, its total
@@ -43,11 +45,13 @@ struct ScanParams {
     float *seg_logdecay;      // (B, H, P) complex, sum of softplus(dt)*A over a segment
     float *chunk_log;         // (B, H, nc) complex, that sum from the segment start to each
                               // chunk start
+    float *y_part;            // (nnb, B, T, H, D): per-slice partial y when N > 64
     int B, T, H, N, D, Q;
     int nc;    // chunks per sequence
     int P;     // segments per sequence
     int spc;   // chunks per segment
     int ndb;   // 64-wide D slices
+    int nnb;   // 64-row N slices
     int groups_per_seq;  // workgroups per sequence and D slice: the P segments
     int fix_groups;      // fix-up workgroups per (sequence, later segment, D slice)
     int64_t tok_stride;  // in_proj layout: floats between consecutive tokens' rows
@@ -59,10 +63,12 @@ struct Plan {
     int P = 1;
     int spc = 0;
     int ndb = 0;
+    int nnb = 0;
     int fix_groups = 0;
     size_t seg_state_bytes = 0;
     size_t seg_decay_bytes = 0;
     size_t chunk_log_bytes = 0;
+    size_t y_part_bytes = 0;
     size_t workspace_bytes = 0;
 };
 
@@ -86,12 +92,13 @@ inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int
     p.R = Q <= 16 ? 16 : (Q <= 32 ? 32 : 64);
     p.nc = (int)((T + Q - 1) / Q);
     p.ndb = (int)((D + kDBlock - 1) / kDBlock);
+    p.nnb = (int)((N + kNPad - 1) / kNPad);
     if (p.nc <= 0) {
         p.P = 1;
         p.spc = 0;
         return p;
     }
-    int64_t seqs = B * H * p.ndb;
+    int64_t seqs = B * H * p.ndb * p.nnb;
     int64_t want = (kTargetGroups + seqs - 1) / seqs;
     if (want < 1)
         want = 1;
@@ -103,11 +110,13 @@ inline Plan make_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int
         p.seg_state_bytes = align_up((size_t)B * H * p.P * N * D * 8, 256);
         p.seg_decay_bytes = align_up((size_t)B * H * p.P * 8, 256);
         p.chunk_log_bytes = align_up((size_t)B * H * p.nc * 8, 256);
-        const int64_t units = B * H * (p.P - 1) * p.ndb;
+        const int64_t units = B * H * (p.P - 1) * p.ndb;  // fix-up work units
         int64_t g = (kFixTargetGroups + units - 1) / units;
         p.fix_groups = (int)(g < p.spc ? g : p.spc);
     }
-    p.workspace_bytes = p.seg_state_bytes + p.seg_decay_bytes + p.chunk_log_bytes;
+    if (p.nnb > 1)
+        p.y_part_bytes = align_up((size_t)p.nnb * B * T * H * D * 4, 256);
+    p.workspace_bytes = p.seg_state_bytes + p.seg_decay_bytes + p.chunk_log_bytes + p.y_part_bytes;
     return p;
 }
 

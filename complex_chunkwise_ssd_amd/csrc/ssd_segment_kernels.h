@@ -109,137 +109,157 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
     const bool dvalid = dl < dsl;
     const int dcol = db * kDBlock + dl;
 
-    // B operand: the state entering the segment (slot seg - 1 after the prefix
-    // pass), rows k of [Re H ; Im H] at this lane's column.
-    float hb[KSTEPS];
-    {
-        const float *hin = p.seg_state + (bh * p.P + (seg - 1)) * (int64_t)p.N * p.D * 2;
+    // With N above 64 the state is taken in 64-row slices, one after another: the
+    // term is a sum over n, so each slice's share is added to y in turn.
+    for (int ns = 0; ns < p.nnb; ++ns) {
+        const int n0 = ns * kNPad;
+        const int nsl = p.N - n0 < kNPad ? p.N - n0 : kNPad;  // rows of this slice
+
+        // B operand: the state entering the segment (slot seg - 1 after the prefix
+        // pass), rows k of [Re H ; Im H] of this slice at this lane's column.
+        float hb[KSTEPS];
+        {
+            const float *hin = p.seg_state + (bh * p.P + (seg - 1)) * (int64_t)p.N * p.D * 2;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const int k = 16 * (s >> 2) + 4 * Lk + (s & 3);
-            const int n = k < kNPad ? k : k - kNPad;
-            hb[s] = n < p.N && dvalid ? hin[((int64_t)n * p.D + dcol) * 2 + (k < kNPad ? 0 : 1)]
-                                      : 0.f;
-        }
-    }
-
-    const uint32_t prow = (uint32_t)p.tok_stride * ES;                  // in_proj row bytes
-    const uint32_t brow = PROJ ? prow : (uint32_t)(p.H * p.N) * 8u;     // C_t row bytes
-    const uint32_t drow = PROJ ? prow : (uint32_t)p.H * 4u;             // dt row bytes
-    const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;
-    const uint32_t imoff = (uint32_t)(p.H * p.N) * ES;                  // PROJ: Im plane
-    const int64_t bt0 = (int64_t)b * p.T;
-    auto at = [&](const float *base, int64_t e) { return (const void *)((const char *)base + e * ES); };
-    auto rows_of = [&](int c) { return p.Q < p.T - c * p.Q ? p.Q : p.T - c * p.Q; };
-
-    // C rows: thread (row r0 + tid / 32 of each pass, complex pair ncol/2 .. +1)
-    const int ncol = (tid & 31) * 2;
-    const uint32_t offC = ncol < p.N ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
-    const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
-
-    // A chunk's inputs in registers: dt (wave 0's lanes), C rows, and the y
-    // values this lane will update. fetch(c) issues the loads for chunk c; past
-    // the group's last chunk every buffer is empty, so the loads still issue
-    // (the wait counters stay exact) and read zero.
-    struct Inputs {
-        float dt;
-        v4f cv[R / ROWS_PER_PASS];
-        float yv[NR][4];
-    };
-    auto ybuf = [&](int c) {
-        const int64_t tok = bt0 + (int64_t)c * p.Q;
-        return c < c_end ? make_buf(p.y + (tok * p.H + h) * (int64_t)p.D + db * kDBlock,
-                                    (uint32_t)(rows_of(c) - 1) * yrow + (uint32_t)dsl * 4u)
-                         : make_buf(p.y, 0u);
-    };
-    auto fetch = [&](int c, Inputs &in) {
-        const bool live = c < c_end;
-        const uint32_t rows = live ? (uint32_t)rows_of(c) : 1u;
-        const int64_t tok = bt0 + (int64_t)(live ? c : c_begin) * p.Q;
-        const void *dt0 = PROJ ? at(p.dt, tok * p.tok_stride + h) : (const void *)(p.dt + tok * p.H + h);
-        const buf_t bT = make_buf(dt0, live ? (rows - 1) * drow + ES : 0u);
-        const uint32_t od = w == 0 ? (uint32_t)lane * drow : kOut;
-        in.dt = BF16 ? bf16_lo(buf_load_u16(bT, od)) : buf_load1(bT, od);
-        const void *c0 = PROJ ? at(p.Ct, tok * p.tok_stride + (int64_t)h * p.N)
-                              : (const void *)(p.Ct + (tok * p.H + h) * (int64_t)p.N * 2);
-        const buf_t bC = make_buf(c0, live ? (rows - 1) * brow + (PROJ ? imoff : 0u) +
-                                                 p.N * (PROJ ? ES : 8u)
-                                           : 0u);
-#pragma unroll
-        for (int i = 0; i < R / ROWS_PER_PASS; ++i) {
-            const uint32_t o = offC + (uint32_t)(ROWS_PER_PASS * i) * brow;
-            if constexpr (BF16) {
-                const uint32_t re = buf_load_u32(bC, o), im = buf_load_u32(bC, o + imoff);
-                in.cv[i] = v4f{bf16_lo(re), bf16_lo(im), bf16_hi(re), bf16_hi(im)};
-            } else if constexpr (PROJ) {
-                const v2f re = buf_load2(bC, o), im = buf_load2(bC, o + imoff);
-                in.cv[i] = v4f{re.x, im.x, re.y, im.y};
-            } else {
-                in.cv[i] = buf_load4(bC, o);
+            for (int s = 0; s < KSTEPS; ++s) {
+                const int k = 16 * (s >> 2) + 4 * Lk + (s & 3);
+                const int n = k < kNPad ? k : k - kNPad;
+                hb[s] = n < nsl && dvalid
+                            ? hin[((int64_t)(n0 + n) * p.D + dcol) * 2 + (k < kNPad ? 0 : 1)]
+                            : 0.f;
             }
         }
-        const buf_t bY = ybuf(c);
-#pragma unroll
-        for (int t = 0; t < NR; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                in.yv[t][r] = buf_load1(bY, offY + (uint32_t)(16 * t + r) * yrow);
-    };
 
-    Inputs nx;
-    fetch(c_begin, nx);
-    for (int c = c_begin; c < c_end; ++c) {
-        const Inputs cur = nx;
-        const uint32_t rows = (uint32_t)rows_of(c);
-        // Lambda_t for the chunk's rows: wave 0 scans a = softplus(dt) A.
-        if (w == 0) {
-            const float sp = softplus_f(cur.dt);
-            const v2f a = (uint32_t)lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
-            v2f lam = a;
-            lam += v2f{row_shr<1>(lam.x), row_shr<1>(lam.y)};
-            lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
-            lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
-            lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
-            // add the totals of the earlier 16-row tiles and the chunk-start log
-            v2f base = *(const v2f *)&p.chunk_log[(bh * p.nc + c) * 2];
-            for (int t = 0; t < NR - 1; ++t) {
-                const v2f tt = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
-                if ((lane >> 4) > t)
-                    base += tt;
+        const uint32_t prow = (uint32_t)p.tok_stride * ES;                  // in_proj row bytes
+        const uint32_t brow = PROJ ? prow : (uint32_t)(p.H * p.N) * 8u;     // C_t row bytes
+        const uint32_t drow = PROJ ? prow : (uint32_t)p.H * 4u;             // dt row bytes
+        const uint32_t yrow = (uint32_t)(p.H * p.D) * 4u;
+        const uint32_t imoff = (uint32_t)(p.H * p.N) * ES;                  // PROJ: Im plane
+        const int64_t bt0 = (int64_t)b * p.T;
+        auto at = [&](const float *base, int64_t e) { return (const void *)((const char *)base + e * ES); };
+        auto rows_of = [&](int c) { return p.Q < p.T - c * p.Q ? p.Q : p.T - c * p.Q; };
+
+        // C rows: thread (row r0 + tid / 32 of each pass, complex pair ncol/2 .. +1)
+        const int ncol = (tid & 31) * 2;
+        const uint32_t offC = ncol < nsl ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
+        const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
+
+        // A chunk's inputs in registers: dt (wave 0's lanes), C rows, and the y
+        // values this lane will update. fetch(c) issues the loads for chunk c; past
+        // the group's last chunk every buffer is empty, so the loads still issue
+        // (the wait counters stay exact) and read zero.
+        struct Inputs {
+            float dt;
+            v4f cv[R / ROWS_PER_PASS];
+            float yv[NR][4];
+        };
+        auto ybuf = [&](int c) {
+            const int64_t tok = bt0 + (int64_t)c * p.Q;
+            return c < c_end ? make_buf(p.y + (tok * p.H + h) * (int64_t)p.D + db * kDBlock,
+                                        (uint32_t)(rows_of(c) - 1) * yrow + (uint32_t)dsl * 4u)
+                             : make_buf(p.y, 0u);
+        };
+        auto fetch = [&](int c, Inputs &in) {
+            const bool live = c < c_end;
+            const uint32_t rows = live ? (uint32_t)rows_of(c) : 1u;
+            const int64_t tok = bt0 + (int64_t)(live ? c : c_begin) * p.Q;
+            const void *dt0 = PROJ ? at(p.dt, tok * p.tok_stride + h) : (const void *)(p.dt + tok * p.H + h);
+            const buf_t bT = make_buf(dt0, live ? (rows - 1) * drow + ES : 0u);
+            const uint32_t od = w == 0 ? (uint32_t)lane * drow : kOut;
+            in.dt = BF16 ? bf16_lo(buf_load_u16(bT, od)) : buf_load1(bT, od);
+            const void *c0 = PROJ ? at(p.Ct, tok * p.tok_stride + (int64_t)h * p.N + n0)
+                                  : (const void *)(p.Ct + ((tok * p.H + h) * (int64_t)p.N + n0) * 2);
+            const buf_t bC = make_buf(c0, live ? (rows - 1) * brow + (PROJ ? imoff : 0u) +
+                                                     nsl * (PROJ ? ES : 8u)
+                                               : 0u);
+#pragma unroll
+            for (int i = 0; i < R / ROWS_PER_PASS; ++i) {
+                const uint32_t o = offC + (uint32_t)(ROWS_PER_PASS * i) * brow;
+                if constexpr (BF16) {
+                    const uint32_t re = buf_load_u32(bC, o), im = buf_load_u32(bC, o + imoff);
+                    in.cv[i] = v4f{bf16_lo(re), bf16_lo(im), bf16_hi(re), bf16_hi(im)};
+                } else if constexpr (PROJ) {
+                    const v2f re = buf_load2(bC, o), im = buf_load2(bC, o + imoff);
+                    in.cv[i] = v4f{re.x, im.x, re.y, im.y};
+                } else {
+                    in.cv[i] = buf_load4(bC, o);
+                }
             }
-            if (lane < R)
-                sE[lane] = cexp_f(lam + base);
-        }
-        block_sync();  // sE ready; the previous chunk's products have read sCp
+            const buf_t bY = ybuf(c);
 #pragma unroll
-        for (int i = 0; i < R / ROWS_PER_PASS; ++i) {
-            const int row = ROWS_PER_PASS * i + (tid >> 5);
-            const v2f e = sE[row];
-            const v2f a0 = cmul(e, v2f{cur.cv[i].x, cur.cv[i].y});
-            const v2f a1 = cmul(e, v2f{cur.cv[i].z, cur.cv[i].w});
-            *(v2f *)&sCp[row * LDK + ncol] = v2f{a0.x, a1.x};
-            *(v2f *)&sCp[row * LDK + kNPad + ncol] = v2f{-a0.y, -a1.y};
-        }
-        block_sync();
-        fetch(c + 1, nx);  // in flight during the products
-        const buf_t bY = ybuf(c);
+            for (int t = 0; t < NR; ++t)
 #pragma unroll
-        for (int t = 0; t < NR; ++t) {
-            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-            const float *arow = sCp + (16 * t + Lr) * LDK + 4 * Lk;
-#pragma unroll
-            for (int u = 0; u < KSTEPS / 4; ++u) {
-                const v4f a4 = *(const v4f *)(arow + 16 * u);
-                acc = mfma_16x16x4(a4.x, hb[4 * u + 0], acc);
-                acc = mfma_16x16x4(a4.y, hb[4 * u + 1], acc);
-                acc = mfma_16x16x4(a4.z, hb[4 * u + 2], acc);
-                acc = mfma_16x16x4(a4.w, hb[4 * u + 3], acc);
+                for (int r = 0; r < 4; ++r)
+                    in.yv[t][r] = buf_load1(bY, offY + (uint32_t)(16 * t + r) * yrow);
+        };
+
+        Inputs nx;
+        fetch(c_begin, nx);
+        for (int c = c_begin; c < c_end; ++c) {
+            const Inputs cur = nx;
+            const uint32_t rows = (uint32_t)rows_of(c);
+            // Lambda_t for the chunk's rows: wave 0 scans a = softplus(dt) A.
+            if (w == 0) {
+                const float sp = softplus_f(cur.dt);
+                const v2f a = (uint32_t)lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
+                v2f lam = a;
+                lam += v2f{row_shr<1>(lam.x), row_shr<1>(lam.y)};
+                lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
+                lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
+                lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
+                // add the totals of the earlier 16-row tiles and the chunk-start log
+                v2f base = *(const v2f *)&p.chunk_log[(bh * p.nc + c) * 2];
+                for (int t = 0; t < NR - 1; ++t) {
+                    const v2f tt = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
+                    if ((lane >> 4) > t)
+                        base += tt;
+                }
+                if (lane < R)
+                    sE[lane] = cexp_f(lam + base);
             }
-            // lane holds rows 16t + 4Lk + r of column dl
+            block_sync();  // sE ready; the previous chunk's products have read sCp
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                buf_store1(bY, offY + (uint32_t)(16 * t + r) * yrow, cur.yv[t][r] + acc[r]);
+            for (int i = 0; i < R / ROWS_PER_PASS; ++i) {
+                const int row = ROWS_PER_PASS * i + (tid >> 5);
+                const v2f e = sE[row];
+                const v2f a0 = cmul(e, v2f{cur.cv[i].x, cur.cv[i].y});
+                const v2f a1 = cmul(e, v2f{cur.cv[i].z, cur.cv[i].w});
+                *(v2f *)&sCp[row * LDK + ncol] = v2f{a0.x, a1.x};
+                *(v2f *)&sCp[row * LDK + kNPad + ncol] = v2f{-a0.y, -a1.y};
+            }
+            block_sync();
+            fetch(c + 1, nx);  // in flight during the products
+            const buf_t bY = ybuf(c);
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+                v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+                const float *arow = sCp + (16 * t + Lr) * LDK + 4 * Lk;
+#pragma unroll
+                for (int u = 0; u < KSTEPS / 4; ++u) {
+                    const v4f a4 = *(const v4f *)(arow + 16 * u);
+                    acc = mfma_16x16x4(a4.x, hb[4 * u + 0], acc);
+                    acc = mfma_16x16x4(a4.y, hb[4 * u + 1], acc);
+                    acc = mfma_16x16x4(a4.z, hb[4 * u + 2], acc);
+                    acc = mfma_16x16x4(a4.w, hb[4 * u + 3], acc);
+                }
+                // lane holds rows 16t + 4Lk + r of column dl
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    buf_store1(bY, offY + (uint32_t)(16 * t + r) * yrow, cur.yv[t][r] + acc[r]);
+            }
         }
+    }  // slices of N
+}
+
+// y = the sum of the per-slice partial outputs (N above 64), slices in order.
+SSD_KERNEL(256) void slice_sum_kernel(const float *part, int nnb, int64_t n, float *y)
+{
+    const int64_t stride = grid_blocks() * 256;
+    for (int64_t e = block_id() * 256 + thread_id(); e < n; e += stride) {
+        float s = part[e];
+        for (int k = 1; k < nnb; ++k)
+            s += part[k * n + e];
+        y[e] = s;
     }
 }
 

@@ -112,10 +112,13 @@ size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, in
  *   workspace    device scratch of at least
  *                ssd_chunk_forward_workspace_bytes(...) bytes, 256-byte
  *                aligned; may be NULL when that size is 0. Its contents on
- *                entry are ignored.
+ *                entry are ignored. It is needed when there are fewer
+ *                (batch, head) sequences than the GPU has compute units (the
+ *                sequences are then cut into segments) and when N > 64 (the
+ *                state is then split into 64-row slices whose partial outputs
+ *                are added up).
  * Constraints: N even (SSD_ERR_ODD_N); N, D, chunk_size <= 256
- * (SSD_ERR_BLOCK_DIMS); this build covers N <= 64 (SSD_ERR_UNSUPPORTED
- * otherwise).
+ * (SSD_ERR_BLOCK_DIMS).
  * Alignment: B_t and C_t 16 bytes; x, A, initial_state, final_state 8 bytes;
  * dt and y 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 copies initial_state (or
@@ -205,7 +208,7 @@ size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, i
  *                  aligned (required whenever T > 0). Contents on entry ignored.
  * The chunk evaluated at once is min(chunk_size, 32) tokens; the result does
  * not depend on chunk_size beyond rounding.
- * Constraints: as ssd_chunk_forward, and D <= 64 (SSD_ERR_UNSUPPORTED).
+ * Constraints: as ssd_chunk_forward, and N <= 64 and D <= 64 (SSD_ERR_UNSUPPORTED).
  * Alignment: complex arrays 8 bytes; dt, grad_y, grad_dt 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 writes grad_final_state (or
  * zeros) to grad_initial_state and zeros to grad_A.
@@ -230,7 +233,7 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
  *                block dl/ddt. Floats past the blocks are not written.
  *   grad_A, grad_initial_state, workspace: as for ssd_chunk_backward (same
  *                workspace size).
- * Constraints: as ssd_chunk_backward (D <= 64 among them).
+ * Constraints: as ssd_chunk_backward (N <= 64 and D <= 64 among them).
  * Alignment: proj, grad_proj, grad_y 4 bytes; A and the states 8 bytes.
  */
 int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,

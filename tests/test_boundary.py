@@ -92,8 +92,14 @@ def test_workspace_checks(lib):
     assert _fwd(lib, ws=ctypes.c_void_p(0x200010), ws_n=need, **args) == ssd.SSD_ERR_ALIGN
 
 
-def test_unsupported_state_size(lib):
-    assert _fwd(lib, N=66, D=4) == ssd.SSD_ERR_UNSUPPORTED
+def test_state_sizes_above_64(lib):
+    # the forward takes N up to 256 in 64-row slices; their partial outputs need
+    # workspace, so a call without one is refused
+    need = lib.ssd_chunk_forward_workspace_bytes(1, 16, 2, 66, 4, 4)
+    assert need >= 2 * 1 * 16 * 2 * 4 * 4
+    assert _fwd(lib, N=66, D=4) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd(lib, N=256, D=4) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd(lib, N=258, D=4) == ssd.SSD_ERR_BLOCK_DIMS
     assert _fwd(lib, N=64, Q=256) != ssd.SSD_ERR_UNSUPPORTED
 
 
@@ -106,6 +112,8 @@ def test_workspace_sizes(lib):
     assert n >= 8 * 16 * 64 * 64 * 8
     assert f(-1, 16, 2, 4, 4, 4) == 0 and f(1, 16, 2, 3, 4, 4) == 0
     assert f(0, 16, 2, 4, 4, 4) == 0 and f(1, 0, 2, 4, 4, 4) == 0
+    # N = 128 at the network shape: two slices' partial outputs, no segments
+    assert f(32, 2048, 16, 128, 64, 64) >= 2 * 32 * 2048 * 16 * 64 * 4
 
 
 def test_empty_batch_is_a_noop(lib):
@@ -200,7 +208,7 @@ def _proj(lib, B=1, T=16, H=2, N=4, D=4, Q=4, S=None, ptrs=True, align=0, ws=Non
 def test_proj_argument_checks(lib):
     assert _proj(lib, S=2 * (4 + 16 + 1) - 2) == ssd.SSD_ERR_SHAPE   # row shorter than its blocks
     assert _proj(lib, N=3) == ssd.SSD_ERR_ODD_N
-    assert _proj(lib, N=66, D=4) == ssd.SSD_ERR_UNSUPPORTED
+    assert _proj(lib, N=66, D=4) == ssd.SSD_ERR_WORKSPACE      # N slices need workspace
     assert _proj(lib, S=1 << 23) == ssd.SSD_ERR_UNSUPPORTED
     assert _proj(lib, ptrs=False) == ssd.SSD_ERR_NULL
     assert _proj(lib, align=4) == ssd.SSD_ERR_ALIGN                  # proj needs 8 bytes

@@ -45,6 +45,11 @@ CASES = [
     (3, 7, 1, 2, 2, 64),       # T < Q
     (1, 300, 1, 8, 8, 128),    # chunk longer than the 64-row block
     (1, 200, 1, 4, 4, 256),
+    (1, 130, 1, 64, 256, 256),  # the largest D and chunk_size
+    (1, 5, 1, 2, 1, 1),         # the smallest N and D
+    (1, 70, 2, 66, 10, 16),     # N above 64: two slices, the second 2 rows
+    (2, 37, 1, 130, 70, 32),    # three N slices and two D slices
+    (1, 45, 1, 256, 8, 64),     # the largest N
 ]
 
 
@@ -176,6 +181,7 @@ def test_emulated_backward_zero_length(emu):
 PROJ_CASES = [
     # B, T, H, N, D, Q, extra floats per row (NaN: must never be read; the row
     # length must be even)
+    (1, 60, 2, 128, 8, 16, 2),     # two N slices from in_proj rows
     (2, 16, 2, 4, 4, 4, 0),
     (1, 97, 2, 8, 6, 32, 6),
     (1, 150, 1, 64, 64, 64, 1),    # several segments

@@ -75,6 +75,12 @@ SMALL = [
     (1, 12, 1, 4, 4, 12),
     (3, 7, 1, 2, 2, 64),
     (4, 300, 4, 32, 64, 48),
+    (1, 300, 1, 64, 256, 256),  # the largest D and chunk_size: four D slices, 64-row blocks
+    (1, 5, 1, 2, 1, 1),         # the smallest N and D, chunk 1
+    (1, 3, 64, 2, 2, 4),        # many heads, one partial chunk
+    (1, 150, 2, 128, 64, 64),   # N above 64: two slices of the state, segments
+    (2, 77, 1, 130, 70, 32),    # three N slices and two D slices
+    (1, 300, 1, 256, 64, 256),  # the largest N with the largest chunk
 ]
 
 
@@ -222,3 +228,22 @@ def test_discretise_matches_oracle(Q):
     if Q:
         l = lam.cpu().numpy()
         assert (np.abs(l - lo) <= 1e-4 + 1e-5 * np.abs(lo)).all()
+
+
+def test_state_above_64_initial_state_and_network_batch():
+    """N = 128 on 32 sequences of 2048 tokens (two slices, no segments) with an
+    initial state: sampled sequences and the final state against the oracle."""
+    B, T, H, N, D = 2, 2048, 16, 128, 64
+    inp = ssd_inputs.layer_case(B, T, H, N, D, seed=21, device="cpu")
+    init = (torch.randn(B, H, N, D, generator=torch.Generator().manual_seed(5)) * 0.1).to(
+        torch.complex64)
+    g = inp.to(DEV)
+    y, fs = ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=64,
+                              initial_state=init.to(DEV))
+    torch.cuda.synchronize()
+    y, fs = y.cpu().numpy(), fs.cpu().numpy()
+    for b, h in [(0, 3), (1, 15)]:
+        one = inp.select(b, h)
+        yo, fo = oracle.scan(one.x, one.A, one.B_t, one.C_t, one.dt,
+                             initial_state=init[b:b + 1, h:h + 1])
+        _check(y[b:b + 1, :, h:h + 1], yo, fs[b:b + 1, h:h + 1], fo, "N=128 (%d, %d)" % (b, h))

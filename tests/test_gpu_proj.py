@@ -43,6 +43,7 @@ CASES = [
     (3, 7, 1, 2, 2, 64, 1),
     (2, 300, 4, 32, 64, 48, 0),
     (1, 260, 2, 64, 64, 256, 6),
+    (2, 90, 2, 128, 32, 32, 2),    # two N slices from in_proj rows
 ]
 
 
