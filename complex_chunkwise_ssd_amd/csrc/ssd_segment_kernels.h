@@ -32,17 +32,23 @@ SSD_KERNEL(256) void segment_prefix_kernel(ScanParams p)
     const int64_t bh = e / nd, k = e - bh * nd;
     float *slot = p.seg_state + (bh * p.P * nd + k) * 2;
     v2f hs = *(const v2f *)slot;
-    // four segments' states are read before any of their slots is written
-    for (int q0 = 1; q0 < p.P; q0 += 4) {
-        v2f sq[4], ef[4];
+    // eight segments' states are read before any of their slots is written (one
+    // memory round trip per eight segments)
+    constexpr int QB = 8;
+    for (int q0 = 1; q0 < p.P; q0 += QB) {
+        v2f sq[QB], lg[QB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < QB; ++j) {
             const int q = q0 + j < p.P ? q0 + j : p.P - 1;
             sq[j] = *(const v2f *)(slot + q * nd * 2);
-            ef[j] = cexp_f(*(const v2f *)&p.seg_logdecay[(bh * p.P + q) * 2]);
+            lg[j] = *(const v2f *)&p.seg_logdecay[(bh * p.P + q) * 2];
         }
+        v2f ef[QB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < QB; ++j)
+            ef[j] = cexp_f(lg[j]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
             if (q0 + j < p.P) {
                 *(v2f *)(slot + (q0 + j - 1) * nd * 2) = hs;
                 hs = cmul(ef[j], hs) + sq[j];
