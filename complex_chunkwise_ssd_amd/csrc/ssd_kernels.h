@@ -18,8 +18,11 @@
 //   Y  += Re(M X) + Re(C' H)          M and H feed the next MFMA straight from
 //                                     their accumulator layout
 //   H   = decay H + B^T (decay' X)    K = chunk rows
-// The exponents of L are formed from running sums restarted on each 16-row
-// tile, so no difference of two long running sums is ever taken.
+// The complex-by-complex products (G and the state update) take three real
+// MFMAs per complex product (Gauss's form) instead of four; the products whose
+// real part alone is needed take two. The exponents of L are formed from
+// running sums restarted on each 16-row tile, so no difference of two long
+// running sums is ever taken.
 #pragma once
 
 #include <ssd_device.h>
@@ -204,7 +207,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     SSD_LDS float sB[R * LDI];                // B[s][n] interleaved (re, im)
     SSD_LDS float sC[R * LDI];                // C[l][n]
     SSD_LDS float sP[R * LDI];                // exp(Lam[l]) C[l][n] as (re, -im)
-    SSD_LDS v4f sMre[NT * 64], sMim[NT * 64]; // M tiles (re, -im), lane-major
+    // M tiles (re, -im), lane-major; slots NT .. NT + NSPLIT - 1 hold the second K
+    // halves of the tiles k >= NWHOLE (their first halves sit in slot k)
+    SSD_LDS v4f sMre[(NT + NSPLIT) * 64], sMim[(NT + NSPLIT) * 64];
     SSD_LDS v4f sYx[4 * NR * 64];             // partial-y exchange
     SSD_LDS v4f sLdre[NR * 64], sLdim[NR * 64];  // L on diagonal tiles, lane-major
     SSD_LDS v2f sDout[R];      // exp(sum of a over rows s+1 .. chunk end)
@@ -300,8 +305,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     v4f pB[LOADS], pC[LOADS];
     float pdt = 0.f;
     XT pX[NR][4];
-    // The next chunk's loads are spread over the MFMA steps of phase 1 (a burst of
-    // them would hold each wave's in-order issue). Item i < LOADS: a B_t block;
+    // The next chunk's loads are spread over MFMA steps (a burst of them would hold
+    // each wave's in-order issue). Item i < LOADS: a B_t block;
     // then the C_t blocks; then x at (q, j).
     constexpr int NLOAD = 2 * LOADS + 4 * NR;
     buf_t nbB, nbC, nbX;
@@ -375,10 +380,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         fetch_begin(c);
         static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
     };
-    // The B_t and C_t items go out with the state steps of phase 1 and the x items
-    // with the Re(M X) steps of phase 2 (x of the next chunk then shares no
-    // registers' lifetime with phase 1).
-    constexpr int NBC = 2 * LOADS;
+    // Complex layout: all of them go out with the Re(M X) steps of phase 2, so the
+    // next chunk's inputs share no registers' lifetime with phase 1. In_proj
+    // layouts (twice the B_t and C_t load instructions, half the phase 2 MFMAs):
+    // the B_t and C_t items go out with the state steps of phase 1.
+    constexpr int NBC = PROJ ? 2 * LOADS : 0;  // items the state steps issue
     constexpr int PER_S = (NBC + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
@@ -525,13 +531,6 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
                 X[q][j] = pX[q][j];
-        if (NSPLIT > 0 && tid < NSPLIT * 64 * 2) {
-            const int slot = NWHOLE * 64 + (tid & (NSPLIT * 64 - 1));
-            if (tid < NSPLIT * 64)
-                sMre[slot] = v4f{0.f, 0.f, 0.f, 0.f};
-            else
-                sMim[slot] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
         block_sync();
         const bool more = c + 1 < c_end;
         fetch_dt(c + 1);
@@ -546,10 +545,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             auto produce = [&](auto kc, auto q0c, auto q1c) {
                 constexpr int k = decltype(kc)::value;
                 constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
-                // G^T[s][l] = sum_n B[s][n] C[l][n]: re = Bre Cre - Bim Cim,
-                // im = Bre Cim + Bim Cre (the second sum kept apart to avoid negations).
-                v4f gre = v4f{0.f, 0.f, 0.f, 0.f}, gim = v4f{0.f, 0.f, 0.f, 0.f};
-                v4f gsub = v4f{0.f, 0.f, 0.f, 0.f};
+                // G^T[s][l] = sum_n B[s][n] C[l][n] with three real products per
+                // complex one (Gauss): P1 = sum Bre Cre, P2 = sum Bim Cim,
+                // P3 = sum (Bre + Bim)(Cre + Cim); re = P1 - P2, im = P3 - P1 - P2.
+                v4f p1 = v4f{0.f, 0.f, 0.f, 0.f}, p2 = v4f{0.f, 0.f, 0.f, 0.f};
+                v4f p3 = v4f{0.f, 0.f, 0.f, 0.f};
                 constexpr int Q0 = decltype(q0c)::value, Q1 = decltype(q1c)::value;
                 // operand blocks of half-step h (B and C rows, two n each), in flight one
                 // half-step ahead
@@ -569,14 +569,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     const float bre[2] = {bb.x, bb.z}, bim[2] = {bb.y, bb.w};
                     const float cre[2] = {cc.x, cc.z}, cim[2] = {cc.y, cc.w};
                     for (int j = 0; j < 2; ++j) {
-                        gre = mfma_16x16x4(bre[j], cre[j], gre);
-                        gsub = mfma_16x16x4(bim[j], cim[j], gsub);
-                        gim = mfma_16x16x4(bre[j], cim[j], gim);
-                        gim = mfma_16x16x4(bim[j], cre[j], gim);
+                        p1 = mfma_16x16x4(bre[j], cre[j], p1);
+                        p2 = mfma_16x16x4(bim[j], cim[j], p2);
+                        p3 = mfma_16x16x4(bre[j] + bim[j], cre[j] + cim[j], p3);
                     }
                     sched_fence();
                 });
-                gre -= gsub;
+                const v4f gre = p1 - p2, gim = p3 - p1 - p2;
                 // Accumulator element r of this lane: s = 16 st + 4 Lk + r, l = 16 lt + Lr.
                 v4f mre, mim;
                 if constexpr (st == lt) {
@@ -593,17 +592,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                         mim[r] = -(gre[r] * L.y + gim[r] * L.x);
                     }
                 }
-                if constexpr (k < NWHOLE) {
-                    sMre[k * 64 + lane] = mre;
-                    if constexpr (!PROJ)
-                        sMim[k * 64 + lane] = mim;
-                } else {
-                    for (int r = 0; r < 4; ++r) {
-                        lds_add(&((float *)sMre)[(k * 64 + lane) * 4 + r], mre[r]);
-                        if constexpr (!PROJ)
-                            lds_add(&((float *)sMim)[(k * 64 + lane) * 4 + r], mim[r]);
-                    }
-                }
+                // a split tile's halves go to two slots (plain stores; the consumer adds them)
+                constexpr int slot = k < NWHOLE || Q0 == 0 ? k : NT + (k - NWHOLE);
+                sMre[slot * 64 + lane] = mre;
+                if constexpr (!PROJ)
+                    sMim[slot * 64 + lane] = mim;
             };
             using I0 = std::integral_constant<int, 0>;
             using I2 = std::integral_constant<int, 2>;
@@ -672,13 +665,18 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 }
             };
             load(0, ob[0], od[0]);
-            v2f xs[4];
+            // complex x, three real products per complex one (Gauss): with x' = decay' o x,
+            // k1 = (Bre + Bim) x're, k2 = Bim (x're + x'im), k3 = Bre (x'im - x're);
+            // the update's re = k1 - k2 and im = k1 + k3, k1 summed apart and added to both
+            float xr[4], xn[4], xd[4];
+            v4f K1[2];
+            for (int i = 0; i < 2; ++i)
+                K1[i] = v4f{0.f, 0.f, 0.f, 0.f};
             static_for<0, 2 * NR>([&](auto gc) {
                 constexpr int g = decltype(gc)::value, q = g >> 1, i = g & 1, cur = g & 1;
                 if constexpr (g + 1 < 2 * NR)
                     load(g + 1, ob[cur ^ 1], od[q & 1 ^ (i == 1 ? 1 : 0)]);
-                constexpr int SL = NBC;  // items the state steps issue
-                static_for<g * PER_S, ((g + 1) * PER_S < SL ? (g + 1) * PER_S : SL)>(
+                static_for<g * PER_S, ((g + 1) * PER_S < NBC ? (g + 1) * PER_S : NBC)>(
                     [&](auto ic) { fetch_item(ic); });
                 sched_fence();
                 if constexpr (PROJ) {
@@ -690,18 +688,26 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     }
                 } else {
                     if constexpr (i == 0)
-                        for (int j = 0; j < 4; ++j)
-                            xs[j] = cmul(od[q & 1][j], X[q][j]);
+                        for (int j = 0; j < 4; ++j) {
+                            const v2f xs = cmul(od[q & 1][j], X[q][j]);
+                            xr[j] = xs.x;
+                            xn[j] = -xs.x - xs.y;
+                            xd[j] = xs.y - xs.x;
+                        }
                     for (int j = 0; j < 4; ++j) {
                         const v2f bv = ob[cur][j];
-                        Hre[i] = mfma_16x16x4(bv.x, xs[j].x, Hre[i]);
-                        Hre[i] = mfma_16x16x4(bv.y, -xs[j].y, Hre[i]);
-                        Him[i] = mfma_16x16x4(bv.x, xs[j].y, Him[i]);
-                        Him[i] = mfma_16x16x4(bv.y, xs[j].x, Him[i]);
+                        K1[i] = mfma_16x16x4(bv.x + bv.y, xr[j], K1[i]);
+                        Hre[i] = mfma_16x16x4(bv.y, xn[j], Hre[i]);
+                        Him[i] = mfma_16x16x4(bv.x, xd[j], Him[i]);
                     }
                 }
                 sched_fence();
             });
+            if constexpr (!PROJ)
+                for (int i = 0; i < 2; ++i) {
+                    Hre[i] += K1[i];
+                    Him[i] += K1[i];
+                }
         }
         if (more && w == kScanWave)
             scan(c + 1);
@@ -714,26 +720,36 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             auto ydiag = [&](auto nhc) {
                 constexpr int NH = decltype(nhc)::value;
                 constexpr int NK = (NT + 1 - NH) / 2;  // tiles k = NH, NH + 2, ...
-                constexpr int NX = NLOAD - NBC;         // x items of the next chunk
+                constexpr int NX = NLOAD - NBC;         // items left for phase 2
                 constexpr int PER_K = NK > 0 ? (NX + NK - 1) / NK : 0;
-                // M tiles in flight one tile ahead
-                v4f mre[2], mim[2];
-                if constexpr (NK > 0) {
-                    mre[0] = sMre[NH * 64 + lane];
+                // M tiles in flight one tile ahead (a split tile: both halves)
+                v4f mre[2], mim[2], mre2, mim2;
+                auto loadm = [&](auto kc, int b) {
+                    constexpr int k = decltype(kc)::value;
+                    mre[b] = sMre[k * 64 + lane];
                     if constexpr (!PROJ)
-                        mim[0] = sMim[NH * 64 + lane];
-                }
+                        mim[b] = sMim[k * 64 + lane];
+                    if constexpr (k >= NWHOLE) {
+                        mre2 = sMre[(NT + k - NWHOLE) * 64 + lane];
+                        if constexpr (!PROJ)
+                            mim2 = sMim[(NT + k - NWHOLE) * 64 + lane];
+                    }
+                };
+                if constexpr (NK > 0)
+                    loadm(std::integral_constant<int, NH>{}, 0);
                 static_for<0, NK>([&](auto ic) {
                     constexpr int i = decltype(ic)::value, k = 2 * i + NH, cur = i & 1;
                     constexpr int st = tile_st(k, NR), lt = tile_lt(k, NR);
-                    if constexpr (i + 1 < NK) {
-                        mre[cur ^ 1] = sMre[(k + 2) * 64 + lane];
-                        if constexpr (!PROJ)
-                            mim[cur ^ 1] = sMim[(k + 2) * 64 + lane];
-                    }
+                    if constexpr (i + 1 < NK)
+                        loadm(std::integral_constant<int, k + 2>{}, cur ^ 1);
                     constexpr int a = NBC + i * PER_K, e = NBC + (i + 1) * PER_K;
                     static_for<a, (e < NLOAD ? e : NLOAD)>([&](auto xc) { fetch_item(xc); });
                     sched_fence();
+                    if constexpr (k >= NWHOLE) {
+                        mre[cur] += mre2;
+                        if constexpr (!PROJ)
+                            mim[cur] += mim2;
+                    }
                     for (int r = 0; r < 4; ++r) {
                         if constexpr (PROJ) {
                             Y[lt] = mfma_16x16x4(mre[cur][r], X[st][r], Y[lt]);

@@ -39,9 +39,11 @@ SSD_KERNEL(256) void segment_prefix_kernel(ScanParams p)
         v2f sq[QB], lg[QB];
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-            const int q = q0 + j < p.P ? q0 + j : p.P - 1;
-            sq[j] = *(const v2f *)(slot + q * nd * 2);
-            lg[j] = *(const v2f *)&p.seg_logdecay[(bh * p.P + q) * 2];
+            sq[j] = lg[j] = v2f{0.f, 0.f};
+            if (q0 + j < p.P) {  // the same for every thread
+                sq[j] = *(const v2f *)(slot + (q0 + j) * nd * 2);
+                lg[j] = *(const v2f *)&p.seg_logdecay[(bh * p.P + q0 + j) * 2];
+            }
         }
         v2f ef[QB];
 #pragma unroll
