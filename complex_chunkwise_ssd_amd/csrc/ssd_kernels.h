@@ -477,11 +477,14 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before
             // lt; slot NR * NR: the whole chunk (the decay of the state).
             const int st = ri / NR, lt = ri % NR;
+            v2f tau[NR];  // read before any branch: one LDS round trip
+            for (int t = 0; t < NR; ++t)
+                tau[t] = sTau[t];
             if (ri <= NR * NR && (ri == NR * NR || st <= lt)) {
                 v2f z = v2f{0.f, 0.f};
                 for (int t = 0; t < NR; ++t)
                     if (ri == NR * NR || (st < lt ? (t > st && t < lt) : t < lt))
-                        z += sTau[t];
+                        z += tau[t];
                 const v2f e = cexp_f(z);
                 if (ri == NR * NR)
                     sDecay[0] = e;
@@ -489,11 +492,14 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     sK[ri] = e;
             }
         } else if (role == 2) {
+            v2f tau[NR];
+            for (int t = 0; t < NR; ++t)
+                tau[t] = sTau[t];
             if (ri < R) {
                 v2f z = sSig[ri];
                 for (int t = 0; t < NR; ++t)
                     if (t > (ri >> 4))
-                        z += sTau[t];
+                        z += tau[t];
                 sDout[ri] = cexp_f(z);
             }
         } else {
@@ -517,13 +523,20 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         const int rows = rows_of(c);
         const int64_t r0 = tok0(c);
 
-        // ---- stage: chunk inputs into LDS, x into registers.
+        // ---- stage: chunk inputs into LDS, x into registers. The factors of
+        // exp(Lam[row]) are all read before the first store, so one LDS round trip
+        // covers them.
+        v2f fw[LOADS], fk[LOADS];
+        for (int i = 0; i < LOADS; ++i) {
+            fw[i] = sW[16 * i + (tid >> 5)];
+            fk[i] = sK[i * (NR + 1)];
+        }
         for (int i = 0; i < LOADS; ++i) {
             const int row = 16 * i + (tid >> 5);
             *(v4f *)&sB[row * LDI + 2 * ncol] = pB[i];
             const v4f vc = pC[i];
             *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
-            const v2f e = cmul(sW[row], sK[(row >> 4) * (NR + 1)]);  // exp(Lam[row])
+            const v2f e = cmul(fw[i], fk[i]);  // exp(Lam[row])
             const v2f c0 = cmul(e, v2f{vc.x, vc.y}), c1 = cmul(e, v2f{vc.z, vc.w});
             *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
         }
