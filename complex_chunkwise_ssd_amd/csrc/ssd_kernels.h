@@ -380,11 +380,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         fetch_begin(c);
         static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
     };
-    // Complex layout: all of them go out with the Re(M X) steps of phase 2, so the
-    // next chunk's inputs share no registers' lifetime with phase 1. In_proj
-    // layouts (twice the B_t and C_t load instructions, half the phase 2 MFMAs):
-    // the B_t and C_t items go out with the state steps of phase 1.
-    constexpr int NBC = PROJ ? 2 * LOADS : 0;  // items the state steps issue
+    // The first NBC items go out with the state steps of phase 1, the rest with the
+    // Re(M X) steps of phase 2. Complex layout: the B_t items only (the C_t ones too
+    // would outgrow the register budget of the state steps); they then land well
+    // before the next stage instead of queuing behind phase 2's MFMAs. In_proj
+    // layouts (twice the B_t and C_t load instructions, half the phase 2 MFMAs,
+    // real x): all B_t and C_t items.
+    constexpr int NBC = PROJ ? 2 * LOADS : LOADS;  // items the state steps issue
     constexpr int PER_S = (NBC + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
