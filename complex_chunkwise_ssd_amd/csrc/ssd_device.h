@@ -23,6 +23,11 @@ SSD_DEVICE v4f mfma_16x16x4(float a, float b, v4f c)
 
 SSD_DEVICE void block_sync() { __syncthreads(); }
 
+// The hardware's base-2 exponential and logarithm (v_exp_f32, v_log_f32; about
+// 1 ulp, results below the normal range flushed to zero).
+SSD_DEVICE float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+SSD_DEVICE float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 // Orders one wave's shared-memory accesses around this point: the wave's LDS
 // instructions complete in the order they issue, so its earlier writes are
 // seen by its later reads; this only keeps the compiler from moving memory

@@ -34,6 +34,16 @@ namespace ssd {
 
 SSD_DEVICE float softplus_f(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
 
+// The same through the hardware's base-2 exponential and logarithm (v_exp_f32,
+// v_log_f32, about 1 ulp each): exp(u) = 2^(u log2 e), log(1 + e) = log2(1 + e) ln 2.
+// Absolute error below 2e-7 for every v; used where the scan kernel forms its
+// decays, whose exponents are later summed over at most a chunk.
+SSD_DEVICE float softplus_fast(float v)
+{
+    const float e = hw_exp2(-fabsf(v) * 1.44269504f);
+    return fmaxf(v, 0.f) + hw_log2(1.f + e) * 0.693147181f;
+}
+
 SSD_DEVICE v2f cmul(v2f a, v2f b) { return v2f{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
 
 // sin and cos by Cody and Waite's additive range reduction (x - k pi/2 with pi/2
@@ -72,6 +82,17 @@ SSD_DEVICE v2f cexp_f(v2f z)
     float s, c;
     sincos_cw(z.y, &s, &c);
     const float m = expf(z.x);
+    return v2f{m * c, m * s};
+}
+
+// exp(z) with the modulus from v_exp_f32 (relative error about 1 ulp plus
+// |Re z| 2^-24 from rounding Re z log2 e: under 4e-6 wherever e^{Re z} is a
+// normal float). The scan kernel's decays and factors.
+SSD_DEVICE v2f cexp_fast(v2f z)
+{
+    float s, c;
+    sincos_cw(z.y, &s, &c);
+    const float m = hw_exp2(z.x * 1.44269504f);
     return v2f{m * c, m * s};
 }
 
@@ -342,8 +363,15 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             nbX = make_buf(p.x, 0u);
         }
     };
+    // Issue order (complex layout): the B_t items, the first KX x items, the C_t
+    // items, the other x items; the in_proj layouts keep the storage order.
+    constexpr int KX = 2;
     auto fetch_item = [&](auto ic) {
-        constexpr int i = decltype(ic)::value;
+        constexpr int o = decltype(ic)::value;
+        constexpr int i = PROJ || o < LOADS ? o
+                          : o < LOADS + KX  ? 2 * LOADS + (o - LOADS)
+                          : o < 2 * LOADS + KX ? o - KX
+                                               : o;
         if constexpr (i < LOADS) {
             const uint32_t o = offB + (uint32_t)(16 * i) * brow;
             if constexpr (BF16) {  // two n of the real and of the imaginary plane
@@ -380,13 +408,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         fetch_begin(c);
         static_for<0, NLOAD>([&](auto ic) { fetch_item(ic); });
     };
-    // The first NBC items go out with the state steps of phase 1, the rest with the
-    // Re(M X) steps of phase 2. Complex layout: the B_t items only (the C_t ones too
-    // would outgrow the register budget of the state steps); they then land well
-    // before the next stage instead of queuing behind phase 2's MFMAs. In_proj
-    // layouts (twice the B_t and C_t load instructions, half the phase 2 MFMAs,
-    // real x): all B_t and C_t items.
-    constexpr int NBC = PROJ ? 2 * LOADS : LOADS;  // items the state steps issue
+    // The first NBC items (in issue order) go out with the state steps of phase 1,
+    // the rest with the Re(M X) steps of phase 2. Complex layout: the B_t items and
+    // two x items (the C_t ones too would outgrow the register budget of the state
+    // steps); they then land well before the next stage instead of queuing behind
+    // phase 2's MFMAs. In_proj layouts (twice the B_t and C_t load instructions,
+    // half the phase 2 MFMAs, real x): all B_t and C_t items.
+    constexpr int NBC = PROJ ? 2 * LOADS : LOADS + KX;  // items the state steps issue
     constexpr int PER_S = (NBC + 2 * NR - 1) / (2 * NR);
     // The step logits of chunk c (the scan wave's), loaded a phase ahead of the rest.
     auto fetch_dt = [&](int c) {
@@ -409,7 +437,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     // One wave: running sums of a = softplus(dt) A inside each 16-row tile of chunk c.
     auto scan = [&](int c) {
         const int rows = rows_of(c);
-        const float sp = softplus_f(pdt);
+        const float sp = softplus_fast(pdt);
         const v2f a = lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
         // inclusive running sums inside the tile, forwards (lam) and backwards (rs)
         v2f lam = a, rs = a;
@@ -431,7 +459,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         if (lane < R) {
             sLam[lane] = lam;
             sSig[lane] = sig;
-            sAbar[lane] = cexp_f(a);
+            sAbar[lane] = cexp_fast(a);
         }
         if (lane == 0) {
             for (int t = 0; t < NR; ++t)
@@ -454,7 +482,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 const int tile = tid >> 6, ln = tid & 63;
                 const int l = ln & 15, g = 4 * (ln >> 4);
                 const v2f *lam = sLam + 16 * tile;
-                v2f L = l >= g + 3 ? cexp_f(lam[l] - lam[g + 3]) : v2f{0.f, 0.f};
+                v2f L = l >= g + 3 ? cexp_fast(lam[l] - lam[g + 3]) : v2f{0.f, 0.f};
                 v4f lre, lim;
                 lre[3] = L.x;
                 lim[3] = L.y;
@@ -474,7 +502,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         const int role = (tid >> 6) - 4, ri = tid & 63;
         if (role == 0) {
             if (ri < R)
-                sW[ri] = cexp_f(sLam[ri]);
+                sW[ri] = cexp_fast(sLam[ri]);
         } else if (role == 1) {
             // K(st, lt), st < lt: the tiles strictly between; K(lt, lt): the tiles before
             // lt; slot NR * NR: the whole chunk (the decay of the state).
@@ -487,7 +515,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 for (int t = 0; t < NR; ++t)
                     if (ri == NR * NR || (st < lt ? (t > st && t < lt) : t < lt))
                         z += tau[t];
-                const v2f e = cexp_f(z);
+                const v2f e = cexp_fast(z);
                 if (ri == NR * NR)
                     sDecay[0] = e;
                 else
@@ -502,11 +530,11 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 for (int t = 0; t < NR; ++t)
                     if (t > (ri >> 4))
                         z += tau[t];
-                sDout[ri] = cexp_f(z);
+                sDout[ri] = cexp_fast(z);
             }
         } else {
             if (ri < R)
-                sV[ri] = cexp_f(sSig[ri]);
+                sV[ri] = cexp_fast(sSig[ri]);
         }
     };
     static_assert(R <= 64 && NR * NR < 63, "role layout assumes at most 64 rows");

@@ -37,6 +37,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define SSD_KERNEL(threads)
 #define SSD_LDS static __attribute__((aligned(16)))
 
+// Base-2 exponential and logarithm (the gfx950 header uses v_exp_f32 / v_log_f32).
+SSD_DEVICE float hw_exp2(float x) { return exp2f(x); }
+SSD_DEVICE float hw_log2(float x) { return log2f(x); }
+
 // ---------------------------------------------------------------- HIP host API
 typedef void *hipStream_t;
 typedef int hipError_t;
