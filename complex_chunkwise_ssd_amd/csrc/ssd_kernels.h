@@ -243,6 +243,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     SSD_LDS v2f sAbar[R];      // exp(a)
     SSD_LDS v2f sTau[NR + 1];  // tile totals; [NR] = chunk total
     SSD_LDS v2f sDecay[1];     // exp(chunk total)
+    SSD_LDS v2f sE[R];         // exp(sum of a over rows 0 .. l): the C' row factors
 
     const int tid = thread_id();
     const int lane = tid & 63;
@@ -363,14 +364,15 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             nbX = make_buf(p.x, 0u);
         }
     };
-    // Issue order (complex layout): the B_t items, the first KX x items, the C_t
+    // Issue order (complex layout): the C_t items, the first KX x items, the B_t
     // items, the other x items; the in_proj layouts keep the storage order.
     constexpr int KX = 2;
     auto fetch_item = [&](auto ic) {
         constexpr int o = decltype(ic)::value;
-        constexpr int i = PROJ || o < LOADS ? o
+        constexpr int i = PROJ ? o
+                          : o < LOADS       ? LOADS + o
                           : o < LOADS + KX  ? 2 * LOADS + (o - LOADS)
-                          : o < 2 * LOADS + KX ? o - KX
+                          : o < 2 * LOADS + KX ? o - LOADS - KX
                                                : o;
         if constexpr (i < LOADS) {
             const uint32_t o = offB + (uint32_t)(16 * i) * brow;
@@ -428,6 +430,25 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             pdt = buf_load1(bT, od);
     };
 
+    // Rows of C_t (and C' = exp(Lam) C_t, stored as (re, -im)) and of B_t into LDS
+    // from the prefetch registers.
+    auto stage_c = [&]() {
+        v2f e[LOADS];
+        for (int i = 0; i < LOADS; ++i)
+            e[i] = sE[16 * i + (tid >> 5)];
+        for (int i = 0; i < LOADS; ++i) {
+            const int row = 16 * i + (tid >> 5);
+            const v4f vc = pC[i];
+            *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
+            const v2f c0 = cmul(e[i], v2f{vc.x, vc.y}), c1 = cmul(e[i], v2f{vc.z, vc.w});
+            *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
+        }
+    };
+    auto stage_b = [&]() {
+        for (int i = 0; i < LOADS; ++i)
+            *(v4f *)&sB[(16 * i + (tid >> 5)) * LDI + 2 * ncol] = pB[i];
+    };
+
     // The segment's log-decay at each chunk start, for the fix-up pass (one slice of
     // D writes it).
     const buf_t bLog = make_buf(p.chunk_log ? (const void *)(p.chunk_log + bh * p.nc * 2)
@@ -456,10 +477,15 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             tau[t] = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
             tot += tau[t];
         }
+        v2f before = v2f{0.f, 0.f};  // the tiles before this lane's
+        for (int t = 0; t < NR - 1; ++t)
+            if (t < (lane >> 4))
+                before += tau[t];
         if (lane < R) {
             sLam[lane] = lam;
             sSig[lane] = sig;
             sAbar[lane] = cexp_fast(a);
+            sE[lane] = cexp_fast(lam + before);
         }
         if (lane == 0) {
             for (int t = 0; t < NR; ++t)
@@ -546,6 +572,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
             scan(c_begin);
         block_sync();
         factors();
+        stage_c();
+        if constexpr (PROJ)
+            stage_b();
         block_sync();
     }
 
@@ -553,23 +582,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         const int rows = rows_of(c);
         const int64_t r0 = tok0(c);
 
-        // ---- stage: chunk inputs into LDS, x into registers. The factors of
-        // exp(Lam[row]) are all read before the first store, so one LDS round trip
-        // covers them.
-        v2f fw[LOADS], fk[LOADS];
-        for (int i = 0; i < LOADS; ++i) {
-            fw[i] = sW[16 * i + (tid >> 5)];
-            fk[i] = sK[i * (NR + 1)];
-        }
-        for (int i = 0; i < LOADS; ++i) {
-            const int row = 16 * i + (tid >> 5);
-            *(v4f *)&sB[row * LDI + 2 * ncol] = pB[i];
-            const v4f vc = pC[i];
-            *(v4f *)&sC[row * LDI + 2 * ncol] = vc;
-            const v2f e = cmul(fw[i], fk[i]);  // exp(Lam[row])
-            const v2f c0 = cmul(e, v2f{vc.x, vc.y}), c1 = cmul(e, v2f{vc.z, vc.w});
-            *(v4f *)&sP[row * LDI + 2 * ncol] = v4f{c0.x, -c0.y, c1.x, -c1.y};
-        }
+        // ---- stage: the chunk's B_t rows into LDS (complex layout; its C_t rows and
+        // C' went in during the previous chunk's phase 2), x into registers.
+        if constexpr (!PROJ)
+            stage_b();
         XT X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
@@ -757,9 +773,19 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         block_sync();
 
         // ---- phase 2: intra-chunk term Re(M X) = Mre Xre + (-Mim) Xim; the tiles of a
-        // column tile are split between its two waves by parity. Then the next
-        // chunk's decay factors.
+        // column tile are split between its two waves by parity. Behind the MFMAs of
+        // the second tile, the next chunk's C_t rows and C' (all its rows in the
+        // in_proj layouts) go into LDS, which phase 1 has finished reading. Then the
+        // next chunk's decay factors.
         {
+            constexpr int kStageTile = 1;
+            auto stage_next = [&]() {
+                if (more) {
+                    stage_c();
+                    if constexpr (PROJ)
+                        stage_b();
+                }
+            };
             auto ydiag = [&](auto nhc) {
                 constexpr int NH = decltype(nhc)::value;
                 constexpr int NK = (NT + 1 - NH) / 2;  // tiles k = NH, NH + 2, ...
@@ -801,10 +827,14 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                             Y[lt] = mfma_16x16x4(mim[cur][r], X[st][r].y, Y[lt]);
                         }
                     }
+                    if constexpr (i == kStageTile)
+                        stage_next();
                     sched_fence();
                 });
                 if constexpr (NK == 0)
                     static_for<NBC, NLOAD>([&](auto xc) { fetch_item(xc); });
+                if constexpr (NK <= kStageTile)
+                    stage_next();
             };
             if (nh == 0)
                 ydiag(std::integral_constant<int, 0>{});
