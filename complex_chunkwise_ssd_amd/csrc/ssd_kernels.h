@@ -774,11 +774,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
 
         // ---- phase 2: intra-chunk term Re(M X) = Mre Xre + (-Mim) Xim; the tiles of a
         // column tile are split between its two waves by parity. Behind the MFMAs of
-        // the second tile, the next chunk's C_t rows and C' (all its rows in the
-        // in_proj layouts) go into LDS, which phase 1 has finished reading. Then the
-        // next chunk's decay factors.
+        // the first tile, the next chunk's C_t rows and C' (all its rows in the
+        // in_proj layouts) go into LDS, which phase 1 has finished reading; behind
+        // those of the second, the next chunk's decay factors (phase 2 reads none of
+        // the arrays they overwrite), so that their LDS round trips overlap MFMAs.
         {
-            constexpr int kStageTile = 1;
+            constexpr int kStageTile = 0;
+            constexpr int kFactorTile = 1;
             auto stage_next = [&]() {
                 if (more) {
                     stage_c();
@@ -829,12 +831,18 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     }
                     if constexpr (i == kStageTile)
                         stage_next();
+                    if constexpr (i == kFactorTile)
+                        if (more)
+                            factors();
                     sched_fence();
                 });
                 if constexpr (NK == 0)
                     static_for<NBC, NLOAD>([&](auto xc) { fetch_item(xc); });
                 if constexpr (NK <= kStageTile)
                     stage_next();
+                if constexpr (NK <= kFactorTile)
+                    if (more)
+                        factors();
             };
             if (nh == 0)
                 ydiag(std::integral_constant<int, 0>{});
@@ -848,8 +856,6 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                     sYx[(dtl * NR + lt) * 64 + lane] = nh ? Y[2 * j] : Y[2 * j + 1 < NR ? 2 * j + 1 : 0];
             }
         }
-        if (more)
-            factors();
         block_sync();
 
         // ---- store y. Straight-line stores (a tile this wave does not own is aimed
