@@ -193,14 +193,17 @@ constexpr int tile_st(int k, int nr)
 // complex-x steps).
 //
 // Per chunk c (three barriers):
-//   stage   B_t, C_t rows (loaded during chunk c-1) copied into LDS as
-//           interleaved complex, plus C' = exp(Lam) C stored as (re, -im); x
+//   stage   B_t rows (loaded during chunk c-1) copied into LDS as interleaved
+//           complex (its C_t rows and C' = exp(Lam) C, stored as (re, -im), went in
+//           during chunk c-1's phase 2; all rows there in the in_proj layouts); x
 //           stays in the registers it was loaded into.
 //   phase 1 (a) M = (B C^T)^T o L^T on the causal tiles (stored as (re, -im)),
 //           (b) Re(C' H), (c) H = exp(sum a) H + B^T (decay' o x); wave 0 then
-//           forms chunk c+1's per-tile running sums from its dt (already loaded).
-//   phase 2 Re(M X); all threads evaluate chunk c+1's decay factors, at most
-//           one complex exponential each.
+//           forms chunk c+1's per-tile running sums from its dt (already loaded)
+//           and the factors exp(Lam) of its C' rows.
+//   phase 2 Re(M X); behind its first tile of MFMAs chunk c+1's C_t rows and C'
+//           go into LDS, behind its second all threads evaluate chunk c+1's decay
+//           factors, at most one complex exponential each.
 //   store   the two waves sharing a column tile combine their partial y.
 //
 // L on a diagonal 16x16 tile: each lane holds four consecutive s of one row l;
