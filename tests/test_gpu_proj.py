@@ -58,6 +58,47 @@ def test_proj_small_shapes(case):
     _check(y.cpu().numpy(), fs.cpu().numpy(), yo, fo, str(case))
 
 
+# The decay extremes of the complex-layout tests, read from float32 and bfloat16 in_proj
+# rows (B=2, T=300 with a ragged last chunk, H=4, N=D=64, chunk 64): the memoryless
+# limit (Re A = -1e4), pure rotation (Re A = 0, dt = 0), very strong decay
+# (dt ~ N(4, 1)), and slow growth (Re A = +0.02, dt = 0) with the float32-attainable
+# bar of a growing state: 5e-5 times the running maximum of |y| is added.
+PROJ_EXTREMES = ["memoryless", "rotation", "strong", "growth"]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("regime", PROJ_EXTREMES)
+def test_proj_extreme_decay_regimes(regime, bf16):
+    H, N, D = 4, 64, 64
+    seed = 31 + PROJ_EXTREMES.index(regime)
+    proj, A = ssd_inputs.proj_case(2, 300, H, N, D, seed=seed,
+                                   dt_mean=4.0 if regime == "strong" else 0.0)
+    if regime != "strong":
+        re = {"memoryless": -1e4, "rotation": 0.0, "growth": 0.02}[regime]
+        A = torch.complex(torch.full_like(A.real, re), A.imag)
+    if regime in ("rotation", "growth"):
+        proj[..., H * (D + 4 * N):H * (D + 4 * N + 1)] = 0.0
+    if bf16:
+        proj = proj.to(torch.bfloat16)
+    y, fs = ssd.chunk_forward_proj(proj.to(DEV), A.to(DEV), H, N, D, chunk_size=64)
+    torch.cuda.synchronize()
+    inp = ssd_inputs.unpack_proj(proj, A, H, N, D)
+    yo, fo = oracle.scan(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt)
+    y, fs = y.cpu().numpy(), fs.cpu().numpy()
+    what = "%s bf16=%s" % (regime, bf16)
+    if regime != "growth":
+        _check(y, fs, yo, fo, what)
+        return
+    yr = yo.real
+    scale = np.maximum.accumulate(np.abs(yr).max(axis=3, keepdims=True), axis=1)
+    e = np.abs(y - yr)
+    assert np.isfinite(y).all() and (e <= 1e-4 + 1e-4 * np.abs(yr) + 5e-5 * scale).all(), what
+    for comp in (np.real, np.imag):
+        ref = comp(fo)
+        top = np.abs(ref).max(axis=(2, 3), keepdims=True)
+        assert (np.abs(comp(fs) - ref) <= 1e-4 + 1e-4 * np.abs(ref) + 5e-5 * top).all(), what
+
+
 def test_proj_layer_b1_full():
     """One Mamba-3-Lite layer (B=1, T=2048, H=16, N=D=64, chunk 64) in the in_proj layout."""
     proj, A = ssd_inputs.proj_case(1, 2048, 16, 64, 64, seed=1, extra=2)
