@@ -100,6 +100,65 @@ def test_small_shapes_gradients(case, edges):
     _check_all(got, _oracle_grads(inp, gy, gf, init), str(case), B * T)
 
 
+# Decay extremes (B=2, T=300 with a ragged last chunk, H=4, N=D=64, chunk 64, upstream
+# gradients for y and the final state, an initial state): the memoryless limit
+# (Re A = -1e4, every decay underflows), pure rotation (Re A = 0, dt = 0: nothing decays,
+# so every adjoint sums the whole rest of the sequence) and very strong decay
+# (dt ~ N(4, 2)). Strong decay keeps the bar above. Two derived bars:
+# * memoryless, grad dt: the kernel forms dF/da_t from output-side minus input-side row
+#   sums, in which each token's own pair (decay factor 1) cancels only up to rounding,
+#   about 1e-6 at these magnitudes; grad dt = Re(conj(A) ga) sigmoid(dt) multiplies
+#   that by |A| = 1e4, so its absolute term grows by 2e-6 |A_h| (at the workloads'
+#   |A| <= 3 that is under 1e-5);
+# * rotation: undecayed sums over ~300 tokens cancel to values far below the sequence's
+#   largest, where float32 rounding of that largest value remains (a plain float32
+#   reverse walk errs by up to 7.7e-6 of max |grad B_t|), so 5e-5 times the largest
+#   magnitude of that gradient over its (b, h) sequence is added.
+def _close_scaled(name, got, ref, scale):
+    comps = (np.real, np.imag) if np.iscomplexobj(ref) else (lambda v: v,)
+    assert np.isfinite(got).all(), name
+    for comp in comps:
+        e = np.abs(comp(got) - comp(ref))
+        bad = e > ATOL + RTOL * np.abs(comp(ref)) + scale
+        assert not bad.any(), "%s: %d violations, max err %.3e" % (name, int(bad.sum()), e.max())
+
+
+@pytest.mark.parametrize("regime", ["memoryless", "rotation", "strong"])
+def test_backward_extreme_decay_regimes(regime):
+    B, T, H, N, D = 2, 300, 4, 64, 64
+    kw = dict(dt_mean=4.0, dt_scale=2.0) if regime == "strong" else {}
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=51 + len(regime), **kw)
+    A, dt = inp.A, inp.dt
+    if regime != "strong":
+        re = -1e4 if regime == "memoryless" else 0.0
+        A = torch.complex(torch.full_like(A.real, re), A.imag)
+    if regime == "rotation":
+        dt = torch.zeros_like(dt)
+    inp = ssd_inputs.ScanInputs(inp.x, A, inp.B_t, inp.C_t, dt)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=5, with_final=False)
+    gf, init = _edges(B, H, N, D, 6)
+    got = _gpu_grads(inp, 64, gy, gf, init)
+    ref = _oracle_grads(inp, gy, gf, init)
+    if regime == "strong":
+        _check_all(got, ref, regime, B * T)
+        return
+    absA = np.abs(inp.A.numpy())
+    for name, a, r in zip(ref._fields, got, ref):
+        if a is None:
+            continue
+        what = "%s grad %s" % (regime, name)
+        if name == "A":
+            _close(what, a, r, atol=ATOL + 1e-6 * B * T)
+        elif regime == "memoryless":
+            extra = 2e-6 * absA[None, None, :] if name == "dt" else 0.0
+            _close_scaled(what, a, r, extra)
+        else:
+            seq_axes = (1,) + tuple(range(3, r.ndim)) if r.ndim >= 3 and name != "initial_state" \
+                else tuple(range(2, r.ndim))
+            top = np.abs(r).max(axis=seq_axes, keepdims=True)
+            _close_scaled(what, a, r, 5e-5 * top)
+
+
 def test_layer_b1_gradients_full():
     """Single layer B=1, T=2048, H=16, N=D=64: every gradient compared."""
     w = ssd_inputs.WORKLOADS["layer_b1_t2048"]
