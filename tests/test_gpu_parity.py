@@ -142,6 +142,20 @@ def test_extreme_decay_regimes(regime):
         assert np.abs(y - direct).max() <= 1e-4 * (1 + np.abs(direct).max())
 
 
+def test_long_sequence_many_segments():
+    """One sequence of 65,536 tokens (B=1, H=1, N=D=64, chunk 64) from an initial state:
+    256 segments of four chunks run side by side, the prefix pass composes 256 segment
+    states (32 rounds of eight) and the fix-up pass corrects 255 segments; every output
+    and the final state compared."""
+    inp = ssd_inputs.random_case(1, 65536, 1, 64, 64, seed=77)
+    rng = np.random.default_rng(78)
+    init = ((rng.standard_normal((1, 1, 64, 64)) + 1j * rng.standard_normal((1, 1, 64, 64)))
+            * 0.5).astype(np.complex64)
+    y, fs = _gpu(inp, 64, init=init)
+    yo, fo = _oracle(inp, initial_state=init)
+    _check(y, yo, fs, fo, "T=65536, 256 segments")
+
+
 def test_layer_b1_full():
     """Single Mamba-3-Lite layer, B=1, T=2048, H=16, N=D=64, Q=64: every output compared."""
     w = ssd_inputs.WORKLOADS["layer_b1_t2048"]
