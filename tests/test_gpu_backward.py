@@ -159,6 +159,19 @@ def test_backward_extreme_decay_regimes(regime):
             _close_scaled(what, a, r, 5e-5 * top)
 
 
+def test_backward_long_sequence():
+    """One sequence of 65,536 tokens (B=1, H=1, N=D=64): the state and adjoint passes
+    walk 2,048 chunks in order and grad A adds 2,048 per-chunk shares; every gradient
+    compared."""
+    B, T, H, N, D = 1, 65536, 1, 64, 64
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=79)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=80, with_final=False)
+    rng = np.random.default_rng(81)
+    gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+    got = _gpu_grads(inp, 64, gy, gf)
+    _check_all(got, _oracle_grads(inp, gy, gf), "T=65536", B * T)
+
+
 def test_layer_b1_gradients_full():
     """Single layer B=1, T=2048, H=16, N=D=64: every gradient compared."""
     w = ssd_inputs.WORKLOADS["layer_b1_t2048"]
