@@ -197,6 +197,8 @@ int main()
     fails += run(1, 130, 1, 8, 8, 3, true, true);     // many segments
     fails += run(1, 40, 1, 130, 70, 16, true, true);  // N and D slices, segments
     fails += run(2, 9, 1, 256, 3, 4, false, true);    // the largest N, Q < 16
+    fails += run(16, 20, 16, 4, 6, 16, true, true);   // 256 sequences: two chunks per workgroup
+    fails += run(16, 100, 16, 4, 6, 64, true, true);  // the same with 64-row blocks, partial last chunk
     fails += run_bwd(1, 40, 2, 4, 5, 16, true, true, true);     // padded N, D; partial chunk
     fails += run_bwd(1, 70, 1, 64, 64, 64, false, true, true);  // full tiles, R = 32
     fails += run_bwd(2, 9, 1, 2, 3, 4, false, false, false);    // R = 16, no optional arrays
@@ -206,6 +208,7 @@ int main()
     fails += run_proj(1, 150, 1, 64, 64, 64, 1); // full tiles, segments (stride made even)
     fails += run_proj(2, 9, 1, 2, 4, 4, 1);      // Q < 16
     fails += run_proj(1, 70, 1, 128, 6, 32, 1);  // two N slices (row length made even)
+    fails += run_proj(16, 100, 16, 4, 6, 64, 2); // 256 sequences, two chunks per workgroup
     fails += run_bwd_proj(1, 40, 2, 4, 6, 16, 1);   // gradient rows with a spare float
     fails += run_bwd_proj(1, 70, 1, 64, 64, 64, 0); // full tiles
     fails += run_bwd_proj_bf16(1, 40, 2, 4, 6, 16, 1);  // bfloat16 rows, odd row length

@@ -50,6 +50,8 @@ CASES = [
     (1, 70, 2, 66, 10, 16),     # N above 64: two slices, the second 2 rows
     (2, 37, 1, 130, 70, 32),    # three N slices and two D slices
     (1, 45, 1, 256, 8, 64),     # the largest N
+    (16, 40, 16, 4, 6, 16),     # 256 sequences: each workgroup walks several chunks
+    (16, 150, 16, 4, 6, 64),    # the same with 64-row blocks and a partial last chunk
 ]
 
 
@@ -187,6 +189,7 @@ PROJ_CASES = [
     (1, 150, 1, 64, 64, 64, 1),    # several segments
     (2, 45, 2, 10, 70, 16, 4),     # two D slices
     (1, 300, 1, 8, 8, 128, 1),
+    (16, 150, 16, 4, 6, 64, 2),    # 256 sequences, several chunks per workgroup
 ]
 
 
