@@ -192,18 +192,18 @@ constexpr int tile_st(int k, int nr)
 // Re M and the state update only (decay o B)^T x (half the MFMAs of the
 // complex-x steps).
 //
-// Per chunk c (three barriers):
-//   stage   B_t rows (loaded during chunk c-1) copied into LDS as interleaved
-//           complex (its C_t rows and C' = exp(Lam) C, stored as (re, -im), went in
-//           during chunk c-1's phase 2; all rows there in the in_proj layouts); x
-//           stays in the registers it was loaded into.
+// Per chunk c (two barriers, after phase 1 and after phase 2):
+//   stage   x moves into the registers phase 1 reads (its B_t and C_t rows and
+//           C' = exp(Lam) C, stored as (re, -im), went into LDS during chunk c-1's
+//           phase 2, before its closing barrier, so no barrier is needed here).
 //   phase 1 (a) M = (B C^T)^T o L^T on the causal tiles (stored as (re, -im)),
 //           (b) Re(C' H), (c) H = exp(sum a) H + B^T (decay' o x); wave 0 then
 //           forms chunk c+1's per-tile running sums from its dt (already loaded)
 //           and the factors exp(Lam) of its C' rows.
 //   phase 2 Re(M X); behind its first tile of MFMAs chunk c+1's C_t rows and C'
 //           go into LDS, behind its second all threads evaluate chunk c+1's decay
-//           factors, at most one complex exponential each.
+//           factors, at most one complex exponential each; at its end chunk c+1's
+//           B_t rows go in (phase 1 of chunk c has finished reading all of these).
 //   store   the two waves sharing a column tile combine their partial y.
 //
 // L on a diagonal 16x16 tile: each lane holds four consecutive s of one row l;
@@ -576,8 +576,7 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         block_sync();
         factors();
         stage_c();
-        if constexpr (PROJ)
-            stage_b();
+        stage_b();
         block_sync();
     }
 
@@ -585,15 +584,13 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
         const int rows = rows_of(c);
         const int64_t r0 = tok0(c);
 
-        // ---- stage: the chunk's B_t rows into LDS (complex layout; its C_t rows and
-        // C' went in during the previous chunk's phase 2), x into registers.
-        if constexpr (!PROJ)
-            stage_b();
+        // ---- stage: x into the registers phase 1 reads. The chunk's rows are in LDS
+        // already (staged in the previous chunk's phase 2 or the prologue, before a
+        // barrier), so phase 1 starts without one.
         XT X[NR][4];  // x[s][dcol] with s = 16 q + 4 Lk + j
         for (int q = 0; q < NR; ++q)
             for (int j = 0; j < 4; ++j)
                 X[q][j] = pX[q][j];
-        block_sync();
         const bool more = c + 1 < c_end;
         fetch_dt(c + 1);
         fetch_begin(c + 1);
@@ -858,6 +855,9 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 if (lt < NR)
                     sYx[(dtl * NR + lt) * 64 + lane] = nh ? Y[2 * j] : Y[2 * j + 1 < NR ? 2 * j + 1 : 0];
             }
+            if constexpr (!PROJ)
+                if (more)
+                    stage_b();
         }
         block_sync();
 
