@@ -7,7 +7,9 @@ code: the oracle is the plain sequential recurrence written in C
 
 Functions
 ---------
-build(out_dir=None, extra_cflags=(), source=None) -> path of the shared object
+build(out_path=None, extra_cflags=(), source=None) -> path of the shared object
+build_timing(out_path) -> path of a float (complex64) build at -O3 -march=native,
+    used only to time the plain recurrence as the CPU baseline
 scan(x, A, B_t, C_t, dt, initial_state=None, threads=0, lib=None)
     -> (y complex128 (B,T,H,D), final_state complex128 (B,H,N,D))
 discretise(dt, A, chunk=0, lib=None)
@@ -18,7 +20,8 @@ scan_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None,
        sum(grad_y * y.real) + sum(Re(conj(grad_final_state) * final_state)),
        complex ones as dl/dRe + i dl/dIm (torch's convention), in float64
 head_mix(y, W, lib=None) -> z float64, same shape as y (..., H, D):
-    z[..., i, :] = sum_j W[i, j] y[..., j, :]   (the MIMO head mixer)
+    with F = H * D and each token's heads flattened head-major (k = h*D + d),
+    z[..., o] = sum_k W[o, k] y[..., k] for a dense (F, F) W (the MIMO mixer)
 head_mix_backward(y, W, grad_z, lib=None) -> (grad_y, grad_W) float64
 """
 
@@ -50,6 +53,13 @@ def build(out_path: str | None = None, extra_cflags=(), source: str | None = Non
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
     return out_path
+
+
+def build_timing(out_path: str) -> str:
+    """The same source with the recurrence in float (the pages' complex64),
+    -O3 -march=native for the host it runs on: the timed CPU baseline. The
+    outputs are still returned as float64 arrays; no parity check uses it."""
+    return build(out_path, extra_cflags=("-O3", "-march=native", "-DORACLE_REAL=float"))
 
 
 def _bind(lib):
@@ -207,14 +217,16 @@ def _mix_operands(y, W):
     if yf.ndim < 2:
         raise ValueError("y must be (..., H, D)")
     H, D = yf.shape[-2:]
-    if Wf.shape != (H, H):
-        raise ValueError("W must be (H, H) = (%d, %d)" % (H, H))
+    F = H * D
+    if Wf.shape != (F, F):
+        raise ValueError("W must be (H*D, H*D) = (%d, %d)" % (F, F))
     M = int(np.prod(yf.shape[:-2], dtype=np.int64))
     return yf, Wf, M, H, D
 
 
 def head_mix(y, W, lib=None):
-    """z[..., i, :] = sum_j W[i, j] y[..., j, :] in double, from float32 inputs."""
+    """z[..., o] = sum_k W[o, k] y[..., k] over the flattened heads (k = h*D + d),
+    in double, from float32 inputs."""
     lib = lib or load()
     yf, Wf, M, H, D = _mix_operands(y, W)
     z = np.zeros(yf.shape, np.float64)
@@ -232,7 +244,7 @@ def head_mix_backward(y, W, grad_z, lib=None):
     if gzf.shape != yf.shape:
         raise ValueError("grad_z must have the shape of y")
     gy = np.zeros(yf.shape, np.float64)
-    gW = np.zeros((H, H), np.float64)
+    gW = np.zeros((H * D, H * D), np.float64)
     rc = lib.oracle_head_mix_backward(yf.ctypes.data, Wf.ctypes.data, gzf.ctypes.data, M, H, D,
                                       gy.ctypes.data, gW.ctypes.data)
     if rc != 0:

@@ -60,7 +60,13 @@
 #include <omp.h>
 #endif
 
-typedef double complex cplx;
+/* Working precision of the recurrence: double for every parity use. A float
+ * build (-DORACLE_REAL=float, the pages' complex64) exists only to time the
+ * plain recurrence as the CPU baseline; nothing compares against it. */
+#ifndef ORACLE_REAL
+#define ORACLE_REAL double
+#endif
+typedef ORACLE_REAL complex cplx;
 
 static double softplus(double v)
 {
@@ -285,57 +291,85 @@ int oracle_scan_backward(const float *x, const float *A, const float *Bt, const 
     return failed ? -2 : 0;
 }
 
-/* MIMO head mixer after the scan -- index.html lab 02 "MIMO MIXER" (a 16 x 16
- * fully connected mixer across the SSM heads, 1024 -> 1024 as 16 heads of 64,
- * identity at initialisation), the AGENTS page "Knows cold" item 2, and the
- * in_proj -> scan -> MIMO -> out_proj order of the "Extending" guide, Path A.
- * Read as one H x H real matrix shared by every token and every head-dim
- * channel:
- *     z[m, i, d] = sum_j W[i, j] y[m, j, d]
- * y, z (M, H, D) with M = batch * T tokens; W (H, H) row-major. */
+/* MIMO head mixer after the scan -- index.html lab 02 "MIMO MIXER" (a fully
+ * connected mixer across the 16 SSM heads, 1024 -> 1024 as 16 heads of 64
+ * channels, identity (eye_) at initialisation, 240 off-diagonal head-to-head
+ * links), the AGENTS page "Knows cold" item 2, the in_proj -> scan -> MIMO ->
+ * out_proj order of the "Extending" guide (Path A), and the model's parameter
+ * count in the "Extending" guide's documentation rule (433,662,400, which
+ * holds only with a dense 1024 x 1024 matrix in each of the 28 layers).
+ * A token's H heads of D channels are flattened head-major, k = h * D + d,
+ * and mapped by one dense real F x F matrix (F = H * D), without bias:
+ *     z[m, o] = sum_k W[o, k] y[m, k]
+ * y, z (M, F) with M = batch * T tokens; W (F, F) row-major (row o holds the
+ * weights of output o, as a linear layer stores them). Each block
+ * W[i*D:(i+1)*D, j*D:(j+1)*D] is the link from head j to head i. */
 int oracle_head_mix(const float *y, const float *W, int64_t M, int64_t H, int64_t D, double *z)
 {
     if (!y || !W || !z || M < 0 || H <= 0 || D <= 0)
         return -1;
+    const int64_t F = H * D;
+#pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
-        for (int64_t i = 0; i < H; ++i)
-            for (int64_t d = 0; d < D; ++d) {
-                double acc = 0.0;
-                for (int64_t j = 0; j < H; ++j)
-                    acc += (double)W[i * H + j] * (double)y[(m * H + j) * D + d];
-                z[(m * H + i) * D + d] = acc;
-            }
+        for (int64_t o = 0; o < F; ++o) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < F; ++k)
+                acc += (double)W[o * F + k] * (double)y[m * F + k];
+            z[m * F + o] = acc;
+        }
     return 0;
 }
 
 /* Gradients of l = sum gz * z for the mixer above, by the chain rule on its
  * definition:
- *     gy[m, j, d] = sum_i W[i, j] gz[m, i, d]
- *     gW[i, j]    = sum_{m, d} gz[m, i, d] y[m, j, d]
- * Either output may be NULL. */
+ *     gy[m, :] = sum_o gz[m, o] W[o, :]        (gy = W^T gz per token)
+ *     gW       = sum_m gz[m, :] (outer) y[m, :]
+ * Each sum runs over its index in increasing order; the loops are arranged so
+ * that the rows of W and y are read in storage order. Either output may be
+ * NULL. */
 int oracle_head_mix_backward(const float *y, const float *W, const float *gz, int64_t M,
                              int64_t H, int64_t D, double *gy, double *gW)
 {
     if (!y || !W || !gz || M < 0 || H <= 0 || D <= 0)
         return -1;
-    if (gy)
-        for (int64_t m = 0; m < M; ++m)
-            for (int64_t j = 0; j < H; ++j)
-                for (int64_t d = 0; d < D; ++d) {
-                    double acc = 0.0;
-                    for (int64_t i = 0; i < H; ++i)
-                        acc += (double)W[i * H + j] * (double)gz[(m * H + i) * D + d];
-                    gy[(m * H + j) * D + d] = acc;
-                }
-    if (gW)
-        for (int64_t i = 0; i < H; ++i)
-            for (int64_t j = 0; j < H; ++j) {
-                double acc = 0.0;
-                for (int64_t m = 0; m < M; ++m)
-                    for (int64_t d = 0; d < D; ++d)
-                        acc += (double)gz[(m * H + i) * D + d] * (double)y[(m * H + j) * D + d];
-                gW[i * H + j] = acc;
+    const int64_t F = H * D;
+    if (gy) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            double *row = gy + m * F;
+            for (int64_t k = 0; k < F; ++k)
+                row[k] = 0.0;
+            for (int64_t o = 0; o < F; ++o) {
+                const double g = (double)gz[m * F + o];
+                for (int64_t k = 0; k < F; ++k)
+                    row[k] += g * (double)W[o * F + k];
             }
+        }
+    }
+    if (gW) {
+        /* every thread owns whole rows o of gW and adds the outer products
+         * token by token */
+#pragma omp parallel for schedule(static)
+        for (int64_t o = 0; o < F; ++o)
+            for (int64_t k = 0; k < F; ++k)
+                gW[o * F + k] = 0.0;
+#pragma omp parallel
+        {
+#ifdef _OPENMP
+            const int64_t nth = omp_get_num_threads(), me = omp_get_thread_num();
+#else
+            const int64_t nth = 1, me = 0;
+#endif
+            const int64_t o0 = F * me / nth, o1 = F * (me + 1) / nth;
+            for (int64_t m = 0; m < M; ++m)
+                for (int64_t o = o0; o < o1; ++o) {
+                    const double g = (double)gz[m * F + o];
+                    double *row = gW + o * F;
+                    for (int64_t k = 0; k < F; ++k)
+                        row[k] += g * (double)y[m * F + k];
+                }
+        }
+    }
     return 0;
 }
 

@@ -205,15 +205,15 @@ def pack_proj_grads(gx, gB, gC, gdt, S):
     return rows
 
 
-def mix_case(shape, seed, device="cpu", spread=0.1):
+def mix_case(shape, seed, device="cpu", spread=0.02):
     """Inputs of the MIMO head mixer: y and the upstream gradient gz of the
-    given (..., H, D) shape, standard normal float32, and W = identity plus
-    spread * N(0, 1) per entry (the pages start the mixer at the identity and
-    let training grow cross-head links; the perturbation stands in for a
-    trained mixer). Draw order: W noise, y, gz."""
+    given (..., H, D) shape, standard normal float32, and the dense (F, F)
+    weight W = identity + spread * N(0, 1) per entry, F = H * D (the pages start
+    the mixer at the identity and let training grow the cross-head links; the
+    perturbation stands in for a trained mixer). Draw order: W noise, y, gz."""
     g = _gen(seed, device)
-    H = shape[-2]
-    W = torch.eye(H, device=device) + spread * torch.randn(H, H, generator=g, device=device)
+    F = shape[-2] * shape[-1]
+    W = torch.eye(F, device=device) + spread * torch.randn(F, F, generator=g, device=device)
     y = torch.randn(*shape, generator=g, device=device)
     gz = torch.randn(*shape, generator=g, device=device)
     return y, W.contiguous(), gz
