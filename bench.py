@@ -108,26 +108,69 @@ def write_traffic_profile(root):
     return 0
 
 
-def cpu_baseline(layer0, batch_rows=32):
-    """The oracle as it stands, on a bounded sample of layer 0: batch rows
-    0..batch_rows-1, all heads, full T (host cores, OpenMP over sequences)."""
-    import oracle
-    x, A, B_t, C_t, dt = (layer0.x[:batch_rows].cpu(), layer0.A.cpu(), layer0.B_t[:batch_rows].cpu(),
-                          layer0.C_t[:batch_rows].cpu(), layer0.dt[:batch_rows].cpu())
+def _cpu_model():
     try:
-        cores = len(os.sched_getaffinity(0))
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layer0, rows_all=32, rows_one=2):
+    """The oracle's plain recurrence timed on the host cores, on a bounded sample
+    of layer 0 (all 16 heads, full T): a float (complex64) build at -O3
+    -march=native, compiled here for this host, on every core the process may
+    use (batch rows 0..rows_all-1, OpenMP over sequences) and on one thread
+    (rows 0..rows_one-1); and the double-precision parity build as it is used
+    by the tests, on every core. Inputs are on the host before the clock starts."""
+    import tempfile
+
+    import oracle
+    try:
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        cores = os.cpu_count()
-    lib = oracle.load()
-    threads = min(cores, batch_rows * A.shape[0])
-    t = time.perf_counter()
-    oracle.scan(x, A, B_t, C_t, dt, threads=threads, lib=lib)
-    el = time.perf_counter() - t
-    T = x.shape[1]
-    return {"value": batch_rows * T / el, "unit": "tokens*layers/s", "cores": threads,
+        avail = os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    cores = min(avail, int(omp)) if omp.isdigit() and int(omp) > 0 else avail
+    A = layer0.A.cpu()
+    T = layer0.x.shape[1]
+
+    def sample(rows):
+        return (layer0.x[:rows].cpu(), A, layer0.B_t[:rows].cpu(), layer0.C_t[:rows].cpu(),
+                layer0.dt[:rows].cpu())
+
+    def timed(lib, rows, threads):
+        args = sample(rows)
+        # untimed first call on a few tokens: thread start-up and first-touch paging
+        oracle.scan(*(a if a is A else a[:, :16] for a in args), threads=threads, lib=lib)
+        t = time.perf_counter()
+        oracle.scan(*args, threads=threads, lib=lib)
+        return time.perf_counter() - t
+
+    tmp = tempfile.mkdtemp(prefix="ssd_oracle_f32_")
+    f32 = oracle.load(oracle.build_timing(os.path.join(tmp, "liboracle_f32.so")))
+    H = A.shape[0]
+    all_threads = min(cores, rows_all * H)
+    el_all = timed(f32, rows_all, all_threads)
+    el_one = timed(f32, rows_one, 1)
+    el_dbl = timed(oracle.load(), rows_all, all_threads)
+    return {"value": rows_all * T / el_all, "unit": "tokens*layers/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": "layer 0, batch rows 0-%d, all %d heads, T=%d (%d sequences, %.1f s wall)"
-                      % (batch_rows - 1, A.shape[0], T, batch_rows * A.shape[0], el)}
+            "sample": "layer 0, batch rows 0-%d, all %d heads, T=%d (%d sequences, %.2f s wall); "
+                      "float build (-O3 -march=native), OpenMP over sequences"
+                      % (rows_all - 1, H, T, rows_all * H, el_all),
+            "cpu_model": _cpu_model(),
+            "build": "gcc -O3 -march=native -fno-fast-math -DORACLE_REAL=float (complex64)",
+            "single_thread": {"value": rows_one * T / el_one, "unit": "tokens*layers/s",
+                              "cores": 1,
+                              "sample": "layer 0, batch rows 0-%d, all %d heads (%d sequences, "
+                                        "%.2f s wall)" % (rows_one - 1, H, rows_one * H, el_one)},
+            "double_parity_build": {"value": rows_all * T / el_dbl, "unit": "tokens*layers/s",
+                                    "cores": all_threads,
+                                    "sample": "as the headline sample (%.2f s wall); gcc -O2, "
+                                              "double" % el_dbl}}
 
 
 def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20, dtype=None):
@@ -170,24 +213,29 @@ def proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev, reps=20, dtype=None)
 
 
 def mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev, reps=20):
-    """The MIMO head mixer after the scan (ssd_head_mix) and its gradients
-    (ssd_head_mix_backward) at the network layer shape; median of `reps`
-    event-timed calls each. Both are bound by HBM: the forward reads y and
-    writes z once (8 bytes per element), the backward reads y and grad_z and
-    writes grad_y (12 bytes per element; W, grad_W and the partial gW tiles
-    are a few KB)."""
+    """The MIMO head mixer after the scan (ssd_head_mix: z = y W^T with a dense
+    (H*D, H*D) W) and its gradients (ssd_head_mix_backward: grad_y = grad_z W,
+    grad_W = grad_z^T y) at the network layer shape; median of `reps` calls
+    each, bracketed by HIP events on the stream the library launches on. Each
+    product is 2 M F^2 flops for ~500 flops per byte at F = 1024, so the bound
+    is the fp32 MFMA peak."""
     y, W, gz = ssd_inputs.mix_case((B, T, H, D), seed=0, device=dev)
+    F = H * D
+    M = B * T
     z = torch.empty_like(y)
     gy = torch.empty_like(y)
-    gW = torch.empty((H, H), device=dev)
-    ws = torch.empty(max(ssd.head_mix_workspace_bytes(B * T, H, D), 1), dtype=torch.uint8,
+    gW = torch.empty((F, F), device=dev)
+    ws = torch.empty(max(ssd.head_mix_workspace_bytes(M, H, D), 1), dtype=torch.uint8,
                      device=dev)
-    out = {"workload": "network layer y (B=%d, T=%d, H=%d, D=%d), W (%d, %d)" % (B, T, H, D, H, H)}
-    elems = B * T * H * D
-    for name, call, nbytes in (
-            ("forward", lambda: ssd.head_mix(y, W, z=z), 8 * elems),
+    out = {"workload": "network layer y (B=%d, T=%d, H=%d, D=%d), dense W (%d, %d)"
+                       % (B, T, H, D, F, F)}
+    one = ssd.mix_algorithmic_flops(M, H, D)
+    for name, call, flops, nbytes in (
+            ("forward", lambda: ssd.head_mix(y, W, z=z), one,
+             ssd.mix_algorithmic_bytes(M, H, D)),
             ("backward", lambda: ssd.head_mix_backward(y, W, gz, grad_y=gy, grad_W=gW,
-                                                       workspace=ws), 12 * elems)):
+                                                       workspace=ws), 2 * one,
+             ssd.mix_algorithmic_bytes(M, H, D, backward=True))):
         for _ in range(3):
             call()
         torch.cuda.synchronize()
@@ -200,11 +248,12 @@ def mix_leg(ssd, torch, ssd_inputs, B, T, H, D, dev, reps=20):
             ev.append((a, b))
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                  "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                  "algorithmic_bytes": nbytes}}
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"median_ms": ms, "tokens_per_s": M / (ms * 1e-3),
+                     "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS,
+                                  "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                                  "achieved_hbm_GBs_algorithmic": nbytes / (ms * 1e-3) / 1e9}}
     del y, W, gz, z, gy, gW, ws
     return out
 
@@ -213,9 +262,8 @@ def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
     """The long-context chunk-size sweep: B=4, T=8192, H=16, N=D=64, dt ~ N(0.5, 1),
     one input set for chunk 32, 64, 128 and 256; median of `reps` event-timed
     ssd_chunk_forward calls per chunk size. A chunk above 64 tokens is evaluated
-    as 64-token sub-chunks (the same sums re-associated), so the executed work is
-    that of chunk 64; both fractions are given: against the algorithmic count at
-    the executed block size and at the nominal chunk size."""
+    as 64-token sub-chunks (the same sums re-associated), so the roofline fraction
+    is taken against the algorithmic count of the block size actually evaluated."""
     w = ssd_inputs.WORKLOADS["sweep_b4_t8192"]
     B, T, H, N, D = w["batch"], w["T"], w["H"], w["N"], w["D"]
     g = ssd_inputs.layer_case(B, T, H, N, D, seed=w["seed"], dt_mean=w["dt_mean"], device=dev)
@@ -243,12 +291,10 @@ def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
         ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
         qe = ssd.block_rows(q)
         fe = th * ssd.algorithmic_flops_per_token_head(N, D, qe)
-        fn = th * ssd.algorithmic_flops_per_token_head(N, D, q)
         out["chunk_%d" % q] = {
             "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "token_heads_per_s": th / (ms * 1e-3), "evaluated_block_rows": qe,
-            "roofline_frac_mfma": fe / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
-            "roofline_frac_mfma_nominal_chunk": fn / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+            "roofline_frac_mfma": fe / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
         del wsp
     del g, y, f
     return out

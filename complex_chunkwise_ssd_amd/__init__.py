@@ -9,7 +9,7 @@ and a visible GPU, and fails loudly otherwise (there is no fallback path).
     y, final_state = chunk_forward_proj(proj, A, H, N, D, chunk_size=64)
     grads = chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None)
     A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
-    z = head_mix(y, W)                       # MIMO head mixer after the scan
+    z = head_mix(y, W)                       # MIMO head mixer after the scan (W: (H*D, H*D))
     grad_y, grad_W = head_mix_backward(y, W, grad_z)
 """
 
@@ -36,6 +36,7 @@ SSD_ERR_WORKSPACE = -5
 SSD_ERR_ALIGN = -6
 SSD_ERR_HIP = -7
 SSD_ERR_UNSUPPORTED = -8
+SSD_ERR_ALIAS = -9
 
 _lock = threading.Lock()
 _lib = None
@@ -414,11 +415,12 @@ def _mix_shape(y, W):
     if not isinstance(y, torch.Tensor) or y.dim() < 2:
         raise ValueError("y must be a (..., H, D) tensor")
     H, D = y.shape[-2], y.shape[-1]
+    F = H * D
     dev = y.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device, got %s" % dev)
     _check(y, "y", torch.float32, tuple(y.shape), dev)
-    _check(W, "W", torch.float32, (H, H), dev)
+    _check(W, "W", torch.float32, (F, F), dev)
     tokens = 1
     for n in y.shape[:-2]:
         tokens *= int(n)
@@ -426,9 +428,10 @@ def _mix_shape(y, W):
 
 
 def head_mix(y, W, z=None):
-    """MIMO head mixer after the scan: z[..., i, :] = sum_j W[i, j] y[..., j, :].
-    y (..., H, D) float32 (e.g. the scan's (B, T, H, D) output), W (H, H)
-    float32; z may be passed in (it may be y itself)."""
+    """MIMO head mixer after the scan: with each token's heads flattened
+    head-major (k = h * D + d, F = H * D), z[..., o] = sum_k W[o, k] y[..., k].
+    y (..., H, D) float32 (e.g. the scan's (B, T, H, D) output), W (F, F)
+    float32 (row o = weights of output o); z, if passed, must not overlap y."""
     lib = load_library()
     tokens, H, D, dev = _mix_shape(y, W)
     if z is None:
@@ -445,16 +448,19 @@ def head_mix_workspace_bytes(tokens: int, H: int, D: int) -> int:
 
 
 def head_mix_backward(y, W, grad_z, grad_y=None, grad_W=None, workspace=None):
-    """Gradients of sum(grad_z * head_mix(y, W)): returns (grad_y, grad_W)."""
+    """Gradients of sum(grad_z * head_mix(y, W)): returns (grad_y, grad_W),
+    grad_y = grad_z W per token and grad_W = sum over tokens of
+    grad_z (outer) y."""
     lib = load_library()
     tokens, H, D, dev = _mix_shape(y, W)
+    F = H * D
     _check(grad_z, "grad_z", torch.float32, tuple(y.shape), dev)
     if grad_y is None:
         grad_y = torch.empty_like(y)
     _check(grad_y, "grad_y", torch.float32, tuple(y.shape), dev)
     if grad_W is None:
-        grad_W = torch.empty((H, H), dtype=torch.float32, device=dev)
-    _check(grad_W, "grad_W", torch.float32, (H, H), dev)
+        grad_W = torch.empty((F, F), dtype=torch.float32, device=dev)
+    _check(grad_W, "grad_W", torch.float32, (F, F), dev)
     ws_n = int(lib.ssd_head_mix_backward_workspace_bytes(tokens, H, D))
     if ws_n and workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
@@ -464,3 +470,18 @@ def head_mix_backward(y, W, grad_z, grad_y=None, grad_W=None, workspace=None):
     if st != SSD_OK:
         raise SSDError(st, "ssd_head_mix_backward")
     return grad_y, grad_W
+
+
+def mix_algorithmic_flops(tokens: int, H: int, D: int) -> float:
+    """Real flops of one mixer product (forward, grad_y or grad_W): 2 M F^2."""
+    F = H * D
+    return 2.0 * tokens * F * F
+
+
+def mix_algorithmic_bytes(tokens: int, H: int, D: int, backward: bool = False) -> float:
+    """Bytes the mixer must move: forward y in, z out, W in (8 M F + 4 F^2);
+    backward y, grad_z in, grad_y out, W in, grad_W out (12 M F + 8 F^2)."""
+    F = H * D
+    if backward:
+        return 12.0 * tokens * F + 8.0 * F * F
+    return 8.0 * tokens * F + 4.0 * F * F

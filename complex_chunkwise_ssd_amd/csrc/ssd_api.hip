@@ -279,51 +279,71 @@ int check_mix(int64_t tokens, int64_t H, int64_t D)
         return SSD_ERR_SHAPE;
     if (D > SSD_MAX_BLOCK)
         return SSD_ERR_BLOCK_DIMS;
-    if (H > ssd::kMixMaxH)
+    if (H * D > ssd::kMixMaxF || tokens > (1LL << 31) - 1)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
-// Workgroups of the gW pass: four tokens per workgroup at most, 1024 at most.
-int64_t mix_gw_groups(int64_t tokens)
+// True when the np floats at p and the nq floats at q share any byte.
+bool overlap(const float *p, int64_t np, const float *q, int64_t nq)
 {
-    const int64_t g = (tokens + 3) / 4;
-    return g < ssd::kMixGwGroups ? g : ssd::kMixGwGroups;
+    return p && q && np > 0 && nq > 0 && p < q + nq && q < p + np;
 }
 
-template <int HMAX>
-int launch_mix_h(const ssd::MixParams &p, bool vec, hipStream_t stream)
+// Token splits of the gW product: enough workgroups for about one per CU, at
+// least kMixMinSplitTokens tokens each; kchunk is the tokens per split.
+struct MixSplits {
+    int splits, kchunk;
+};
+MixSplits mix_splits(int64_t tokens, int64_t F)
 {
-    const int64_t cols = p.M * (vec ? p.D / 4 : p.D);
-    int64_t blocks = (cols + ssd::kMixThreads - 1) / ssd::kMixThreads;
-    if (blocks > 16384)
-        blocks = 16384;  // the kernel strides over the rest
-    if (blocks == 0)
-        return SSD_OK;
+    const int64_t t = (F + ssd::kGemmBM - 1) / ssd::kGemmBM;
+    const int64_t tiles = t * t;
+    int64_t s = ssd::kMixMaxWorkgroups / tiles;
+    const int64_t by_tokens = (tokens + ssd::kMixMinSplitTokens - 1) / ssd::kMixMinSplitTokens;
+    s = s < by_tokens ? s : by_tokens;
+    s = s < 1 ? 1 : s;
+    int64_t kc = (tokens + s - 1) / s;
+    kc = (kc + ssd::kGemmBK - 1) / ssd::kGemmBK * ssd::kGemmBK;
+    if (kc < ssd::kGemmBK)
+        kc = ssd::kGemmBK;
+    s = (tokens + kc - 1) / kc;
+    return MixSplits{(int)(s < 1 ? 1 : s), (int)kc};
+}
+
+template <bool AT, bool BT>
+int launch_gemm(const ssd::GemmParams &p, bool vec, hipStream_t stream)
+{
+    const int64_t groups = (int64_t)p.tiles_m * p.tiles_n * p.splits;
     if (vec)
-        hipLaunchKernelGGL((ssd::mix_kernel<HMAX, 4>), dim3((unsigned)blocks),
-                           dim3(ssd::kMixThreads), 0, stream, p);
+        hipLaunchKernelGGL((ssd::gemm_kernel<AT, BT, true>), dim3((unsigned)groups),
+                           dim3(ssd::kGemmThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((ssd::mix_kernel<HMAX, 1>), dim3((unsigned)blocks),
-                           dim3(ssd::kMixThreads), 0, stream, p);
+        hipLaunchKernelGGL((ssd::gemm_kernel<AT, BT, false>), dim3((unsigned)groups),
+                           dim3(ssd::kGemmThreads), 0, stream, p);
     return launch_status();
 }
 
-int launch_mix(const ssd::MixParams &p, bool vec, hipStream_t stream)
+// C (M x N) = sum_k A(m, k) B(n, k) over the whole K (one split).
+ssd::GemmParams gemm_params(const float *a, int64_t lda, const float *b, int64_t ldb, float *c,
+                            int64_t ldc, int64_t M, int64_t N, int64_t K)
 {
-    return p.H <= 16 ? launch_mix_h<16>(p, vec, stream) : launch_mix_h<32>(p, vec, stream);
-}
-
-template <int HT>
-int launch_mix_gw(const ssd::MixGradParams &p, int64_t groups, bool vec, hipStream_t stream)
-{
-    if (vec)
-        hipLaunchKernelGGL((ssd::mix_gw_kernel<HT, 4>), dim3((unsigned)groups),
-                           dim3(ssd::kMixThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((ssd::mix_gw_kernel<HT, 1>), dim3((unsigned)groups),
-                           dim3(ssd::kMixThreads), 0, stream, p);
-    return launch_status();
+    ssd::GemmParams p{};
+    p.a = a;
+    p.b = b;
+    p.c = c;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)((M + ssd::kGemmBM - 1) / ssd::kGemmBM);
+    p.tiles_n = (int)((N + ssd::kGemmBN - 1) / ssd::kGemmBN);
+    p.splits = 1;
+    p.kchunk = (int)((K + ssd::kGemmBK - 1) / ssd::kGemmBK * ssd::kGemmBK);
+    p.c_split = 0;
+    return p;
 }
 
 }  // namespace
@@ -344,7 +364,8 @@ const char *ssd_status_string(int status)
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
     case SSD_ERR_UNSUPPORTED:
-        return "size not covered by this build (gradients: N <= 64 and D <= 64; mixer: H <= 32)";
+        return "size not covered by this build (gradients: N <= 64 and D <= 64; mixer: H * D <= 16384)";
+    case SSD_ERR_ALIAS: return "an output overlaps an input";
     default: return "unknown status";
     }
 }
@@ -599,25 +620,26 @@ int ssd_head_mix(const float *y, const float *W, int64_t tokens, int64_t H, int6
         return SSD_OK;
     if (!y || !W || !z)
         return SSD_ERR_NULL;
+    const int64_t F = H * D;
     if (!aligned(y, 4) || !aligned(W, 4) || !aligned(z, 4))
         return SSD_ERR_ALIGN;
-    ssd::MixParams p{};
-    p.in = y;
-    p.W = W;
-    p.out = z;
-    p.M = tokens;
-    p.H = (int)H;
-    p.D = (int)D;
-    p.transpose = 0;
-    const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(z, 16);
-    return launch_mix(p, vec, (hipStream_t)stream);
+    if (overlap(z, tokens * F, y, tokens * F) || overlap(z, tokens * F, W, F * F))
+        return SSD_ERR_ALIAS;
+    // z = y W^T: A = y (K-contiguous rows), B = W (row o holds output o's weights)
+    const ssd::GemmParams p = gemm_params(y, F, W, F, z, F, tokens, F, F);
+    const bool vec = F % 4 == 0 && aligned(y, 16) && aligned(W, 16);
+    return launch_gemm<false, false>(p, vec, (hipStream_t)stream);
 }
 
 size_t ssd_head_mix_backward_workspace_bytes(int64_t tokens, int64_t H, int64_t D)
 {
-    if (check_mix(tokens, H, D))
+    if (check_mix(tokens, H, D) || tokens == 0)
         return 0;
-    return ssd::align_up((size_t)mix_gw_groups(tokens) * (size_t)(H * H) * 4, 256);
+    const int64_t F = H * D;
+    const MixSplits sp = mix_splits(tokens, F);
+    if (sp.splits < 2)
+        return 0;
+    return ssd::align_up((size_t)sp.splits * (size_t)(F * F) * 4, 256);
 }
 
 int ssd_head_mix_backward(const float *y, const float *W, const float *grad_z, int64_t tokens,
@@ -631,54 +653,52 @@ int ssd_head_mix_backward(const float *y, const float *W, const float *grad_z, i
     if (!aligned(y, 4) || !aligned(W, 4) || !aligned(grad_z, 4) || !aligned(grad_y, 4) ||
         !aligned(grad_W, 4))
         return SSD_ERR_ALIGN;
+    const int64_t F = H * D;
     const size_t need = ssd_head_mix_backward_workspace_bytes(tokens, H, D);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return SSD_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 4))
+    if (need > 0 && !aligned(workspace, 256))
         return SSD_ERR_ALIGN;
     const hipStream_t s = (hipStream_t)stream;
     if (tokens == 0) {  // grad_W = 0
-        hipLaunchKernelGGL(ssd::mix_gw_reduce_kernel, dim3((unsigned)(H * H)), dim3(64), 0, s,
-                           (const float *)nullptr, 0, (int)(H * H), grad_W);
+        hipLaunchKernelGGL(ssd::fill_zero_kernel, dim3((unsigned)((F * F + 255) / 256 < 4096 ? (F * F + 255) / 256 : 4096)),
+                           dim3(256), 0, s, grad_W, F * F);
         return launch_status();
     }
+    const int64_t MF = tokens * F;
+    const float *ws = (const float *)workspace;
+    const int64_t nws = (int64_t)(need / 4), FF = F * F;
+    if (overlap(grad_y, MF, y, MF) || overlap(grad_y, MF, W, FF) || overlap(grad_y, MF, grad_z, MF) ||
+        overlap(grad_W, FF, y, MF) || overlap(grad_W, FF, W, FF) || overlap(grad_W, FF, grad_z, MF) ||
+        overlap(grad_W, FF, grad_y, MF) || overlap(ws, nws, y, MF) || overlap(ws, nws, grad_z, MF) ||
+        overlap(ws, nws, W, FF) || overlap(ws, nws, grad_y, MF) || overlap(ws, nws, grad_W, FF))
+        return SSD_ERR_ALIAS;
 
-    const int64_t groups = mix_gw_groups(tokens);
-    ssd::MixGradParams g{};
-    g.y = y;
-    g.gz = grad_z;
-    g.partial = (float *)workspace;
-    g.M = tokens;
-    g.H = (int)H;
-    g.D = (int)D;
-    g.W = W;
-    g.gy = grad_y;
-    const bool vec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16) && aligned(grad_y, 16);
-    if (H <= 16 && vec) {
-        // one pass: grad_y and the gW tiles
-        hipLaunchKernelGGL(ssd::mix_bwd_fused_kernel, dim3((unsigned)groups),
-                           dim3(ssd::kMixThreads), 0, s, g);
-        if (int st = launch_status())
-            return st;
-    } else {
-        ssd::MixParams p{};
-        p.in = grad_z;
-        p.W = W;
-        p.out = grad_y;
-        p.M = tokens;
-        p.H = (int)H;
-        p.D = (int)D;
-        p.transpose = 1;
-        if (int st = launch_mix(p, D % 4 == 0 && aligned(grad_z, 16) && aligned(grad_y, 16), s))
-            return st;
-        const bool gvec = D % 4 == 0 && aligned(y, 16) && aligned(grad_z, 16);
-        const int st = H <= 16 ? launch_mix_gw<1>(g, groups, gvec, s) : launch_mix_gw<2>(g, groups, gvec, s);
-        if (st)
-            return st;
+    // grad_y = gz W: A = gz (K = o contiguous), B(n = k, o) = W[o, k] (transposed)
+    const ssd::GemmParams py = gemm_params(grad_z, F, W, F, grad_y, F, tokens, F, F);
+    const bool vy = F % 4 == 0 && aligned(grad_z, 16) && aligned(W, 16);
+    if (int st = launch_gemm<false, true>(py, vy, s))
+        return st;
+
+    // grad_W = gz^T y: A(o, m) = gz[m, o], B(k, m) = y[m, k]; the sum over tokens
+    // is cut into splits written to the workspace and added in a fixed order.
+    const MixSplits sp = mix_splits(tokens, F);
+    ssd::GemmParams pw = gemm_params(grad_z, F, y, F, sp.splits > 1 ? (float *)workspace : grad_W,
+                                     F, F, F, tokens);
+    pw.splits = sp.splits;
+    pw.kchunk = sp.kchunk;
+    pw.c_split = F * F;
+    const bool vw = F % 4 == 0 && aligned(grad_z, 16) && aligned(y, 16);
+    if (int st = launch_gemm<true, true>(pw, vw, s))
+        return st;
+    if (sp.splits > 1) {
+        const int64_t n = F * F;
+        const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+        hipLaunchKernelGGL(ssd::split_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const float *)workspace, n, sp.splits, n, grad_W);
+        return launch_status();
     }
-    hipLaunchKernelGGL(ssd::mix_gw_reduce_kernel, dim3((unsigned)(H * H)), dim3(64), 0, s,
-                       (const float *)workspace, (int)groups, (int)(H * H), grad_W);
-    return launch_status();
+    return SSD_OK;
 }
 
 }  // extern "C"

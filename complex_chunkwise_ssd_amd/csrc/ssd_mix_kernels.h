@@ -1,339 +1,256 @@
-// ssd_mix_kernels.h -- the MIMO head mixer that follows the scan (index.html
-// lab 02 "MIMO MIXER": a fully connected mixer across the SSM heads, identity
-// at initialisation; the AGENTS page, "Knows cold" item 2). One H x H real
-// matrix W mixes the heads of every token, the same for every head-dim channel:
-//     z[m, i, d] = sum_j W[i, j] y[m, j, d]           (m = token, i, j = heads)
-// and, for a loss with upstream gradient gz,
-//     gy[m, j, d] = sum_i W[i, j] gz[m, i, d]           (the mixer with W^T)
-//     gW[i, j]    = sum_{m, d} gz[m, i, d] y[m, j, d]
+// ssd_mix_kernels.h -- the MIMO head mixer that follows the scan, and its
+// gradients, as fp32 MFMA matrix products.
 //
-// The mix itself moves 8 bytes per element for 2H flops: it is bound by HBM,
-// so it runs on the vector ALUs with every token row read and written once,
-// coalesced. gW is a genuine contraction over all M*D (token, channel) pairs
-// into a 16 x 16 tile per pair of head blocks, so it runs on fp32 MFMA: each
-// wave accumulates its tokens' outer products in four accumulator registers
-// per tile, and a second small kernel adds the per-workgroup tiles in a fixed
-// order (bit-identical results from run to run).
+// The mixer (index.html lab 02 "MIMO MIXER": 1024 -> 1024 as 16 heads of 64
+// channels, fully connected across the heads, identity at initialisation; the
+// model's parameter count in the "Extending" guide's documentation rule, which
+// holds only with a dense 1024 x 1024 matrix per layer) maps the heads of each
+// token, flattened head-major (k = h * D + d, F = H * D), by one dense real
+// F x F matrix W (row o = the weights of output o):
+//     z[m, o]  = sum_k W[o, k] y[m, k]          z  = y W^T
+//     gy[m, k] = sum_o gz[m, o] W[o, k]         gy = gz W
+//     gW[o, k] = sum_m gz[m, o] y[m, k]         gW = gz^T y
+// Each costs 2 M F^2 flops for about 8 M F + 4 F^2 bytes -- near 500 flops per
+// byte at F = 1024, far past the fp32 MFMA ridge of ~20 -- so all three run on
+// one tiled fp32 MFMA 16x16x4 product, gemm_kernel, whose operand layouts are
+// template arguments:
+//     C[m, n] = sum_k A(m, k) B(n, k)
+//     A(m, k) = a[m * lda + k]  (AT = false)   or  a[k * lda + m]  (AT = true)
+//     B(n, k) = b[n * ldb + k]  (BT = false)   or  b[k * ldb + n]  (BT = true)
+// z takes A = y, B = W; gy takes A = gz and B = W with BT; gW takes A = gz and
+// B = y, both with AT/BT (its sum runs over the tokens), cut into token ranges
+// ("splits") whose partial products split_sum_kernel adds in a fixed order.
+//
+// Tiling: a workgroup of 8 wave64s computes a 256 x 256 tile of C; wave w holds
+// rows 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63 as 8 x 4 MFMA blocks
+// (128 accumulator registers per lane). K advances 16 at a time through two
+// shared-memory stages: while the waves multiply one 256 x 16 tile of A and B,
+// each thread holds its share of the next tile in registers (loaded one tile
+// ahead) and writes it to the other stage halfway through, so one workgroup
+// barrier per 16-wide step orders everything.
+//
+// MFMA k order: in step s (0..3) of a 16-wide tile, the lanes with q = L / 16
+// supply k = 4 q + s. A K-contiguous operand is staged as rows of 16 floats
+// (stride 20), so a lane reads its four k with one 16-byte load; a
+// row-contiguous (transposed) operand is staged as 16 rows of 256 (stride 260)
+// and read one float per step. Both strides keep the reads free of bank
+// conflicts.
 #pragma once
 
 #include <ssd_device.h>
 
 namespace ssd {
 
-constexpr int kMixThreads = 256;    // four wave64s
-constexpr int kMixMaxH = 32;        // heads the mixer kernels support
-constexpr int kMixGwGroups = 1024;  // most workgroups (partial gW tiles) of the gW pass
-constexpr int kMixUB = 4;           // channel groups of one gW load batch
+constexpr int kGemmThreads = 512;          // 8 wave64s: 2 (rows) x 4 (columns)
+constexpr int kGemmBM = 256;               // rows of C per workgroup
+constexpr int kGemmBN = 256;               // columns of C per workgroup
+constexpr int kGemmBK = 16;                // K of one staged tile (4 MFMA steps)
+constexpr int kGemmLdK = kGemmBK + 4;      // row stride of a K-contiguous staged tile
+constexpr int kGemmLdT = kGemmBM + 4;      // row stride of a transposed staged tile
+constexpr int kGemmStage = kGemmBM * kGemmLdK;  // floats per stage (>= kGemmBK * kGemmLdT)
+constexpr uint32_t kGemmOut = 0x80000000u;      // a byte offset past every buffer
+constexpr int kMixMaxF = 16384;                 // largest H * D the mixer takes
+constexpr int kMixMinSplitTokens = 1024;        // fewest tokens per gW split
+constexpr int kMixMaxWorkgroups = 256;          // gW splits aim at one workgroup per CU
 
-struct MixParams {
-    const float *in;  // (M, H, D)
-    const float *W;   // (H, H) row-major
-    float *out;       // (M, H, D); may be `in` itself (each thread reads a column before writing it)
-    int64_t M;        // tokens
-    int H, D;
-    int transpose;    // 0: out_i = sum_j W[i][j] in_j    1: out_i = sum_j W[j][i] in_j
+static_assert(kGemmBK * kGemmLdT <= kGemmStage, "stage too small for a transposed tile");
+
+struct GemmParams {
+    const float *a;
+    const float *b;
+    float *c;
+    int64_t lda, ldb, ldc;
+    int64_t c_split;  // floats between the C blocks of two K splits
+    int M, N, K;
+    int tiles_m, tiles_n, splits;
+    int kchunk;       // K per split, a multiple of kGemmBK
 };
 
-struct MixGradParams {
-    const float *y;    // (M, H, D) mixer input of the forward
-    const float *gz;   // (M, H, D) upstream gradient of the mixer output
-    float *partial;    // (gridDim.x, H, H) one gW tile set per workgroup
-    int64_t M;
-    int H, D;
-    const float *W;    // (H, H): the fused pass also forms grad_y
-    float *gy;         // (M, H, D)
-};
-
-constexpr int kMixCB = 64;            // channels of one staged token tile in the fused pass
-constexpr int kMixLd = kMixCB + 4;    // its row stride (floats) in shared memory
-
-template <int DV>
-struct MixVec;
-template <>
-struct MixVec<4> {
-    typedef v4f T;
-    static SSD_DEVICE T zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
-    static SSD_DEVICE T load(const float *p) { return *(const v4f *)p; }
-    static SSD_DEVICE T load(buf_t r, uint32_t off) { return buf_load4(r, off); }
-    static SSD_DEVICE void store(float *p, T v) { *(v4f *)p = v; }
-    static SSD_DEVICE float at(T v, int c) { return v[c]; }
-};
-template <>
-struct MixVec<1> {
-    typedef float T;
-    static SSD_DEVICE T zero() { return 0.f; }
-    static SSD_DEVICE T load(const float *p) { return *p; }
-    static SSD_DEVICE T load(buf_t r, uint32_t off) { return buf_load1(r, off); }
-    static SSD_DEVICE void store(float *p, T v) { *p = v; }
-    static SSD_DEVICE float at(T v, int) { return v; }
-};
-
-// One thread per (token, group of DV head-dim channels): it reads that column
-// of all H heads (consecutive threads read consecutive channels of one head
-// row, so each head row of a token is one contiguous run), forms every output
-// head from the weights in shared memory and writes the column back.
-// DV = 4 needs D % 4 == 0 and 16-byte aligned rows.
-template <int HMAX, int DV>
-SSD_KERNEL(kMixThreads) void mix_kernel(MixParams p)
+// One thread's share of a staged 256 x 16 operand tile: two groups of four
+// floats. K-contiguous (TR = false): group f = tid + 512 g is row f / 4,
+// k = k0 + 4 (f % 4) .. +3; the buffer starts at row r0 and holds `rows` rows
+// (fewer at the edge of the matrix), and k at or past kend reads zero.
+// Transposed (TR = true): group f is k row k0 + f / 64, rows r0 + 4 (f % 64)
+// .. +3; the buffer holds the k rows below kend, and rows at or past `extent`
+// read zero. VEC = false loads each float on its own (any alignment).
+template <bool TR, bool VEC>
+SSD_DEVICE void gemm_stage_load(v4f (&g)[2], const float *x, int64_t ld, int r0, int extent,
+                                int k0, int kend, int tid)
 {
-    typedef MixVec<DV> V;
-    typedef typename V::T VT;
-    SSD_LDS float sW[HMAX * HMAX];  // sW[i * HMAX + j]: weight of input head j in output head i
-    const int tid = thread_id();
-    for (int e = tid; e < HMAX * HMAX; e += kMixThreads) {
-        const int i = e / HMAX, j = e % HMAX;
-        float w = 0.f;
-        if (i < p.H && j < p.H)
-            w = p.transpose ? p.W[j * p.H + i] : p.W[i * p.H + j];
-        sW[e] = w;
-    }
-    block_sync();
-    const int G = p.D / DV;
-    const int64_t HD = (int64_t)p.H * p.D;
-    const int64_t cols = p.M * G;
-    const int64_t stride = grid_blocks() * kMixThreads;
-    for (int64_t c = block_id() * kMixThreads + tid; c < cols; c += stride) {
-        const int64_t m = c / G;
-        const int64_t base = m * HD + (int64_t)(c - m * G) * DV;
-        // heads past H re-read the last head; their weights are zero
-        VT v[HMAX];
-#pragma unroll
-        for (int j = 0; j < HMAX; ++j)
-            v[j] = V::load(p.in + base + (int64_t)(j < p.H ? j : p.H - 1) * p.D);
-#pragma unroll
-        for (int i = 0; i < HMAX; ++i) {
-            if (i >= p.H)
-                break;
-            VT acc = V::zero();
-#pragma unroll
-            for (int j = 0; j < HMAX; ++j)
-                acc += sW[i * HMAX + j] * v[j];
-            V::store(p.out + base + (int64_t)i * p.D, acc);
-        }
-    }
-}
-
-// gW partial tiles. The head blocks are 16 wide (HT of them); wave w of
-// workgroup b takes tokens m = 4b + w, 4b + w + 4*grid, ... For one token, lane
-// L = (r = L % 16, q = L / 16) reads DV channels of head 16a + r at channel
-// d0 = 4*DV*u + DV*q of gz (the MFMA's A operand, row = output head i) and of
-// y (its B operand, column = input head j); the four q lanes supply the four
-// k values of one 16x16x4 step, so every (token, channel) pair is one k of the
-// contraction. Heads past H and channels past D enter as zeros.
-template <int HT, int DV>
-SSD_KERNEL(kMixThreads) void mix_gw_kernel(MixGradParams p)
-{
-    typedef MixVec<DV> V;
-    typedef typename V::T VT;
-    constexpr int HP = 16 * HT;
-    SSD_LDS float sPart[4][HP * HP];
-    const int tid = thread_id();
-    const int wave = wave_id();
-    const int lane = tid & 63;
-    const int r = lane & 15, q = lane >> 4;
-    const int64_t HD = (int64_t)p.H * p.D;
-    const int KG = (p.D + 4 * DV - 1) / (4 * DV);
-    v4f acc[HT][HT];
-#pragma unroll
-    for (int a = 0; a < HT; ++a)
-#pragma unroll
-        for (int b = 0; b < HT; ++b)
-            acc[a][b] = MixVec<4>::zero();
-    const int64_t wstride = grid_blocks() * 4;
-    const uint32_t row_bytes = (uint32_t)(HD * 4);
-    for (int64_t m = block_id() * 4 + wave; m < p.M; m += wstride) {
-        // one token's rows; an offset at the end of the row reads zeros
-        const buf_t gzm = make_buf(p.gz + m * HD, row_bytes);
-        const buf_t ym = make_buf(p.y + m * HD, row_bytes);
-        // UB channel groups are loaded together (all loads in flight at once),
-        // then contracted; channels past D read zeros
-        for (int u0 = 0; u0 < KG; u0 += kMixUB) {
-            VT g[kMixUB][HT], v[kMixUB][HT];
-#pragma unroll
-            for (int uu = 0; uu < kMixUB; ++uu) {
-                const int d0 = 4 * DV * (u0 + uu) + DV * q;
-#pragma unroll
-                for (int a = 0; a < HT; ++a) {
-                    const int h = 16 * a + r;
-                    const uint32_t off =
-                        (h < p.H && d0 < p.D) ? (uint32_t)(h * p.D + d0) * 4 : row_bytes;
-                    g[uu][a] = V::load(gzm, off);
-                    v[uu][a] = V::load(ym, off);
-                }
+    if (!TR) {
+        const int rows = extent - r0 < kGemmBM ? extent - r0 : kGemmBM;
+        const buf_t rs = make_buf(x + (int64_t)r0 * ld, (uint32_t)(rows * ld * 4));
+        for (int gi = 0; gi < 2; ++gi) {
+            const int f = tid + kGemmThreads * gi;
+            const int r = f >> 2, k = k0 + 4 * (f & 3);
+            const uint32_t base = (uint32_t)(r * ld + k) * 4u;
+            if (VEC) {
+                g[gi] = buf_load4(rs, k < kend ? base : kGemmOut);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    g[gi][e] = buf_load1(rs, k + e < kend ? base + 4u * e : kGemmOut);
             }
-            sched_fence();  // issue every load of the batch before the first MFMA
-#pragma unroll
-            for (int uu = 0; uu < kMixUB; ++uu)
-#pragma unroll
-                for (int c = 0; c < DV; ++c)
-#pragma unroll
-                    for (int a = 0; a < HT; ++a)
-#pragma unroll
-                        for (int b = 0; b < HT; ++b)
-                            acc[a][b] = mfma_16x16x4(V::at(g[uu][a], c), V::at(v[uu][b], c),
-                                                     acc[a][b]);
         }
-    }
-    // lane L holds rows 4q..4q+3 of column r of each tile
-#pragma unroll
-    for (int a = 0; a < HT; ++a)
-#pragma unroll
-        for (int b = 0; b < HT; ++b)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                sPart[wave][(16 * a + 4 * q + k) * HP + 16 * b + r] = acc[a][b][k];
-    block_sync();
-    float *dst = p.partial + block_id() * (int64_t)p.H * p.H;
-    for (int e = tid; e < p.H * p.H; e += kMixThreads) {
-        const int i = e / p.H, j = e % p.H;
-        const int o = i * HP + j;
-        dst[e] = ((sPart[0][o] + sPart[1][o]) + sPart[2][o]) + sPart[3][o];
+    } else {
+        int krows = kend - k0;
+        krows = krows < 0 ? 0 : (krows > kGemmBK ? kGemmBK : krows);
+        const buf_t rs = make_buf(x + (int64_t)k0 * ld + r0, (uint32_t)(krows * ld * 4));
+        for (int gi = 0; gi < 2; ++gi) {
+            const int f = tid + kGemmThreads * gi;
+            const int kr = f >> 6, c = 4 * (f & 63);
+            const uint32_t base = (uint32_t)(kr * ld + c) * 4u;
+            if (VEC) {
+                g[gi] = buf_load4(rs, r0 + c < extent ? base : kGemmOut);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    g[gi][e] = buf_load1(rs, r0 + c + e < extent ? base + 4u * e : kGemmOut);
+            }
+        }
     }
 }
 
-// The fused backward for H <= 16 and D % 4 == 0 (16-byte aligned rows): one
-// pass over grad_z and y forms both grad_y and the gW partial tiles, so grad_z
-// is read once. Each wave takes whole tokens (4b + w, then every 4*grid); per
-// token and 64-channel block it loads the 16 x 64 tiles of grad_z and y with
-// row-contiguous 16-byte loads (lane l covers floats 4l + 256k of the tile),
-// issued one token ahead, and stages them in its own shared-memory tiles. From
-// there: the gW tile on MFMA exactly as in mix_gw_kernel (lane (r, q) reads
-// head r, channels 16u + 4q ..), and grad_y on the vector ALUs: lane (g, s)
-// forms output heads 4s .. 4s+3 at channels 4g .. 4g+3 from all 16 input
-// heads, reading W[i][4s .. 4s+3] from shared memory (a broadcast read).
-SSD_KERNEL(kMixThreads) void mix_bwd_fused_kernel(MixGradParams p)
+template <bool TR>
+SSD_DEVICE void gemm_stage_store(float *s, const v4f (&g)[2], int tid)
 {
-    SSD_LDS float sG[4][16 * kMixLd];
-    SSD_LDS float sY[4][16 * kMixLd];
-    SSD_LDS float sPart[4][16 * 16];
-    SSD_LDS float sW[16 * 16];  // sW[i * 16 + j] = W[i][j], zero past H
+    for (int gi = 0; gi < 2; ++gi) {
+        const int f = tid + kGemmThreads * gi;
+        if (!TR)
+            *(v4f *)&s[(f >> 2) * kGemmLdK + 4 * (f & 3)] = g[gi];
+        else
+            *(v4f *)&s[(f >> 6) * kGemmLdT + 4 * (f & 63)] = g[gi];
+    }
+}
+
+// The four k (4 q + s, s = 0..3) of staged row `row` that lane group q supplies.
+template <bool TR>
+SSD_DEVICE v4f gemm_operand(const float *s, int row, int q)
+{
+    if (!TR)
+        return *(const v4f *)&s[row * kGemmLdK + 4 * q];
+    return v4f{s[(4 * q + 0) * kGemmLdT + row], s[(4 * q + 1) * kGemmLdT + row],
+               s[(4 * q + 2) * kGemmLdT + row], s[(4 * q + 3) * kGemmLdT + row]};
+}
+
+template <bool AT, bool BT, bool VEC>
+SSD_KERNEL(kGemmThreads) void gemm_kernel(GemmParams p)
+{
+    SSD_LDS float sA[2 * kGemmStage];
+    SSD_LDS float sB[2 * kGemmStage];
     const int tid = thread_id();
-    const int wave = wave_id();
     const int lane = tid & 63;
-    const int r = lane & 15, q = lane >> 4;  // MFMA roles; also (g, s) of grad_y
-    const int64_t HD = (int64_t)p.H * p.D;
-    const uint32_t row_bytes = (uint32_t)(HD * 4);
-    const int nblk = (p.D + kMixCB - 1) / kMixCB;
+    const int w = wave_id();
+    const int wm = w >> 2, wn = w & 3;
+    const int l16 = lane & 15, q = lane >> 4;
 
-    static_assert(kMixThreads == 16 * 16, "one thread per weight");
-    {
-        const int i = tid >> 4, j = tid & 15;
-        sW[tid] = i < p.H && j < p.H ? p.W[i * p.H + j] : 0.f;
+    // Workgroup -> (split, row tile, column tile). The workgroups that share a
+    // block of A rows (one split and row tile) go to one XCD when the number of
+    // such blocks allows it (workgroup i runs on XCD i % 8), so that the XCD's L2
+    // serves their A loads.
+    const int64_t id = block_id();
+    const int units = p.splits * p.tiles_m;
+    int unit, tn;
+    if (units % 8 == 0) {
+        const int64_t slot = id >> 3;
+        unit = (int)((slot / p.tiles_n) * 8 + (id & 7));
+        tn = (int)(slot % p.tiles_n);
+    } else {
+        unit = (int)(id / p.tiles_n);
+        tn = (int)(id % p.tiles_n);
     }
+    const int split = unit / p.tiles_m, tm = unit % p.tiles_m;
+    const int m0 = tm * kGemmBM, n0 = tn * kGemmBN;
+    const int kb = split * p.kchunk;
+    const int ke = p.K < kb + p.kchunk ? p.K : kb + p.kchunk;
+    const int nkt = ke > kb ? (ke - kb + kGemmBK - 1) / kGemmBK : 0;
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    v4f ga[2], gb[2];
+    gemm_stage_load<AT, VEC>(ga, p.a, p.lda, m0, p.M, kb, ke, tid);
+    gemm_stage_load<BT, VEC>(gb, p.b, p.ldb, n0, p.N, kb, ke, tid);
+    gemm_stage_store<AT>(sA, ga, tid);
+    gemm_stage_store<BT>(sB, gb, tid);
+    gemm_stage_load<AT, VEC>(ga, p.a, p.lda, m0, p.M, kb + kGemmBK, ke, tid);
+    gemm_stage_load<BT, VEC>(gb, p.b, p.ldb, n0, p.N, kb + kGemmBK, ke, tid);
     block_sync();
 
-    // tile element f = 4 lane + 256 k (k < 4): head f / 64, channel f % 64 of the
-    // block; heads past H and channels past D read zero
-    auto tile_off = [&](int cb, int k) {
-        const int f = 4 * lane + 256 * k, i = f >> 6, c = f & 63;
-        const int d = kMixCB * cb + c;
-        return i < p.H && d < p.D ? (uint32_t)(i * p.D + d) * 4 : row_bytes;
-    };
-    struct Tiles {
-        v4f g[4], v[4];
-    };
-    auto fetch = [&](int64_t m, int cb, Tiles &t) {
-        const bool live = m < p.M;
-        const buf_t bg = make_buf(p.gz + (live ? m : 0) * HD, live ? row_bytes : 0u);
-        const buf_t by = make_buf(p.y + (live ? m : 0) * HD, live ? row_bytes : 0u);
+    const int arow = wm * 128 + l16, bcol = wn * 64 + l16;
+    for (int kt = 0; kt < nkt; ++kt) {
+        const float *cA = sA + (kt & 1) * kGemmStage;
+        const float *cB = sB + (kt & 1) * kGemmStage;
+        v4f bv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t o = tile_off(cb, k);
-            t.g[k] = buf_load4(bg, o);
-            t.v[k] = buf_load4(by, o);
-        }
-    };
-
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    const int64_t wstride = grid_blocks() * 4;
-    int64_t m = block_id() * 4 + wave;
-    int cb = 0;
-    Tiles nx;
-    fetch(m, cb, nx);
-    float *tg = sG[wave];
-    float *ty = sY[wave];
-    while (m < p.M) {
-        const Tiles cur = nx;
-        const int64_t mc = m;
-        const int cbc = cb;
-        if (++cb == nblk) {
-            cb = 0;
-            m += wstride;
-        }
-        fetch(m, cb, nx);  // the next tile is in flight while this one is used
-        wave_lds_sync();   // the previous tile's reads are done
+        for (int j = 0; j < 4; ++j)
+            bv[j] = gemm_operand<BT>(cB, bcol + 16 * j, q);
+        v4f av = gemm_operand<AT>(cA, arow, q);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int f = 4 * lane + 256 * k, i = f >> 6, c = f & 63;
-            *(v4f *)&tg[i * kMixLd + c] = cur.g[k];
-            *(v4f *)&ty[i * kMixLd + c] = cur.v[k];
-        }
-        wave_lds_sync();
-        // gW: head r of grad_z against head r of y at channels 16u + 4q + 0..3
+        for (int i = 0; i < 8; ++i) {
+            const v4f a_cur = av;
+            if (i + 1 < 8)
+                av = gemm_operand<AT>(cA, arow + 16 * (i + 1), q);
 #pragma unroll
-        for (int u = 0; u < kMixCB / 16; ++u) {
-            const v4f a4 = *(const v4f *)&tg[r * kMixLd + 16 * u + 4 * q];
-            const v4f b4 = *(const v4f *)&ty[r * kMixLd + 16 * u + 4 * q];
-            acc = mfma_16x16x4(a4.x, b4.x, acc);
-            acc = mfma_16x16x4(a4.y, b4.y, acc);
-            acc = mfma_16x16x4(a4.z, b4.z, acc);
-            acc = mfma_16x16x4(a4.w, b4.w, acc);
-        }
-        // grad_y at output heads 4q + jj, channels 4r .. 4r + 3 of the block
-        v4f o[4];
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            o[jj] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const v4f gv = *(const v4f *)&tg[i * kMixLd + 4 * r];
-            const v4f w4 = *(const v4f *)&sW[i * 16 + 4 * q];
-            o[0] += w4.x * gv;
-            o[1] += w4.y * gv;
-            o[2] += w4.z * gv;
-            o[3] += w4.w * gv;
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma_16x16x4(a_cur[s], bv[j][s], acc[i][j]);
+            if (i == 3) {
+                // The other stage was last read before the previous barrier:
+                // write the next tile there and start loading the one after.
+                // Past the end of K the loads read zeros and the stage written
+                // is never read.
+                float *nA = sA + ((kt + 1) & 1) * kGemmStage;
+                float *nB = sB + ((kt + 1) & 1) * kGemmStage;
+                gemm_stage_store<AT>(nA, ga, tid);
+                gemm_stage_store<BT>(nB, gb, tid);
+                const int k2 = kb + (kt + 2) * kGemmBK;
+                gemm_stage_load<AT, VEC>(ga, p.a, p.lda, m0, p.M, k2, ke, tid);
+                gemm_stage_load<BT, VEC>(gb, p.b, p.ldb, n0, p.N, k2, ke, tid);
+            }
         }
-        const int d = kMixCB * cbc + 4 * r;
-        float *gyrow = p.gy + mc * HD + d;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int j = 4 * q + jj;
-            if (j < p.H && d < p.D)
-                *(v4f *)(gyrow + (int64_t)j * p.D) = o[jj];
-        }
+        block_sync();
     }
-    // lane L holds rows 4q..4q+3 of column r of the wave's tile
+
+    // Lane (l16, q) holds C[16 i + 4 q + r][16 j + l16] of the wave's blocks.
+    const int rows = p.M - m0 < kGemmBM ? p.M - m0 : kGemmBM;
+    const buf_t cs = make_buf(p.c + split * p.c_split + (int64_t)m0 * p.ldc + n0,
+                              (uint32_t)(rows * p.ldc * 4));
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        sPart[wave][(4 * q + k) * 16 + r] = acc[k];
-    block_sync();
-    float *dst = p.partial + block_id() * (int64_t)p.H * p.H;
-    for (int e = tid; e < p.H * p.H; e += kMixThreads) {
-        const int o = (e / p.H) * 16 + e % p.H;
-        dst[e] = ((sPart[0][o] + sPart[1][o]) + sPart[2][o]) + sPart[3][o];
+    for (int j = 0; j < 4; ++j) {
+        const int col = wn * 64 + 16 * j + l16;
+        const bool cin = n0 + col < p.N;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 128 + 16 * i + 4 * q + r;
+                buf_store1(cs, cin ? (uint32_t)(row * p.ldc + col) * 4u : kGemmOut, acc[i][j][r]);
+            }
     }
 }
 
-// gW[i][j] = the sum of the partial tiles, one wave64 per entry: lane l adds
-// tiles l, l + 64, ... in double, and lane 0 adds the 64 lane sums in lane
-// order (a fixed order, so the result does not vary from run to run).
-SSD_KERNEL(64) void mix_gw_reduce_kernel(const float *partial, int groups, int HH, float *gW)
+// out[e] = sum over s of part[s * stride + e], s in increasing order.
+SSD_KERNEL(256) void split_sum_kernel(const float *part, int64_t stride, int splits, int64_t n,
+                                      float *out)
 {
-    SSD_LDS double sSum[64];
-    const int e = (int)block_id();
-    const int lane = thread_id();
-    double s = 0.0;
-#pragma unroll 8
-    for (int g = lane; g < groups; g += 64)
-        s += (double)partial[(int64_t)g * HH + e];
-    sSum[lane] = s;
-    block_sync();
-    if (lane == 0) {
-        double t = 0.0;
-        for (int k = 0; k < 64; ++k)
-            t += sSum[k];
-        gW[e] = (float)t;
+    const int64_t step = grid_blocks() * 256;
+    for (int64_t e = block_id() * 256 + thread_id(); e < n; e += step) {
+        float acc = 0.f;
+        for (int s = 0; s < splits; ++s)
+            acc += part[s * stride + e];
+        out[e] = acc;
     }
+}
+
+SSD_KERNEL(256) void fill_zero_kernel(float *out, int64_t n)
+{
+    const int64_t step = grid_blocks() * 256;
+    for (int64_t e = block_id() * 256 + thread_id(); e < n; e += step)
+        out[e] = 0.f;
 }
 
 }  // namespace ssd

@@ -58,7 +58,8 @@ enum {
     SSD_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
     SSD_ERR_ALIGN = -6,       /* a pointer is not aligned as documented */
     SSD_ERR_HIP = -7,         /* the HIP runtime reported an error */
-    SSD_ERR_UNSUPPORTED = -8  /* a valid size this build does not cover yet */
+    SSD_ERR_UNSUPPORTED = -8, /* a valid size this build does not cover yet */
+    SSD_ERR_ALIAS = -9        /* an output overlaps an input it must not */
 };
 
 /* Largest N, D and chunk_size accepted (the pages cap kernel blocks at 256). */
@@ -265,46 +266,55 @@ int ssd_chunk_backward_proj_bf16(const uint16_t *proj, int64_t token_stride, con
 
 /*
  * ssd_head_mix -- the MIMO head mixer that follows the scan (index.html lab 02
- * "MIMO MIXER": a fully connected mixer across the SSM heads, 16 x 16 for the
- * 16 heads of 64 channels, identity at initialisation; "Knows cold" item 2 of
- * the AGENTS page; the in_proj -> scan -> MIMO -> out_proj order of
- * "Extending", Path A). One H x H real matrix mixes the heads of each token,
- * the same for every head-dim channel:
+ * "MIMO MIXER": fully connected across the SSM heads, 1024 -> 1024 as 16 heads
+ * of 64 channels, identity at initialisation; "Knows cold" item 2 of the AGENTS
+ * page; the in_proj -> scan -> MIMO -> out_proj order of "Extending", Path A;
+ * the model's parameter count in the "Extending" guide's documentation rule,
+ * which holds only with a dense 1024 x 1024 matrix per layer). Each token's
+ * heads are flattened head-major, k = h * D + d (F = H * D), and mapped by one
+ * dense real F x F matrix:
  *
- *   z[m, i, d] = sum_j W[i, j] * y[m, j, d]
+ *   z[m, o] = sum_k W[o, k] * y[m, k]          (z = y W^T, no bias)
  *
  *   y        (tokens, H, D) float32: the scan output, tokens = batch * T.
- *   W        (H, H) float32, row-major (row i = weights of output head i).
- *   z        out: (tokens, H, D) float32. z may be y itself (in place); any
- *            other overlap of z with y or W gives undefined results.
+ *   W        (F, F) float32, row-major: row o holds the weights of output o
+ *            (the layout of a linear layer's weight); the block
+ *            W[i*D:(i+1)*D, j*D:(j+1)*D] links head j to head i.
+ *   z        out: (tokens, H, D) float32; must not overlap y or W
+ *            (SSD_ERR_ALIAS).
  *   tokens   >= 0; with 0 nothing is launched and y, W, z may be NULL.
- *            1 <= H <= 32; 1 <= D <= 256.
- * Alignment: 4 bytes (16-byte aligned y, z with D % 4 == 0 take the vector path).
+ *            H, D >= 1; D <= 256; H * D <= 16384.
+ * Arithmetic: float32 products summed in float32 (fp32 MFMA).
+ * Alignment: 4 bytes (16-byte aligned y and W with H * D % 4 == 0 take the
+ * vector loads).
  * Status: SSD_ERR_SHAPE for sizes out of range, SSD_ERR_BLOCK_DIMS for D > 256,
- * SSD_ERR_UNSUPPORTED for H > 32.
+ * SSD_ERR_UNSUPPORTED for H * D > 16384.
  */
 int ssd_head_mix(const float *y, const float *W, int64_t tokens, int64_t H, int64_t D, float *z,
                  ssd_stream_t stream);
 
-/* Workspace bytes that ssd_head_mix_backward needs (0 for invalid sizes or
- * tokens == 0). At most 1024 * H * H * 4 bytes. */
+/* Workspace bytes that ssd_head_mix_backward needs (0 for invalid sizes, for
+ * tokens == 0, and when the weight gradient is formed in one pass). It holds
+ * partial weight gradients over token ranges: at most 256 * (H*D)^2 * 4 bytes,
+ * 64 MiB at H * D = 1024 with 65,536 tokens. */
 size_t ssd_head_mix_backward_workspace_bytes(int64_t tokens, int64_t H, int64_t D);
 
 /*
  * ssd_head_mix_backward -- gradients of l = sum grad_z * z for ssd_head_mix,
  * by the chain rule on its definition:
  *
- *   grad_y[m, j, d] = sum_i W[i, j] * grad_z[m, i, d]
- *   grad_W[i, j]    = sum_{m, d} grad_z[m, i, d] * y[m, j, d]
+ *   grad_y[m, k] = sum_o grad_z[m, o] * W[o, k]      (grad_y = grad_z W)
+ *   grad_W[o, k] = sum_m grad_z[m, o] * y[m, k]      (grad_W = grad_z^T y)
  *
  *   y, W, tokens, H, D  as for ssd_head_mix (y is the forward's input).
  *   grad_z    (tokens, H, D) float32.
- *   grad_y    out: (tokens, H, D) float32; may be grad_z itself (in place).
- *   grad_W    out: (H, H) float32, overwritten. The sum runs in a fixed
- *             order: repeated calls give identical bits. With tokens == 0 it is
- *             set to zero and every other pointer may be NULL.
- *   workspace device memory of ssd_head_mix_backward_workspace_bytes bytes
- *             (NULL allowed when that is 0), 4-byte aligned.
+ *   grad_y    out: (tokens, H, D) float32.
+ *   grad_W    out: (F, F) float32, overwritten. The sum over tokens runs in a
+ *             fixed order: repeated calls give identical bits. With tokens == 0
+ *             it is set to zero and every other pointer may be NULL.
+ *   workspace device memory of ssd_head_mix_backward_workspace_bytes bytes,
+ *             256-byte aligned (NULL allowed when that is 0).
+ * No output may overlap an input, each other or the workspace (SSD_ERR_ALIAS).
  * Alignment and status codes as ssd_head_mix; SSD_ERR_WORKSPACE when the
  * workspace is missing or too small.
  */

@@ -167,19 +167,20 @@ static int run_mix(int64_t M, int H, int D)
     unsigned seed = 31u + (unsigned)M * 7 + H * 17 + D * 23;
     const size_t n = (size_t)M * H * D;
     float *y = alloc_fill(n, seed);
-    float *W = alloc_fill((size_t)H * H, seed);
+    const size_t F = (size_t)H * D;
+    float *W = alloc_fill(F * F, seed);
     float *gz = alloc_fill(n, seed);
     float *z = (float *)malloc(n * sizeof(float) + (n == 0));
     float *gy = (float *)malloc(n * sizeof(float) + (n == 0));
-    float *gW = (float *)malloc((size_t)H * H * sizeof(float));
+    float *gW = (float *)malloc(F * F * sizeof(float));
     size_t ws = ssd_head_mix_backward_workspace_bytes(M, H, D);
-    void *w = ws ? malloc(ws) : nullptr;
+    void *w = ws ? aligned_alloc(256, ws) : nullptr;
     int st = ssd_head_mix(y, W, M, H, D, z, nullptr);
     int st2 = ssd_head_mix_backward(y, W, gz, M, H, D, gy, gW, w, ws, nullptr);
     int bad = 0;
     for (size_t i = 0; i < n; ++i)
         bad += !isfinite(z[i]) + !isfinite(gy[i]);
-    for (int i = 0; i < H * H; ++i)
+    for (size_t i = 0; i < F * F; ++i)
         bad += !isfinite(gW[i]);
     printf("mix M=%lld H=%d D=%d ws=%zu status=%d,%d nonfinite=%d\n", (long long)M, H, D, ws, st,
            st2, bad);
@@ -212,10 +213,10 @@ int main()
     fails += run_bwd_proj(1, 40, 2, 4, 6, 16, 1);   // gradient rows with a spare float
     fails += run_bwd_proj(1, 70, 1, 64, 64, 64, 0); // full tiles
     fails += run_bwd_proj_bf16(1, 40, 2, 4, 6, 16, 1);  // bfloat16 rows, odd row length
-    fails += run_mix(5, 16, 64);    // vector path
-    fails += run_mix(3, 7, 10);     // scalar path, padded heads
-    fails += run_mix(9, 20, 8);     // two head blocks
-    fails += run_mix(2100, 3, 4);   // many gW workgroups, strided tokens
+    fails += run_mix(5, 16, 64);    // F = 1024: four column tiles, vector loads
+    fails += run_mix(3, 7, 10);     // F = 70: scalar loads, ragged tiles
+    fails += run_mix(300, 4, 80);   // two ragged row and column tiles
+    fails += run_mix(2100, 2, 4);   // the token sum of gW cut into three splits
     fails += run_mix(0, 4, 8);      // no tokens
     printf("%s\n", fails ? "FAIL" : "OK");
     return fails;

@@ -205,7 +205,7 @@ def chunk_backward_proj(lib, proj, A, H, N, D, chunk, grad_y, grad_final=None):
 
 
 def head_mix(lib, y, W, offset=0):
-    """y (..., H, D) float32 numpy, W (H, H); returns (status, z). `offset`
+    """y (..., H, D) float32 numpy, W (H*D, H*D); returns (status, z). `offset`
     floats shift y and z off 16-byte alignment (the scalar path)."""
     y = np.asarray(y, np.float32)
     H, D = y.shape[-2:]
@@ -227,7 +227,7 @@ def head_mix_backward(lib, y, W, gz):
     M = int(np.prod(y.shape[:-2], dtype=np.int64))
     Wv = np.ascontiguousarray(W, np.float32)
     gy = np.full(y.shape, np.nan, np.float32)
-    gW = np.full((H, H), np.nan, np.float32)
+    gW = np.full((H * D, H * D), np.nan, np.float32)
     ws_n = lib.ssd_head_mix_backward_workspace_bytes(M, H, D)
     ws = np.full(ws_n // 4 + 64, np.nan, np.float32)
     ws_p = ws.ctypes.data

@@ -44,7 +44,7 @@ def test_library_is_built_for_gfx950():
 
 
 def test_status_strings(lib):
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         s = ssd.status_string(st)
         assert s and s != "unknown status"
     assert ssd.status_string(-99) == "unknown status"
@@ -242,44 +242,60 @@ def test_backward_proj_argument_checks(lib):
 
 
 def test_head_mix_argument_checks(lib):
-    p = ctypes.c_void_p(0x100000)
+    # distinct fake device addresses, far enough apart not to overlap
+    y, W, z = (ctypes.c_void_p(a) for a in (0x10000000, 0x20000000, 0x30000000))
     f = lib.ssd_head_mix
-    assert f(None, p, 4, 16, 64, p, None) == ssd.SSD_ERR_NULL
-    assert f(p, None, 4, 16, 64, p, None) == ssd.SSD_ERR_NULL
-    assert f(p, p, 4, 16, 64, None, None) == ssd.SSD_ERR_NULL
-    assert f(p, p, -1, 16, 64, p, None) == ssd.SSD_ERR_SHAPE
-    assert f(p, p, 4, 0, 64, p, None) == ssd.SSD_ERR_SHAPE
-    assert f(p, p, 4, 16, 0, p, None) == ssd.SSD_ERR_SHAPE
-    assert f(p, p, 4, 16, 257, p, None) == ssd.SSD_ERR_BLOCK_DIMS
-    assert f(p, p, 4, 33, 64, p, None) == ssd.SSD_ERR_UNSUPPORTED
-    assert f(ctypes.c_void_p(0x100002), p, 4, 16, 64, p, None) == ssd.SSD_ERR_ALIGN
-    assert f(p, p, 0, 16, 64, p, None) == ssd.SSD_OK  # no tokens: nothing launched
+    assert f(None, W, 4, 16, 64, z, None) == ssd.SSD_ERR_NULL
+    assert f(y, None, 4, 16, 64, z, None) == ssd.SSD_ERR_NULL
+    assert f(y, W, 4, 16, 64, None, None) == ssd.SSD_ERR_NULL
+    assert f(y, W, -1, 16, 64, z, None) == ssd.SSD_ERR_SHAPE
+    assert f(y, W, 4, 0, 64, z, None) == ssd.SSD_ERR_SHAPE
+    assert f(y, W, 4, 16, 0, z, None) == ssd.SSD_ERR_SHAPE
+    assert f(y, W, 4, 16, 257, z, None) == ssd.SSD_ERR_BLOCK_DIMS
+    assert f(y, W, 4, 257, 64, z, None) == ssd.SSD_ERR_UNSUPPORTED  # H * D above 16384
+    assert f(ctypes.c_void_p(0x10000002), W, 4, 16, 64, z, None) == ssd.SSD_ERR_ALIGN
+    assert f(y, W, 4, 16, 64, y, None) == ssd.SSD_ERR_ALIAS  # in place is not a GEMM
+    # z's 4 * 1024 floats reach into W only when W starts inside them
+    assert f(y, ctypes.c_void_p(0x30000000 + 4 * 4095), 4, 16, 64, z, None) == ssd.SSD_ERR_ALIAS
+    assert f(y, W, 0, 16, 64, z, None) == ssd.SSD_OK  # no tokens: nothing launched
+
+
+def test_head_mix_workspace_sizes(lib):
+    ws = lib.ssd_head_mix_backward_workspace_bytes
+    # the network layer: 65,536 tokens of 1024 -> 16 token splits of (1024, 1024) floats
+    assert ws(65536, 16, 64) == 16 * 1024 * 1024 * 4
+    assert ws(5, 16, 64) == 0           # one split: written straight to grad_W
+    assert ws(0, 16, 64) == 0
+    assert ws(4, 257, 64) == 0          # invalid
+    assert ws(2100, 2, 4) == 768        # three splits of an 8 x 8 gradient, rounded to 256
 
 
 def test_head_mix_backward_argument_checks(lib):
-    p = ctypes.c_void_p(0x100000)
+    y, W, gz, gy, gW, w = (ctypes.c_void_p(a) for a in (0x10000000, 0x20000000, 0x30000000,
+                                                         0x40000000, 0x50000000, 0x60000000))
     f = lib.ssd_head_mix_backward
     need = lib.ssd_head_mix_backward_workspace_bytes(65536, 16, 64)
-    assert need == 1024 * 16 * 16 * 4
-    assert lib.ssd_head_mix_backward_workspace_bytes(5, 16, 64) == 256 * ((2 * 1024 + 255) // 256)
-    assert lib.ssd_head_mix_backward_workspace_bytes(0, 16, 64) == 0
-    assert lib.ssd_head_mix_backward_workspace_bytes(4, 33, 64) == 0
-    assert f(p, p, p, 8, 16, 64, p, None, p, need, None) == ssd.SSD_ERR_NULL
-    assert f(p, p, None, 8, 16, 64, p, p, p, need, None) == ssd.SSD_ERR_NULL
-    assert f(p, p, p, 8, 40, 64, p, p, p, need, None) == ssd.SSD_ERR_UNSUPPORTED
-    assert f(p, p, p, 8, 16, 64, p, p, None, need, None) == ssd.SSD_ERR_WORKSPACE
-    assert f(p, p, p, 8, 16, 64, p, p, p, 16, None) == ssd.SSD_ERR_WORKSPACE
-    assert f(p, p, p, 8, 16, 64, ctypes.c_void_p(0x100001), p, p, need, None) == \
+    assert f(y, W, gz, 8, 16, 64, gy, None, w, need, None) == ssd.SSD_ERR_NULL
+    assert f(y, W, None, 8, 16, 64, gy, gW, w, need, None) == ssd.SSD_ERR_NULL
+    assert f(y, W, gz, 8, 257, 64, gy, gW, w, need, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert f(y, W, gz, 65536, 16, 64, gy, gW, None, need, None) == ssd.SSD_ERR_WORKSPACE
+    assert f(y, W, gz, 65536, 16, 64, gy, gW, w, 16, None) == ssd.SSD_ERR_WORKSPACE
+    assert f(y, W, gz, 65536, 16, 64, gy, gW, ctypes.c_void_p(0x60000010), need, None) == \
+        ssd.SSD_ERR_ALIGN                # the workspace must be 256-byte aligned
+    assert f(y, W, gz, 8, 16, 64, ctypes.c_void_p(0x40000001), gW, w, need, None) == \
         ssd.SSD_ERR_ALIGN
+    assert f(y, W, gz, 8, 16, 64, gz, gW, w, need, None) == ssd.SSD_ERR_ALIAS
+    assert f(y, W, gz, 8, 16, 64, gy, W, w, need, None) == ssd.SSD_ERR_ALIAS
+    assert f(y, W, gz, 65536, 16, 64, gy, gW, y, need, None) == ssd.SSD_ERR_ALIAS
 
 
 def test_python_head_mix_rejects_bad_tensors():
     import torch
     y = torch.zeros(2, 3, 4, 8)
     with pytest.raises(ValueError):
-        ssd.head_mix(y, torch.eye(4))  # CPU tensors
+        ssd.head_mix(y, torch.eye(32))  # CPU tensors
     with pytest.raises(ValueError):
-        ssd.head_mix_backward(y, torch.eye(4), y)
+        ssd.head_mix_backward(y, torch.eye(32), y)
 
 
 def test_backward_proj_bf16_argument_checks(lib):

@@ -7,6 +7,7 @@ global and shared-memory access for bounds."""
 import subprocess
 
 import numpy as np
+import torch
 import pytest
 
 import emu_harness
@@ -170,6 +171,25 @@ def test_emulated_backward_matches_oracle(emu, case, edges):
     _check_grads(got, ref)
 
 
+def test_emulated_backward_memoryless_limit_is_exact(emu):
+    """Re A = -1e4: every decay between two tokens underflows to zero, so dF/da
+    is a sum of exact zeros and grad dt must be zero to the bit (grad dt scales
+    dF/da by |A| = 1e4, so any leftover of a token's pair with itself would show).
+    The other gradients keep the plain bar."""
+    B, T, H, N, D, Q = 1, 70, 2, 64, 64, 64
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=91)
+    A = torch.complex(torch.full_like(inp.A.real, -1e4), inp.A.imag)
+    inp = ssd_inputs.ScanInputs(inp.x, A, inp.B_t, inp.C_t, inp.dt)
+    rng = np.random.default_rng(92)
+    gy = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    st, *got = emu_harness.chunk_backward(emu, inp, Q, gy)
+    assert st == 0
+    ref = oracle.scan_backward(inp.x, inp.A, inp.B_t, inp.C_t, inp.dt, gy)
+    assert np.abs(ref.dt).max() < 1e-30
+    assert np.array_equal(got[4], np.zeros_like(got[4]))
+    _check_grads(got, ref)
+
+
 def test_emulated_backward_zero_length(emu):
     inp = ssd_inputs.random_case(2, 0, 2, 4, 4, seed=6)
     rng = np.random.default_rng(2)
@@ -245,12 +265,11 @@ def test_emulated_backward_proj_matches_oracle(emu, case):
 
 MIX_CASES = [
     # tokens shape, H, D, float offset (1 = off 16-byte alignment)
-    ((5,), 16, 64, 0),      # vector path, the pages' 16 heads of 64
-    ((2, 3), 7, 10, 0),     # D % 4 != 0: scalar path; H < 16 padded
-    ((9,), 20, 8, 0),       # H > 16: two head blocks
+    ((5,), 16, 64, 0),      # the pages' 16 heads of 64: F = 1024, four column tiles
+    ((2, 3), 7, 10, 0),     # F = 70, not a multiple of 4: scalar loads
+    ((300,), 4, 80, 0),     # two row and two column tiles, both ragged
     ((1,), 1, 1, 0),
-    ((4,), 16, 64, 1),      # misaligned rows take the scalar path
-    ((3,), 32, 12, 0),
+    ((4,), 4, 16, 1),       # misaligned rows take the scalar loads
 ]
 
 
@@ -263,30 +282,33 @@ def test_emulated_head_mix_matches_oracle(emu, case):
     ref = oracle.head_mix(y, W)
     assert np.isfinite(z).all()
     err = np.abs(z - ref)
-    assert (err <= 1e-4 + 1e-4 * np.abs(ref)).all(), err.max()
+    tol = 1e-4 + 1e-4 * np.abs(ref) + tolerances.mix_forward_extra(y.numpy(), W.numpy())
+    assert (err <= tol).all(), err.max()
 
 
-@pytest.mark.parametrize("case", MIX_CASES[:3] + [((70,), 16, 64, 0), ((2100,), 4, 4, 0),
-                                  ((3,), 16, 100, 0), ((5,), 12, 132, 0)])
+@pytest.mark.parametrize("case", MIX_CASES[1:3] + [((2100,), 2, 4, 0), ((40,), 8, 34, 0)])
 def test_emulated_head_mix_backward_matches_oracle(emu, case):
+    """(2100,) x 8 channels cuts the token sum into three splits; (40,) x 272
+    channels has ragged row and column tiles in both products."""
     lead, H, D, _ = case
     y, W, gz = ssd_inputs.mix_case(lead + (H, D), seed=H * 100 + D + 1)
     st, gy, gW = emu_harness.head_mix_backward(emu, y.numpy(), W.numpy(), gz.numpy())
     assert st == 0
     ry, rW = oracle.head_mix_backward(y, W, gz)
     assert np.isfinite(gy).all() and np.isfinite(gW).all()
-    assert (np.abs(gy - ry) <= 1e-4 + 1e-4 * np.abs(ry)).all()
-    tol = 1e-4 * (1 + np.abs(rW)) + tolerances.grad_w_extra(gz.numpy(), y.numpy())
-    assert (np.abs(gW - rW) <= tol).all(), np.abs(gW - rW).max()
+    ty = 1e-4 + 1e-4 * np.abs(ry) + tolerances.mix_grad_y_extra(gz.numpy(), W.numpy())
+    assert (np.abs(gy - ry) <= ty).all()
+    tw = 1e-4 * (1 + np.abs(rW)) + tolerances.mix_grad_w_extra(gz.numpy(), y.numpy())
+    assert (np.abs(gW - rW) <= tw).all(), np.abs(gW - rW).max()
 
 
 def test_emulated_head_mix_zero_tokens(emu):
     y = np.zeros((0, 4, 8), np.float32)
-    W = np.eye(4, dtype=np.float32)
+    W = np.eye(32, dtype=np.float32)
     st, z = emu_harness.head_mix(emu, y, W)
     assert st == 0 and z.shape == (0, 4, 8)
     st, gy, gW = emu_harness.head_mix_backward(emu, y, W, y)
-    assert st == 0 and np.array_equal(gW, np.zeros((4, 4), np.float32))
+    assert st == 0 and np.array_equal(gW, np.zeros((32, 32), np.float32))
 
 
 @pytest.mark.parametrize("case", [(2, 16, 2, 4, 4, 4, 0), (1, 97, 2, 8, 6, 32, 6)])
