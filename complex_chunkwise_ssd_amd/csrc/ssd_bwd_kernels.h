@@ -472,6 +472,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sTc[16];
     SSD_LDS float sEv[2 * R];  // per row: (O - I + Off) and In, all column tiles
     SSD_LDS float sEe[2 * R];
+    SSD_LDS float sVd[2 * R];  // the diagonal V[l][l], kept out of the V tiles
 
     const int tid = thread_id();
     const int lane = tid & 63;
@@ -646,7 +647,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             fetch(P1{}, next);
             fetch(P2{}, next);
         }
-        // M = Gram o L and V = (gy x^T) o L, zero above the diagonal.
+        // M = Gram o L and V = (gy x^T) o L, zero above the diagonal. V's
+        // diagonal goes to sVd and the V tiles hold only the pairs l > s: the
+        // decay gradients sum row dots of the products with V, and a token's
+        // pair with itself, which no decay multiplies, must not enter them (it
+        // would cancel between two differently rounded sums). The output tiles
+        // add the diagonal term back from sVd.
         for (int i = tid; i < R * R; i += 512) {
             const int l = i / R, s = i % R;
             float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
@@ -659,6 +665,11 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 vr = v.x;
                 vi = v.y;
             }
+            if (l == s) {
+                *(v2f *)&sVd[2 * l] = v2f{vr, vi};
+                vr = 0.f;
+                vi = 0.f;
+            }
             sMre[l * RL + s] = mr;
             sMim[l * RL + s] = mi;
             sVre[l * RL + s] = vr;
@@ -669,10 +680,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         // Output tiles: gx (rows s, columns d), gB (rows s, columns n), gC (rows l,
         // columns n); NT x 4 tiles of each, dealt round-robin over the eight
         // waves. Each tile also leaves one row dot product for the decay
-        // gradients (sRow slot q, column tile ct):
-        //   gx: In_s = x_s . (e_end B G)_s            (q = 2)
-        //   gB: I_s  = B_s . (V^T C)_s                 (q = 1)
-        //   gC: (O + Off)_l = C_l . conj(gC)_l         (q = 0)
+        // gradients (sRow slot q, column tile ct), with V's diagonal left out:
+        //   gx: In_s = x_s . (e_end B G)_s                           (q = 2)
+        //   gB: I_s  = B_s . (V^T C)_s  over l > s                    (q = 1)
+        //   gC: (O + Off)_l = C_l . ((V B)_l over s < l + e_in (gy H^T)_l)  (q = 0)
         if (has_next)
             fetch(P3{}, next);
         for (int tile = w; tile < 3 * NT * 4; tile += 8) {
@@ -722,16 +733,21 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const float *fac = kind == 2 ? sEin : sEend;
             const float *qre = kind == 0 ? sXre : (kind == 1 ? sBre : sCre);
             const float *qim = kind == 0 ? sXim : (kind == 1 ? sBim : sCim);
+            // the diagonal pair's term of gB (V[s][s] C_s) and gC (V[l][l] B_l)
+            const float *ore = kind == 1 ? sCre : sBre;
+            const float *oim = kind == 1 ? sCim : sBim;
             v4f outr, outi, dr, di;
             for (int r = 0; r < 4; ++r) {
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
                 const v2f f = *(const v2f *)&fac[2 * row];
                 const v2f e2 = cmul(f, v2f{p2r[r] - p2n[r], p2i[r]});
                 const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
-                outr[r] = e1.x + e2.x;
-                outi[r] = e1.y + e2.y;
+                const v2f vd = kind == 0 ? v2f{0.f, 0.f} : *(const v2f *)&sVd[2 * row];
+                const v2f e0 = cmul(vd, v2f{ore[row * LD + col], oim[row * LD + col]});
+                const v2f m = kind == 0 ? e2 : (kind == 1 ? e1 : v2f{e1.x + e2.x, e1.y + e2.y});
+                outr[r] = (e1.x + e2.x) + e0.x;
+                outi[r] = (e1.y + e2.y) + e0.y;
                 const v2f q = v2f{qre[row * LD + col], qim[row * LD + col]};
-                const v2f m = kind == 0 ? e2 : (kind == 1 ? e1 : v2f{outr[r], outi[r]});
                 const v2f d = cmul(q, m);
                 dr[r] = d.x;
                 di[r] = d.y;
