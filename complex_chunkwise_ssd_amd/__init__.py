@@ -6,6 +6,7 @@ current stream. Importing works without a GPU; calling needs the built library
 and a visible GPU, and fails loudly otherwise (there is no fallback path).
 
     y, final_state = chunk_forward(x, A, B_t, C_t, dt, chunk_size=64)
+    y, final_state = chunk_forward_noalloc(x, A, B_t, C_t, dt)   # no device allocation
     y, final_state = chunk_forward_proj(proj, A, H, N, D, chunk_size=64)
     grads = chunk_backward(x, A, B_t, C_t, dt, grad_y, grad_final_state=None)
     A_bar, log_decay_cumsum = discretise(dt, A, chunk_size=64)
@@ -37,6 +38,7 @@ SSD_ERR_ALIGN = -6
 SSD_ERR_HIP = -7
 SSD_ERR_UNSUPPORTED = -8
 SSD_ERR_ALIAS = -9
+SSD_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # include/ssd.h
 
 _lock = threading.Lock()
 _lib = None
@@ -69,6 +71,9 @@ def load_library(path: str | None = None):
         lib.ssd_chunk_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                           vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_forward.restype = ctypes.c_int
+        lib.ssd_chunk_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                  vp, vp, vp, vp]
+        lib.ssd_chunk_forward_noalloc.restype = ctypes.c_int
         lib.ssd_chunk_forward_proj.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                                vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_forward_proj.restype = ctypes.c_int
@@ -177,6 +182,43 @@ def chunk_forward(x, A, B_t, C_t, dt, chunk_size: int = 64, initial_state=None,
                                _ptr(workspace), ws_size, _stream(dev))
     if st != SSD_OK:
         raise SSDError(st, "ssd_chunk_forward")
+    return y, final_state
+
+
+def chunk_forward_noalloc(x, A, B_t, C_t, dt, chunk_size: int = 64, initial_state=None,
+                          want_final_state: bool = True, y=None, final_state=None):
+    """chunk_forward through ssd_chunk_forward_noalloc: the library takes its
+    workspace from a static per-GPU device array (SSD_NOALLOC_SCRATCH_BYTES)
+    and allocates nothing. Pass y and final_state to allocate nothing here
+    either. Calls that overlap on one GPU race on that array."""
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or not isinstance(B_t, torch.Tensor) \
+            or B_t.dim() != 4:
+        raise ValueError("x must be (B, T, H, D) and B_t (B, T, H, N) tensors")
+    Bsz, T, H, D = x.shape
+    N = B_t.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % dev)
+    _check(x, "x", torch.complex64, (Bsz, T, H, D), dev)
+    _check(A, "A", torch.complex64, (H,), dev)
+    _check(B_t, "B_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(C_t, "C_t", torch.complex64, (Bsz, T, H, N), dev)
+    _check(dt, "dt", torch.float32, (Bsz, T, H), dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.complex64, (Bsz, H, N, D), dev)
+    if y is None:
+        y = torch.empty((Bsz, T, H, D), dtype=torch.float32, device=dev)
+    _check(y, "y", torch.float32, (Bsz, T, H, D), dev)
+    if want_final_state and final_state is None:
+        final_state = torch.empty((Bsz, H, N, D), dtype=torch.complex64, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", torch.complex64, (Bsz, H, N, D), dev)
+    st = lib.ssd_chunk_forward_noalloc(_ptr(x), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(dt), Bsz, T,
+                                       H, N, D, int(chunk_size), _ptr(initial_state), _ptr(y),
+                                       _ptr(final_state), _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_forward_noalloc")
     return y, final_state
 
 

@@ -7,6 +7,14 @@
 #include <ssd_segment_kernels.h>
 #include <ssd_mix_kernels.h>
 
+#include <mutex>
+
+// Device scratch of ssd_chunk_forward_noalloc: one copy per GPU, held until the
+// process ends. Host code never passes this name to a kernel (on the host it is
+// a stand-in, not a device address); it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -346,6 +354,28 @@ ssd::GemmParams gemm_params(const float *a, int64_t lda, const float *b, int64_t
     return p;
 }
 
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return SSD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return SSD_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,6 +506,25 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     prm.fix_groups = plan.fix_groups;
 
     return launch_forward<ssd::kLayoutC64>(prm, plan, batch * H, s);
+}
+
+int ssd_chunk_forward_noalloc(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t,
+                              const ssd_c64 *C_t, const float *dt, int64_t batch, int64_t T,
+                              int64_t H, int64_t N, int64_t D, int64_t chunk_size,
+                              const ssd_c64 *initial_state, float *y, ssd_c64 *final_state,
+                              ssd_stream_t stream)
+{
+    if (int st = check_sizes(batch, T, H, N, D, chunk_size))
+        return st;
+    const size_t need = ssd_chunk_forward_workspace_bytes(batch, T, H, N, D, chunk_size);
+    if (need > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+        return SSD_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0)
+        if (int st = scratch_address(&ws))
+            return st;
+    return ssd_chunk_forward(x, A, B_t, C_t, dt, batch, T, H, N, D, chunk_size, initial_state, y,
+                             final_state, ws, need, stream);
 }
 
 int ssd_chunk_forward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,

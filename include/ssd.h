@@ -131,6 +131,31 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
                       ssd_c64 *final_state, void *workspace, size_t workspace_bytes,
                       ssd_stream_t stream);
 
+/* Size of the static device scratch of ssd_chunk_forward_noalloc (32 MiB per GPU). */
+#define SSD_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * ssd_chunk_forward_noalloc -- ssd_chunk_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same scan, with the same arguments minus
+ * the workspace. The workspace lives in a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES bytes, one per GPU, created when the library's code
+ * object is loaded on that GPU and held until the process ends; this call and
+ * the kernels it launches allocate nothing.
+ *   Arguments, constraints, alignment and results: as ssd_chunk_forward.
+ *   SSD_ERR_WORKSPACE when ssd_chunk_forward_workspace_bytes(...) for these
+ *   sizes exceeds SSD_NOALLOC_SCRATCH_BYTES (checked before anything runs).
+ * The scratch used is that of the current device; `stream` must belong to it.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller. Its contents on entry are ignored.
+ */
+int ssd_chunk_forward_noalloc(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t,
+                              const ssd_c64 *C_t, const float *dt, int64_t batch, int64_t T,
+                              int64_t H, int64_t N, int64_t D, int64_t chunk_size,
+                              const ssd_c64 *initial_state, float *y, ssd_c64 *final_state,
+                              ssd_stream_t stream);
+
 /*
  * ssd_chunk_forward_proj -- the same scan read straight from the in_proj output
  * ("Extending", Path A Step 2: Mamba3Block._forward_impl slices the projection

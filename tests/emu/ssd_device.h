@@ -263,6 +263,22 @@ static void launch(dim3 grid, dim3 block, std::function<void()> fn)
 
 static inline hipError_t hipGetLastError() { return emu::g_error; }
 
+// Static device arrays are plain host arrays here; their "device address" is
+// their host address, and there is one emulated device.
+#define __device__
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(x) ((const void *)&(x))
+static inline hipError_t hipGetDevice(int *dev)
+{
+    *dev = 0;
+    return hipSuccess;
+}
+static inline hipError_t hipGetSymbolAddress(void **ptr, const void *symbol)
+{
+    *ptr = (void *)symbol;
+    return hipSuccess;
+}
+
 // ------------------------------------------------------------ device primitives
 SSD_DEVICE int thread_id() { return emu::g_cur; }
 SSD_DEVICE int64_t block_id() { return emu::g_block; }

@@ -63,6 +63,9 @@ def load(out_dir):
             lib.ssd_chunk_forward.restype = ctypes.c_int
             lib.ssd_chunk_forward_workspace_bytes.argtypes = [i64] * 6
             lib.ssd_chunk_forward_workspace_bytes.restype = ctypes.c_size_t
+            lib.ssd_chunk_forward_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64,
+                                                      i64, p, p, p, p]
+            lib.ssd_chunk_forward_noalloc.restype = ctypes.c_int
             lib.ssd_discretise.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
             lib.ssd_discretise.restype = ctypes.c_int
             lib.ssd_chunk_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p,

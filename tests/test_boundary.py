@@ -241,6 +241,19 @@ def test_backward_proj_argument_checks(lib):
         ssd.SSD_ERR_WORKSPACE
 
 
+def test_noalloc_argument_checks(lib):
+    p = ctypes.c_void_p(0x100000)
+    f = lib.ssd_chunk_forward_noalloc
+    # sizes whose workspace exceeds the static scratch are refused before anything runs
+    assert lib.ssd_chunk_forward_workspace_bytes(1, 2048, 16, 256, 256, 64) > \
+        ssd.SSD_NOALLOC_SCRATCH_BYTES
+    assert f(p, p, p, p, p, 1, 2048, 16, 256, 256, 64, None, p, None, None) == \
+        ssd.SSD_ERR_WORKSPACE
+    assert f(p, p, p, p, p, 1, 16, 2, 3, 4, 4, None, p, None, None) == ssd.SSD_ERR_ODD_N
+    assert f(None, p, p, p, p, 32, 16, 16, 4, 4, 4, None, p, None, None) == ssd.SSD_ERR_NULL
+    assert f(p, p, p, p, p, 0, 16, 2, 4, 4, 4, None, p, None, None) == ssd.SSD_OK
+
+
 def test_head_mix_argument_checks(lib):
     # distinct fake device addresses, far enough apart not to overlap
     y, W, z = (ctypes.c_void_p(a) for a in (0x10000000, 0x20000000, 0x30000000))

@@ -171,6 +171,24 @@ def test_emulated_backward_matches_oracle(emu, case, edges):
     _check_grads(got, ref)
 
 
+def test_emulated_noalloc_matches_workspace_call(emu):
+    """ssd_chunk_forward_noalloc takes its workspace from the static scratch
+    array: two calls (segments, then a smaller case) equal ssd_chunk_forward."""
+    for B, T, H, N, D, Q, seed in ((1, 130, 1, 8, 8, 16, 1), (1, 45, 2, 6, 10, 8, 2)):
+        inp = ssd_inputs.random_case(B, T, H, N, D, seed=seed + 40)
+        assert emu.ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q) > 0
+        x, A, Bm, Cm = (np.ascontiguousarray(v.numpy()) for v in (inp.x, inp.A, inp.B_t, inp.C_t))
+        dt = np.ascontiguousarray(inp.dt.numpy())
+        y = np.full((B, T, H, D), np.nan, np.float32)
+        fs = np.full((B, H, N, D), np.nan, np.complex64)
+        st = emu.ssd_chunk_forward_noalloc(x.ctypes.data, A.ctypes.data, Bm.ctypes.data,
+                                           Cm.ctypes.data, dt.ctypes.data, B, T, H, N, D, Q, None,
+                                           y.ctypes.data, fs.ctypes.data, None)
+        assert st == 0
+        st, y2, fs2 = emu_harness.chunk_forward(emu, inp, Q)
+        assert st == 0 and np.array_equal(y, y2) and np.array_equal(fs, fs2)
+
+
 def test_emulated_backward_memoryless_limit_is_exact(emu):
     """Re A = -1e4: every decay between two tokens underflows to zero, so dF/da
     is a sum of exact zeros and grad dt must be zero to the bit (grad dt scales
