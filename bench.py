@@ -108,6 +108,50 @@ def write_traffic_profile(root):
     return 0
 
 
+def _short_kernel_name(name):
+    """`ssd::gemm_kernel<false, false, true>(ssd::GemmParams)` -> the part before the
+    argument list; torch's long template names are cut to their first 60 characters."""
+    base = name.split("(")[0] if name.startswith(("void ssd::", "ssd::")) else name
+    base = base.replace("void ", "", 1)
+    return base if len(base) <= 80 else base[:60] + "..."
+
+
+def trace_summary(root, skip_first=0, match="ssd::"):
+    """Per-kernel durations from the rocprofv3 kernel traces (*kernel_trace.csv)
+    under `root`: all calls, and the steady state with each kernel's first
+    `skip_first` dispatches (the warm-up calls) left out. Prints a markdown
+    table and returns the rows."""
+    import csv
+    import glob
+    import statistics
+
+    per = {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if match and match not in r["Kernel_Name"]:
+                continue
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            per.setdefault(_short_kernel_name(r["Kernel_Name"]), []).append(
+                (int(r["Dispatch_Id"]), d))
+    rows = []
+    print("| Kernel | Calls | Steady calls | Median ns | Mean ns | Min ns | Max ns | "
+          "All-call mean ns |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name, calls in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        calls.sort()
+        ds = [d for _, d in calls]
+        steady = ds[skip_first:] or ds
+        row = {"kernel": name, "calls": len(ds), "steady_calls": len(steady),
+               "median_ns": statistics.median(steady), "mean_ns": statistics.fmean(steady),
+               "min_ns": min(steady), "max_ns": max(steady), "all_mean_ns": statistics.fmean(ds)}
+        rows.append(row)
+        print("| `%s` | %d | %d | %s | %s | %s | %s | %s |" % (
+            name, row["calls"], row["steady_calls"], format(int(row["median_ns"]), ","),
+            format(int(row["mean_ns"]), ","), format(row["min_ns"], ","),
+            format(row["max_ns"], ","), format(int(row["all_mean_ns"]), ",")))
+    return rows
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -393,11 +437,19 @@ def main():
     ap.add_argument("--write-traffic-profile", metavar="DIR", default=None,
                     help="read the four rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scan and a "
                          "1 GiB copy) under DIR and write the committed traffic summary")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="print per-kernel steady-state durations from the rocprofv3 kernel "
+                         "traces under DIR and exit")
+    ap.add_argument("--skip-first", type=int, default=0,
+                    help="with --trace-summary: warm-up dispatches of each kernel to leave out")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.write_traffic_profile:
         return write_traffic_profile(args.write_traffic_profile)
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.skip_first)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (the (batch, head) "
               "sequences are independent, so they would shard over GPUs with no communication)",
