@@ -104,35 +104,69 @@ int launch_forward(const ssd::ScanParams &prm, const ssd::Plan &plan, int64_t se
     }
 }
 
+template <int R, int LAYOUT, bool SLICED>
+int launch_backward_r(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
+{
+    const int64_t vseqs = seqs * prm.ns;  // (b, h) x state blocks
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false, LAYOUT>), dim3((unsigned)vseqs), dim3(512),
+                       0, stream, prm);
+    if (int st = launch_status())
+        return st;
+    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, LAYOUT>), dim3((unsigned)vseqs), dim3(512),
+                       0, stream, prm);
+    if (int st = launch_status())
+        return st;
+    const int64_t chunks = vseqs * prm.nc;
+    const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, LAYOUT, SLICED>), dim3((unsigned)groups),
+                       dim3(512), 0, stream, prm);
+    if (int st = launch_status())
+        return st;
+    if (SLICED) {
+        const int64_t n = (int64_t)prm.B * prm.T * prm.H * (prm.D + 2 * prm.N + 1);
+        const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+        hipLaunchKernelGGL((ssd::bwd_slice_sum_kernel<LAYOUT>), dim3((unsigned)blocks), dim3(256),
+                           0, stream, prm);
+        if (int st = launch_status())
+            return st;
+    }
+    // gA shares are laid out (b, h, slice, chunk): ns * nc shares per sequence
+    hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)prm.H), dim3(256), 0, stream,
+                       prm.gA_part, prm.B, prm.H, prm.ns * prm.nc, prm.gA);
+    return launch_status();
+}
+
 template <int R, int LAYOUT>
 int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, false, LAYOUT>), dim3((unsigned)seqs), dim3(512), 0,
-                       stream, prm);
-    if (int st = launch_status())
-        return st;
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, LAYOUT>), dim3((unsigned)seqs), dim3(512), 0,
-                       stream, prm);
-    if (int st = launch_status())
-        return st;
-    const int64_t chunks = seqs * prm.nc;
-    const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
-    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, LAYOUT>), dim3((unsigned)groups), dim3(512), 0, stream,
-                       prm);
-    if (int st = launch_status())
-        return st;
-    hipLaunchKernelGGL(ssd::bwd_reduce_gA_kernel, dim3((unsigned)prm.H), dim3(256), 0, stream,
-                       prm.gA_part, prm.B, prm.H, prm.nc, prm.gA);
-    return launch_status();
+    return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true>(prm, seqs, stream)
+                      : launch_backward_r<R, LAYOUT, false>(prm, seqs, stream);
+}
+
+// Workspace carve-up of the backward: stored states and adjoints, gA shares,
+// and (state slices) the partial gradients.
+void set_backward_workspace(ssd::BwdParams &prm, const ssd::BwdPlan &plan, void *workspace)
+{
+    char *w = (char *)workspace;
+    prm.fwd_states = (float *)w;
+    prm.adj_states = (float *)(w + plan.states_bytes);
+    prm.gA_part = (float *)(w + 2 * plan.states_bytes);
+    char *q = w + 2 * plan.states_bytes + plan.part_bytes;
+    prm.gx_part = plan.ns > 1 ? (float *)q : nullptr;
+    prm.gB_part = plan.ns > 1 ? (float *)(q + plan.gx_part_bytes) : nullptr;
+    prm.gC_part = plan.ns > 1 ? (float *)(q + plan.gx_part_bytes + plan.bc_part_bytes) : nullptr;
+    prm.gdt_part = plan.ns > 1 ? (float *)(q + plan.gx_part_bytes + 2 * plan.bc_part_bytes)
+                               : nullptr;
+    prm.nnb = plan.nnb;
+    prm.ndb = plan.ndb;
+    prm.ns = plan.ns;
+    prm.Q = plan.Q;
+    prm.nc = plan.nc;
 }
 
 int check_backward_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk)
 {
-    if (int st = check_sizes(batch, T, H, N, D, chunk))
-        return st;
-    if (N > ssd::kNPad || D > 64)
-        return SSD_ERR_UNSUPPORTED;
-    return SSD_OK;
+    return check_sizes(batch, T, H, N, D, chunk);
 }
 
 template <int LAYOUT, class E>
@@ -242,7 +276,7 @@ int backward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t
         !aligned(grad_y, 4) ||
         (initial_state && !aligned(initial_state, 8)))
         return SSD_ERR_ALIGN;
-    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
+    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, N, D, chunk_size);
     if (!workspace || workspace_bytes < plan.workspace_bytes)
         return SSD_ERR_WORKSPACE;
     if (!aligned(workspace, 256))
@@ -265,9 +299,7 @@ int backward_proj(const E *proj, int64_t token_stride, const ssd_c64 *A, int64_t
     prm.gC = (float *)(grad_proj + HD + 2 * HN);
     prm.gdt = (float *)(grad_proj + HD + 4 * HN);
     prm.ginit = (float *)grad_initial_state;
-    prm.fwd_states = (float *)workspace;
-    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
-    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
+    set_backward_workspace(prm, plan, workspace);
     prm.B = (int)batch;
     prm.T = (int)T;
     prm.H = (int)H;
@@ -394,7 +426,7 @@ const char *ssd_status_string(int status)
     case SSD_ERR_ALIGN: return "pointer not aligned as required";
     case SSD_ERR_HIP: return "HIP runtime error";
     case SSD_ERR_UNSUPPORTED:
-        return "size not covered by this build (gradients: N <= 64 and D <= 64; mixer: H * D <= 16384)";
+        return "size not covered by this build (mixer: H * D <= 16384)";
     case SSD_ERR_ALIAS: return "an output overlaps an input";
     default: return "unknown status";
     }
@@ -555,7 +587,7 @@ size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, i
     if (check_backward_sizes(batch, T, H, N, D, chunk_size) != SSD_OK || batch == 0 || H == 0 ||
         T == 0)
         return 0;
-    return ssd::make_bwd_plan(batch, T, H, chunk_size).workspace_bytes;
+    return ssd::make_bwd_plan(batch, T, H, N, D, chunk_size).workspace_bytes;
 }
 
 int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, const ssd_c64 *C_t,
@@ -596,7 +628,7 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
         !aligned(grad_C_t, 8) || !aligned(grad_dt, 4) ||
         (initial_state && !aligned(initial_state, 8)))
         return SSD_ERR_ALIGN;
-    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, chunk_size);
+    const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, N, D, chunk_size);
     if (!workspace || workspace_bytes < plan.workspace_bytes)
         return SSD_ERR_WORKSPACE;
     if (!aligned(workspace, 256))
@@ -617,9 +649,7 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
     prm.gC = (float *)grad_C_t;
     prm.gdt = grad_dt;
     prm.ginit = (float *)grad_initial_state;
-    prm.fwd_states = (float *)workspace;
-    prm.adj_states = (float *)((char *)workspace + plan.states_bytes);
-    prm.gA_part = (float *)((char *)workspace + 2 * plan.states_bytes);
+    set_backward_workspace(prm, plan, workspace);
     prm.B = (int)batch;
     prm.T = (int)T;
     prm.H = (int)H;

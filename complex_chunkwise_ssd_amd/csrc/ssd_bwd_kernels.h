@@ -29,6 +29,16 @@
 // parallel from those; bwd_reduce_gA_kernel sums the per-chunk shares of gA
 // in a fixed order. Every contraction is a real-split fp32 MFMA 16x16x4 with
 // operands from LDS planes; running sums of a are taken in double.
+//
+// N or D above 64: the state is cut into 64 x 64 blocks (n-slice S, d-slice T).
+// A block's state and adjoint evolve on their own (B[:, S] and x[:, T] only),
+// and every gradient is a sum over slices of the same expressions on the
+// slices' columns: gx[:, T] = sum_S (M_S^T gy_T + e_end B_S G_ST) with M_S the
+// Gram of the n-slice, gB[:, S] and gC[:, S] sum over T, and dF/da -- whose row
+// sums are products of an n-sum and a d-sum -- over all pairs (S, T). So each
+// (sequence, S, T) is a "virtual sequence" of the passes above, the chunk pass
+// writes partial gradients per slice, and bwd_slice_sum_kernel adds them in a
+// fixed order into the output layout.
 #pragma once
 
 #include <ssd_kernels.h>
@@ -58,8 +68,14 @@ struct BwdParams {
     float *ginit;           // (B, H, N, D) complex or null
     float *fwd_states;      // (B, H, nc, 64, 64) complex: state entering each chunk
     float *adj_states;      // (B, H, nc, 64, 64) complex: adjoint leaving each chunk, conjugated
-    float *gA_part;         // (B, H, nc) complex: each chunk's share of gA
+    float *gA_part;         // (B, H, ns, nc) complex: each chunk's (and slice's) share of gA
     int B, T, H, N, D, Q, nc;
+    // State slices: nnb x ndb blocks of 64 x 64 (ns = nnb * ndb); with ns > 1 the
+    // chunk pass writes partial gradients, complex (or real for dt) in the
+    // (B, T, H, width) layout: gx_part (nnb, ..., D), gB_part and gC_part
+    // (ndb, ..., N), gdt_part (ns, ..., 1).
+    int nnb, ndb, ns;
+    float *gx_part, *gB_part, *gC_part, *gdt_part;
     // In_proj rows (the in_proj layouts): x, Bt, Ct, dt point at the x, Re B, Re C
     // and dt blocks of token (0, 0)'s row and gx, gB, gC, gdt at the same blocks of
     // the gradient rows; rows are tok_stride elements apart (float32, or bfloat16
@@ -72,20 +88,48 @@ struct BwdParams {
 inline int64_t bwd_block_rows(int64_t chunk) { return chunk < kBwdMaxRows ? chunk : kBwdMaxRows; }
 
 struct BwdPlan {
-    int R = 0, Q = 0, nc = 0;
-    size_t states_bytes = 0, part_bytes = 0, workspace_bytes = 0;
+    int R = 0, Q = 0, nc = 0, nnb = 1, ndb = 1, ns = 1;
+    size_t states_bytes = 0, part_bytes = 0, gx_part_bytes = 0, bc_part_bytes = 0,
+           gdt_part_bytes = 0, workspace_bytes = 0;
 };
 
-inline BwdPlan make_bwd_plan(int64_t B, int64_t T, int64_t H, int64_t chunk)
+inline BwdPlan make_bwd_plan(int64_t B, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk)
 {
     BwdPlan p;
     p.Q = (int)bwd_block_rows(chunk);
     p.R = p.Q <= 16 ? 16 : 32;
     p.nc = (int)((T + p.Q - 1) / p.Q);
-    p.states_bytes = align_up((size_t)B * H * p.nc * kStateFloats * 4, 256);
-    p.part_bytes = align_up((size_t)B * H * p.nc * 8, 256);
-    p.workspace_bytes = 2 * p.states_bytes + p.part_bytes;
+    p.nnb = (int)((N + 63) / 64);
+    p.ndb = (int)((D + 63) / 64);
+    p.ns = p.nnb * p.ndb;
+    p.states_bytes = align_up((size_t)B * H * p.ns * p.nc * kStateFloats * 4, 256);
+    p.part_bytes = align_up((size_t)B * H * p.ns * p.nc * 8, 256);
+    if (p.ns > 1) {
+        p.gx_part_bytes = align_up((size_t)p.nnb * B * T * H * D * 8, 256);
+        p.bc_part_bytes = align_up((size_t)p.ndb * B * T * H * N * 8, 256);
+        p.gdt_part_bytes = align_up((size_t)p.ns * B * T * H * 4, 256);
+    }
+    p.workspace_bytes = 2 * p.states_bytes + p.part_bytes + p.gx_part_bytes +
+                        2 * p.bc_part_bytes + p.gdt_part_bytes;
     return p;
+}
+
+// A virtual sequence vs = seq * ns + slice: its (b, h), the slice's first state
+// row n0 and column d0, and how many of its 64 rows and columns exist.
+struct BwdSlice {
+    int64_t seq;
+    int st, n0, d0, nsl, dsl;
+};
+SSD_DEVICE BwdSlice bwd_slice(const BwdParams &p, int64_t vs)
+{
+    BwdSlice r;
+    r.seq = vs / p.ns;
+    r.st = (int)(vs % p.ns);
+    r.n0 = 64 * (r.st / p.ndb);
+    r.d0 = 64 * (r.st % p.ndb);
+    r.nsl = p.N - r.n0 < 64 ? p.N - r.n0 : 64;
+    r.dsl = p.D - r.d0 < 64 ? p.D - r.d0 : 64;
+    return r;
 }
 
 SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i]; }
@@ -257,10 +301,13 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
     const int tid = thread_id();
     const int lane = tid & 63;
     const int w = wave_id();
-    const int64_t seq = block_id();
+    const int64_t vseq = block_id();  // (b, h) and state block
+    const BwdSlice sl = bwd_slice(p, vseq);
+    const int64_t seq = sl.seq;
     const int b = (int)(seq / p.H), h = (int)(seq % p.H);
     const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
-    const int N = p.N, D = p.D;
+    const int N = sl.nsl, D = sl.dsl;  // rows and columns of this state block
+    const int n0 = sl.n0, d0 = sl.d0;
 
     v4f sre[2], sim[2];
     for (int k = 0; k < 2; ++k) {
@@ -271,7 +318,7 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             v2f v = v2f{0.f, 0.f};
             const float *src = REV ? p.gfinal : p.init;
             if (src && n < N && d < D)
-                v = ld_c(src, (seq * N + n) * D + d);
+                v = ld_c(src, (seq * p.N + n0 + n) * p.D + d0 + d);
             sre[k][r] = v.x;
             sim[k][r] = REV ? -v.y : v.y;
         }
@@ -290,19 +337,20 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             // every lane loads (from a clamped element); the stage zeroes the lanes
             // outside the chunk, so no branch or select waits behind the loads
             const int tc = t < p.T ? t : p.T - 1;
-            pa[j] = bwd_load_bc<LAYOUT>(p, REV ? p.Ct : p.Bt, b, tc, h, col < N ? col : N - 1);
+            pa[j] = bwd_load_bc<LAYOUT>(p, REV ? p.Ct : p.Bt, b, tc, h, n0 + (col < N ? col : N - 1));
             if (REV)
-                px[j] = v2f{p.gy[(((int64_t)b * p.T + tc) * p.H + h) * D + (col < D ? col : D - 1)],
+                px[j] = v2f{p.gy[(((int64_t)b * p.T + tc) * p.H + h) * p.D + d0 +
+                                 (col < D ? col : D - 1)],
                             0.f};
             else
-                px[j] = bwd_load_x<LAYOUT>(p, b, tc, h, col < D ? col : D - 1);
+                px[j] = bwd_load_x<LAYOUT>(p, b, tc, h, d0 + (col < D ? col : D - 1));
         }
     };
     fetch(REV ? p.nc - 1 : 0);
 
     for (int ci = 0; ci < p.nc; ++ci) {
         const int c = REV ? p.nc - 1 - ci : ci;
-        float *slot = (REV ? p.adj_states : p.fwd_states) + (seq * p.nc + c) * (int64_t)kStateFloats;
+        float *slot = (REV ? p.adj_states : p.fwd_states) + (vseq * p.nc + c) * (int64_t)kStateFloats;
         for (int k = 0; k < 2; ++k) {
             const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
             const int d = dtl * 16 + (lane & 15);
@@ -378,7 +426,8 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             for (int r = 0; r < 4; ++r) {
                 const int n = nt * 16 + 4 * (lane >> 4) + r;
                 if (n < N && d < D)
-                    *(v2f *)&p.ginit[2 * ((seq * N + n) * D + d)] = v2f{sre[k][r], -sim[k][r]};
+                    *(v2f *)&p.ginit[2 * ((seq * p.N + n0 + n) * p.D + d0 + d)] =
+                        v2f{sre[k][r], -sim[k][r]};
             }
         }
     }
@@ -441,7 +490,7 @@ SSD_DEVICE v4f row_total(v4f v)
 // adjoints. A fixed number of workgroups (about one per compute unit) take the
 // chunks in a strided loop, loading the next chunk's inputs into registers
 // while the current one is evaluated.
-template <int R, int LAYOUT>
+template <int R, int LAYOUT, bool SLICED>
 SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
 {
     constexpr int LD = kBwdLd;
@@ -477,8 +526,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     const int tid = thread_id();
     const int lane = tid & 63;
     const int w = wave_id();
-    const int N = p.N, D = p.D;
-    const int64_t total = (int64_t)p.B * p.H * p.nc;
+    const int64_t total = (int64_t)p.B * p.H * p.ns * p.nc;
 
     // The next chunk's inputs are loaded into registers while the current one
     // is evaluated (PER row elements and PS state elements per thread).
@@ -497,9 +545,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     // wave stalls behind a long burst of loads.
     auto fetch = [&](auto part_c, int64_t k) {
         constexpr int part = decltype(part_c)::value;
-        const int64_t sq = k / p.nc;
         const int cc = (int)(k % p.nc);
-        const int bb = (int)(sq / p.H), hh = (int)(sq % p.H);
+        const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc)
+                                   : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
+        const int bb = (int)(ks.seq / p.H), hh = (int)(ks.seq % p.H);
         if constexpr (part == 0)
             pdt = bwd_load_dt<R, LAYOUT>(p, bb, hh, cc);
         if constexpr (part <= 1) {
@@ -508,13 +557,13 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const int t = cc * p.Q + l;
                 const bool valid = l < p.Q && t < p.T;
                 const int64_t row = ((int64_t)bb * p.T + t) * p.H + hh;
-                const bool vn = valid && col < N, vd = valid && col < D;
+                const bool vn = valid && col < ks.nsl, vd = valid && col < ks.dsl;
                 if constexpr (part == 0) {
-                    pb[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Bt, bb, t, hh, col) : v2f{0.f, 0.f};
-                    pc[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Ct, bb, t, hh, col) : v2f{0.f, 0.f};
+                    pb[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Bt, bb, t, hh, ks.n0 + col) : v2f{0.f, 0.f};
+                    pc[j] = vn ? bwd_load_bc<LAYOUT>(p, p.Ct, bb, t, hh, ks.n0 + col) : v2f{0.f, 0.f};
                 } else {
-                    px[j] = vd ? bwd_load_x<LAYOUT>(p, bb, t, hh, col) : v2f{0.f, 0.f};
-                    pgy[j] = vd ? p.gy[row * D + col] : 0.f;
+                    px[j] = vd ? bwd_load_x<LAYOUT>(p, bb, t, hh, ks.d0 + col) : v2f{0.f, 0.f};
+                    pgy[j] = vd ? p.gy[row * p.D + ks.d0 + col] : 0.f;
                 }
             }
         } else {
@@ -563,7 +612,9 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     stage();
     block_sync();
     for (;;) {
-        const int64_t seq = blk / p.nc;
+        const BwdSlice cs = SLICED ? bwd_slice(p, blk / p.nc)
+                                   : BwdSlice{blk / p.nc, 0, 0, 0, p.N, p.D};
+        const int64_t seq = cs.seq;
         const int c = (int)(blk % p.nc);
         const int b = (int)(seq / p.H), h = (int)(seq % p.H);
         const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
@@ -762,20 +813,32 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     sRow[((q * 4 + ct) * R + row) * 2 + 1] = di[r];
                 }
             }
-            float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
-            const int width = kind == 0 ? D : N;
+            const int width = kind == 0 ? p.D : p.N;
+            const int cols = kind == 0 ? cs.dsl : cs.nsl;
+            const int gcol = (kind == 0 ? cs.d0 : cs.n0) + col;
             for (int r = 0; r < 4; ++r) {
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
                 const int t = c * p.Q + row;
-                if (row < p.Q && t < p.T && col < width) {
+                if (row < p.Q && t < p.T && col < cols) {
+                    if constexpr (SLICED) {
+                        // partial over the other dimension's slices: gx over S, gB and
+                        // gC over T, complex in the (B, T, H, width) layout
+                        const int sl = kind == 0 ? cs.st / p.ndb : cs.st % p.ndb;
+                        float *part = kind == 0 ? p.gx_part : (kind == 1 ? p.gB_part : p.gC_part);
+                        const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
+                        const int64_t e = ((int64_t)sl * p.B * p.T * p.H + g) * width + gcol;
+                        *(v2f *)&part[2 * e] = v2f{outr[r], -outi[r]};
+                        continue;
+                    }
+                    float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
                     if constexpr (LAYOUT != kLayoutC64) {  // real x: its gradient is the real part
-                        const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, width, col);
+                        const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, width, gcol);
                         bwd_row_store<LAYOUT>(dst, e, outr[r]);
                         if (kind != 0)
                             bwd_row_store<LAYOUT>(dst, e + (int64_t)p.H * p.N, -outi[r]);
                     } else {
                         const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
-                        *(v2f *)&dst[2 * (g * width + col)] = v2f{outr[r], -outi[r]};
+                        *(v2f *)&dst[2 * (g * width + gcol)] = v2f{outr[r], -outi[r]};
                     }
                 }
             }
@@ -847,8 +910,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 const float gar = fr, gai = -fi;
                 const float dtv = sDt[t0];
                 const float sig = 1.f / (1.f + expf(-dtv));
-                bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0),
-                                      (Ar * gar + Ai * gai) * sig);
+                if constexpr (SLICED)
+                    p.gdt_part[((int64_t)cs.st * p.B * p.T + (int64_t)b * p.T + t) * p.H + h] =
+                        (Ar * gar + Ai * gai) * sig;
+                else
+                    bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0),
+                                          (Ar * gar + Ai * gai) * sig);
                 const float sp = softplus_f(dtv);
                 gAr = sp * gar;
                 gAi = sp * gai;
@@ -875,6 +942,55 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         if (!has_next)
             break;
         blk = next;
+    }
+}
+
+// Sums the slices' partial gradients in slice order and stores them in the output
+// layout: element e < B*T*H*(D + 2N + 1) of [gx (D) | gB (N) | gC (N) | gdt].
+template <int LAYOUT>
+SSD_KERNEL(256) void bwd_slice_sum_kernel(BwdParams p)
+{
+    const int64_t rows = (int64_t)p.B * p.T * p.H;
+    const int64_t per = (int64_t)p.D + 2 * p.N + 1;
+    const int64_t n = rows * per;
+    const int64_t step = grid_blocks() * 256;
+    for (int64_t e = block_id() * 256 + thread_id(); e < n; e += step) {
+        const int64_t g = e / per;  // (b, t, h) flat
+        int64_t col = e % per;
+        const int64_t bt = g / p.H;
+        const int b = (int)(bt / p.T), t = (int)(bt % p.T), h = (int)(g % p.H);
+        if (col < p.D) {
+            v2f acc = v2f{0.f, 0.f};
+            for (int s = 0; s < p.nnb; ++s)
+                acc += ld_c(p.gx_part, ((int64_t)s * rows + g) * p.D + col);
+            if constexpr (LAYOUT != kLayoutC64)
+                bwd_row_store<LAYOUT>(p.gx, bwd_elem<LAYOUT>(p, b, t, h, p.D, (int)col), acc.x);
+            else
+                *(v2f *)&p.gx[2 * (g * p.D + col)] = acc;
+            continue;
+        }
+        col -= p.D;
+        if (col < 2 * p.N) {
+            const bool isC = col >= p.N;
+            const int nc = (int)(isC ? col - p.N : col);
+            const float *part = isC ? p.gC_part : p.gB_part;
+            float *dst = isC ? p.gC : p.gB;
+            v2f acc = v2f{0.f, 0.f};
+            for (int s = 0; s < p.ndb; ++s)
+                acc += ld_c(part, ((int64_t)s * rows + g) * p.N + nc);
+            if constexpr (LAYOUT != kLayoutC64) {
+                const int64_t o = bwd_elem<LAYOUT>(p, b, t, h, p.N, nc);
+                bwd_row_store<LAYOUT>(dst, o, acc.x);
+                bwd_row_store<LAYOUT>(dst, o + (int64_t)p.H * p.N, acc.y);
+            } else {
+                *(v2f *)&dst[2 * (g * p.N + nc)] = acc;
+            }
+            continue;
+        }
+        float acc = 0.f;
+        for (int s = 0; s < p.ns; ++s)
+            acc += p.gdt_part[(int64_t)s * rows + g];
+        bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0), acc);
     }
 }
 

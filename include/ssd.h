@@ -205,7 +205,10 @@ int ssd_chunk_forward_proj_bf16(const uint16_t *proj, int64_t token_stride, cons
  * ssd_chunk_backward_workspace_bytes -- device workspace that
  * ssd_chunk_backward needs for these sizes (0 when T, batch or H is 0, or the
  * sizes are invalid). It holds the state entering and the adjoint leaving
- * every chunk: about 2 * batch * H * ceil(T / min(chunk_size, 32)) * 32 KiB.
+ * every chunk, in 64 x 64 blocks: about 2 * batch * H * ceil(T / min(chunk_size,
+ * 32)) * ceil(N/64) * ceil(D/64) * 32 KiB; with N or D above 64 also the
+ * per-slice partial gradients (8 * batch * T * H * (ceil(N/64) D +
+ * 2 ceil(D/64) N) + 4 * batch * T * H * ceil(N/64) ceil(D/64) bytes).
  */
 size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, int64_t N,
                                           int64_t D, int64_t chunk_size);
@@ -233,8 +236,10 @@ size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, i
  *                  ssd_chunk_backward_workspace_bytes(...) bytes, 256-byte
  *                  aligned (required whenever T > 0). Contents on entry ignored.
  * The chunk evaluated at once is min(chunk_size, 32) tokens; the result does
- * not depend on chunk_size beyond rounding.
- * Constraints: as ssd_chunk_forward, and N <= 64 and D <= 64 (SSD_ERR_UNSUPPORTED).
+ * not depend on chunk_size beyond rounding. With N or D above 64 the state is
+ * evaluated in 64 x 64 blocks whose partial gradients are added in a fixed
+ * order (deterministic).
+ * Constraints: as ssd_chunk_forward (N even; N, D, chunk_size <= 256).
  * Alignment: complex arrays 8 bytes; dt, grad_y, grad_dt 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 writes grad_final_state (or
  * zeros) to grad_initial_state and zeros to grad_A.
@@ -259,7 +264,7 @@ int ssd_chunk_backward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, c
  *                block dl/ddt. Floats past the blocks are not written.
  *   grad_A, grad_initial_state, workspace: as for ssd_chunk_backward (same
  *                workspace size).
- * Constraints: as ssd_chunk_backward (N <= 64 and D <= 64 among them).
+ * Constraints: as ssd_chunk_backward.
  * Alignment: proj, grad_proj, grad_y 4 bytes; A and the states 8 bytes.
  */
 int ssd_chunk_backward_proj(const float *proj, int64_t token_stride, const ssd_c64 *A,

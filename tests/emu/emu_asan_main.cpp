@@ -205,6 +205,7 @@ int main()
     fails += run_bwd(2, 9, 1, 2, 3, 4, false, false, false);    // R = 16, no optional arrays
     fails += run_bwd(1, 33, 3, 8, 64, 256, true, false, true);  // long chunk as 32-token chunks
     fails += run_bwd(16, 37, 16, 4, 6, 32, true, true, true);   // 256 sequences
+    fails += run_bwd(1, 40, 1, 130, 70, 16, true, true, true);  // 3 x 2 state blocks, partials summed
     fails += run_proj(1, 40, 2, 4, 6, 16, 0);    // the last row's dt is the last float read
     fails += run_proj(1, 150, 1, 64, 64, 64, 1); // full tiles, segments (stride made even)
     fails += run_proj(2, 9, 1, 2, 4, 4, 1);      // Q < 16

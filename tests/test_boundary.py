@@ -167,8 +167,10 @@ def test_backward_argument_checks(lib):
     assert _bwd(lib, Q=0) == ssd.SSD_ERR_SHAPE
     assert _bwd(lib, N=3) == ssd.SSD_ERR_ODD_N
     assert _bwd(lib, D=257) == ssd.SSD_ERR_BLOCK_DIMS
-    assert _bwd(lib, N=66) == ssd.SSD_ERR_UNSUPPORTED
-    assert _bwd(lib, D=65) == ssd.SSD_ERR_UNSUPPORTED     # gradients: D <= 64
+    # N and D up to 256 are covered (64 x 64 state blocks): a valid N = 66 or D = 65
+    # passes the size checks and stops at the missing workspace
+    assert _bwd(lib, N=66) == ssd.SSD_ERR_WORKSPACE
+    assert _bwd(lib, D=65) == ssd.SSD_ERR_WORKSPACE
     assert _bwd(lib, gA=False) == ssd.SSD_ERR_NULL
     assert _bwd(lib, ptrs=False) == ssd.SSD_ERR_NULL
     assert _bwd(lib, align=4, ws=ws, ws_n=need) == ssd.SSD_ERR_ALIGN
@@ -184,7 +186,11 @@ def test_backward_workspace_sizes(lib):
     # two (B, H, chunks, 64, 64) complex state arrays + per-chunk gA shares
     assert f(32, 2048, 16, 64, 64, 64) >= 2 * 32 * 16 * 64 * 64 * 64 * 8
     assert f(1, 100, 2, 4, 4, 8) >= 2 * 2 * 13 * 64 * 64 * 8
-    assert f(1, 16, 2, 4, 65, 4) == 0 and f(0, 16, 2, 4, 4, 4) == 0 and f(1, 0, 2, 4, 4, 4) == 0
+    assert f(1, 16, 2, 4, 257, 4) == 0 and f(0, 16, 2, 4, 4, 4) == 0 and f(1, 0, 2, 4, 4, 4) == 0
+    # N = 130, D = 70: 3 x 2 state blocks and the per-slice partial gradients
+    blocks = 2 * 1 * 2 * 6 * 4 * 64 * 64 * 8   # states + adjoints, 4 chunks of 4 tokens
+    parts = 8 * 16 * 2 * (3 * 70 + 2 * 2 * 130) + 4 * 16 * 2 * 6
+    assert f(1, 16, 2, 130, 70, 4) >= blocks + parts
     assert ssd.backward_workspace_bytes(1, 100, 2, 4, 4, 8) == f(1, 100, 2, 4, 4, 8)
 
 
@@ -230,7 +236,7 @@ def test_backward_proj_argument_checks(lib):
     assert f(p, S - 1, p, 1, 16, 2, 4, 4, 4, None, p, None, p, p, None, p, need, None) == \
         ssd.SSD_ERR_SHAPE
     assert f(p, 1000, p, 1, 16, 2, 4, 65, 4, None, p, None, p, p, None, p, need, None) == \
-        ssd.SSD_ERR_UNSUPPORTED  # the backward's D <= 64
+        ssd.SSD_ERR_WORKSPACE  # D = 65 is covered; its workspace is larger
     assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, None, p, None, p, need, None) == \
         ssd.SSD_ERR_NULL
     assert f(p, S, p, 1, 16, 2, 4, 4, 4, None, p, None, p, None, None, p, need, None) == \

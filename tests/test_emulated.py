@@ -142,6 +142,8 @@ BWD_CASES = [
     (2, 600, 2, 4, 4, 4),      # 600 chunks: each workgroup of the chunk pass takes several
     (16, 40, 16, 4, 6, 8),     # 256 sequences, 1280 chunks over 256 workgroups
     (32, 70, 8, 8, 4, 32),     # the same with 32-row chunks and a ragged last one
+    (1, 40, 1, 130, 70, 16),   # N, D above 64: 3 x 2 state blocks, partial gradients summed
+    (2, 37, 2, 66, 130, 32),   # 2 x 3 blocks with two-row and two-column slivers
 ]
 
 
@@ -257,7 +259,7 @@ def test_emulated_proj_bf16_matches_oracle(emu, case):
 
 
 @pytest.mark.parametrize("case", [(2, 16, 2, 4, 4, 4, 0), (1, 97, 2, 8, 6, 32, 6),
-                                  (2, 50, 2, 6, 10, 16, 4)])
+                                  (2, 50, 2, 6, 10, 16, 4), (1, 40, 2, 130, 70, 16, 2)])
 def test_emulated_backward_proj_matches_oracle(emu, case):
     """Gradient rows of the in_proj layout: every block against the oracle's
     gradients of the complex inputs the rows stand for; floats past the blocks

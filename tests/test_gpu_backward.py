@@ -179,6 +179,35 @@ def test_layer_b1_gradients_full():
     _check_all(got, _oracle_grads(inp, gy, gf), "layer_b1", 2048)
 
 
+# State blocks: N or D above 64 cut the state into 64 x 64 blocks whose partial
+# gradients are summed (N = 128 and D = 128 singly and together, N = 256 with a
+# D sliver, ragged chunks, an initial state and a final-state gradient).
+SLICED = [
+    (2, 150, 3, 128, 64, 32),
+    (2, 150, 3, 64, 128, 64),
+    (1, 200, 2, 128, 128, 16),
+    (1, 97, 2, 256, 70, 32),
+]
+
+
+@pytest.mark.parametrize("case", SLICED)
+def test_state_blocks_above_64(case):
+    B, T, H, N, D, Q = case
+    print("sliced backward case", case, flush=True)
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=sum(case), dt_mean=0.3)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=sum(case), with_final=False)
+    gf, init = _edges(B, H, N, D, sum(case) + 1)
+    got = _gpu_grads(inp, Q, gy.numpy(), gf, init)
+    _check_all(got, _oracle_grads(inp, gy.numpy(), gf, init), "N=%d D=%d" % (N, D), B * T)
+
+
+def test_state_blocks_network_shape_n128():
+    """One network-shaped layer with N = 128 (B=2, T=2048, H=16): every gradient."""
+    g = ssd_inputs.layer_case(2, 2048, 16, 128, 64, seed=23, device=DEV)
+    gy, gf = ssd_inputs.upstream_grads(2, 2048, 16, 128, 64, seed=23, device=DEV)
+    _full_grads(g, gy, gf, 64, "network shape N=128")
+
+
 def _full_grads(g, gy, gf, Q, what):
     """Gradients of the device inputs g at chunk Q against the oracle on the same
     inputs (copied to the host): every component of every gradient."""
