@@ -5,6 +5,9 @@
 
 extern "C" long emu_mfma_count(void) { return emu::g_mfma_count; }
 
+// 0 restores index order; any other value seeds the shuffled thread order.
+extern "C" void emu_set_shuffle_seed(unsigned long long seed) { emu::g_shuffle = seed; }
+
 // The kernels' own sin/cos, for an accuracy test against double precision.
 extern "C" void emu_sincos(const float *x, float *s, float *c, long n)
 {

@@ -8,6 +8,15 @@
 // one after another. A sync point that not every participant reaches (a
 // divergent MFMA, shuffle or barrier) is reported as a deadlock and aborts.
 //
+// Race check: by default the threads between two sync points run in index
+// order. With a nonzero shuffle seed (emu_set_shuffle_seed) every scheduling
+// round runs them in a fresh pseudo-random order instead. Each thread's own
+// arithmetic does not depend on that order, so a kernel whose waves only meet
+// in shared memory across barriers gives bit-identical results under every
+// seed; a missing barrier (one wave reading or overwriting shared memory that
+// another wave writes or reads in the same interval) makes the result depend
+// on the order and shows as a difference between seeds.
+//
 // MFMA 16x16x4 fp32 data layout emulated here (one wave64):
 //   lane L supplies A[L % 16][L / 16] and B[L / 16][L % 16];
 //   component r of lane L's accumulator is D[4 * (L / 16) + r][L % 16].
@@ -78,6 +87,9 @@ static int64_t g_grid = 0;
 static void *g_sched_sp = nullptr;
 static std::function<void()> *g_fn = nullptr;
 static long g_mfma_count = 0;
+static unsigned long long g_shuffle = 0;  // 0: index order; else the state of a xorshift64
+static int *g_order = nullptr;
+static int g_order_cap = 0;
 static int g_error = 0;
 #ifdef EMU_ASAN
 static void *g_fake_stack = nullptr;
@@ -219,13 +231,33 @@ static void launch(dim3 grid, dim3 block, std::function<void()> fn)
         g_block = blk;
         for (int i = 0; i < n; ++i)
             init_fiber(i);
+        if (n > g_order_cap) {
+            free(g_order);
+            g_order = (int *)malloc(sizeof(int) * (size_t)n);
+            g_order_cap = n;
+        }
+        for (int i = 0; i < n; ++i)
+            g_order[i] = i;
         for (;;) {
+            if (g_shuffle) {  // Fisher-Yates with xorshift64
+                for (int i = n - 1; i > 0; --i) {
+                    g_shuffle ^= g_shuffle << 13;
+                    g_shuffle ^= g_shuffle >> 7;
+                    g_shuffle ^= g_shuffle << 17;
+                    const int j = (int)(g_shuffle % (unsigned long long)(i + 1));
+                    const int t = g_order[i];
+                    g_order[i] = g_order[j];
+                    g_order[j] = t;
+                }
+            }
             bool progress = false;
-            for (int i = 0; i < n; ++i)
+            for (int k = 0; k < n; ++k) {
+                const int i = g_order[k];
                 if (g_f[i].state == RUN) {
                     run_fiber(i);
                     progress = true;
                 }
+            }
             int done = 0, at_bar = 0;
             for (int i = 0; i < n; ++i) {
                 done += g_f[i].state == DONE;

@@ -91,6 +91,8 @@ def load(out_dir):
                                                   p]
             lib.ssd_head_mix_backward.restype = ctypes.c_int
             lib.emu_mfma_count.restype = ctypes.c_long
+            lib.emu_set_shuffle_seed.argtypes = [ctypes.c_ulonglong]
+            lib.emu_set_shuffle_seed.restype = None
             lib.emu_sincos.argtypes = [p, p, p, ctypes.c_long]
             lib.emu_sincos.restype = None
             _lib = lib

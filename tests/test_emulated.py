@@ -173,6 +173,82 @@ def test_emulated_backward_matches_oracle(emu, case, edges):
     _check_grads(got, ref)
 
 
+def _run_all_kernels(emu):
+    """Outputs of a forward walking several chunks per workgroup, a segmented
+    forward (prefix and fix-up passes), a backward whose chunk pass takes several
+    chunks per workgroup, and the mixer's three products."""
+    out = []
+    for B, T, H, N, D, Q, seed in ((16, 40, 16, 4, 6, 16, 1), (1, 130, 1, 8, 8, 16, 2)):
+        inp = ssd_inputs.random_case(B, T, H, N, D, seed=seed + 60)
+        st, y, fs = emu_harness.chunk_forward(emu, inp, Q)
+        assert st == 0
+        out += [y, fs]
+    inp = ssd_inputs.random_case(2, 600, 2, 4, 4, seed=63)
+    gy = np.random.default_rng(63).standard_normal((2, 600, 2, 4)).astype(np.float32)
+    st, *g = emu_harness.chunk_backward(emu, inp, 4, gy)
+    assert st == 0
+    out += g
+    y, W, gz = ssd_inputs.mix_case((300, 4, 80), seed=64)
+    st, z = emu_harness.head_mix(emu, y.numpy(), W.numpy())
+    st2, gyy, gW = emu_harness.head_mix_backward(emu, y.numpy(), W.numpy(), gz.numpy())
+    assert st == 0 and st2 == 0
+    return out + [z, gyy, gW]
+
+
+def test_emulated_results_do_not_depend_on_thread_order(emu):
+    """Race check: the threads between sync points run in shuffled orders (two
+    seeds); without a missing barrier every output stays bit-identical."""
+    base = _run_all_kernels(emu)
+    try:
+        for seed in (0x9E3779B97F4A7C15, 12345):
+            emu.emu_set_shuffle_seed(seed)
+            got = _run_all_kernels(emu)
+            for k, (a, b) in enumerate(zip(base, got)):
+                assert np.array_equal(a, b, equal_nan=True), "output %d differs under seed %d" % (
+                    k, seed)
+    finally:
+        emu.emu_set_shuffle_seed(0)
+
+
+def test_shuffled_order_catches_a_missing_barrier(tmp_path):
+    """The race check itself: a copy of the scan kernel without the barrier
+    between phase 2 (each wave leaves its partial y for its partner in shared
+    memory) and the y stores (which read the partner's part) gives different
+    results under different thread orders."""
+    import ctypes
+    import shutil
+    src = tmp_path / "csrc"
+    shutil.copytree(emu_harness.CSRC, src)
+    text = (src / "ssd_kernels.h").read_text()
+    anchor = "        block_sync();\n\n        // ---- store y."
+    assert text.count(anchor) == 1
+    (src / "ssd_kernels.h").write_text(text.replace(anchor, "\n        // ---- store y."))
+    main = tmp_path / "emu_planted.cpp"
+    main.write_text('#include "%s"\n'
+                    'extern "C" void emu_set_shuffle_seed(unsigned long long s) { emu::g_shuffle = s; }\n'
+                    % (src / "ssd_api.hip"))
+    so = tmp_path / "libplanted.so"
+    subprocess.run([emu_harness.CLANG, "-x", "c++", "-std=c++17", "-I" + emu_harness.EMU,
+                    "-I" + str(src), "-I" + emu_harness.INCLUDE, "-O1", "-fPIC", "-shared",
+                    str(main), "-o", str(so)], check=True)
+    lib = ctypes.CDLL(str(so))
+    lib.emu_set_shuffle_seed.argtypes = [ctypes.c_ulonglong]
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.ssd_chunk_forward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p, p, p,
+                                      ctypes.c_size_t, p]
+    lib.ssd_chunk_forward_workspace_bytes.argtypes = [i64] * 6
+    lib.ssd_chunk_forward_workspace_bytes.restype = ctypes.c_size_t
+    inp = ssd_inputs.random_case(16, 40, 16, 4, 6, seed=61)
+    outs = []
+    for seed in (0, 0x9E3779B97F4A7C15, 12345):
+        lib.emu_set_shuffle_seed(seed)
+        st, y, _ = emu_harness.chunk_forward(lib, inp, 16)
+        assert st == 0
+        outs.append(y)
+    assert not (np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])), \
+        "the shuffled order did not expose the missing barrier"
+
+
 def test_emulated_noalloc_matches_workspace_call(emu):
     """ssd_chunk_forward_noalloc takes its workspace from the static scratch
     array: two calls (segments, then a smaller case) equal ssd_chunk_forward."""
