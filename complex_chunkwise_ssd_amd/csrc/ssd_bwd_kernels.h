@@ -50,6 +50,7 @@ constexpr int kBwdLd = 81;       // row stride (floats) of the [row][64] LDS pla
 constexpr int kStLd = 65;        // row stride (floats) of the 64 x 64 state planes
 constexpr int kStateFloats = 64 * 64 * 2;  // one padded complex 64 x 64 state
 constexpr int kBwdGroups = 256;  // workgroups of the chunk pass: one per compute unit
+constexpr uint32_t kBwdOut = 0x80000000u;  // a byte offset past every buffer
 
 struct BwdParams {
     const float *x;         // (B, T, H, D) complex
@@ -325,12 +326,46 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
     }
 
     // The rows of the next chunk are loaded into registers while the current
-    // chunk's MFMA update runs: PER elements of each operand per thread.
+    // chunk's MFMA update runs: PER elements of each operand per thread. For
+    // complex64 tensors (VEC) through buffer resources: B_t or C_t as 16-byte
+    // pairs (PB per thread), x or grad_y per element, with fixed lane offsets and
+    // no conditions (rows past the chunk or T and columns past the block read zero).
+    constexpr bool VEC = LAYOUT == kLayoutC64;
     constexpr int PER = R * 64 / 512;
+    constexpr int PB = R / 16;
     v2f pa[PER], px[PER];
+    v4f va[PB];
     float pdt = 0.f;
+    const uint32_t rowN = (uint32_t)p.H * p.N * 8u, rowD = (uint32_t)p.H * p.D * 8u;
+    const uint32_t rowG = (uint32_t)p.H * p.D * 4u;
     auto fetch = [&](int c) {
         pdt = bwd_load_dt<R, LAYOUT>(p, b, h, c);
+        if constexpr (VEC) {
+            const int64_t rows0 = ((int64_t)b * p.T + (int64_t)c * p.Q) * p.H + h;
+            const int rv = p.T - c * p.Q < p.Q ? p.T - c * p.Q : p.Q;
+            const buf_t ra = make_buf((REV ? p.Ct : p.Bt) + (rows0 * p.N + n0) * 2,
+                                      (uint32_t)(rv - 1) * rowN + (uint32_t)N * 8u);
+            for (int j = 0; j < PB; ++j) {
+                const int e = tid + 512 * j, l = e >> 5, cp = e & 31;
+                va[j] = buf_load4(ra, 2 * cp < N ? (uint32_t)l * rowN + 16u * cp : kBwdOut);
+            }
+            if (REV) {
+                const buf_t rg = make_buf(p.gy + rows0 * p.D + d0,
+                                          (uint32_t)(rv - 1) * rowG + (uint32_t)D * 4u);
+                for (int j = 0; j < PER; ++j) {
+                    const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                    px[j] = v2f{buf_load1(rg, col < D ? (uint32_t)l * rowG + 4u * col : kBwdOut), 0.f};
+                }
+            } else {
+                const buf_t rx = make_buf(p.x + (rows0 * p.D + d0) * 2,
+                                          (uint32_t)(rv - 1) * rowD + (uint32_t)D * 8u);
+                for (int j = 0; j < PER; ++j) {
+                    const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                    px[j] = buf_load2(rx, col < D ? (uint32_t)l * rowD + 8u * col : kBwdOut);
+                }
+            }
+            return;
+        }
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
             const int t = c * p.Q + l;
@@ -351,12 +386,13 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
     for (int ci = 0; ci < p.nc; ++ci) {
         const int c = REV ? p.nc - 1 - ci : ci;
         float *slot = (REV ? p.adj_states : p.fwd_states) + (vseq * p.nc + c) * (int64_t)kStateFloats;
+        const buf_t rslot = make_buf(slot, (uint32_t)kStateFloats * 4u);
         for (int k = 0; k < 2; ++k) {
             const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
             const int d = dtl * 16 + (lane & 15);
             for (int r = 0; r < 4; ++r) {
                 const int n = nt * 16 + 4 * (lane >> 4) + r;
-                *(v2f *)&slot[2 * (n * 64 + d)] = v2f{sre[k][r], sim[k][r]};
+                buf_store2(rslot, 8u * (uint32_t)(n * 64 + d), v2f{sre[k][r], sim[k][r]});
             }
         }
         if (w == 0) {
@@ -370,7 +406,27 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
                 *(v2f *)&sDec[0] = cexp_f(v2f{(float)er, (float)ei});
         }
         block_sync();
-        for (int j = 0; j < PER; ++j) {
+        if constexpr (VEC) {
+            for (int j = 0; j < PB; ++j) {
+                const int e = tid + 512 * j, l = e >> 5, c2 = 2 * (e & 31);
+                const v2f f = *(const v2f *)&sF[2 * l];
+                const v2f a0 = cmul(v2f{va[j].x, va[j].y}, f);
+                const v2f a1 = cmul(v2f{va[j].z, va[j].w}, f);
+                sAre[l * LD + c2] = a0.x;
+                sAim[l * LD + c2] = a0.y;
+                sAimN[l * LD + c2] = -a0.y;
+                sAre[l * LD + c2 + 1] = a1.x;
+                sAim[l * LD + c2 + 1] = a1.y;
+                sAimN[l * LD + c2 + 1] = -a1.y;
+            }
+            for (int j = 0; j < PER; ++j) {
+                const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                sXre[l * LD + col] = px[j].x;
+                if (!REV)
+                    sXim[l * LD + col] = px[j].y;
+            }
+        }
+        for (int j = 0; j < (VEC ? 0 : PER); ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
             // REV: grad_y, always float32; otherwise x as loaded. Lanes outside the
             // chunk (or past N, D) are zeroed here.
@@ -529,12 +585,25 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     const int64_t total = (int64_t)p.B * p.H * p.ns * p.nc;
 
     // The next chunk's inputs are loaded into registers while the current one
-    // is evaluated (PER row elements and PS state elements per thread).
+    // is evaluated (PER row elements and PS state elements per thread). For
+    // complex64 tensors (VEC) B_t, C_t and the stored states move as 16-byte
+    // groups of two complex values (PB and PSV groups per thread), x and grad_y
+    // per element, all through buffer resources: each chunk moves the resource
+    // bases, the lane offsets stay, and every load is unconditional (rows past
+    // the chunk or T and columns past the slice lie outside the resource and
+    // read zero).
+    constexpr bool VEC = LAYOUT == kLayoutC64;
     constexpr int PER = R * 64 / 512;
     constexpr int PS = 64 * 64 / 512;
+    constexpr int PB = R / 16;
+    constexpr int PSV = 4;
     v2f pb[PER], pc[PER], px[PER], ph[PS], pg[PS];
+    v4f vb[PB], vc[PB], vh[PSV], vg[PSV];
     float pgy[PER];
     float pdt = 0.f;
+    const uint32_t rowN = (uint32_t)p.H * p.N * 8u;  // bytes between token rows of B_t, C_t
+    const uint32_t rowD = (uint32_t)p.H * p.D * 8u;  // ... of x
+    const uint32_t rowG = (uint32_t)p.H * p.D * 4u;  // ... of grad_y
     // fetch(part, k): part 0 = dt, B_t and C_t rows; 1 = x and grad_y rows;
     // 2 = the entering state; 3 = the leaving adjoint. The parts of the next
     // chunk are issued at different points of the current one, so that no
@@ -551,7 +620,41 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         const int bb = (int)(ks.seq / p.H), hh = (int)(ks.seq % p.H);
         if constexpr (part == 0)
             pdt = bwd_load_dt<R, LAYOUT>(p, bb, hh, cc);
-        if constexpr (part <= 1) {
+        if constexpr (VEC) {
+            const int64_t rows0 = ((int64_t)bb * p.T + (int64_t)cc * p.Q) * p.H + hh;
+            const int rv = p.T - cc * p.Q < p.Q ? p.T - cc * p.Q : p.Q;  // rows that exist
+            if constexpr (part == 0) {
+                const uint32_t nb = (uint32_t)(rv - 1) * rowN + (uint32_t)ks.nsl * 8u;
+                const buf_t rb = make_buf(p.Bt + (rows0 * p.N + ks.n0) * 2, nb);
+                const buf_t rc = make_buf(p.Ct + (rows0 * p.N + ks.n0) * 2, nb);
+                for (int j = 0; j < PB; ++j) {
+                    const int e = tid + 512 * j, l = e >> 5, cp = e & 31;
+                    const uint32_t off = 2 * cp < ks.nsl ? (uint32_t)l * rowN + 16u * cp : kBwdOut;
+                    vb[j] = buf_load4(rb, off);
+                    vc[j] = buf_load4(rc, off);
+                }
+            } else if constexpr (part == 1) {
+                const buf_t rx = make_buf(p.x + (rows0 * p.D + ks.d0) * 2,
+                                          (uint32_t)(rv - 1) * rowD + (uint32_t)ks.dsl * 8u);
+                const buf_t rg = make_buf(p.gy + rows0 * p.D + ks.d0,
+                                          (uint32_t)(rv - 1) * rowG + (uint32_t)ks.dsl * 4u);
+                for (int j = 0; j < PER; ++j) {
+                    const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                    const bool in = col < ks.dsl;
+                    px[j] = buf_load2(rx, in ? (uint32_t)l * rowD + 8u * col : kBwdOut);
+                    pgy[j] = buf_load1(rg, in ? (uint32_t)l * rowG + 4u * col : kBwdOut);
+                }
+            } else {
+                const float *src = (part == 2 ? p.fwd_states : p.adj_states) + k * (int64_t)kStateFloats;
+                const buf_t rs = make_buf(src, (uint32_t)kStateFloats * 4u);
+                for (int j = 0; j < PSV; ++j) {
+                    if constexpr (part == 2)
+                        vh[j] = buf_load4(rs, 16u * (tid + 512 * j));
+                    else
+                        vg[j] = buf_load4(rs, 16u * (tid + 512 * j));
+                }
+            }
+        } else if constexpr (part <= 1) {
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + 512 * j, l = i >> 6, col = i & 63;
                 const int t = cc * p.Q + l;
@@ -581,6 +684,37 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     auto stage = [&]() {
+        if constexpr (VEC) {
+            for (int j = 0; j < PB; ++j) {
+                const int e = tid + 512 * j, l = e >> 5, c2 = 2 * (e & 31);
+                sBre[l * LD + c2] = vb[j].x;
+                sBim[l * LD + c2] = vb[j].y;
+                sBre[l * LD + c2 + 1] = vb[j].z;
+                sBim[l * LD + c2 + 1] = vb[j].w;
+                sCre[l * LD + c2] = vc[j].x;
+                sCim[l * LD + c2] = vc[j].y;
+                sCre[l * LD + c2 + 1] = vc[j].z;
+                sCim[l * LD + c2 + 1] = vc[j].w;
+            }
+            for (int j = 0; j < PER; ++j) {
+                const int i = tid + 512 * j, l = i >> 6, col = i & 63;
+                sXre[l * LD + col] = px[j].x;
+                sXim[l * LD + col] = px[j].y;
+                sGy[l * LD + col] = pgy[j];
+            }
+            for (int j = 0; j < PSV; ++j) {
+                const int e = tid + 512 * j, n = e >> 5, d2 = 2 * (e & 31);
+                sHre[n * SL + d2] = vh[j].x;
+                sHim[n * SL + d2] = vh[j].y;
+                sHre[n * SL + d2 + 1] = vh[j].z;
+                sHim[n * SL + d2 + 1] = vh[j].w;
+                sGre[n * SL + d2] = vg[j].x;
+                sGim[n * SL + d2] = vg[j].y;
+                sGre[n * SL + d2 + 1] = vg[j].z;
+                sGim[n * SL + d2 + 1] = vg[j].w;
+            }
+            return;
+        }
         for (int j = 0; j < PER; ++j) {
             const int i = tid + 512 * j, l = i >> 6, col = i & 63;
             const v2f bv = bwd_widen2<LAYOUT>(pb[j]), cv = bwd_widen2<LAYOUT>(pc[j]);
@@ -816,6 +950,22 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int width = kind == 0 ? p.D : p.N;
             const int cols = kind == 0 ? cs.dsl : cs.nsl;
             const int gcol = (kind == 0 ? cs.d0 : cs.n0) + col;
+            if constexpr (VEC && !SLICED) {
+                // straight-line stores: rows past the chunk or T and columns past
+                // the width lie outside the resource and are dropped
+                float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
+                const int64_t rows0 = ((int64_t)b * p.T + (int64_t)c * p.Q) * p.H + h;
+                const int rv = p.T - c * p.Q < p.Q ? p.T - c * p.Q : p.Q;
+                const uint32_t rowW = (uint32_t)p.H * width * 8u;
+                const buf_t ro = make_buf(dst + rows0 * width * 2,
+                                          (uint32_t)(rv - 1) * rowW + (uint32_t)cols * 8u);
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rt * 16 + 4 * (lane >> 4) + r;
+                    buf_store2(ro, col < cols ? (uint32_t)row * rowW + 8u * col : kBwdOut,
+                               v2f{outr[r], -outi[r]});
+                }
+                continue;
+            }
             for (int r = 0; r < 4; ++r) {
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
                 const int t = c * p.Q + row;

@@ -70,6 +70,11 @@ SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
 }
+SSD_DEVICE void buf_store2(buf_t r, uint32_t off, v2f v)
+{
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, v), r, (int)off, 0, 0);
+}
 
 // Keeps the instruction scheduler from moving anything across this point (used to
 // hold a software pipeline's loads ahead of the MFMAs that consume older ones).

@@ -422,6 +422,11 @@ SSD_DEVICE void buf_store1(buf_t r, uint32_t off, float v)
     if (emu_buf_in(r, off, 4))
         memcpy((char *)r.base + off, &v, 4);
 }
+SSD_DEVICE void buf_store2(buf_t r, uint32_t off, v2f v)
+{
+    if (emu_buf_in(r, off, 8))
+        memcpy((char *)r.base + off, &v, 8);
+}
 SSD_DEVICE void lds_add(float *p, float v) { *p += v; }
 SSD_DEVICE void sched_fence() {}
 
