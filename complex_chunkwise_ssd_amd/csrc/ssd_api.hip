@@ -104,7 +104,7 @@ int launch_forward(const ssd::ScanParams &prm, const ssd::Plan &plan, int64_t se
     }
 }
 
-template <int R, int LAYOUT, bool SLICED>
+template <int R, int LAYOUT, bool SLICED, bool FUSED>
 int launch_backward_r(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
     const int64_t vseqs = seqs * prm.ns;  // (b, h) x state blocks
@@ -112,13 +112,15 @@ int launch_backward_r(const ssd::BwdParams &prm, int64_t seqs, hipStream_t strea
                        0, stream, prm);
     if (int st = launch_status())
         return st;
-    hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, LAYOUT>), dim3((unsigned)vseqs), dim3(512),
-                       0, stream, prm);
-    if (int st = launch_status())
-        return st;
-    const int64_t chunks = vseqs * prm.nc;
-    const int64_t groups = chunks < ssd::kBwdGroups ? chunks : ssd::kBwdGroups;
-    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, LAYOUT, SLICED>), dim3((unsigned)groups),
+    if (!FUSED) {  // the fused chunk pass walks the adjoint itself
+        hipLaunchKernelGGL((ssd::bwd_state_kernel<R, true, LAYOUT>), dim3((unsigned)vseqs),
+                           dim3(512), 0, stream, prm);
+        if (int st = launch_status())
+            return st;
+    }
+    const int64_t items = FUSED ? vseqs : vseqs * prm.nc;
+    const int64_t groups = items < ssd::kBwdGroups ? items : ssd::kBwdGroups;
+    hipLaunchKernelGGL((ssd::bwd_chunk_kernel<R, LAYOUT, SLICED, FUSED>), dim3((unsigned)groups),
                        dim3(512), 0, stream, prm);
     if (int st = launch_status())
         return st;
@@ -136,11 +138,23 @@ int launch_backward_r(const ssd::BwdParams &prm, int64_t seqs, hipStream_t strea
     return launch_status();
 }
 
+// The fused adjoint walk (complex64 tensors) needs whole sequences per workgroup:
+// it is taken when the (virtual) sequences fill the workgroups evenly.
+inline bool backward_fused(int64_t vseqs)
+{
+    return vseqs >= ssd::kBwdGroups && (vseqs % ssd::kBwdGroups == 0 || vseqs >= 4 * ssd::kBwdGroups);
+}
+
 template <int R, int LAYOUT>
 int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
-    return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true>(prm, seqs, stream)
-                      : launch_backward_r<R, LAYOUT, false>(prm, seqs, stream);
+    if constexpr (LAYOUT == ssd::kLayoutC64) {
+        if (backward_fused(seqs * prm.ns))
+            return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true, true>(prm, seqs, stream)
+                              : launch_backward_r<R, LAYOUT, false, true>(prm, seqs, stream);
+    }
+    return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true, false>(prm, seqs, stream)
+                      : launch_backward_r<R, LAYOUT, false, false>(prm, seqs, stream);
 }
 
 // Workspace carve-up of the backward: stored states and adjoints, gA shares,

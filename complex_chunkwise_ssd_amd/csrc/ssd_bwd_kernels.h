@@ -134,6 +134,15 @@ SSD_DEVICE BwdSlice bwd_slice(const BwdParams &p, int64_t vs)
 }
 
 SSD_DEVICE v2f ld_c(const float *p, int64_t i) { return *(const v2f *)&p[2 * i]; }
+
+// Complex product with its rounding fixed by explicit fused multiply-adds
+// (the compiler may not contract it differently at different call sites): the
+// adjoint pass and the fused chunk pass form the adjoint's update from it and
+// so produce the same bits.
+SSD_DEVICE v2f cmul_fixed(v2f a, v2f b)
+{
+    return v2f{fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x)};
+}
 SSD_DEVICE v2f cmul_d(v2f a, v2f b) { return cmul(a, b); }
 
 // Flat element index of (b, t, h, col) in a (B, T, H, width) tensor, or in
@@ -410,8 +419,8 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             for (int j = 0; j < PB; ++j) {
                 const int e = tid + 512 * j, l = e >> 5, c2 = 2 * (e & 31);
                 const v2f f = *(const v2f *)&sF[2 * l];
-                const v2f a0 = cmul(v2f{va[j].x, va[j].y}, f);
-                const v2f a1 = cmul(v2f{va[j].z, va[j].w}, f);
+                const v2f a0 = cmul_fixed(v2f{va[j].x, va[j].y}, f);
+                const v2f a1 = cmul_fixed(v2f{va[j].z, va[j].w}, f);
                 sAre[l * LD + c2] = a0.x;
                 sAim[l * LD + c2] = a0.y;
                 sAimN[l * LD + c2] = -a0.y;
@@ -435,7 +444,7 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             const v2f av = valid && col < N ? bwd_widen2<LAYOUT>(pa[j]) : v2f{0.f, 0.f};
             const v2f xv = !(valid && col < D) ? v2f{0.f, 0.f}
                                                : (REV ? px[j] : bwd_widen2<LAYOUT>(px[j]));
-            const v2f a = cmul(av, *(const v2f *)&sF[2 * l]);
+            const v2f a = cmul_fixed(av, *(const v2f *)&sF[2 * l]);
             sAre[l * LD + col] = a.x;
             sAim[l * LD + col] = a.y;
             sAimN[l * LD + col] = -a.y;
@@ -449,8 +458,12 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
         const float dr = sDec[0], di = sDec[1];
         for (int k = 0; k < 2; ++k) {
             const int idx = w + 8 * k, nt = idx >> 2, dtl = idx & 3;
-            v4f re = dr * sre[k] - di * sim[k];
-            v4f im = dr * sim[k] + di * sre[k];
+            v4f re, im;
+            for (int r = 0; r < 4; ++r) {
+                const v2f g = cmul_fixed(v2f{dr, di}, v2f{sre[k][r], sim[k][r]});
+                re[r] = g.x;
+                im[r] = g.y;
+            }
             const int n = nt * 16 + (lane & 15);
             const int d = dtl * 16 + (lane & 15);
             for (int l0 = 0; l0 < R; l0 += 4) {
@@ -546,7 +559,16 @@ SSD_DEVICE v4f row_total(v4f v)
 // adjoints. A fixed number of workgroups (about one per compute unit) take the
 // chunks in a strided loop, loading the next chunk's inputs into registers
 // while the current one is evaluated.
-template <int R, int LAYOUT, bool SLICED>
+//
+// FUSED (complex64 tensors, at least as many sequences as workgroups): no
+// stored adjoints. Each workgroup takes whole (virtual) sequences and walks
+// their chunks from the last to the first, keeping the adjoint G in the shared
+// planes: it starts from conj(grad_final), and after a chunk's output tiles the
+// waves fold the chunk in, G <- exp(Lam[R-1]) G + (e_in o C)^T gy -- the
+// adjoint pass's update, in the same order and rounding, so the gradients are
+// the same bits -- and after the first chunk they write the initial-state
+// gradient.
+template <int R, int LAYOUT, bool SLICED, bool FUSED>
 SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
 {
     constexpr int LD = kBwdLd;
@@ -583,6 +605,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     const int lane = tid & 63;
     const int w = wave_id();
     const int64_t total = (int64_t)p.B * p.H * p.ns * p.nc;
+    const int64_t nvseq = (int64_t)p.B * p.H * p.ns;
+    static_assert(!FUSED || LAYOUT == kLayoutC64, "the fused adjoint walk reads complex64 tensors");
 
     // The next chunk's inputs are loaded into registers while the current one
     // is evaluated (PER row elements and PS state elements per thread). For
@@ -644,6 +668,9 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     px[j] = buf_load2(rx, in ? (uint32_t)l * rowD + 8u * col : kBwdOut);
                     pgy[j] = buf_load1(rg, in ? (uint32_t)l * rowG + 4u * col : kBwdOut);
                 }
+            } else if constexpr (FUSED && part == 3) {
+                // the adjoint is walked in shared memory (grad_final is read where a
+                // sequence's first chunk is staged)
             } else {
                 const float *src = (part == 2 ? p.fwd_states : p.adj_states) + k * (int64_t)kStateFloats;
                 const buf_t rs = make_buf(src, (uint32_t)kStateFloats * 4u);
@@ -683,7 +710,25 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
-    auto stage = [&]() {
+    // new_seq (FUSED): the staged chunk k is its sequence's last, so G starts from
+    // conj(grad_final) (read here, once per sequence); otherwise the G planes
+    // already hold the walked adjoint.
+    auto stage = [&](bool new_seq, int64_t k) {
+        if constexpr (FUSED) {
+            if (new_seq) {
+                const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc)
+                                           : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
+                const buf_t rf = make_buf(
+                    p.gfinal ? p.gfinal + ((ks.seq * p.N + ks.n0) * p.D + ks.d0) * 2 : nullptr,
+                    p.gfinal ? (uint32_t)((ks.nsl - 1) * p.D + ks.dsl) * 8u : 0u);
+                for (int j = 0; j < 8; ++j) {
+                    const int i = tid + 512 * j, n = i >> 6, d = i & 63;
+                    const v2f g = buf_load2(rf, d < ks.dsl ? (uint32_t)(n * p.D + d) * 8u : kBwdOut);
+                    sGre[n * SL + d] = g.x;
+                    sGim[n * SL + d] = -g.y;
+                }
+            }
+        }
         if constexpr (VEC) {
             for (int j = 0; j < PB; ++j) {
                 const int e = tid + 512 * j, l = e >> 5, c2 = 2 * (e & 31);
@@ -708,10 +753,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 sHim[n * SL + d2] = vh[j].y;
                 sHre[n * SL + d2 + 1] = vh[j].z;
                 sHim[n * SL + d2 + 1] = vh[j].w;
-                sGre[n * SL + d2] = vg[j].x;
-                sGim[n * SL + d2] = vg[j].y;
-                sGre[n * SL + d2 + 1] = vg[j].z;
-                sGim[n * SL + d2 + 1] = vg[j].w;
+                if constexpr (!FUSED) {
+                    sGre[n * SL + d2] = vg[j].x;
+                    sGim[n * SL + d2] = vg[j].y;
+                    sGre[n * SL + d2 + 1] = vg[j].z;
+                    sGim[n * SL + d2 + 1] = vg[j].w;
+                }
             }
             return;
         }
@@ -736,14 +783,26 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         }
     };
 
-    int64_t blk = block_id();
-    if (blk >= total)
+    // The chunk after chunk k in this workgroup's order, or -1.
+    auto next_of = [&](int64_t k) -> int64_t {
+        if constexpr (FUSED) {
+            if (k % p.nc > 0)
+                return k - 1;
+            const int64_t vs = k / p.nc + grid_blocks();
+            return vs < nvseq ? vs * p.nc + p.nc - 1 : -1;
+        } else {
+            const int64_t n = k + grid_blocks();
+            return n < total ? n : -1;
+        }
+    };
+    if (block_id() >= (FUSED ? nvseq : total))
         return;
+    int64_t blk = FUSED ? block_id() * p.nc + p.nc - 1 : block_id();
     fetch(P0{}, blk);
     fetch(P1{}, blk);
     fetch(P2{}, blk);
     fetch(P3{}, blk);
-    stage();
+    stage(true, blk);
     block_sync();
     for (;;) {
         const BwdSlice cs = SLICED ? bwd_slice(p, blk / p.nc)
@@ -766,8 +825,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 *(v2f *)&sEend[2 * lane] = cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
             }
         }
-        const int64_t next = blk + grid_blocks();
-        const bool has_next = next < total;
+        const int64_t next = next_of(blk);
+        const bool has_next = next >= 0;
         if (has_next)
             fetch(P0{}, next);
 
@@ -870,7 +929,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         //   gB: I_s  = B_s . (V^T C)_s  over l > s                    (q = 1)
         //   gC: (O + Off)_l = C_l . ((V B)_l over s < l + e_in (gy H^T)_l)  (q = 0)
         if (has_next)
-            fetch(P3{}, next);
+            fetch(P3{}, next);  // FUSED: grad_final when next starts a sequence, else nothing
         for (int tile = w; tile < 3 * NT * 4; tile += 8) {
             const int kind = tile / (NT * 4);
             const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
@@ -995,6 +1054,57 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         }
         block_sync();
 
+        if constexpr (FUSED) {
+            // G <- exp(Lam[R-1]) G + (e_in o C)^T gy, wave w on tiles w and w + 8 of
+            // the 4 x 4 grid (as the adjoint pass); after chunk 0 that is the
+            // initial-state gradient (stored conjugated back)
+            const v2f dec = cexp_diff(sLam, R - 1, -1);
+            // tiles w and w + 8 share their columns d (and so the gy operand)
+            const int dtl = w & 3, nt0 = w >> 2, nt1 = 2 + (w >> 2);
+            const int bd = dtl * 16 + (lane & 15);
+            const int an0 = nt0 * 16 + (lane & 15), an1 = nt1 * 16 + (lane & 15);
+            v4f re0, im0, re1, im1;
+            for (int r = 0; r < 4; ++r) {
+                const int n0r = nt0 * 16 + 4 * (lane >> 4) + r, n1r = nt1 * 16 + 4 * (lane >> 4) + r;
+                const v2f g0 = cmul_fixed(dec, v2f{sGre[n0r * SL + bd], sGim[n0r * SL + bd]});
+                const v2f g1 = cmul_fixed(dec, v2f{sGre[n1r * SL + bd], sGim[n1r * SL + bd]});
+                re0[r] = g0.x;
+                im0[r] = g0.y;
+                re1[r] = g1.x;
+                im1[r] = g1.y;
+            }
+#pragma unroll 1
+            for (int l0 = 0; l0 < R; l0 += 4) {
+                const int l = l0 + (lane >> 4);
+                const v2f ein = *(const v2f *)&sEin[2 * l];
+                const v2f a0 = cmul_fixed(v2f{sCre[l * LD + an0], sCim[l * LD + an0]}, ein);
+                const v2f a1 = cmul_fixed(v2f{sCre[l * LD + an1], sCim[l * LD + an1]}, ein);
+                const float g = sGy[l * LD + bd];
+                re0 = mfma_16x16x4(a0.x, g, re0);
+                im0 = mfma_16x16x4(a0.y, g, im0);
+                re1 = mfma_16x16x4(a1.x, g, re1);
+                im1 = mfma_16x16x4(a1.y, g, im1);
+            }
+            for (int r = 0; r < 4; ++r) {
+                const int n0r = nt0 * 16 + 4 * (lane >> 4) + r, n1r = nt1 * 16 + 4 * (lane >> 4) + r;
+                if (c == 0) {
+                    // after the first chunk: the initial-state gradient, conjugated back
+                    if (p.ginit && bd < cs.dsl) {
+                        const int64_t base = seq * p.N + cs.n0;
+                        if (n0r < cs.nsl)
+                            *(v2f *)&p.ginit[2 * ((base + n0r) * p.D + cs.d0 + bd)] = v2f{re0[r], -im0[r]};
+                        if (n1r < cs.nsl)
+                            *(v2f *)&p.ginit[2 * ((base + n1r) * p.D + cs.d0 + bd)] = v2f{re1[r], -im1[r]};
+                    }
+                } else {
+                    sGre[n0r * SL + bd] = re0[r];
+                    sGim[n0r * SL + bd] = im0[r];
+                    sGre[n1r * SL + bd] = re1[r];
+                    sGim[n1r * SL + bd] = im1[r];
+                }
+            }
+        }
+
         // Decay gradients. Rows j < R (wave 0): v_j = (O + Off - I)_j and the
         // edge share In_j, summed over the four column tiles in order.
         if (tid < R) {
@@ -1087,7 +1197,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         // the planes are free once the output tiles are done: stage the next
         // chunk while wave 0 finishes this one's decay gradients
         if (has_next)
-            stage();
+            stage(next % p.nc == p.nc - 1, next);
         block_sync();
         if (!has_next)
             break;

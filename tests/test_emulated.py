@@ -188,6 +188,15 @@ def _run_all_kernels(emu):
     st, *g = emu_harness.chunk_backward(emu, inp, 4, gy)
     assert st == 0
     out += g
+    # 256 sequences: the fused chunk pass walks the adjoint in shared memory
+    inp = ssd_inputs.random_case(16, 40, 16, 4, 6, seed=65)
+    rng = np.random.default_rng(65)
+    gy = rng.standard_normal((16, 40, 16, 6)).astype(np.float32)
+    gf = (rng.standard_normal((16, 16, 4, 6)) + 1j * rng.standard_normal((16, 16, 4, 6))).astype(
+        np.complex64)
+    st, *g = emu_harness.chunk_backward(emu, inp, 16, gy, gf)
+    assert st == 0
+    out += g
     y, W, gz = ssd_inputs.mix_case((300, 4, 80), seed=64)
     st, z = emu_harness.head_mix(emu, y.numpy(), W.numpy())
     st2, gyy, gW = emu_harness.head_mix_backward(emu, y.numpy(), W.numpy(), gz.numpy())
@@ -265,6 +274,32 @@ def test_emulated_noalloc_matches_workspace_call(emu):
         assert st == 0
         st, y2, fs2 = emu_harness.chunk_forward(emu, inp, Q)
         assert st == 0 and np.array_equal(y, y2) and np.array_equal(fs, fs2)
+
+
+@pytest.mark.parametrize("Q", [8, 32])
+def test_emulated_fused_adjoint_walk_matches_the_three_passes(emu, Q):
+    """256 sequences take the fused chunk pass (the adjoint walked in shared
+    memory); the same batch split into two calls of 128 sequences takes the
+    stored-adjoint passes. Same arithmetic in the same order: every per-token
+    and initial-state gradient is bit-identical; grad A (summed over the batch)
+    agrees to rounding."""
+    B, T, H, N, D = 16, 45, 16, 4, 6
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=71 + Q, dt_mean=0.3)
+    rng = np.random.default_rng(72)
+    gy = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    gf = (rng.standard_normal((B, H, N, D)) + 1j * rng.standard_normal((B, H, N, D))).astype(np.complex64)
+    st, *whole = emu_harness.chunk_backward(emu, inp, Q, gy, gf)
+    assert st == 0
+    halves = []
+    for sl in (slice(0, 8), slice(8, 16)):
+        part = ssd_inputs.ScanInputs(inp.x[sl].contiguous(), inp.A, inp.B_t[sl].contiguous(),
+                                     inp.C_t[sl].contiguous(), inp.dt[sl].contiguous())
+        st, *g = emu_harness.chunk_backward(emu, part, Q, gy[sl], gf[sl])
+        assert st == 0
+        halves.append(g)
+    for k in (0, 2, 3, 4, 5):  # gx, gB, gC, gdt, g_init
+        assert np.array_equal(whole[k], np.concatenate([halves[0][k], halves[1][k]], axis=0)), k
+    assert np.allclose(whole[1], halves[0][1] + halves[1][1], rtol=1e-5, atol=1e-4)
 
 
 def test_emulated_backward_memoryless_limit_is_exact(emu):

@@ -247,6 +247,27 @@ def test_sweep_b4_t8192_gradients(Q):
     _full_grads(g, gy, gf, Q, "sweep Q=%d" % Q)
 
 
+@pytest.mark.parametrize("Q", [64, 16])
+def test_fused_adjoint_walk_matches_the_three_passes(Q):
+    """B=16, H=16 (256 sequences) takes the fused chunk pass, which walks the
+    adjoint in shared memory; the same batch in two calls of 128 sequences takes
+    the stored-adjoint passes. Same arithmetic in the same order: the per-token
+    and initial-state gradients are bit-identical, grad A agrees to rounding."""
+    B, T, H, N, D = 16, 300, 16, 64, 64
+    inp = ssd_inputs.random_case(B, T, H, N, D, seed=95 + Q, dt_mean=0.3)
+    gy, _ = ssd_inputs.upstream_grads(B, T, H, N, D, seed=96, with_final=False)
+    gf, init = _edges(B, H, N, D, 97)
+    whole = _gpu_grads(inp, Q, gy.numpy(), gf, init)
+    halves = []
+    for sl in (slice(0, 8), slice(8, 16)):
+        part = ssd_inputs.ScanInputs(inp.x[sl].contiguous(), inp.A, inp.B_t[sl].contiguous(),
+                                     inp.C_t[sl].contiguous(), inp.dt[sl].contiguous())
+        halves.append(_gpu_grads(part, Q, gy.numpy()[sl], gf[sl], init[sl]))
+    for k in (0, 2, 3, 4, 5):
+        assert np.array_equal(whole[k], np.concatenate([halves[0][k], halves[1][k]], axis=0)), k
+    _close("fused grad A", whole[1], halves[0][1] + halves[1][1], atol=ATOL + 1e-6 * B * T)
+
+
 def test_backward_determinism_bitwise():
     inp = ssd_inputs.random_case(2, 300, 4, 64, 64, seed=77)
     gy, gf = ssd_inputs.upstream_grads(2, 300, 4, 64, 64, seed=77)
