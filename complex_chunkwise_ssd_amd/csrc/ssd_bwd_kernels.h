@@ -46,8 +46,9 @@
 namespace ssd {
 
 constexpr int kBwdMaxRows = 32;  // tokens the backward evaluates per chunk, at most
-constexpr int kBwdLd = 81;       // row stride (floats) of the [row][64] LDS planes
-constexpr int kStLd = 65;        // row stride (floats) of the 64 x 64 state planes
+constexpr int kBwdLd = 81;       // row stride (floats) of the chunk pass's [row][64] planes
+constexpr int kStLd = 65;        // ... of its 64 x 64 state planes
+constexpr int kStrideA = 80;     // ... of the state pass's [row][64] planes
 constexpr int kStateFloats = 64 * 64 * 2;  // one padded complex 64 x 64 state
 constexpr int kBwdGroups = 256;  // workgroups of the chunk pass: one per compute unit
 constexpr uint32_t kBwdOut = 0x80000000u;  // a byte offset past every buffer
@@ -85,6 +86,13 @@ struct BwdParams {
     // real.
     int64_t tok_stride;
 };
+
+// The state pass's planes are read only as 4 consecutive rows x 16 consecutive
+// columns (the contraction index runs down the rows). A wave's shared-memory
+// read is served in two halves of 32 lanes over 32 4-byte banks, and a bank
+// used twice costs a whole extra pass; a row stride of 16 mod 32 puts the two
+// rows of each half 16 banks apart.
+SSD_DEVICE int psa(int row, int col) { return row * kStrideA + col; }
 
 inline int64_t bwd_block_rows(int64_t chunk) { return chunk < kBwdMaxRows ? chunk : kBwdMaxRows; }
 
@@ -299,12 +307,11 @@ SSD_DEVICE v2f cexp_diff(const double *sLam, int l, int s)
 template <int R, bool REV, int LAYOUT>
 SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
 {
-    constexpr int LD = kBwdLd;
-    SSD_LDS float sAre[R * LD];
-    SSD_LDS float sAim[R * LD];
-    SSD_LDS float sAimN[R * LD];
-    SSD_LDS float sXre[R * LD];
-    SSD_LDS float sXim[R * LD];
+    SSD_LDS float sAre[R * kStrideA];
+    SSD_LDS float sAim[R * kStrideA];
+    SSD_LDS float sAimN[R * kStrideA];
+    SSD_LDS float sXre[R * kStrideA];
+    SSD_LDS float sXim[R * kStrideA];
     SSD_LDS float sF[2 * R];
     SSD_LDS float sDec[2];
 
@@ -421,18 +428,15 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
                 const v2f f = *(const v2f *)&sF[2 * l];
                 const v2f a0 = cmul_fixed(v2f{va[j].x, va[j].y}, f);
                 const v2f a1 = cmul_fixed(v2f{va[j].z, va[j].w}, f);
-                sAre[l * LD + c2] = a0.x;
-                sAim[l * LD + c2] = a0.y;
-                sAimN[l * LD + c2] = -a0.y;
-                sAre[l * LD + c2 + 1] = a1.x;
-                sAim[l * LD + c2 + 1] = a1.y;
-                sAimN[l * LD + c2 + 1] = -a1.y;
+                *(v2f *)&sAre[psa(l, c2)] = v2f{a0.x, a1.x};
+                *(v2f *)&sAim[psa(l, c2)] = v2f{a0.y, a1.y};
+                *(v2f *)&sAimN[psa(l, c2)] = v2f{-a0.y, -a1.y};
             }
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + 512 * j, l = i >> 6, col = i & 63;
-                sXre[l * LD + col] = px[j].x;
+                sXre[psa(l, col)] = px[j].x;
                 if (!REV)
-                    sXim[l * LD + col] = px[j].y;
+                    sXim[psa(l, col)] = px[j].y;
             }
         }
         for (int j = 0; j < (VEC ? 0 : PER); ++j) {
@@ -445,12 +449,12 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             const v2f xv = !(valid && col < D) ? v2f{0.f, 0.f}
                                                : (REV ? px[j] : bwd_widen2<LAYOUT>(px[j]));
             const v2f a = cmul_fixed(av, *(const v2f *)&sF[2 * l]);
-            sAre[l * LD + col] = a.x;
-            sAim[l * LD + col] = a.y;
-            sAimN[l * LD + col] = -a.y;
-            sXre[l * LD + col] = xv.x;
+            sAre[psa(l, col)] = a.x;
+            sAim[psa(l, col)] = a.y;
+            sAimN[psa(l, col)] = -a.y;
+            sXre[psa(l, col)] = xv.x;
             if (!REV)
-                sXim[l * LD + col] = xv.y;
+                sXim[psa(l, col)] = xv.y;
         }
         block_sync();
         if (ci + 1 < p.nc)
@@ -468,14 +472,14 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             const int d = dtl * 16 + (lane & 15);
             for (int l0 = 0; l0 < R; l0 += 4) {
                 const int l = l0 + (lane >> 4);
-                const float a_re = sAre[l * LD + n], a_im = sAim[l * LD + n];
+                const float a_re = sAre[psa(l, n)], a_im = sAim[psa(l, n)];
                 if (REV) {
-                    const float g = sXre[l * LD + d];
+                    const float g = sXre[psa(l, d)];
                     re = mfma_16x16x4(a_re, g, re);
                     im = mfma_16x16x4(a_im, g, im);
                 } else {
-                    const float a_imn = sAimN[l * LD + n];
-                    const float x_re = sXre[l * LD + d], x_im = sXim[l * LD + d];
+                    const float a_imn = sAimN[psa(l, n)];
+                    const float x_re = sXre[psa(l, d)], x_im = sXim[psa(l, d)];
                     re = mfma_16x16x4(a_re, x_re, re);
                     re = mfma_16x16x4(a_imn, x_im, re);
                     im = mfma_16x16x4(a_re, x_im, im);
