@@ -50,6 +50,8 @@ constexpr int kBwdLd = 81;       // row stride (floats) of the chunk pass's [row
 constexpr int kStLd = 65;        // ... of its 64 x 64 state planes
 constexpr int kStrideA = 80;     // ... of the state pass's [row][64] planes
 constexpr int kStateFloats = 64 * 64 * 2;  // one padded complex 64 x 64 state
+constexpr int kDecayWave = 3;   // chunk pass: the running sums of a chunk (no Gram tile)
+constexpr int kGradWave = 7;    // ... the previous chunk's decay gradients
 constexpr int kBwdGroups = 256;  // workgroups of the chunk pass: one per compute unit
 constexpr uint32_t kBwdOut = 0x80000000u;  // a byte offset past every buffer
 
@@ -236,9 +238,9 @@ SSD_DEVICE v2f bwd_load_x(const BwdParams &p, int b, int t, int h, int col)
 template <int R, int LAYOUT>
 SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
 {
-    const int tid = thread_id();
-    const int t = c * p.Q + tid;
-    return (tid < R && tid < p.Q && t < p.T)
+    const int lane = thread_id() & 63;  // every wave holds the chunk's dt in lanes < R
+    const int t = c * p.Q + lane;
+    return (lane < R && lane < p.Q && t < p.T)
                ? bwd_row_load<LAYOUT>(p.dt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0))
                : 0.f;
 }
@@ -595,12 +597,14 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sMim[R * RL];
     SSD_LDS float sVre[R * RL];
     SSD_LDS float sVim[R * RL];
-    SSD_LDS double sLam[2 * R];
-    SSD_LDS float sDt[R];
+    // running sums, dt and <H, G> partial sums of a chunk, in two slots: a chunk's
+    // decay gradients are taken while the next chunk starts
+    SSD_LDS double sLam[2][2 * R];
+    SSD_LDS float sDt[2][R];
     SSD_LDS float sEin[2 * R];
     SSD_LDS float sEend[2 * R];
     SSD_LDS float sRow[3 * 4 * 2 * R];  // [O + Off, I, In][column tile][row] complex
-    SSD_LDS float sTc[16];
+    SSD_LDS float sTc[2][16];
     SSD_LDS float sEv[2 * R];  // per row: (O - I + Off) and In, all column tiles
     SSD_LDS float sEe[2 * R];
     SSD_LDS float sVd[2 * R];  // the diagonal V[l][l], kept out of the V tiles
@@ -799,6 +803,85 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             return n < total ? n : -1;
         }
     };
+    // Decay gradients of chunk k (one wave): its row sums sEv, sEe (kept until the
+    // next chunk's output tiles), and its running sums, dt and <H, G> partial sums
+    // in slot q.
+    auto decay_grads = [&](int64_t k, int q) {
+        const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc) : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
+        const int kc = (int)(k % p.nc);
+        const int kb = (int)(ks.seq / p.H), kh = (int)(ks.seq % p.H);
+        const float kAr = p.A[2 * kh], kAi = p.A[2 * kh + 1];
+            // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>: the
+            // suffix and prefix sums over the chunk rows as lane scans (fixed trees)
+            const int t0 = lane;
+            const bool row = t0 < R;
+            float vr = row ? sEv[2 * t0] : 0.f, vi = row ? sEv[2 * t0 + 1] : 0.f;
+            float er = row ? sEe[2 * t0] : 0.f, ei = row ? sEe[2 * t0 + 1] : 0.f;
+            vr += row_shl<1>(vr);
+            vi += row_shl<1>(vi);
+            vr += row_shl<2>(vr);
+            vi += row_shl<2>(vi);
+            vr += row_shl<4>(vr);
+            vi += row_shl<4>(vi);
+            vr += row_shl<8>(vr);
+            vi += row_shl<8>(vi);
+            const float nr = lane_read(vr, 16), ni = lane_read(vi, 16);
+            if (t0 < 16) {
+                vr += nr;
+                vi += ni;
+            }
+            er += row_shr<1>(er);
+            ei += row_shr<1>(ei);
+            er += row_shr<2>(er);
+            ei += row_shr<2>(ei);
+            er += row_shr<4>(er);
+            ei += row_shr<4>(ei);
+            er += row_shr<8>(er);
+            ei += row_shr<8>(ei);
+            float xr = row_shr<1>(er), xi = row_shr<1>(ei);  // exclusive
+            const float pr = lane_read(er, 15), pi = lane_read(ei, 15);
+            if (t0 >= 16) {
+                xr += pr;
+                xi += pi;
+            }
+            float tr = 0.f, ti = 0.f;
+            for (int i = 0; i < 8; ++i) {
+                tr += sTc[q][2 * i];
+                ti += sTc[q][2 * i + 1];
+            }
+            const v2f Tc = cmul(cexp_diff(sLam[q], R - 1, -1), v2f{tr, ti});
+            const float fr = (vr + xr) + Tc.x, fi = (vi + xi) + Tc.y;
+            float gAr = 0.f, gAi = 0.f;
+            const int t = kc * p.Q + t0;
+            if (row && t0 < p.Q && t < p.T) {
+                // ga = conj(dF/da)
+                const float gar = fr, gai = -fi;
+                const float dtv = sDt[q][t0];
+                const float sig = 1.f / (1.f + expf(-dtv));
+                if constexpr (SLICED)
+                    p.gdt_part[((int64_t)ks.st * p.B * p.T + (int64_t)kb * p.T + t) * p.H + kh] =
+                        (kAr * gar + kAi * gai) * sig;
+                else
+                    bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, kb, t, kh, 1, 0),
+                                          (kAr * gar + kAi * gai) * sig);
+                const float sp = softplus_f(dtv);
+                gAr = sp * gar;
+                gAi = sp * gai;
+            }
+            // this chunk's share of gA: a fixed-order sum over the wave
+            gAr += row_shr<1>(gAr);
+            gAr += row_shr<2>(gAr);
+            gAr += row_shr<4>(gAr);
+            gAr += row_shr<8>(gAr);
+            gAi += row_shr<1>(gAi);
+            gAi += row_shr<2>(gAi);
+            gAi += row_shr<4>(gAi);
+            gAi += row_shr<8>(gAi);
+            const float r0 = lane_read(gAr, 15), r1 = lane_read(gAr, 31);
+            const float i0 = lane_read(gAi, 15), i1 = lane_read(gAi, 31);
+            if (lane == 0)
+                *(v2f *)&p.gA_part[2 * k] = v2f{r0 + r1, i0 + i1};
+    };
     if (block_id() >= (FUSED ? nvseq : total))
         return;
     int64_t blk = FUSED ? block_id() * p.nc + p.nc - 1 : block_id();
@@ -808,6 +891,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     fetch(P3{}, blk);
     stage(true, blk);
     block_sync();
+    int par = 0;         // slot of this chunk's running sums, dt and <H, G> sums
+    int64_t prev = -1;   // the chunk whose decay gradients are still to be taken
     for (;;) {
         const BwdSlice cs = SLICED ? bwd_slice(p, blk / p.nc)
                                    : BwdSlice{blk / p.nc, 0, 0, 0, p.N, p.D};
@@ -815,20 +900,22 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         const int c = (int)(blk % p.nc);
         const int b = (int)(seq / p.H), h = (int)(seq % p.H);
         const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
-        if (w == 0) {
+        if (w == kDecayWave) {
             // running sums and row factors of this chunk; read after the next barrier
             double lr, li, er, ei;
             const float dtv = bwd_widen<LAYOUT>(pdt);
             wave_decays<R>(p, c, dtv, Ar, Ai, lr, li, er, ei);
             if (lane < R) {
                 const int t = c * p.Q + lane;
-                sLam[2 * lane] = lr;
-                sLam[2 * lane + 1] = li;
-                sDt[lane] = (lane < p.Q && t < p.T) ? dtv : 0.f;
+                sLam[par][2 * lane] = lr;
+                sLam[par][2 * lane + 1] = li;
+                sDt[par][lane] = (lane < p.Q && t < p.T) ? dtv : 0.f;
                 *(v2f *)&sEin[2 * lane] = cexp_f(v2f{(float)lr, (float)li});
                 *(v2f *)&sEend[2 * lane] = cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
             }
         }
+        if (w == kGradWave && prev >= 0)
+            decay_grads(prev, par ^ 1);
         const int64_t next = next_of(blk);
         const bool has_next = next >= 0;
         if (has_next)
@@ -885,8 +972,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const float t0i = lane_read(ti, 15), t1i = lane_read(ti, 31);
             const float t2i = lane_read(ti, 47), t3i = lane_read(ti, 63);
             if (lane == 0) {
-                sTc[2 * w] = (t0r + t1r) + (t2r + t3r);
-                sTc[2 * w + 1] = (t0i + t1i) + (t2i + t3i);
+                sTc[par][2 * w] = (t0r + t1r) + (t2r + t3r);
+                sTc[par][2 * w + 1] = (t0i + t1i) + (t2i + t3i);
             }
         }
         block_sync();
@@ -905,7 +992,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int l = i / R, s = i % R;
             float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
             if (l >= s) {
-                const v2f L = cexp_diff(sLam, l, s);
+                const v2f L = cexp_diff(sLam[par], l, s);
                 const v2f m = cmul(v2f{sMre[l * RL + s], sMim[l * RL + s]}, L);
                 const v2f v = cmul(v2f{sVre[l * RL + s], sVim[l * RL + s]}, L);
                 mr = m.x;
@@ -1062,7 +1149,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             // G <- exp(Lam[R-1]) G + (e_in o C)^T gy, wave w on tiles w and w + 8 of
             // the 4 x 4 grid (as the adjoint pass); after chunk 0 that is the
             // initial-state gradient (stored conjugated back)
-            const v2f dec = cexp_diff(sLam, R - 1, -1);
+            const v2f dec = cexp_diff(sLam[par], R - 1, -1);
             // tiles w and w + 8 share their columns d (and so the gy operand)
             const int dtl = w & 3, nt0 = w >> 2, nt1 = 2 + (w >> 2);
             const int bd = dtl * 16 + (lane & 15);
@@ -1126,87 +1213,18 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             *(v2f *)&sEe[2 * tid] = e;
         }
         block_sync();
-        if (w == 0) {
-            // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>: the
-            // suffix and prefix sums over the chunk rows as lane scans (fixed trees)
-            const int t0 = lane;
-            const bool row = t0 < R;
-            float vr = row ? sEv[2 * t0] : 0.f, vi = row ? sEv[2 * t0 + 1] : 0.f;
-            float er = row ? sEe[2 * t0] : 0.f, ei = row ? sEe[2 * t0 + 1] : 0.f;
-            vr += row_shl<1>(vr);
-            vi += row_shl<1>(vi);
-            vr += row_shl<2>(vr);
-            vi += row_shl<2>(vi);
-            vr += row_shl<4>(vr);
-            vi += row_shl<4>(vi);
-            vr += row_shl<8>(vr);
-            vi += row_shl<8>(vi);
-            const float nr = lane_read(vr, 16), ni = lane_read(vi, 16);
-            if (t0 < 16) {
-                vr += nr;
-                vi += ni;
-            }
-            er += row_shr<1>(er);
-            ei += row_shr<1>(ei);
-            er += row_shr<2>(er);
-            ei += row_shr<2>(ei);
-            er += row_shr<4>(er);
-            ei += row_shr<4>(ei);
-            er += row_shr<8>(er);
-            ei += row_shr<8>(ei);
-            float xr = row_shr<1>(er), xi = row_shr<1>(ei);  // exclusive
-            const float pr = lane_read(er, 15), pi = lane_read(ei, 15);
-            if (t0 >= 16) {
-                xr += pr;
-                xi += pi;
-            }
-            float tr = 0.f, ti = 0.f;
-            for (int i = 0; i < 8; ++i) {
-                tr += sTc[2 * i];
-                ti += sTc[2 * i + 1];
-            }
-            const v2f Tc = cmul(cexp_diff(sLam, R - 1, -1), v2f{tr, ti});
-            const float fr = (vr + xr) + Tc.x, fi = (vi + xi) + Tc.y;
-            float gAr = 0.f, gAi = 0.f;
-            const int t = c * p.Q + t0;
-            if (row && t0 < p.Q && t < p.T) {
-                // ga = conj(dF/da)
-                const float gar = fr, gai = -fi;
-                const float dtv = sDt[t0];
-                const float sig = 1.f / (1.f + expf(-dtv));
-                if constexpr (SLICED)
-                    p.gdt_part[((int64_t)cs.st * p.B * p.T + (int64_t)b * p.T + t) * p.H + h] =
-                        (Ar * gar + Ai * gai) * sig;
-                else
-                    bwd_row_store<LAYOUT>(p.gdt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0),
-                                          (Ar * gar + Ai * gai) * sig);
-                const float sp = softplus_f(dtv);
-                gAr = sp * gar;
-                gAi = sp * gai;
-            }
-            // this chunk's share of gA: a fixed-order sum over the wave
-            gAr += row_shr<1>(gAr);
-            gAr += row_shr<2>(gAr);
-            gAr += row_shr<4>(gAr);
-            gAr += row_shr<8>(gAr);
-            gAi += row_shr<1>(gAi);
-            gAi += row_shr<2>(gAi);
-            gAi += row_shr<4>(gAi);
-            gAi += row_shr<8>(gAi);
-            const float r0 = lane_read(gAr, 15), r1 = lane_read(gAr, 31);
-            const float i0 = lane_read(gAi, 15), i1 = lane_read(gAi, 31);
-            if (lane == 0)
-                *(v2f *)&p.gA_part[2 * blk] = v2f{r0 + r1, i0 + i1};
-        }
-        // the planes are free once the output tiles are done: stage the next
-        // chunk while wave 0 finishes this one's decay gradients
+        // the planes are free once the output tiles and the G update are done
         if (has_next)
             stage(next % p.nc == p.nc - 1, next);
         block_sync();
+        prev = blk;
+        par ^= 1;
         if (!has_next)
             break;
         blk = next;
     }
+    if (w == kGradWave)
+        decay_grads(prev, par ^ 1);
 }
 
 // Sums the slices' partial gradients in slice order and stores them in the output
