@@ -603,6 +603,9 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     SSD_LDS float sDt[2][R];
     SSD_LDS float sEin[2 * R];
     SSD_LDS float sEend[2 * R];
+    // R = 32: exp(Lam[l] - Lam[15]) for l >= 16 and exp(Lam[15] - Lam[s]) for s < 16,
+    // whose products are the decays of the pairs (l >= 16, s < 16)
+    SSD_LDS float sFac[2 * R];
     SSD_LDS float sRow[3 * 4 * 2 * R];  // [O + Off, I, In][column tile][row] complex
     SSD_LDS float sTc[2][16];
     SSD_LDS float sEv[2 * R];  // per row: (O - I + Off) and In, all column tiles
@@ -905,6 +908,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             double lr, li, er, ei;
             const float dtv = bwd_widen<LAYOUT>(pdt);
             wave_decays<R>(p, c, dtv, Ar, Ai, lr, li, er, ei);
+            const double mr = lane_read_d(lr, 15), mi = lane_read_d(li, 15);
+            if (R == 32 && lane < R)
+                *(v2f *)&sFac[2 * lane] = lane < 16 ? cexp_f(v2f{(float)(mr - lr), (float)(mi - li)})
+                                                    : cexp_f(v2f{(float)(lr - mr), (float)(li - mi)});
             if (lane < R) {
                 const int t = c * p.Q + lane;
                 sLam[par][2 * lane] = lr;
@@ -988,11 +995,15 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         // pair with itself, which no decay multiplies, must not enter them (it
         // would cancel between two differently rounded sums). The output tiles
         // add the diagonal term back from sVd.
-        for (int i = tid; i < R * R; i += 512) {
-            const int l = i / R, s = i % R;
+        // R = 32, two passes of the 512 threads: first the two diagonal 16 x 16
+        // tiles (an exponential of a difference of running sums per pair), then
+        // the tile below them (a product of the two factors in sFac) on waves 0-3
+        // and the zero tile above on waves 4-7. R = 16: one diagonal tile.
+        auto pair = [&](int l, int s, int how) {  // how: 0 exponential, 1 factors, 2 zero
             float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
-            if (l >= s) {
-                const v2f L = cexp_diff(sLam[par], l, s);
+            if (how == 1 || (how == 0 && l >= s)) {
+                const v2f L = how == 0 ? cexp_diff(sLam[par], l, s)
+                                       : cmul(*(const v2f *)&sFac[2 * l], *(const v2f *)&sFac[2 * s]);
                 const v2f m = cmul(v2f{sMre[l * RL + s], sMim[l * RL + s]}, L);
                 const v2f v = cmul(v2f{sVre[l * RL + s], sVim[l * RL + s]}, L);
                 mr = m.x;
@@ -1009,6 +1020,17 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             sMim[l * RL + s] = mi;
             sVre[l * RL + s] = vr;
             sVim[l * RL + s] = vi;
+        };
+        if constexpr (R == 32) {
+            const int e = tid & 255, hi = tid >> 8;  // hi: waves 4-7
+            pair(16 * hi + (e >> 4), 16 * hi + (e & 15), 0);
+            if (hi == 0)
+                pair(16 + (e >> 4), e & 15, 1);
+            else
+                pair(e >> 4, 16 + (e & 15), 2);
+        } else {
+            for (int i = tid; i < R * R; i += 512)
+                pair(i / R, i % R, 0);
         }
         block_sync();
 
