@@ -120,6 +120,11 @@ SSD_DEVICE float lane_read(float v, int src)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
 }
 // A wave-uniform value kept in scalar registers.
+// v from lane src (any lane of the wave, chosen per lane).
+SSD_DEVICE float lane_fetch(float v, int src)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
 SSD_DEVICE float uniform(float v)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));

@@ -67,9 +67,11 @@ SSD_KERNEL(256) void segment_prefix_kernel(ScanParams p)
 // a real fp32 MFMA product with K = 2N:
 //   Re(C' H) = [Re C' | -Im C'] [Re H ; Im H],  C' = exp(Lambda_t) C_t,
 // with H (the wave's columns) held in registers for the whole group and C'
-// staged in shared memory by all threads. Step s = 4u + j of the 32 K-steps
-// uses k = 16u + 4 (L / 16) + j on lane L, so each lane reads its four A values
-// of four steps as one 16-byte word.
+// staged in shared memory by all threads, in two buffers taken in turn: one
+// barrier per chunk. Every wave takes the chunk's decays itself. Step s = 4u + j
+// of the 32 K-steps uses k = 16u + 4 (L / 16) + j on lane L, so each lane reads
+// its four A values of four steps as one 16-byte word; the chunk's row tiles
+// are independent accumulators, interleaved step by step.
 template <int R, int LAYOUT>
 SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
 {
@@ -83,8 +85,7 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
     constexpr uint32_t kOut = 0x80000000u;
     static_assert(R % ROWS_PER_PASS == 0, "row passes must tile the chunk");
 
-    SSD_LDS float sCp[R * LDK];
-    SSD_LDS v2f sE[R];  // exp(Lambda_t)
+    SSD_LDS float sCp[2][R * LDK];
 
     const int tid = thread_id();
     const int lane = tid & 63;
@@ -152,8 +153,8 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
         const uint32_t offC = ncol < nsl ? (uint32_t)(tid >> 5) * brow + ncol * (PROJ ? ES : 8u) : kOut;
         const uint32_t offY = dvalid ? (uint32_t)(4 * Lk) * yrow + dl * 4u : kOut;
 
-        // A chunk's inputs in registers: dt (wave 0's lanes), C rows, and the y
-        // values this lane will update. fetch(c) issues the loads for chunk c; past
+        // A chunk's inputs in registers: dt (lanes below R, every wave), C rows, and
+        // the y values this lane will update. fetch(c) issues the loads for chunk c; past
         // the group's last chunk every buffer is empty, so the loads still issue
         // (the wait counters stay exact) and read zero.
         struct Inputs {
@@ -173,7 +174,7 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
             const int64_t tok = bt0 + (int64_t)(live ? c : c_begin) * p.Q;
             const void *dt0 = PROJ ? at(p.dt, tok * p.tok_stride + h) : (const void *)(p.dt + tok * p.H + h);
             const buf_t bT = make_buf(dt0, live ? (rows - 1) * drow + ES : 0u);
-            const uint32_t od = w == 0 ? (uint32_t)lane * drow : kOut;
+            const uint32_t od = lane < R ? (uint32_t)lane * drow : kOut;
             in.dt = BF16 ? bf16_lo(buf_load_u16(bT, od)) : buf_load1(bT, od);
             const void *c0 = PROJ ? at(p.Ct, tok * p.tok_stride + (int64_t)h * p.N + n0)
                                   : (const void *)(p.Ct + ((tok * p.H + h) * (int64_t)p.N + n0) * 2);
@@ -203,58 +204,62 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
 
         Inputs nx;
         fetch(c_begin, nx);
+        if (ns > 0)
+            block_sync();  // every wave is done with the previous slice's last buffers
         for (int c = c_begin; c < c_end; ++c) {
             const Inputs cur = nx;
             const uint32_t rows = (uint32_t)rows_of(c);
-            // Lambda_t for the chunk's rows: wave 0 scans a = softplus(dt) A.
-            if (w == 0) {
-                const float sp = softplus_f(cur.dt);
-                const v2f a = (uint32_t)lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
-                v2f lam = a;
-                lam += v2f{row_shr<1>(lam.x), row_shr<1>(lam.y)};
-                lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
-                lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
-                lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
-                // add the totals of the earlier 16-row tiles and the chunk-start log
-                v2f base = *(const v2f *)&p.chunk_log[(bh * p.nc + c) * 2];
-                for (int t = 0; t < NR - 1; ++t) {
-                    const v2f tt = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
-                    if ((lane >> 4) > t)
-                        base += tt;
-                }
-                if (lane < R)
-                    sE[lane] = cexp_f(lam + base);
+            float *cp = sCp[(c - c_begin) & 1];
+            // Lambda_t for the chunk's rows (lane t): a = softplus(dt) A summed in
+            // 16-lane rows, then the earlier rows' totals and the chunk-start log.
+            const float sp = softplus_f(cur.dt);
+            const v2f a = (uint32_t)lane < rows ? v2f{Ah.x * sp, Ah.y * sp} : v2f{0.f, 0.f};
+            v2f lam = a;
+            lam += v2f{row_shr<1>(lam.x), row_shr<1>(lam.y)};
+            lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
+            lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
+            lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
+            v2f base = *(const v2f *)&p.chunk_log[(bh * p.nc + c) * 2];
+            for (int t = 0; t < NR - 1; ++t) {
+                const v2f tt = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
+                if ((lane >> 4) > t)
+                    base += tt;
             }
-            block_sync();  // sE ready; the previous chunk's products have read sCp
+            const v2f e = cexp_f(lam + base);
 #pragma unroll
             for (int i = 0; i < R / ROWS_PER_PASS; ++i) {
                 const int row = ROWS_PER_PASS * i + (tid >> 5);
-                const v2f e = sE[row];
-                const v2f a0 = cmul(e, v2f{cur.cv[i].x, cur.cv[i].y});
-                const v2f a1 = cmul(e, v2f{cur.cv[i].z, cur.cv[i].w});
-                *(v2f *)&sCp[row * LDK + ncol] = v2f{a0.x, a1.x};
-                *(v2f *)&sCp[row * LDK + kNPad + ncol] = v2f{-a0.y, -a1.y};
+                const v2f er = v2f{lane_fetch(e.x, row), lane_fetch(e.y, row)};
+                const v2f a0 = cmul(er, v2f{cur.cv[i].x, cur.cv[i].y});
+                const v2f a1 = cmul(er, v2f{cur.cv[i].z, cur.cv[i].w});
+                *(v2f *)&cp[row * LDK + ncol] = v2f{a0.x, a1.x};
+                *(v2f *)&cp[row * LDK + kNPad + ncol] = v2f{-a0.y, -a1.y};
             }
             block_sync();
             fetch(c + 1, nx);  // in flight during the products
             const buf_t bY = ybuf(c);
+            v4f acc[NR];
 #pragma unroll
-            for (int t = 0; t < NR; ++t) {
-                v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-                const float *arow = sCp + (16 * t + Lr) * LDK + 4 * Lk;
+            for (int t = 0; t < NR; ++t)
+                acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < KSTEPS / 4; ++u) {
-                    const v4f a4 = *(const v4f *)(arow + 16 * u);
-                    acc = mfma_16x16x4(a4.x, hb[4 * u + 0], acc);
-                    acc = mfma_16x16x4(a4.y, hb[4 * u + 1], acc);
-                    acc = mfma_16x16x4(a4.z, hb[4 * u + 2], acc);
-                    acc = mfma_16x16x4(a4.w, hb[4 * u + 3], acc);
-                }
-                // lane holds rows 16t + 4Lk + r of column dl
+            for (int u = 0; u < KSTEPS / 4; ++u) {
+                v4f a4[NR];
+#pragma unroll
+                for (int t = 0; t < NR; ++t)
+                    a4[t] = *(const v4f *)(cp + (16 * t + Lr) * LDK + 4 * Lk + 16 * u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int t = 0; t < NR; ++t)
+                        acc[t] = mfma_16x16x4(a4[t][j], hb[4 * u + j], acc[t]);
+            }
+            // lane holds rows 16t + 4Lk + r of column dl
+#pragma unroll
+            for (int t = 0; t < NR; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    buf_store1(bY, offY + (uint32_t)(16 * t + r) * yrow, cur.yv[t][r] + acc[r]);
-            }
+                    buf_store1(bY, offY + (uint32_t)(16 * t + r) * yrow, cur.yv[t][r] + acc[t][r]);
         }
     }  // slices of N
 }

@@ -62,7 +62,7 @@ struct dim3 {
 namespace emu {
 
 enum { RUN = 0, AT_MFMA, AT_BARRIER, AT_SHFL, DONE };
-enum { SH_SHR = 0, SH_SHL, SH_READ };
+enum { SH_SHR = 0, SH_SHL, SH_READ, SH_IDX };
 
 struct Fiber {
     void *sp;
@@ -196,6 +196,8 @@ static void resolve_wave(int w, bool &progress)
             } else if (mode == SH_SHL) {
                 zero = (l & 15) + f.arg >= 16;
                 src = l + f.arg;
+            } else if (mode == SH_IDX) {
+                src = f.arg & 63;
             } else {
                 if (f.arg != g_f[lo].arg) {
                     fprintf(stderr, "emu: lane_read with a non-uniform source lane\n");
@@ -360,6 +362,7 @@ SSD_DEVICE int lane_read_i(int v, int src)
 {
     return __builtin_bit_cast(int, emu_shfl(__builtin_bit_cast(float, v), emu::SH_READ, src));
 }
+SSD_DEVICE float lane_fetch(float v, int src) { return emu_shfl(v, emu::SH_IDX, src); }
 SSD_DEVICE float uniform(float v) { return v; }
 // A wave-level meeting point: every lane of the wave arrives before any goes on.
 SSD_DEVICE void wave_lds_sync() { (void)emu_shfl(0.f, emu::SH_READ, 0); }
