@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 #include <vector>
 
 static float *alloc_fill(size_t n, unsigned &seed)
@@ -188,9 +189,38 @@ static int run_mix(int64_t M, int H, int D)
     return st != 0 || st2 != 0 || bad != 0;
 }
 
-int main()
+// With the argument "races": a subset for the ThreadSanitizer build (each kind of
+// kernel and every barrier pattern once, small enough for the sanitizer's cost).
+static int races()
 {
+    setvbuf(stdout, nullptr, _IOLBF, 0);
     int fails = 0;
+    fails += run(16, 20, 16, 4, 6, 16, true, true);   // two chunks per workgroup, staged ahead
+    fails += run(1, 130, 1, 8, 8, 3, true, true);     // many segments: prefix and fix-up
+    fails += run(1, 40, 1, 130, 70, 16, true, true);  // N and D slices, segments
+    fails += run_bwd(16, 37, 16, 4, 6, 32, true, true, true);   // the fused adjoint walk
+    fails += run_bwd(1, 70, 1, 64, 64, 64, false, true, true);  // three passes, R = 32
+    fails += run_bwd(1, 40, 1, 130, 70, 16, true, true, true);  // state blocks, partials summed
+    fails += run_mix(300, 4, 80);   // ragged GEMM tiles, two LDS stages
+    fails += run_mix(2100, 2, 4);   // split grad_W and its sum
+    printf("%s\n", fails ? "FAIL" : "OK");
+    return fails;
+}
+
+// With the argument "half0" or "half1": every other case (two processes can split the list).
+int main(int argc, char **argv)
+{
+    if (argc > 1 && strcmp(argv[1], "races") == 0)
+        return races();
+    const int half = argc > 1 && strcmp(argv[1], "half0") == 0 ? 0
+                     : argc > 1 && strcmp(argv[1], "half1") == 0 ? 1 : -1;
+    int fails = 0, k = 0;
+#define run(...) (half < 0 || (k++ & 1) == half ? run(__VA_ARGS__) : 0)
+#define run_bwd(...) (half < 0 || (k++ & 1) == half ? run_bwd(__VA_ARGS__) : 0)
+#define run_proj(...) (half < 0 || (k++ & 1) == half ? run_proj(__VA_ARGS__) : 0)
+#define run_bwd_proj(...) (half < 0 || (k++ & 1) == half ? run_bwd_proj(__VA_ARGS__) : 0)
+#define run_bwd_proj_bf16(...) (half < 0 || (k++ & 1) == half ? run_bwd_proj_bf16(__VA_ARGS__) : 0)
+#define run_mix(...) (half < 0 || (k++ & 1) == half ? run_mix(__VA_ARGS__) : 0)
     fails += run(1, 40, 2, 4, 5, 16, true, true);    // padded N, D; partial chunk
     fails += run(1, 70, 1, 64, 64, 64, false, true);  // full tiles, partial last chunk
     fails += run(1, 45, 1, 6, 70, 32, true, true);    // two D slices

@@ -17,6 +17,18 @@
 // another wave writes or reads in the same interval) makes the result depend
 // on the order and shows as a difference between seeds.
 //
+// Under ThreadSanitizer (a -fsanitize=thread host build) every wave is one
+// sanitizer fiber (its lanes run in lockstep on the GPU, so their accesses are
+// in program order), switched to without implied ordering, and the only
+// happens-before edges between waves are the GPU's own: a workgroup barrier
+// orders every access of the workgroup before it against every access after it,
+// and launches and workgroups are ordered one after another. Two accesses to the
+// same word of shared (or global) memory by different waves with no barrier
+// between them, one of them a write, are reported as a race, whatever order the
+// fibers happened to run in. Each ordering token alternates between two slots by
+// generation, so that a wave resuming late cannot pick up releases that faster
+// waves made after the point it is synchronising on.
+//
 // MFMA 16x16x4 fp32 data layout emulated here (one wave64):
 //   lane L supplies A[L % 16][L / 16] and B[L / 16][L % 16];
 //   component r of lane L's accumulator is D[4 * (L / 16) + r][L % 16].
@@ -37,6 +49,19 @@
 #endif
 #ifdef EMU_ASAN
 #include <sanitizer/common_interface_defs.h>
+#endif
+#if defined(__has_feature)
+#if __has_feature(thread_sanitizer)
+#define EMU_TSAN 1
+#endif
+#elif defined(__SANITIZE_THREAD__)
+#define EMU_TSAN 1
+#endif
+#ifdef EMU_TSAN
+#include <sanitizer/tsan_interface.h>
+extern "C" void AnnotateBenignRaceSized(const char *file, int line, const volatile void *mem,
+                                        size_t size, const char *desc);
+#define EMU_TSAN_BENIGN(p, n) AnnotateBenignRaceSized(__FILE__, __LINE__, (p), (n), "emulator state")
 #endif
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -75,6 +100,9 @@ struct Fiber {
     int mode, arg;
     float sv, sr;
     long sync_count;  // number of collectives this thread has joined
+#ifdef EMU_TSAN
+    int bars;         // workgroup barriers passed in this workgroup
+#endif
 };
 
 static const size_t kStack = 256 * 1024;
@@ -91,6 +119,12 @@ static unsigned long long g_shuffle = 0;  // 0: index order; else the state of a
 static int *g_order = nullptr;
 static int g_order_cap = 0;
 static int g_error = 0;
+#ifdef EMU_TSAN
+static void *g_sched_tsan = nullptr;
+static void *g_wave_tsan[16];  // this workgroup's waves
+static char g_tok_block[2];    // workgroup k releases slot k % 2 and acquires the other
+static char g_tok_bar[2];      // barrier generation g: slot g % 2
+#endif
 #ifdef EMU_ASAN
 static void *g_fake_stack = nullptr;
 static const void *g_sched_bottom = nullptr;
@@ -111,6 +145,9 @@ __asm__(".text\n"
 static void to_scheduler()
 {
     Fiber &f = g_f[g_cur];
+#ifdef EMU_TSAN
+    __tsan_switch_to_fiber(g_sched_tsan, __tsan_switch_to_fiber_no_sync);
+#endif
 #ifdef EMU_ASAN
     void *fake = nullptr;
     __sanitizer_start_switch_fiber(f.state == DONE ? nullptr : &fake, g_sched_bottom, g_sched_size);
@@ -126,7 +163,13 @@ static void trampoline()
 #ifdef EMU_ASAN
     __sanitizer_finish_switch_fiber(nullptr, &g_sched_bottom, &g_sched_size);
 #endif
+#ifdef EMU_TSAN
+    __tsan_acquire(&g_tok_block[(g_block & 1) ^ 1]);
+#endif
     (*g_fn)();
+#ifdef EMU_TSAN
+    __tsan_release(&g_tok_block[g_block & 1]);
+#endif
     g_f[g_cur].state = DONE;
     to_scheduler();
     abort();  // never resumed
@@ -135,6 +178,9 @@ static void trampoline()
 static void run_fiber(int i)
 {
     g_cur = i;
+#ifdef EMU_TSAN
+    __tsan_switch_to_fiber(g_wave_tsan[i >> 6], __tsan_switch_to_fiber_no_sync);
+#endif
 #ifdef EMU_ASAN
     __sanitizer_start_switch_fiber(&g_fake_stack, g_f[i].stack, kStack);
 #endif
@@ -156,6 +202,11 @@ static void init_fiber(int i)
     f.sp = sp;
     f.state = RUN;
     f.sync_count = 0;
+#ifdef EMU_TSAN
+    f.bars = 0;
+    if ((i & 63) == 0)
+        g_wave_tsan[i >> 6] = __tsan_create_fiber(0);
+#endif
 }
 
 static void resolve_wave(int w, bool &progress)
@@ -224,7 +275,21 @@ static void launch(dim3 grid, dim3 block, std::function<void()> fn)
         for (int i = 0; i < n; ++i)
             g_f[i].stack = (char *)aligned_alloc(64, kStack);
         g_cap = n;
+#ifdef EMU_TSAN
+        EMU_TSAN_BENIGN(g_f, (size_t)n * sizeof(Fiber));
+#endif
     }
+#ifdef EMU_TSAN
+    // the scheduler's bookkeeping, read by every thread (thread and block ids)
+    EMU_TSAN_BENIGN(&g_cur, sizeof(g_cur));
+    EMU_TSAN_BENIGN(&g_block, sizeof(g_block));
+    EMU_TSAN_BENIGN(&g_grid, sizeof(g_grid));
+    EMU_TSAN_BENIGN(&g_fn, sizeof(g_fn));
+    EMU_TSAN_BENIGN(&g_f, sizeof(g_f));
+    EMU_TSAN_BENIGN(&g_sched_tsan, sizeof(g_sched_tsan));
+    g_sched_tsan = __tsan_get_current_fiber();
+    __tsan_release(&g_tok_block[1]);  // the host's writes before the launch, for workgroup 0
+#endif
     g_n = n;
     g_fn = &fn;
     const int64_t blocks = (int64_t)grid.x * grid.y * grid.z;
@@ -286,7 +351,15 @@ static void launch(dim3 grid, dim3 block, std::function<void()> fn)
                 abort();
             }
         }
+#ifdef EMU_TSAN
+        for (int w = 0; w * 64 < n; ++w)
+            __tsan_destroy_fiber(g_wave_tsan[w]);
+#endif
     }
+#ifdef EMU_TSAN
+    __tsan_acquire(&g_tok_block[0]);  // the host reads what the launch wrote
+    __tsan_acquire(&g_tok_block[1]);
+#endif
     g_fn = nullptr;
 }
 
@@ -435,6 +508,13 @@ SSD_DEVICE void sched_fence() {}
 
 SSD_DEVICE void block_sync()
 {
+#ifdef EMU_TSAN
+    const int slot = emu::g_f[emu::g_cur].bars++ & 1;
+    __tsan_release(&emu::g_tok_bar[slot]);
+#endif
     emu::g_f[emu::g_cur].state = emu::AT_BARRIER;
     emu::to_scheduler();
+#ifdef EMU_TSAN
+    __tsan_acquire(&emu::g_tok_bar[slot]);
+#endif
 }

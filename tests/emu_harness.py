@@ -51,6 +51,18 @@ def build_asan_exe(out_dir):
     return out
 
 
+def build_tsan_exe(out_dir):
+    """The bounds-check driver built under ThreadSanitizer (host code only): the
+    emulator turns every GPU thread into a sanitizer fiber whose only ordering is
+    the GPU's (barriers, a wave's collectives, launches), so a shared-memory
+    access pair that no barrier orders is reported."""
+    out = os.path.join(out_dir, "ssd_emu_tsan")
+    cmd = [CLANG, *_flags(), "-O1", "-g", "-fsanitize=thread",
+           os.path.join(EMU, "emu_asan_main.cpp"), "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def load(out_dir):
     global _lib
     with _lock:

@@ -103,9 +103,13 @@ def test_emulated_chunk_size_invariance(emu):
 
 def test_asan_bounds(tmp_path):
     exe = emu_harness.build_asan_exe(str(tmp_path))
-    res = subprocess.run([exe], capture_output=True, text=True, timeout=600)
-    assert res.returncode == 0, res.stdout + res.stderr
-    assert "OK" in res.stdout
+    # the case list in two halves, run side by side
+    procs = [subprocess.Popen([exe, half], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                              text=True) for half in ("half0", "half1")]
+    for p in procs:
+        out, err = p.communicate(timeout=600)
+        assert p.returncode == 0, out + err
+        assert "OK" in out
 
 
 def test_kernel_sincos_accuracy(emu):
@@ -256,6 +260,56 @@ def test_shuffled_order_catches_a_missing_barrier(tmp_path):
         outs.append(y)
     assert not (np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])), \
         "the shuffled order did not expose the missing barrier"
+
+
+def test_tsan_finds_no_unordered_shared_memory_access(tmp_path):
+    """The kernels under ThreadSanitizer (host build): every GPU thread is a
+    sanitizer fiber, ordered only by barriers, its wave's collectives and the
+    launches, so any pair of accesses to one word of shared or global memory by
+    two threads with no barrier between them, one a write, is reported. Cases:
+    workgroups that stage the next chunk behind the current one, segments with
+    their prefix and fix-up passes, N and D slices, the fused adjoint walk (its
+    deferred decay gradients and two-slot per-chunk values), the three-pass
+    backward, state blocks, and the mixer's two-stage GEMM."""
+    exe = emu_harness.build_tsan_exe(str(tmp_path))
+    res = subprocess.run([exe, "races"], capture_output=True, text=True, timeout=1200)
+    out = res.stdout + res.stderr
+    assert "WARNING: ThreadSanitizer" not in out, out[:6000]
+    assert res.returncode == 0 and "OK" in res.stdout, out[-3000:]
+
+
+def test_tsan_reports_a_missing_barrier(tmp_path):
+    """The check itself: a copy of the scan kernel without the barrier between
+    phase 2 (each wave leaves its partial y in shared memory) and the y stores
+    (which read the partner wave's part) is reported as a race."""
+    import shutil
+    src = tmp_path / "csrc"
+    shutil.copytree(emu_harness.CSRC, src)
+    text = (src / "ssd_kernels.h").read_text()
+    anchor = "        block_sync();\n\n        // ---- store y."
+    assert text.count(anchor) == 1
+    (src / "ssd_kernels.h").write_text(text.replace(anchor, "\n        // ---- store y."))
+    main = tmp_path / "tsan_planted.cpp"
+    main.write_text('#include "%s"\n'
+                    'int main() {\n'
+                    '  const int B = 1, T = 40, H = 1, N = 4, D = 6, Q = 16;\n'
+                    '  static float x[B * T * H * D * 2], A[2] = {-0.5f, 1.f}, Bt[B * T * H * N * 2],\n'
+                    '      Ct[B * T * H * N * 2], dt[B * T * H], y[B * T * H * D];\n'
+                    '  for (int i = 0; i < B * T * H * D * 2; ++i) x[i] = 0.01f * (i %% 7);\n'
+                    '  for (int i = 0; i < B * T * H * N * 2; ++i) Bt[i] = Ct[i] = 0.02f * (i %% 5);\n'
+                    '  size_t ws = ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q);\n'
+                    '  void *w = ws ? aligned_alloc(256, ws) : nullptr;\n'
+                    '  return ssd_chunk_forward((ssd_c64 *)x, (ssd_c64 *)A, (ssd_c64 *)Bt, (ssd_c64 *)Ct, dt,\n'
+                    '                           B, T, H, N, D, Q, nullptr, y, nullptr, w, ws, nullptr);\n'
+                    '}\n' % (src / "ssd_api.hip"))
+    exe = tmp_path / "tsan_planted"
+    subprocess.run([emu_harness.CLANG, "-x", "c++", "-std=c++17", "-I" + emu_harness.EMU,
+                    "-I" + str(src), "-I" + emu_harness.INCLUDE, "-O1", "-g", "-fsanitize=thread",
+                    str(main), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    out = res.stdout + res.stderr
+    assert "WARNING: ThreadSanitizer: data race" in out, out[-3000:]
+    assert "scan_kernel" in out, out[-3000:]
 
 
 def test_emulated_noalloc_matches_workspace_call(emu):
