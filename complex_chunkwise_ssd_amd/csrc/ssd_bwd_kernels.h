@@ -909,7 +909,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const float dtv = bwd_widen<LAYOUT>(pdt);
             wave_decays<R>(p, c, dtv, Ar, Ai, lr, li, er, ei);
             const double mr = lane_read_d(lr, 15), mi = lane_read_d(li, 15);
-            if (R == 32 && lane < R)
+            if (R == 32 && LAYOUT == kLayoutC64 && lane < R)
                 *(v2f *)&sFac[2 * lane] = lane < 16 ? cexp_f(v2f{(float)(mr - lr), (float)(mi - li)})
                                                     : cexp_f(v2f{(float)(lr - mr), (float)(li - mi)});
             if (lane < R) {
@@ -995,10 +995,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         // pair with itself, which no decay multiplies, must not enter them (it
         // would cancel between two differently rounded sums). The output tiles
         // add the diagonal term back from sVd.
-        // R = 32, two passes of the 512 threads: first the two diagonal 16 x 16
-        // tiles (an exponential of a difference of running sums per pair), then
-        // the tile below them (a product of the two factors in sFac) on waves 0-3
-        // and the zero tile above on waves 4-7. R = 16: one diagonal tile.
+        // R = 32 (complex64 tensors), two passes of the 512 threads: first the two
+        // diagonal 16 x 16 tiles (an exponential of a difference of running sums per
+        // pair), then the tile below them (a product of the two factors in sFac) on
+        // waves 0-3 and the zero tile above on waves 4-7. Otherwise every pair takes
+        // its exponential (the in_proj variants hold more prefetch registers, and the
+        // split pass would push them into spills).
         auto pair = [&](int l, int s, int how) {  // how: 0 exponential, 1 factors, 2 zero
             float mr = 0.f, mi = 0.f, vr = 0.f, vi = 0.f;
             if (how == 1 || (how == 0 && l >= s)) {
@@ -1021,7 +1023,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             sVre[l * RL + s] = vr;
             sVim[l * RL + s] = vi;
         };
-        if constexpr (R == 32) {
+        if constexpr (R == 32 && LAYOUT == kLayoutC64) {
             const int e = tid & 255, hi = tid >> 8;  // hi: waves 4-7
             pair(16 * hi + (e >> 4), 16 * hi + (e & 15), 0);
             if (hi == 0)
