@@ -516,7 +516,7 @@ int ssd_chunk_forward(const ssd_c64 *x, const ssd_c64 *A, const ssd_c64 *B_t, co
     }
     if (!x || !A || !B_t || !C_t || !dt || !y)
         return SSD_ERR_NULL;
-    if (!aligned(B_t, 16) || !aligned(C_t, 16) || !aligned(x, 8) || !aligned(A, 8) ||
+    if (!aligned(B_t, 8) || !aligned(C_t, 8) || !aligned(x, 8) || !aligned(A, 8) ||
         !aligned(dt, 4) || !aligned(y, 4) || (initial_state && !aligned(initial_state, 8)) ||
         (final_state && !aligned(final_state, 8)))
         return SSD_ERR_ALIGN;

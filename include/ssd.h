@@ -120,8 +120,8 @@ size_t ssd_chunk_forward_workspace_bytes(int64_t batch, int64_t T, int64_t H, in
  *                are added up).
  * Constraints: N even (SSD_ERR_ODD_N); N, D, chunk_size <= 256
  * (SSD_ERR_BLOCK_DIMS).
- * Alignment: B_t and C_t 16 bytes; x, A, initial_state, final_state 8 bytes;
- * dt and y 4 bytes.
+ * Alignment: x, A, B_t, C_t, initial_state, final_state 8 bytes (B_t and C_t
+ * rows are read 16 bytes at a time, at any 8-byte alignment); dt and y 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 copies initial_state (or
  * zeros) into final_state.
  */

@@ -299,3 +299,36 @@ def test_state_above_64_initial_state_and_network_batch():
     torch.cuda.synchronize()
     yo, fo = _oracle(inp, initial_state=init.numpy())
     _check(y.cpu().numpy(), yo, fs.cpu().numpy(), fo, "N=128")
+
+
+def _offset_by_one(t):
+    """t's values in a view that starts one complex element (8 bytes) past a
+    16-byte boundary of its allocation."""
+    buf = torch.zeros(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 8
+    return v
+
+
+def test_b_and_c_at_8_byte_alignment():
+    """B_t and C_t need only complex64's own 8-byte alignment: rows read as
+    16-byte words from an address 8 bytes past a 16-byte boundary give the same
+    bits as from an aligned copy, in the scan, the segment fix-up (a few
+    sequences, so they are cut into segments) and every gradient."""
+    inp = ssd_inputs.random_case(2, 150, 2, 64, 64, seed=71)
+    g = inp.to(DEV)
+    Bm, Cm = _offset_by_one(g.B_t), _offset_by_one(g.C_t)
+    ya, fa = ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=64)
+    ym, fm = ssd.chunk_forward(g.x, g.A, Bm, Cm, g.dt, chunk_size=64)
+    gy, gf = ssd_inputs.upstream_grads(2, 150, 2, 64, 64, seed=72, with_final=True)
+    gy, gf = gy.to(DEV), gf.to(DEV)
+    ga = ssd.chunk_backward(g.x, g.A, g.B_t, g.C_t, g.dt, gy, gf, chunk_size=64)
+    gm = ssd.chunk_backward(g.x, g.A, Bm, Cm, g.dt, gy, gf, chunk_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, ym) and torch.equal(fa, fm)
+    for a, m in zip(ga, gm):
+        if a is not None:
+            assert torch.equal(a, m)
+    yo, fo = _oracle(inp)
+    _check(ym.cpu().numpy(), yo, fm.cpu().numpy(), fo, "8-byte aligned B_t, C_t")
