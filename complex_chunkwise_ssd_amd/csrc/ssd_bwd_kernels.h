@@ -306,14 +306,26 @@ SSD_DEVICE v2f cexp_diff(const double *sLam, int l, int s)
 // leaves (adjoint) each chunk before folding the chunk in. The 64 x 64 value
 // lives in MFMA accumulators: wave w holds tiles w and w + 8 of the 4 x 4 grid
 // (rows n, columns d).
+// Four waves per SIMD (two workgroups per CU, one staging while the other runs
+// its MFMAs): at most 128 registers.
 template <int R, bool REV, int LAYOUT>
-SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
+SSD_KERNEL_WAVES(512, 4) void bwd_state_kernel(BwdParams p)
 {
+    // The update's right operand is complex only for the forward state from
+    // complex64 tensors; it then takes three real products per complex one
+    // (Gauss's form, as the scan): with a = f o B and x,
+    //   k1 = (a_re + a_im) x_re,  k2 = a_im (x_re + x_im),  k3 = a_re (x_im - x_re),
+    //   re += k1 - k2,  im += k1 + k3,
+    // k1 summed over the chunk apart from the carried state and added to both at
+    // the end. grad_y and in_proj's x are real: two products.
+    constexpr bool CPLX = !REV && LAYOUT == kLayoutC64;
+    constexpr int XP = CPLX ? R * kStrideA : 1;
     SSD_LDS float sAre[R * kStrideA];
     SSD_LDS float sAim[R * kStrideA];
-    SSD_LDS float sAimN[R * kStrideA];
+    SSD_LDS float sAsum[XP];  // a_re + a_im
     SSD_LDS float sXre[R * kStrideA];
-    SSD_LDS float sXim[R * kStrideA];
+    SSD_LDS float sXn[XP];    // -(x_re + x_im)
+    SSD_LDS float sXd[XP];    // x_im - x_re
     SSD_LDS float sF[2 * R];
     SSD_LDS float sDec[2];
 
@@ -432,13 +444,16 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
                 const v2f a1 = cmul_fixed(v2f{va[j].z, va[j].w}, f);
                 *(v2f *)&sAre[psa(l, c2)] = v2f{a0.x, a1.x};
                 *(v2f *)&sAim[psa(l, c2)] = v2f{a0.y, a1.y};
-                *(v2f *)&sAimN[psa(l, c2)] = v2f{-a0.y, -a1.y};
+                if constexpr (CPLX)
+                    *(v2f *)&sAsum[psa(l, c2)] = v2f{a0.x + a0.y, a1.x + a1.y};
             }
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + 512 * j, l = i >> 6, col = i & 63;
                 sXre[psa(l, col)] = px[j].x;
-                if (!REV)
-                    sXim[psa(l, col)] = px[j].y;
+                if constexpr (CPLX) {
+                    sXn[psa(l, col)] = -(px[j].x + px[j].y);
+                    sXd[psa(l, col)] = px[j].y - px[j].x;
+                }
             }
         }
         for (int j = 0; j < (VEC ? 0 : PER); ++j) {
@@ -453,10 +468,7 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             const v2f a = cmul_fixed(av, *(const v2f *)&sF[2 * l]);
             sAre[psa(l, col)] = a.x;
             sAim[psa(l, col)] = a.y;
-            sAimN[psa(l, col)] = -a.y;
-            sXre[psa(l, col)] = xv.x;
-            if (!REV)
-                sXim[psa(l, col)] = xv.y;
+            sXre[psa(l, col)] = xv.x;  // real (grad_y, or in_proj's x)
         }
         block_sync();
         if (ci + 1 < p.nc)
@@ -472,21 +484,25 @@ SSD_KERNEL(512) void bwd_state_kernel(BwdParams p)
             }
             const int n = nt * 16 + (lane & 15);
             const int d = dtl * 16 + (lane & 15);
+            v4f k1 = {0.f, 0.f, 0.f, 0.f};
             for (int l0 = 0; l0 < R; l0 += 4) {
                 const int l = l0 + (lane >> 4);
                 const float a_re = sAre[psa(l, n)], a_im = sAim[psa(l, n)];
-                if (REV) {
+                if constexpr (CPLX) {
+                    const float a_s = sAsum[psa(l, n)];
+                    const float x_re = sXre[psa(l, d)], x_n = sXn[psa(l, d)], x_d = sXd[psa(l, d)];
+                    k1 = mfma_16x16x4(a_s, x_re, k1);
+                    re = mfma_16x16x4(a_im, x_n, re);
+                    im = mfma_16x16x4(a_re, x_d, im);
+                } else {
                     const float g = sXre[psa(l, d)];
                     re = mfma_16x16x4(a_re, g, re);
                     im = mfma_16x16x4(a_im, g, im);
-                } else {
-                    const float a_imn = sAimN[psa(l, n)];
-                    const float x_re = sXre[psa(l, d)], x_im = sXim[psa(l, d)];
-                    re = mfma_16x16x4(a_re, x_re, re);
-                    re = mfma_16x16x4(a_imn, x_im, re);
-                    im = mfma_16x16x4(a_re, x_im, im);
-                    im = mfma_16x16x4(a_im, x_re, im);
                 }
+            }
+            if constexpr (CPLX) {
+                re += k1;
+                im += k1;
             }
             sre[k] = re;
             sim[k] = im;

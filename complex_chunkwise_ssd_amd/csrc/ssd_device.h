@@ -11,6 +11,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 #define SSD_DEVICE __device__ __forceinline__
 #define SSD_KERNEL(threads) __global__ __launch_bounds__(threads)
+// ... with at least `waves` waves per SIMD (a register budget of 512 / waves)
+#define SSD_KERNEL_WAVES(threads, waves) __global__ __launch_bounds__(threads, waves)
 #define SSD_LDS __shared__ __attribute__((aligned(16)))
 
 // D(16x16) += A(16x4) * B(4x16), fp32, one wave64. Lane L supplies

@@ -69,6 +69,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 #define SSD_DEVICE static inline
 #define SSD_KERNEL(threads)
+#define SSD_KERNEL_WAVES(threads, waves)
 #define SSD_LDS static __attribute__((aligned(16)))
 
 // Base-2 exponential and logarithm (the gfx950 header uses v_exp_f32 / v_log_f32).
