@@ -1081,12 +1081,18 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     return v4f{sMre[l * RL + arow], sMim[l * RL + arow], sGy[l * LD + bcol], 0.f};
                 }, p1r, p1n, p1i);
             } else if (kind == 1) {
-                // conj(gB) = V^T C + e_end (x G^T)
-                mma_steps<kCC>(0, 16, [&](int k) {
-                    const int d = 4 * k + g4;
-                    return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
-                               sGim[bcol * SL + d]};
-                }, p2r, p2n, p2i);
+                // conj(gB) = V^T C + e_end (x G^T); in_proj's x is real
+                if constexpr (LAYOUT == kLayoutC64)
+                    mma_steps<kCC>(0, 16, [&](int k) {
+                        const int d = 4 * k + g4;
+                        return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
+                                   sGim[bcol * SL + d]};
+                    }, p2r, p2n, p2i);
+                else
+                    mma_steps<kRC>(0, 16, [&](int k) {
+                        const int d = 4 * k + g4;
+                        return v4f{sXre[arow * LD + d], 0.f, sGre[bcol * SL + d], sGim[bcol * SL + d]};
+                    }, p2r, p2n, p2i);
                 mma_steps<kCC>(rt * 4, R / 4, [&](int k) {
                     const int l = 4 * k + g4;
                     return v4f{sVre[l * RL + arow], sVim[l * RL + arow], sCre[l * LD + bcol],
