@@ -1061,15 +1061,19 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         //   gC: (O + Off)_l = C_l . ((V B)_l over s < l + e_in (gy H^T)_l)  (q = 0)
         if (has_next)
             fetch(P3{}, next);  // FUSED: grad_final when next starts a sequence, else nothing
-        for (int tile = w; tile < 3 * NT * 4; tile += 8) {
-            const int kind = tile / (NT * 4);
+        // Complex64 tensors: one body per kind (KC a compile-time kind), so each
+        // epilogue carries only its own terms (-2.5 % per call). The in_proj layouts
+        // keep one body for all kinds below: measured, the per-kind form pushes them
+        // into register spills and costs them 10 %.
+        auto c64_tile = [&](auto kc, int tile) {
+            constexpr int kind = decltype(kc)::value;
             const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
             const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
             const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
             const int g4 = lane >> 4;
             v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
             v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
-            if (kind == 0) {
+            if constexpr (kind == 0) {
                 // conj(gx) = M^T gy + e_end (B G)
                 mma_steps<kCC>(0, 16, [&](int k) {
                     const int n = 4 * k + g4;
@@ -1080,19 +1084,13 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     const int l = 4 * k + g4;
                     return v4f{sMre[l * RL + arow], sMim[l * RL + arow], sGy[l * LD + bcol], 0.f};
                 }, p1r, p1n, p1i);
-            } else if (kind == 1) {
-                // conj(gB) = V^T C + e_end (x G^T); in_proj's x is real
-                if constexpr (LAYOUT == kLayoutC64)
-                    mma_steps<kCC>(0, 16, [&](int k) {
-                        const int d = 4 * k + g4;
-                        return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
-                                   sGim[bcol * SL + d]};
-                    }, p2r, p2n, p2i);
-                else
-                    mma_steps<kRC>(0, 16, [&](int k) {
-                        const int d = 4 * k + g4;
-                        return v4f{sXre[arow * LD + d], 0.f, sGre[bcol * SL + d], sGim[bcol * SL + d]};
-                    }, p2r, p2n, p2i);
+            } else if constexpr (kind == 1) {
+                // conj(gB) = V^T C + e_end (x G^T)
+                mma_steps<kCC>(0, 16, [&](int k) {
+                    const int d = 4 * k + g4;
+                    return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
+                               sGim[bcol * SL + d]};
+                }, p2r, p2n, p2i);
                 mma_steps<kCC>(rt * 4, R / 4, [&](int k) {
                     const int l = 4 * k + g4;
                     return v4f{sVre[l * RL + arow], sVim[l * RL + arow], sCre[l * LD + bcol],
@@ -1146,7 +1144,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int width = kind == 0 ? p.D : p.N;
             const int cols = kind == 0 ? cs.dsl : cs.nsl;
             const int gcol = (kind == 0 ? cs.d0 : cs.n0) + col;
-            if constexpr (VEC && !SLICED) {
+            if constexpr (!SLICED) {
                 // straight-line stores: rows past the chunk or T and columns past
                 // the width lie outside the resource and are dropped
                 float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
@@ -1160,7 +1158,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     buf_store2(ro, col < cols ? (uint32_t)row * rowW + 8u * col : kBwdOut,
                                v2f{outr[r], -outi[r]});
                 }
-                continue;
+                return;
             }
             for (int r = 0; r < 4; ++r) {
                 const int row = rt * 16 + 4 * (lane >> 4) + r;
@@ -1177,16 +1175,120 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                         continue;
                     }
                     float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
-                    if constexpr (LAYOUT != kLayoutC64) {  // real x: its gradient is the real part
+                    const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
+                    *(v2f *)&dst[2 * (g * width + gcol)] = v2f{outr[r], -outi[r]};
+                }
+            }
+        };
+        for (int tile = w; tile < 3 * NT * 4; tile += 8) {
+            const int kind = tile / (NT * 4);
+            if constexpr (LAYOUT == kLayoutC64) {
+                if (kind == 0)
+                    c64_tile(std::integral_constant<int, 0>{}, tile);
+                else if (kind == 1)
+                    c64_tile(std::integral_constant<int, 1>{}, tile);
+                else
+                    c64_tile(std::integral_constant<int, 2>{}, tile);
+            } else {
+                const int rt = (tile % (NT * 4)) >> 2, ct = tile & 3;
+                const int arow = rt * 16 + (lane & 15);      // row this lane feeds as A
+                const int bcol = ct * 16 + (lane & 15);      // column this lane feeds as B
+                const int g4 = lane >> 4;
+                v4f p2r = {0.f, 0.f, 0.f, 0.f}, p2n = p2r, p2i = p2r;  // edge term (re+, re-, im)
+                v4f p1r = p2r, p1n = p2r, p1i = p2r;                   // in-chunk term
+                if (kind == 0) {
+                    // conj(gx) = M^T gy + e_end (B G)
+                    mma_steps<kCC>(0, 16, [&](int k) {
+                        const int n = 4 * k + g4;
+                        return v4f{sBre[arow * LD + n], sBim[arow * LD + n], sGre[n * SL + bcol],
+                                   sGim[n * SL + bcol]};
+                    }, p2r, p2n, p2i);
+                    mma_steps<kCR>(rt * 4, R / 4, [&](int k) {
+                        const int l = 4 * k + g4;
+                        return v4f{sMre[l * RL + arow], sMim[l * RL + arow], sGy[l * LD + bcol], 0.f};
+                    }, p1r, p1n, p1i);
+                } else if (kind == 1) {
+                    // conj(gB) = V^T C + e_end (x G^T); x is real
+                    mma_steps<kRC>(0, 16, [&](int k) {
+                        const int d = 4 * k + g4;
+                        return v4f{sXre[arow * LD + d], 0.f, sGre[bcol * SL + d], sGim[bcol * SL + d]};
+                    }, p2r, p2n, p2i);
+                    mma_steps<kCC>(rt * 4, R / 4, [&](int k) {
+                        const int l = 4 * k + g4;
+                        return v4f{sVre[l * RL + arow], sVim[l * RL + arow], sCre[l * LD + bcol],
+                                   sCim[l * LD + bcol]};
+                    }, p1r, p1n, p1i);
+                } else {
+                    // conj(gC) = V B + e_in (gy H^T)
+                    mma_steps<kRC>(0, 16, [&](int k) {
+                        const int d = 4 * k + g4;
+                        return v4f{sGy[arow * LD + d], 0.f, sHre[bcol * SL + d], sHim[bcol * SL + d]};
+                    }, p2r, p2n, p2i);
+                    mma_steps<kCC>(0, rt * 4 + 4, [&](int k) {
+                        const int sx = 4 * k + g4;
+                        return v4f{sVre[arow * RL + sx], sVim[arow * RL + sx], sBre[sx * LD + bcol],
+                                   sBim[sx * LD + bcol]};
+                    }, p1r, p1n, p1i);
+                }
+                const int col = ct * 16 + (lane & 15);
+                const float *fac = kind == 2 ? sEin : sEend;
+                const float *qre = kind == 0 ? sXre : (kind == 1 ? sBre : sCre);
+                const float *qim = kind == 0 ? sXim : (kind == 1 ? sBim : sCim);
+                // the diagonal pair's term of gB (V[s][s] C_s) and gC (V[l][l] B_l)
+                const float *ore = kind == 1 ? sCre : sBre;
+                const float *oim = kind == 1 ? sCim : sBim;
+                v4f outr, outi, dr, di;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rt * 16 + 4 * (lane >> 4) + r;
+                    const v2f f = *(const v2f *)&fac[2 * row];
+                    const v2f e2 = cmul(f, v2f{p2r[r] - p2n[r], p2i[r]});
+                    const v2f e1 = v2f{p1r[r] - p1n[r], p1i[r]};
+                    const v2f vd = kind == 0 ? v2f{0.f, 0.f} : *(const v2f *)&sVd[2 * row];
+                    const v2f e0 = cmul(vd, v2f{ore[row * LD + col], oim[row * LD + col]});
+                    const v2f m = kind == 0 ? e2 : (kind == 1 ? e1 : v2f{e1.x + e2.x, e1.y + e2.y});
+                    outr[r] = (e1.x + e2.x) + e0.x;
+                    outi[r] = (e1.y + e2.y) + e0.y;
+                    const v2f q = v2f{qre[row * LD + col], qim[row * LD + col]};
+                    const v2f d = cmul(q, m);
+                    dr[r] = d.x;
+                    di[r] = d.y;
+                }
+                dr = row_total(dr);
+                di = row_total(di);
+                if ((lane & 15) == 15) {
+                    const int q = 2 - kind;
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = rt * 16 + 4 * (lane >> 4) + r;
+                        sRow[((q * 4 + ct) * R + row) * 2] = dr[r];
+                        sRow[((q * 4 + ct) * R + row) * 2 + 1] = di[r];
+                    }
+                }
+                const int width = kind == 0 ? p.D : p.N;
+                const int cols = kind == 0 ? cs.dsl : cs.nsl;
+                const int gcol = (kind == 0 ? cs.d0 : cs.n0) + col;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = rt * 16 + 4 * (lane >> 4) + r;
+                    const int t = c * p.Q + row;
+                    if (row < p.Q && t < p.T && col < cols) {
+                        if constexpr (SLICED) {
+                            // partial over the other dimension's slices: gx over S, gB and
+                            // gC over T, complex in the (B, T, H, width) layout
+                            const int sl = kind == 0 ? cs.st / p.ndb : cs.st % p.ndb;
+                            float *part = kind == 0 ? p.gx_part : (kind == 1 ? p.gB_part : p.gC_part);
+                            const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
+                            const int64_t e = ((int64_t)sl * p.B * p.T * p.H + g) * width + gcol;
+                            *(v2f *)&part[2 * e] = v2f{outr[r], -outi[r]};
+                            continue;
+                        }
+                        // real x: its gradient is the real part
+                        float *dst = kind == 0 ? p.gx : (kind == 1 ? p.gB : p.gC);
                         const int64_t e = bwd_elem<LAYOUT>(p, b, t, h, width, gcol);
                         bwd_row_store<LAYOUT>(dst, e, outr[r]);
                         if (kind != 0)
                             bwd_row_store<LAYOUT>(dst, e + (int64_t)p.H * p.N, -outi[r]);
-                    } else {
-                        const int64_t g = ((int64_t)b * p.T + t) * p.H + h;
-                        *(v2f *)&dst[2 * (g * width + gcol)] = v2f{outr[r], -outi[r]};
                     }
                 }
+
             }
         }
         block_sync();
