@@ -792,7 +792,8 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
                 constexpr int NH = decltype(nhc)::value;
                 constexpr int NK = (NT + 1 - NH) / 2;  // tiles k = NH, NH + 2, ...
                 constexpr int NX = NLOAD - NBC;         // items left for phase 2
-                constexpr int PER_K = NK > 0 ? (NX + NK - 1) / NK : 0;
+                constexpr int NKD = NK > 0 ? NK : 1;     // (no tiles: PER_K unused)
+                constexpr int PER_K = NK > 0 ? (NX + NKD - 1) / NKD : 0;
                 // M tiles in flight one tile ahead (a split tile: both halves)
                 v4f mre[2], mim[2], mre2, mim2;
                 auto loadm = [&](auto kc, int b) {
