@@ -41,8 +41,10 @@
 extern "C" {
 #endif
 
-/* Opaque stream handle; pass a hipStream_t (or NULL for the null stream). */
-typedef void *ssd_stream_t;
+/* A HIP stream, or NULL for the null stream. The same type as hipStream_t
+ * (a pointer to struct ihipStream_t), declared here so that this header needs
+ * no HIP header. */
+typedef struct ihipStream_t *ssd_stream_t;
 
 /* One complex64 value, laid out as torch.complex64. */
 typedef struct {
