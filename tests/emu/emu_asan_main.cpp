@@ -207,20 +207,25 @@ static int races()
     return fails;
 }
 
-// With the argument "half0" or "half1": every other case (two processes can split the list).
+// With the argument "part=I/N": cases I, I + N, I + 2N, ... of the list (N processes
+// can split it); with no argument, every case.
 int main(int argc, char **argv)
 {
     if (argc > 1 && strcmp(argv[1], "races") == 0)
         return races();
-    const int half = argc > 1 && strcmp(argv[1], "half0") == 0 ? 0
-                     : argc > 1 && strcmp(argv[1], "half1") == 0 ? 1 : -1;
+    int part = 0, parts = 1;
+    if (argc > 1 && (sscanf(argv[1], "part=%d/%d", &part, &parts) != 2 || parts < 1 || part < 0 ||
+                     part >= parts)) {
+        fprintf(stderr, "usage: %s [races | part=I/N]\n", argv[0]);
+        return 2;
+    }
     int fails = 0, k = 0;
-#define run(...) (half < 0 || (k++ & 1) == half ? run(__VA_ARGS__) : 0)
-#define run_bwd(...) (half < 0 || (k++ & 1) == half ? run_bwd(__VA_ARGS__) : 0)
-#define run_proj(...) (half < 0 || (k++ & 1) == half ? run_proj(__VA_ARGS__) : 0)
-#define run_bwd_proj(...) (half < 0 || (k++ & 1) == half ? run_bwd_proj(__VA_ARGS__) : 0)
-#define run_bwd_proj_bf16(...) (half < 0 || (k++ & 1) == half ? run_bwd_proj_bf16(__VA_ARGS__) : 0)
-#define run_mix(...) (half < 0 || (k++ & 1) == half ? run_mix(__VA_ARGS__) : 0)
+#define run(...) (k++ % parts == part ? run(__VA_ARGS__) : 0)
+#define run_bwd(...) (k++ % parts == part ? run_bwd(__VA_ARGS__) : 0)
+#define run_proj(...) (k++ % parts == part ? run_proj(__VA_ARGS__) : 0)
+#define run_bwd_proj(...) (k++ % parts == part ? run_bwd_proj(__VA_ARGS__) : 0)
+#define run_bwd_proj_bf16(...) (k++ % parts == part ? run_bwd_proj_bf16(__VA_ARGS__) : 0)
+#define run_mix(...) (k++ % parts == part ? run_mix(__VA_ARGS__) : 0)
     fails += run(1, 40, 2, 4, 5, 16, true, true);    // padded N, D; partial chunk
     fails += run(1, 70, 1, 64, 64, 64, false, true);  // full tiles, partial last chunk
     fails += run(1, 45, 1, 6, 70, 32, true, true);    // two D slices

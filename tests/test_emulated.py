@@ -4,7 +4,9 @@ layouts, tiling, padding and segment logic without a GPU; the same cases run
 on the GPU in test_gpu_parity.py. An AddressSanitizer build checks every
 global and shared-memory access for bounds."""
 
+import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -101,14 +103,88 @@ def test_emulated_chunk_size_invariance(emu):
         assert np.abs(o - outs[0]).max() <= 1e-4 * (1 + np.abs(outs[0]).max())
 
 
-def test_asan_bounds(tmp_path):
-    exe = emu_harness.build_asan_exe(str(tmp_path))
-    # the case list in two halves, run side by side
-    procs = [subprocess.Popen([exe, half], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
-                              text=True) for half in ("half0", "half1")]
+def _build_planted_tsan(root):
+    """A copy of the kernels without the barrier between phase 2 (each wave leaves
+    its partial y in shared memory) and the y stores (which read the partner
+    wave's part), driven by one small forward call, under ThreadSanitizer."""
+    src = root / "csrc"
+    shutil.copytree(emu_harness.CSRC, src)
+    text = (src / "ssd_kernels.h").read_text()
+    anchor = "        block_sync();\n\n        // ---- store y."
+    assert text.count(anchor) == 1
+    (src / "ssd_kernels.h").write_text(text.replace(anchor, "\n        // ---- store y."))
+    main = root / "tsan_planted.cpp"
+    main.write_text('#include "%s"\n'
+                    'int main() {\n'
+                    '  const int B = 1, T = 40, H = 1, N = 4, D = 6, Q = 16;\n'
+                    '  static float x[B * T * H * D * 2], A[2] = {-0.5f, 1.f}, Bt[B * T * H * N * 2],\n'
+                    '      Ct[B * T * H * N * 2], dt[B * T * H], y[B * T * H * D];\n'
+                    '  for (int i = 0; i < B * T * H * D * 2; ++i) x[i] = 0.01f * (i %% 7);\n'
+                    '  for (int i = 0; i < B * T * H * N * 2; ++i) Bt[i] = Ct[i] = 0.02f * (i %% 5);\n'
+                    '  size_t ws = ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q);\n'
+                    '  void *w = ws ? aligned_alloc(256, ws) : nullptr;\n'
+                    '  return ssd_chunk_forward((ssd_c64 *)x, (ssd_c64 *)A, (ssd_c64 *)Bt, (ssd_c64 *)Ct, dt,\n'
+                    '                           B, T, H, N, D, Q, nullptr, y, nullptr, w, ws, nullptr);\n'
+                    '}\n' % (src / "ssd_api.hip"))
+    exe = root / "tsan_planted"
+    subprocess.run([emu_harness.CLANG, "-x", "c++", "-std=c++17", "-I" + emu_harness.EMU,
+                    "-I" + str(src), "-I" + emu_harness.INCLUDE, "-O1", "-g", "-fsanitize=thread",
+                    str(main), "-o", str(exe)], check=True)
+    return str(exe)
+
+
+def _asan_job(root):
+    exe = emu_harness.build_asan_exe(str(root))
+    # the case list in four parts, run side by side
+    procs = [subprocess.Popen([exe, "part=%d/4" % i], stdout=subprocess.PIPE,
+                              stderr=subprocess.PIPE, text=True) for i in range(4)]
+    results = []
     for p in procs:
-        out, err = p.communicate(timeout=600)
-        assert p.returncode == 0, out + err
+        out, err = p.communicate(timeout=900)
+        results.append((p.returncode, out, err))
+    return results
+
+
+def _tsan_job(root):
+    exe = emu_harness.build_tsan_exe(str(root))
+    res = subprocess.run([exe, "races"], capture_output=True, text=True, timeout=1200)
+    return res.returncode, res.stdout, res.stderr
+
+
+def _planted_job(root):
+    res = subprocess.run([_build_planted_tsan(root)], capture_output=True, text=True, timeout=600)
+    return res.returncode, res.stdout, res.stderr
+
+
+# test -> (job name, job): each job builds a sanitizer executable and runs it
+SANITIZER_JOBS = {
+    "test_asan_bounds": ("asan", _asan_job),
+    "test_tsan_finds_no_unordered_shared_memory_access": ("tsan", _tsan_job),
+    "test_tsan_reports_a_missing_barrier": ("planted", _planted_job),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def sanitizer_run(request, tmp_path_factory):
+    """The sanitizer jobs that this session's tests need, started side by side when
+    the module's first test starts (each build and run is a process of its own,
+    beside the other tests); returns job name -> its result, waiting for that job."""
+    wanted = {SANITIZER_JOBS[i.name] for i in request.session.items if i.name in SANITIZER_JOBS}
+    root = tmp_path_factory.mktemp("sanitizers")
+    pool = ThreadPoolExecutor(max_workers=max(len(wanted), 1))
+    futures = {}
+    for name, job in wanted:
+        (root / name).mkdir()
+        futures[name] = pool.submit(job, root / name)
+    yield lambda name: futures[name].result()
+    pool.shutdown(wait=True)
+
+
+def test_asan_bounds(sanitizer_run):
+    """Every case of the bounds-check driver under AddressSanitizer (host build):
+    every global and shared-memory access of the kernels and the ABI layer."""
+    for rc, out, err in sanitizer_run("asan"):
+        assert rc == 0, out + err
         assert "OK" in out
 
 
@@ -262,7 +338,7 @@ def test_shuffled_order_catches_a_missing_barrier(tmp_path):
         "the shuffled order did not expose the missing barrier"
 
 
-def test_tsan_finds_no_unordered_shared_memory_access(tmp_path):
+def test_tsan_finds_no_unordered_shared_memory_access(sanitizer_run):
     """The kernels under ThreadSanitizer (host build): every GPU thread is a
     sanitizer fiber, ordered only by barriers, its wave's collectives and the
     launches, so any pair of accesses to one word of shared or global memory by
@@ -271,43 +347,17 @@ def test_tsan_finds_no_unordered_shared_memory_access(tmp_path):
     their prefix and fix-up passes, N and D slices, the fused adjoint walk (its
     deferred decay gradients and two-slot per-chunk values), the three-pass
     backward, state blocks, and the mixer's two-stage GEMM."""
-    exe = emu_harness.build_tsan_exe(str(tmp_path))
-    res = subprocess.run([exe, "races"], capture_output=True, text=True, timeout=1200)
-    out = res.stdout + res.stderr
+    rc, stdout, stderr = sanitizer_run("tsan")
+    out = stdout + stderr
     assert "WARNING: ThreadSanitizer" not in out, out[:6000]
-    assert res.returncode == 0 and "OK" in res.stdout, out[-3000:]
+    assert rc == 0 and "OK" in stdout, out[-3000:]
 
 
-def test_tsan_reports_a_missing_barrier(tmp_path):
+def test_tsan_reports_a_missing_barrier(sanitizer_run):
     """The check itself: a copy of the scan kernel without the barrier between
-    phase 2 (each wave leaves its partial y in shared memory) and the y stores
-    (which read the partner wave's part) is reported as a race."""
-    import shutil
-    src = tmp_path / "csrc"
-    shutil.copytree(emu_harness.CSRC, src)
-    text = (src / "ssd_kernels.h").read_text()
-    anchor = "        block_sync();\n\n        // ---- store y."
-    assert text.count(anchor) == 1
-    (src / "ssd_kernels.h").write_text(text.replace(anchor, "\n        // ---- store y."))
-    main = tmp_path / "tsan_planted.cpp"
-    main.write_text('#include "%s"\n'
-                    'int main() {\n'
-                    '  const int B = 1, T = 40, H = 1, N = 4, D = 6, Q = 16;\n'
-                    '  static float x[B * T * H * D * 2], A[2] = {-0.5f, 1.f}, Bt[B * T * H * N * 2],\n'
-                    '      Ct[B * T * H * N * 2], dt[B * T * H], y[B * T * H * D];\n'
-                    '  for (int i = 0; i < B * T * H * D * 2; ++i) x[i] = 0.01f * (i %% 7);\n'
-                    '  for (int i = 0; i < B * T * H * N * 2; ++i) Bt[i] = Ct[i] = 0.02f * (i %% 5);\n'
-                    '  size_t ws = ssd_chunk_forward_workspace_bytes(B, T, H, N, D, Q);\n'
-                    '  void *w = ws ? aligned_alloc(256, ws) : nullptr;\n'
-                    '  return ssd_chunk_forward((ssd_c64 *)x, (ssd_c64 *)A, (ssd_c64 *)Bt, (ssd_c64 *)Ct, dt,\n'
-                    '                           B, T, H, N, D, Q, nullptr, y, nullptr, w, ws, nullptr);\n'
-                    '}\n' % (src / "ssd_api.hip"))
-    exe = tmp_path / "tsan_planted"
-    subprocess.run([emu_harness.CLANG, "-x", "c++", "-std=c++17", "-I" + emu_harness.EMU,
-                    "-I" + str(src), "-I" + emu_harness.INCLUDE, "-O1", "-g", "-fsanitize=thread",
-                    str(main), "-o", str(exe)], check=True)
-    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
-    out = res.stdout + res.stderr
+    phase 2 and the y stores is reported as a race."""
+    rc, stdout, stderr = sanitizer_run("planted")
+    out = stdout + stderr
     assert "WARNING: ThreadSanitizer: data race" in out, out[-3000:]
     assert "scan_kernel" in out, out[-3000:]
 
