@@ -316,13 +316,20 @@ def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
     out = {"workload": "B=%d, T=%d, H=%d, N=D=%d, dt ~ N(%.1f, 1), one input set" % (
         B, T, H, N, w["dt_mean"])}
     th = B * T * H
-    for q in w["chunks"]:
+    for i, q in enumerate(w["chunks"]):
         n = ssd.workspace_bytes(B, T, H, N, D, q)
         wsp = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         call = lambda: ssd.chunk_forward(g.x, g.A, g.B_t, g.C_t, g.dt, chunk_size=q, y=y,
                                          final_state=f, workspace=wsp)
-        for _ in range(3):
+        # untimed calls; before the first chunk size for about a second, so that the
+        # clock has settled also when the sweep runs alone (--sweep-only)
+        t_end = time.time() + (1.0 if i == 0 else 0.0)
+        for k in range(1 << 30):
             call()
+            if k >= 2 and time.time() >= t_end:
+                break
+            if k % 64 == 63:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = []
         for _ in range(reps):

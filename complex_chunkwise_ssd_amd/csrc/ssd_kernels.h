@@ -226,7 +226,10 @@ SSD_KERNEL(kThreads) void scan_kernel(ScanParams p)
     constexpr int LOADS = R * (kNPad / 2) / kThreads;  // 16-byte loads per thread per B or C tile
     static_assert(LOADS >= 1, "tile too small for the thread count");
     constexpr uint32_t kOut = 0x80000000u;   // a byte offset past every buffer
-    constexpr int kScanWave = 0;             // the wave that scans each chunk's log-decay
+    // The wave that scans each chunk's log-decay: below 64 rows (three or one M
+    // tiles, on waves 0-2) wave 3, whose SIMD carries no M tile; with ten tiles every
+    // SIMD carries two and a half, and wave 0 measured fastest.
+    constexpr int kScanWave = NT < 4 ? 3 : 0;
 
     SSD_LDS float sB[R * LDI];                // B[s][n] interleaved (re, im)
     SSD_LDS float sC[R * LDI];                // C[l][n]
