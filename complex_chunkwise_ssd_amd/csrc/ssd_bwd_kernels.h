@@ -1288,7 +1288,6 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                             bwd_row_store<LAYOUT>(dst, e + (int64_t)p.H * p.N, -outi[r]);
                     }
                 }
-
             }
         }
         block_sync();
