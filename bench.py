@@ -375,10 +375,17 @@ def backward_proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, dev, reps=10, dtype
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
     del proj, gy, gf, ws, rows
+    qe = ssd.backward_block_rows(64)
+    fl = B * T * H * ssd.proj_backward_algorithmic_flops_per_token_head(N, D, qe)
+    achieved = fl / (ms * 1e-3) / 1e12
     return {"workload": "network layer backward from %s in_proj rows (B=%d, T=%d, H=%d, "
                         "N=D=%d, chunk 64)" % ("bfloat16" if dtype == torch.bfloat16 else
                                               "float32", B, T, H, N),
-            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3)}
+            "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                         "scope": "whole call at the real-x algorithmic count",
+                         "algorithmic_flops": fl, "evaluated_chunk": qe}}
 
 
 def backward_leg(ssd, torch, g, reps=10, warmup=3):

@@ -447,6 +447,15 @@ def backward_algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
     return 32 * N * D + 16 * N * D / Q + 24 * N * pairs + 8 * D * pairs
 
 
+def proj_backward_algorithmic_flops_per_token_head(N: int, D: int, Q: int) -> float:
+    """As backward_algorithmic_flops_per_token_head with real x (in_proj rows):
+    the chunk states B^T x take 4ND, gy x^T and the real part of M^T gy 2D per
+    pair each, and of the edge terms only Re(B G) (4ND), x G^T (4ND) and gy H^T
+    (4ND) remain."""
+    pairs = (Q + 1) / 2
+    return 20 * N * D + 16 * N * D / Q + 24 * N * pairs + 4 * D * pairs
+
+
 def backward_algorithmic_bytes_per_token_head(N: int, D: int, T: int) -> float:
     """Bytes the gradients must move per (token, head): x, B_t, C_t, dt, grad_y
     in; grad_x, grad_B_t, grad_C_t, grad_dt out; the state gradients amortised."""
