@@ -138,7 +138,7 @@ int launch_backward_r(const ssd::BwdParams &prm, int64_t seqs, hipStream_t strea
     return launch_status();
 }
 
-// The fused adjoint walk (complex64 tensors) needs whole sequences per workgroup:
+// The fused adjoint walk (any input layout) needs whole sequences per workgroup:
 // it is taken when the (virtual) sequences fill the workgroups evenly.
 inline bool backward_fused(int64_t vseqs)
 {
@@ -148,11 +148,9 @@ inline bool backward_fused(int64_t vseqs)
 template <int R, int LAYOUT>
 int launch_backward(const ssd::BwdParams &prm, int64_t seqs, hipStream_t stream)
 {
-    if constexpr (LAYOUT == ssd::kLayoutC64) {
-        if (backward_fused(seqs * prm.ns))
-            return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true, true>(prm, seqs, stream)
-                              : launch_backward_r<R, LAYOUT, false, true>(prm, seqs, stream);
-    }
+    if (backward_fused(seqs * prm.ns))
+        return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true, true>(prm, seqs, stream)
+                          : launch_backward_r<R, LAYOUT, false, true>(prm, seqs, stream);
     return prm.ns > 1 ? launch_backward_r<R, LAYOUT, true, false>(prm, seqs, stream)
                       : launch_backward_r<R, LAYOUT, false, false>(prm, seqs, stream);
 }

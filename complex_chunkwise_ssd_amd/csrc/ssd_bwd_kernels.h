@@ -582,7 +582,7 @@ SSD_DEVICE v4f row_total(v4f v)
 // chunks in a strided loop, loading the next chunk's inputs into registers
 // while the current one is evaluated.
 //
-// FUSED (complex64 tensors, at least as many sequences as workgroups): no
+// FUSED (at least as many sequences as workgroups, any input layout): no
 // stored adjoints. Each workgroup takes whole (virtual) sequences and walks
 // their chunks from the last to the first, keeping the adjoint G in the shared
 // planes: it starts from conj(grad_final), and after a chunk's output tiles the
@@ -633,7 +633,6 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     const int w = wave_id();
     const int64_t total = (int64_t)p.B * p.H * p.ns * p.nc;
     const int64_t nvseq = (int64_t)p.B * p.H * p.ns;
-    static_assert(!FUSED || LAYOUT == kLayoutC64, "the fused adjoint walk reads complex64 tensors");
 
     // The next chunk's inputs are loaded into registers while the current one
     // is evaluated (PER row elements and PS state elements per thread). For
@@ -723,7 +722,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     pgy[j] = vd ? p.gy[row * p.D + ks.d0 + col] : 0.f;
                 }
             }
-        } else {
+        } else if constexpr (!(FUSED && part == 3)) {
             const float *src = (part == 2 ? p.fwd_states : p.adj_states) + k * (int64_t)kStateFloats;
             for (int j = 0; j < PS; ++j) {
                 if constexpr (part == 2)
@@ -805,8 +804,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             const int i = tid + 512 * j, n = i >> 6, d = i & 63;
             sHre[n * SL + d] = ph[j].x;
             sHim[n * SL + d] = ph[j].y;
-            sGre[n * SL + d] = pg[j].x;
-            sGim[n * SL + d] = pg[j].y;
+            if constexpr (!FUSED) {
+                sGre[n * SL + d] = pg[j].x;
+                sGim[n * SL + d] = pg[j].y;
+            }
         }
     };
 

@@ -201,6 +201,7 @@ static int races()
     fails += run_bwd(16, 37, 16, 4, 6, 32, true, true, true);   // the fused adjoint walk
     fails += run_bwd(1, 70, 1, 64, 64, 64, false, true, true);  // three passes, R = 32
     fails += run_bwd(1, 40, 1, 130, 70, 16, true, true, true);  // state blocks, partials summed
+    fails += run_bwd_proj(16, 37, 16, 4, 6, 32, 1);             // the fused walk from in_proj rows
     fails += run_mix(300, 4, 80);   // ragged GEMM tiles, two LDS stages
     fails += run_mix(2100, 2, 4);   // split grad_W and its sum
     printf("%s\n", fails ? "FAIL" : "OK");
@@ -248,6 +249,7 @@ int main(int argc, char **argv)
     fails += run_proj(16, 100, 16, 4, 6, 64, 2); // 256 sequences, two chunks per workgroup
     fails += run_bwd_proj(1, 40, 2, 4, 6, 16, 1);   // gradient rows with a spare float
     fails += run_bwd_proj(1, 70, 1, 64, 64, 64, 0); // full tiles
+    fails += run_bwd_proj(16, 37, 16, 4, 6, 32, 1); // 256 sequences: the fused adjoint walk
     fails += run_bwd_proj_bf16(1, 40, 2, 4, 6, 16, 1);  // bfloat16 rows, odd row length
     fails += run_mix(5, 16, 64);    // F = 1024: four column tiles, vector loads
     fails += run_mix(3, 7, 10);     // F = 70: scalar loads, ragged tiles

@@ -474,7 +474,8 @@ def test_emulated_proj_bf16_matches_oracle(emu, case):
 
 
 @pytest.mark.parametrize("case", [(2, 16, 2, 4, 4, 4, 0), (1, 97, 2, 8, 6, 32, 6),
-                                  (2, 50, 2, 6, 10, 16, 4), (1, 40, 2, 130, 70, 16, 2)])
+                                  (2, 50, 2, 6, 10, 16, 4), (1, 40, 2, 130, 70, 16, 2),
+                                  (16, 37, 16, 4, 6, 32, 1)])  # 256 sequences: the fused walk
 def test_emulated_backward_proj_matches_oracle(emu, case):
     """Gradient rows of the in_proj layout: every block against the oracle's
     gradients of the complex inputs the rows stand for; floats past the blocks
