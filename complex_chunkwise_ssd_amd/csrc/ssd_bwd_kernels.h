@@ -528,8 +528,9 @@ SSD_KERNEL_WAVES(512, 4) void bwd_state_kernel(BwdParams p)
 
 // Kinds of one MFMA step over a 4-wide K block: complex x complex (four MFMAs:
 // rp += ar br, rn += ai bi, im += ar bi + ai br), real x complex (rp += a br,
-// im += a bi) and complex x real (rp += ar b, im += ai b).
-enum { kCC = 0, kRC = 1, kCR = 2 };
+// im += a bi), complex x real (rp += ar b, im += ai b) and real x real, or the
+// real part alone of complex x real (rp += ar b).
+enum { kCC = 0, kRC = 1, kCR = 2, kRR = 3 };
 
 // Steps k0 .. k1-1 of a tile product. ld(k) returns this lane's operands of
 // step k as {ar, ai, br, bi}; the next step's operands are read from LDS before
@@ -553,9 +554,11 @@ SSD_DEVICE void mma_steps(int k0, int k1, Ld ld, v4f &rp, v4f &rn, v4f &im)
         } else if (KIND == kRC) {
             rp = mfma_16x16x4(cur.x, cur.z, rp);
             im = mfma_16x16x4(cur.x, cur.w, im);
-        } else {
+        } else if (KIND == kCR) {
             rp = mfma_16x16x4(cur.x, cur.z, rp);
             im = mfma_16x16x4(cur.y, cur.z, im);
+        } else {
+            rp = mfma_16x16x4(cur.x, cur.z, rp);
         }
         sched_fence();
         cur = nxt;
@@ -959,10 +962,16 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     return v4f{sCre[lrow * LD + kk], sCim[lrow * LD + kk], sBre[scol * LD + kk],
                                sBim[scol * LD + kk]};
                 }, rp, rn, im);
-            } else {
+            } else if constexpr (LAYOUT == kLayoutC64) {
                 mma_steps<kRC>(0, 16, [&](int k) {
                     const int kk = 4 * k + g4;
                     return v4f{sGy[lrow * LD + kk], 0.f, sXre[scol * LD + kk], sXim[scol * LD + kk]};
+                }, rp, rn, im);
+            } else {
+                // in_proj's x is real: gy x^T is real
+                mma_steps<kRR>(0, 16, [&](int k) {
+                    const int kk = 4 * k + g4;
+                    return v4f{sGy[lrow * LD + kk], 0.f, sXre[scol * LD + kk], 0.f};
                 }, rp, rn, im);
             }
             float *dre = gram ? sMre : sVre;
@@ -1204,9 +1213,11 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                         return v4f{sBre[arow * LD + n], sBim[arow * LD + n], sGre[n * SL + bcol],
                                    sGim[n * SL + bcol]};
                     }, p2r, p2n, p2i);
-                    mma_steps<kCR>(rt * 4, R / 4, [&](int k) {
+                    // x is real: grad x is the real part, and this term enters neither
+                    // the imaginary part nor the row dot product
+                    mma_steps<kRR>(rt * 4, R / 4, [&](int k) {
                         const int l = 4 * k + g4;
-                        return v4f{sMre[l * RL + arow], sMim[l * RL + arow], sGy[l * LD + bcol], 0.f};
+                        return v4f{sMre[l * RL + arow], 0.f, sGy[l * LD + bcol], 0.f};
                     }, p1r, p1n, p1i);
                 } else if (kind == 1) {
                     // conj(gB) = V^T C + e_end (x G^T); x is real
