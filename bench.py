@@ -342,10 +342,12 @@ def sweep_leg(ssd, torch, ssd_inputs, dev, reps=10):
         ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
         qe = ssd.block_rows(q)
         fe = th * ssd.algorithmic_flops_per_token_head(N, D, qe)
+        by = th * ssd.algorithmic_bytes_per_token_head(N, D, T)
         out["chunk_%d" % q] = {
             "median_ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "token_heads_per_s": th / (ms * 1e-3), "evaluated_block_rows": qe,
-            "roofline_frac_mfma": fe / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+            "roofline_frac_mfma": fe / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+            "achieved_hbm_GBs_algorithmic": by / (ms * 1e-3) / 1e9}
         del wsp
     del g, y, f
     return out
@@ -617,9 +619,11 @@ def main():
             ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
             th = w["batch"] * w["T"] * w["H"]
             fl = th * ssd.algorithmic_flops_per_token_head(w["N"], w["D"], q)
+            by = th * ssd.algorithmic_bytes_per_token_head(w["N"], w["D"], w["T"])
             extra[name] = {"median_ms": ms, "tokens_per_s": w["batch"] * w["T"] / (ms * 1e-3),
                            "token_heads_per_s": th / (ms * 1e-3),
-                           "roofline_frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+                           "roofline_frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+                           "achieved_hbm_GBs_algorithmic": by / (ms * 1e-3) / 1e9}
             del g, y, f, wsp
         out["single_layer"] = extra
         out["proj_layer"] = proj_leg(ssd, torch, ssd_inputs, B, T, H, N, D, Q, dev)
