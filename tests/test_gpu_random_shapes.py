@@ -9,7 +9,9 @@ which then belongs among the fixed cases.
 
 Bars, elementwise: |y - Re y_oracle| <= 1e-4 + 1e-4 |Re y_oracle| (final state per
 complex component likewise); every gradient the same per component, grad A with
-1e-6 per token summed added to its absolute term.
+1e-6 per token summed added to its absolute term. The head mixer's random shapes
+(tokens, H, D) keep its own bars: 1e-4 + 1e-4 |ref| + 1e-5 sqrt(sum of squared
+products) (tests/tolerances.py).
 """
 
 import numpy as np
@@ -19,6 +21,7 @@ import torch
 import complex_chunkwise_ssd_amd as ssd
 import oracle
 import ssd_inputs
+import tolerances
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +157,33 @@ def test_random_shape_backward_from_proj_rows(case):
     assert (r[..., W:] == 0).all(), "%s: spare floats written" % (case,)
     _close("%s proj grad A" % (case,), gA.cpu().numpy(), ref.A, atol=ATOL + 1e-6 * B * T)
     _close("%s proj grad initial state" % (case,), gi.cpu().numpy(), ref.initial_state)
+
+
+def _mix_draw(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(rng.integers(1, 17))
+        D = int(rng.integers(1, 129))
+        M = int(rng.integers(0, 3001))
+        out.append((M, H, D))
+    return out
+
+
+@pytest.mark.parametrize("case", _mix_draw(16, 79))
+def test_random_shape_head_mix(case):
+    M, H, D = case
+    y, W, gz = ssd_inputs.mix_case((M, H, D), seed=M + 7 * H + 13 * D)
+    z = ssd.head_mix(y.to(DEV), W.to(DEV))
+    gy, gW = ssd.head_mix_backward(y.to(DEV), W.to(DEV), gz.to(DEV))
+    torch.cuda.synchronize()
+    yn, Wn, gzn = y.numpy(), W.numpy(), gz.numpy()
+    zo = oracle.head_mix(y, W)
+    ry, rW = oracle.head_mix_backward(y, W, gz)
+    for name, got, ref, extra in (("z", z, zo, tolerances.mix_forward_extra(yn, Wn)),
+                                  ("grad_y", gy, ry, tolerances.mix_grad_y_extra(gzn, Wn)),
+                                  ("grad_W", gW, rW, tolerances.mix_grad_w_extra(gzn, yn))):
+        g = got.cpu().numpy()
+        assert np.isfinite(g).all(), (case, name)
+        e = np.abs(g - ref)
+        assert (e <= 1e-4 + 1e-4 * np.abs(ref) + extra).all(), "%s %s max %.3e" % (case, name, e.max())
