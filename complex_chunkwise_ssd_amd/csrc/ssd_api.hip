@@ -178,7 +178,15 @@ void set_backward_workspace(ssd::BwdParams &prm, const ssd::BwdPlan &plan, void 
 
 int check_backward_sizes(int64_t batch, int64_t T, int64_t H, int64_t N, int64_t D, int64_t chunk)
 {
-    return check_sizes(batch, T, H, N, D, chunk);
+    if (int st = check_sizes(batch, T, H, N, D, chunk))
+        return st;
+    // the chunk pass indexes (virtual sequence, chunk) pairs with 32-bit integers
+    if (batch > 0 && H > 0 && T > 0) {
+        const ssd::BwdPlan plan = ssd::make_bwd_plan(batch, T, H, N, D, chunk);
+        if (batch * H * plan.ns * plan.nc >= (1LL << 31))
+            return SSD_ERR_UNSUPPORTED;
+    }
+    return SSD_OK;
 }
 
 template <int LAYOUT, class E>

@@ -134,8 +134,9 @@ struct BwdSlice {
 SSD_DEVICE BwdSlice bwd_slice(const BwdParams &p, int64_t vs)
 {
     BwdSlice r;
-    r.seq = vs / p.ns;
-    r.st = (int)(vs % p.ns);
+    const uint32_t v = (uint32_t)vs, ns = (uint32_t)p.ns;  // vs < 2^31 (host check)
+    r.seq = v / ns;
+    r.st = (int)(v - (uint32_t)r.seq * ns);
     r.n0 = 64 * (r.st / p.ndb);
     r.d0 = 64 * (r.st % p.ndb);
     r.nsl = p.N - r.n0 < 64 ? p.N - r.n0 : 64;
@@ -661,16 +662,37 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     // 2 = the entering state; 3 = the leaving adjoint. The parts of the next
     // chunk are issued at different points of the current one, so that no
     // wave stalls behind a long burst of loads.
-    // fetch<part>(k): part 0 = dt, B_t and C_t rows; 1 = x and grad_y rows;
+    // Where chunk k lies: its index in the sequence, the (virtual) sequence's
+    // state block, batch row and head, from 32-bit divisions (the host keeps the
+    // (virtual sequence, chunk) count below 2^31), worked out once per chunk.
+    struct Pos {
+        int64_t k, vs;  // chunk, virtual sequence
+        int c, b, h;
+        BwdSlice ks;
+    };
+    auto pos_of = [&](int64_t k) {
+        Pos r;
+        r.k = k;
+        const uint32_t ku = (uint32_t)k, nc = (uint32_t)p.nc;
+        const uint32_t vs = ku / nc;
+        r.vs = vs;
+        r.c = (int)(ku - vs * nc);
+        r.ks = SLICED ? bwd_slice(p, vs) : BwdSlice{(int64_t)vs, 0, 0, 0, p.N, p.D};
+        const uint32_t sq = (uint32_t)r.ks.seq, nh = (uint32_t)p.H;
+        r.b = (int)(sq / nh);
+        r.h = (int)(sq - (uint32_t)r.b * nh);
+        return r;
+    };
+    // fetch(part, pos): part 0 = dt, B_t and C_t rows; 1 = x and grad_y rows;
     // 2 = the entering state; 3 = the leaving adjoint. The parts of the next
     // chunk are issued at different points of the current one, so that no
     // wave stalls behind a long burst of loads.
-    auto fetch = [&](auto part_c, int64_t k) {
+    auto fetch = [&](auto part_c, const Pos &pos) {
         constexpr int part = decltype(part_c)::value;
-        const int cc = (int)(k % p.nc);
-        const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc)
-                                   : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
-        const int bb = (int)(ks.seq / p.H), hh = (int)(ks.seq % p.H);
+        const int64_t k = pos.k;
+        const int cc = pos.c;
+        const BwdSlice ks = pos.ks;
+        const int bb = pos.b, hh = pos.h;
         if constexpr (part == 0)
             pdt = bwd_load_dt<R, LAYOUT>(p, bb, hh, cc);
         if constexpr (VEC) {
@@ -742,11 +764,10 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     // new_seq (FUSED): the staged chunk k is its sequence's last, so G starts from
     // conj(grad_final) (read here, once per sequence); otherwise the G planes
     // already hold the walked adjoint.
-    auto stage = [&](bool new_seq, int64_t k) {
+    auto stage = [&](bool new_seq, const Pos &pos) {
         if constexpr (FUSED) {
             if (new_seq) {
-                const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc)
-                                           : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
+                const BwdSlice ks = pos.ks;
                 const buf_t rf = make_buf(
                     p.gfinal ? p.gfinal + ((ks.seq * p.N + ks.n0) * p.D + ks.d0) * 2 : nullptr,
                     p.gfinal ? (uint32_t)((ks.nsl - 1) * p.D + ks.dsl) * 8u : 0u);
@@ -815,24 +836,25 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     };
 
     // The chunk after chunk k in this workgroup's order, or -1.
-    auto next_of = [&](int64_t k) -> int64_t {
+    auto next_of = [&](const Pos &pos) -> int64_t {
         if constexpr (FUSED) {
-            if (k % p.nc > 0)
-                return k - 1;
-            const int64_t vs = k / p.nc + grid_blocks();
+            if (pos.c > 0)
+                return pos.k - 1;
+            const int64_t vs = pos.vs + grid_blocks();
             return vs < nvseq ? vs * p.nc + p.nc - 1 : -1;
         } else {
-            const int64_t n = k + grid_blocks();
+            const int64_t n = pos.k + grid_blocks();
             return n < total ? n : -1;
         }
     };
     // Decay gradients of chunk k (one wave): its row sums sEv, sEe (kept until the
     // next chunk's output tiles), and its running sums, dt and <H, G> partial sums
     // in slot q.
-    auto decay_grads = [&](int64_t k, int q) {
-        const BwdSlice ks = SLICED ? bwd_slice(p, k / p.nc) : BwdSlice{k / p.nc, 0, 0, 0, p.N, p.D};
-        const int kc = (int)(k % p.nc);
-        const int kb = (int)(ks.seq / p.H), kh = (int)(ks.seq % p.H);
+    auto decay_grads = [&](const Pos &pos, int q) {
+        const int64_t k = pos.k;
+        const BwdSlice ks = pos.ks;
+        const int kc = pos.c;
+        const int kb = pos.b, kh = pos.h;
         const float kAr = p.A[2 * kh], kAi = p.A[2 * kh + 1];
             // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>: the
             // suffix and prefix sums over the chunk rows as lane scans (fixed trees)
@@ -907,21 +929,21 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
     };
     if (block_id() >= (FUSED ? nvseq : total))
         return;
-    int64_t blk = FUSED ? block_id() * p.nc + p.nc - 1 : block_id();
-    fetch(P0{}, blk);
-    fetch(P1{}, blk);
-    fetch(P2{}, blk);
-    fetch(P3{}, blk);
-    stage(true, blk);
+    Pos cur = pos_of(FUSED ? block_id() * p.nc + p.nc - 1 : block_id());
+    fetch(P0{}, cur);
+    fetch(P1{}, cur);
+    fetch(P2{}, cur);
+    fetch(P3{}, cur);
+    stage(true, cur);
     block_sync();
     int par = 0;         // slot of this chunk's running sums, dt and <H, G> sums
-    int64_t prev = -1;   // the chunk whose decay gradients are still to be taken
+    Pos prev;            // the chunk whose decay gradients are still to be taken
+    bool has_prev = false;
     for (;;) {
-        const BwdSlice cs = SLICED ? bwd_slice(p, blk / p.nc)
-                                   : BwdSlice{blk / p.nc, 0, 0, 0, p.N, p.D};
+        const BwdSlice cs = cur.ks;
         const int64_t seq = cs.seq;
-        const int c = (int)(blk % p.nc);
-        const int b = (int)(seq / p.H), h = (int)(seq % p.H);
+        const int c = cur.c;
+        const int b = cur.b, h = cur.h;
         const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
         if (w == kDecayWave) {
             // running sums and row factors of this chunk; read after the next barrier
@@ -941,12 +963,13 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                 *(v2f *)&sEend[2 * lane] = cexp_f(v2f{(float)(er - lr), (float)(ei - li)});
             }
         }
-        if (w == kGradWave && prev >= 0)
+        if (w == kGradWave && has_prev)
             decay_grads(prev, par ^ 1);
-        const int64_t next = next_of(blk);
+        const int64_t next = next_of(cur);
         const bool has_next = next >= 0;
+        const Pos npos = pos_of(has_next ? next : cur.k);
         if (has_next)
-            fetch(P0{}, next);
+            fetch(P0{}, npos);
 
         // Raw Gram (C B^T) tiles on waves 0.., raw gy x^T tiles on waves 4..
         if (w < NPAIR || (w >= 4 && w < 4 + NPAIR)) {
@@ -1012,8 +1035,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         block_sync();
 
         if (has_next) {
-            fetch(P1{}, next);
-            fetch(P2{}, next);
+            fetch(P1{}, npos);
+            fetch(P2{}, npos);
         }
         // M = Gram o L and V = (gy x^T) o L, zero above the diagonal. V's
         // diagonal goes to sVd and the V tiles hold only the pairs l > s: the
@@ -1070,7 +1093,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         //   gB: I_s  = B_s . (V^T C)_s  over l > s                    (q = 1)
         //   gC: (O + Off)_l = C_l . ((V B)_l over s < l + e_in (gy H^T)_l)  (q = 0)
         if (has_next)
-            fetch(P3{}, next);  // FUSED: grad_final when next starts a sequence, else nothing
+            fetch(P3{}, npos);  // FUSED: grad_final when next starts a sequence, else nothing
         // Complex64 tensors: one body per kind (KC a compile-time kind), so each
         // epilogue carries only its own terms (-2.5 % per call). The in_proj layouts
         // keep one body for all kinds below: measured, the per-kind form pushes them
@@ -1374,13 +1397,14 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         block_sync();
         // the planes are free once the output tiles and the G update are done
         if (has_next)
-            stage(next % p.nc == p.nc - 1, next);
+            stage(npos.c == p.nc - 1, npos);
         block_sync();
-        prev = blk;
+        prev = cur;
+        has_prev = true;
         par ^= 1;
         if (!has_next)
             break;
-        blk = next;
+        cur = npos;
     }
     if (w == kGradWave)
         decay_grads(prev, par ^ 1);
