@@ -235,15 +235,25 @@ SSD_DEVICE v2f bwd_load_x(const BwdParams &p, int b, int t, int h, int col)
 }
 
 // dt of chunk row tid (tid < R), or 0 past the chunk or past T (as loaded:
-// bwd_widen gives the value).
+// bwd_widen gives the value). Every lane loads, through a buffer resource that
+// ends after the chunk's last row, so lanes past it read zero and no branch
+// makes the wave wait on the load.
 template <int R, int LAYOUT>
 SSD_DEVICE float bwd_load_dt(const BwdParams &p, int b, int h, int c)
 {
     const int lane = thread_id() & 63;  // every wave holds the chunk's dt in lanes < R
-    const int t = c * p.Q + lane;
-    return (lane < R && lane < p.Q && t < p.T)
-               ? bwd_row_load<LAYOUT>(p.dt, bwd_elem<LAYOUT>(p, b, t, h, 1, 0))
-               : 0.f;
+    const int t0 = c * p.Q;
+    int rows = p.T - t0 < p.Q ? p.T - t0 : p.Q;
+    rows = rows < R ? rows : R;
+    constexpr uint32_t es = LAYOUT == kLayoutProjBf16 ? 2u : 4u;  // bytes per element
+    const uint32_t step = (uint32_t)(LAYOUT != kLayoutC64 ? p.tok_stride : p.H) * es;
+    const buf_t r = make_buf((const char *)p.dt + bwd_elem<LAYOUT>(p, b, t0, h, 1, 0) * es,
+                             (uint32_t)(rows - 1) * step + es);
+    const uint32_t off = lane < rows ? (uint32_t)lane * step : kBwdOut;
+    if constexpr (LAYOUT == kLayoutProjBf16)
+        return __builtin_bit_cast(float, buf_load_u16(r, off));
+    else
+        return buf_load1(r, off);
 }
 
 // Double-precision lane moves (two 32-bit DPP / readlane moves).
@@ -674,12 +684,12 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         Pos r;
         r.k = k;
         const uint32_t ku = (uint32_t)k, nc = (uint32_t)p.nc;
-        const uint32_t vs = ku / nc;
+        const uint32_t vs = (uint32_t)uniform_i((int)(ku / nc));
         r.vs = vs;
         r.c = (int)(ku - vs * nc);
         r.ks = SLICED ? bwd_slice(p, vs) : BwdSlice{(int64_t)vs, 0, 0, 0, p.N, p.D};
         const uint32_t sq = (uint32_t)r.ks.seq, nh = (uint32_t)p.H;
-        r.b = (int)(sq / nh);
+        r.b = uniform_i((int)(sq / nh));
         r.h = (int)(sq - (uint32_t)r.b * nh);
         return r;
     };
@@ -855,7 +865,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         const BwdSlice ks = pos.ks;
         const int kc = pos.c;
         const int kb = pos.b, kh = pos.h;
-        const float kAr = p.A[2 * kh], kAi = p.A[2 * kh + 1];
+        const v2f kA = ld_c_uniform(p.A, kh);
+        const float kAr = kA.x, kAi = kA.y;
             // dF/da_t = sum_{j>=t} v_j + sum_{j<t} In_j + exp(Lam[R-1]) <H, G>: the
             // suffix and prefix sums over the chunk rows as lane scans (fixed trees)
             const int t0 = lane;
@@ -944,7 +955,8 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
         const int64_t seq = cs.seq;
         const int c = cur.c;
         const int b = cur.b, h = cur.h;
-        const float Ar = p.A[2 * h], Ai = p.A[2 * h + 1];
+        const v2f Ah = ld_c_uniform(p.A, h);
+        const float Ar = Ah.x, Ai = Ah.y;
         if (w == kDecayWave) {
             // running sums and row factors of this chunk; read after the next barrier
             double lr, li, er, ei;

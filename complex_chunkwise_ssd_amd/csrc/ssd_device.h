@@ -121,13 +121,23 @@ SSD_DEVICE float lane_read(float v, int src)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
 }
-// A wave-uniform value kept in scalar registers.
 // v from lane src (any lane of the wave, chosen per lane).
 SSD_DEVICE float lane_fetch(float v, int src)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
+// A wave-uniform value kept in scalar registers.
 SSD_DEVICE float uniform(float v)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+SSD_DEVICE int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Complex element i (interleaved float pairs) of an array that no kernel writes,
+// at a wave-uniform index: read through the constant address space, a scalar
+// load, so no vector-memory wait counter covers it.
+SSD_DEVICE v2f ld_c_uniform(const float *p, int i)
+{
+    using cv2f = __attribute__((address_space(4))) const v2f;
+    return ((cv2f *)p)[i];
 }
