@@ -136,7 +136,7 @@ SSD_DEVICE int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // Complex element i (interleaved float pairs) of an array that no kernel writes,
 // at a wave-uniform index: read through the constant address space, a scalar
 // load, so no vector-memory wait counter covers it.
-SSD_DEVICE v2f ld_c_uniform(const float *p, int i)
+SSD_DEVICE v2f ld_c_uniform(const float *p, int64_t i)
 {
     using cv2f = __attribute__((address_space(4))) const v2f;
     return ((cv2f *)p)[i];

@@ -219,7 +219,9 @@ SSD_KERNEL(kFixThreads) void segment_fixup_kernel(ScanParams p)
             lam += v2f{row_shr<2>(lam.x), row_shr<2>(lam.y)};
             lam += v2f{row_shr<4>(lam.x), row_shr<4>(lam.y)};
             lam += v2f{row_shr<8>(lam.x), row_shr<8>(lam.y)};
-            v2f base = *(const v2f *)&p.chunk_log[(bh * p.nc + c) * 2];
+            // a scalar load: a vector load here would make the wave wait for its
+            // last chunk's y stores as well (one wait counter covers both)
+            v2f base = ld_c_uniform(p.chunk_log, bh * p.nc + c);
             for (int t = 0; t < NR - 1; ++t) {
                 const v2f tt = v2f{lane_read(lam.x, 16 * t + 15), lane_read(lam.y, 16 * t + 15)};
                 if ((lane >> 4) > t)

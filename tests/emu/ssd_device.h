@@ -439,7 +439,7 @@ SSD_DEVICE int lane_read_i(int v, int src)
 SSD_DEVICE float lane_fetch(float v, int src) { return emu_shfl(v, emu::SH_IDX, src); }
 SSD_DEVICE float uniform(float v) { return v; }
 SSD_DEVICE int uniform_i(int v) { return v; }
-SSD_DEVICE v2f ld_c_uniform(const float *p, int i) { return v2f{p[2 * i], p[2 * i + 1]}; }
+SSD_DEVICE v2f ld_c_uniform(const float *p, int64_t i) { return v2f{p[2 * i], p[2 * i + 1]}; }
 // A wave-level meeting point: every lane of the wave arrives before any goes on.
 SSD_DEVICE void wave_lds_sync() { (void)emu_shfl(0.f, emu::SH_READ, 0); }
 
