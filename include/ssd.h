@@ -241,7 +241,10 @@ size_t ssd_chunk_backward_workspace_bytes(int64_t batch, int64_t T, int64_t H, i
  * not depend on chunk_size beyond rounding. With N or D above 64 the state is
  * evaluated in 64 x 64 blocks whose partial gradients are added in a fixed
  * order (deterministic).
- * Constraints: as ssd_chunk_forward (N even; N, D, chunk_size <= 256).
+ * Constraints: as ssd_chunk_forward (N even; N, D, chunk_size <= 256), and
+ * batch * H * ceil(N/64) * ceil(D/64) * ceil(T / min(chunk_size, 32)) below 2^31
+ * (the chunks are indexed with 32-bit integers; SSD_ERR_UNSUPPORTED otherwise, and
+ * the workspace size is then 0).
  * Alignment: complex arrays 8 bytes; dt, grad_y, grad_dt 4 bytes.
  * batch or H equal to 0 is a no-op; T equal to 0 writes grad_final_state (or
  * zeros) to grad_initial_state and zeros to grad_A.

@@ -193,6 +193,15 @@ def test_backward_workspace_sizes(lib):
     parts = 8 * 16 * 2 * (3 * 70 + 2 * 2 * 130) + 4 * 16 * 2 * 6
     assert f(1, 16, 2, 130, 70, 4) >= blocks + parts
     assert ssd.backward_workspace_bytes(1, 100, 2, 4, 4, 8) == f(1, 100, 2, 4, 4, 8)
+    # the chunk pass indexes (virtual sequence, chunk) pairs in 32 bits: 2^20 sequences of
+    # 2^11 32-token chunks are 2^31 pairs, one too many
+    assert f(1 << 20, 1 << 16, 1, 2, 2, 32) == 0
+    assert f(1 << 20, (1 << 16) - 32, 1, 2, 2, 32) > 0
+
+
+def test_backward_chunk_count_limit(lib):
+    args = dict(B=1 << 20, T=1 << 16, H=1, N=2, D=2, Q=32)
+    assert _bwd(lib, **args) == ssd.SSD_ERR_UNSUPPORTED
 
 
 def test_python_backward_rejects_bad_tensors():
