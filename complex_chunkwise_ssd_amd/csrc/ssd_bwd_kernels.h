@@ -540,8 +540,10 @@ SSD_KERNEL_WAVES(512, 4) void bwd_state_kernel(BwdParams p)
 // Kinds of one MFMA step over a 4-wide K block: complex x complex (four MFMAs:
 // rp += ar br, rn += ai bi, im += ar bi + ai br), real x complex (rp += a br,
 // im += a bi), complex x real (rp += ar b, im += ai b) and real x real, or the
-// real part alone of complex x real (rp += ar b).
-enum { kCC = 0, kRC = 1, kCR = 2, kRR = 3 };
+// real part alone of complex x real (rp += ar b). kCC3: complex x complex in three
+// MFMAs, rp += ar br, rn += ai bi, im += (ar + ai)(br + bi), the product's imaginary
+// part then being im - rp - rn.
+enum { kCC = 0, kRC = 1, kCR = 2, kRR = 3, kCC3 = 4 };
 
 // Steps k0 .. k1-1 of a tile product. ld(k) returns this lane's operands of
 // step k as {ar, ai, br, bi}; the next step's operands are read from LDS before
@@ -562,6 +564,10 @@ SSD_DEVICE void mma_steps(int k0, int k1, Ld ld, v4f &rp, v4f &rn, v4f &im)
             rn = mfma_16x16x4(cur.y, cur.w, rn);
             im = mfma_16x16x4(cur.x, cur.w, im);
             im = mfma_16x16x4(cur.y, cur.z, im);
+        } else if (KIND == kCC3) {
+            rp = mfma_16x16x4(cur.x, cur.z, rp);
+            rn = mfma_16x16x4(cur.y, cur.w, rn);
+            im = mfma_16x16x4(cur.x + cur.y, cur.z + cur.w, im);
         } else if (KIND == kRC) {
             rp = mfma_16x16x4(cur.x, cur.z, rp);
             im = mfma_16x16x4(cur.x, cur.w, im);
@@ -992,7 +998,9 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             v4f rp = {0.f, 0.f, 0.f, 0.f}, rn = rp, im = rp;
             const int g4 = lane >> 4;
             if (gram) {
-                mma_steps<kCC>(0, 16, [&](int k) {
+                // three MFMAs per step (Gauss's form): the Gram waves' SIMDs carry the
+                // section's MFMAs, and this section holds few registers
+                mma_steps<kCC3>(0, 16, [&](int k) {
                     const int kk = 4 * k + g4;
                     return v4f{sCre[lrow * LD + kk], sCim[lrow * LD + kk], sBre[scol * LD + kk],
                                sBim[scol * LD + kk]};
@@ -1014,7 +1022,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
             for (int r = 0; r < 4; ++r) {
                 const int l = lt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
                 dre[l * RL + s] = rp[r] - rn[r];
-                dim[l * RL + s] = im[r];
+                dim[l * RL + s] = gram ? im[r] - rp[r] - rn[r] : im[r];
             }
         }
         // <H, G> partial sums
