@@ -1144,7 +1144,7 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     return v4f{sXre[arow * LD + d], sXim[arow * LD + d], sGre[bcol * SL + d],
                                sGim[bcol * SL + d]};
                 }, p2r, p2n, p2i);
-                mma_steps<kCC>(rt * 4, R / 4, [&](int k) {
+                mma_steps<kCC3>(rt * 4, R / 4, [&](int k) {
                     const int l = 4 * k + g4;
                     return v4f{sVre[l * RL + arow], sVim[l * RL + arow], sCre[l * LD + bcol],
                                sCim[l * LD + bcol]};
@@ -1155,11 +1155,15 @@ SSD_KERNEL(512) void bwd_chunk_kernel(BwdParams p)
                     const int d = 4 * k + g4;
                     return v4f{sGy[arow * LD + d], 0.f, sHre[bcol * SL + d], sHim[bcol * SL + d]};
                 }, p2r, p2n, p2i);
-                mma_steps<kCC>(0, rt * 4 + 4, [&](int k) {
+                mma_steps<kCC3>(0, rt * 4 + 4, [&](int k) {
                     const int sx = 4 * k + g4;
                     return v4f{sVre[arow * RL + sx], sVim[arow * RL + sx], sBre[sx * LD + bcol],
                                sBim[sx * LD + bcol]};
                 }, p1r, p1n, p1i);
+            }
+            if constexpr (kind != 0) {  // the in-chunk products' imaginary parts (kCC3)
+                for (int r = 0; r < 4; ++r)
+                    p1i[r] = p1i[r] - p1r[r] - p1n[r];
             }
             const int col = ct * 16 + (lane & 15);
             const float *fac = kind == 2 ? sEin : sEend;
